@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""GroupNorm forward+backward throughput on one MI355X.
+
+A step is one forward (statistics + normalize/affine) and one backward
+(per-slice reductions, dx, dgamma/dbeta) over every shape of the workload,
+on synthetic seeded inputs already resident in HBM.  The default workload is
+the LayerNorm-shaped GroupNorm (G = 1, one spatial position) at 4096 x 1024
+and 8192 x 768, float16 activations, float32 affine parameters.
+
+Prints ONE JSON line on stdout.  ``value`` is the step's algorithmic bytes
+(read x, write y, gamma/beta, mean/rstd; read dy, x, gamma, mean/rstd, write
+dx, dgamma/dbeta) divided by the measured step time, in GB/s.  The
+``roofline`` object covers the kernel that takes most of the step, timed with
+HIP events that the library records on the call's stream around that kernel.
+``cpu_baseline`` times the fp64 oracle on the host cores over a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "GroupNorm fwd+bwd achieved HBM GB/s (% of MI355X peak) and µs/call"
+HBM_PEAK_GBS = 8000.0
+
+# (name, workload names)
+WORKLOADS = {
+    "rows_f16_4096x1024+8192x768": ("rows_f16_4096x1024", "rows_f16_8192x768"),
+    "tiny_nchw_f32_2x32x16x16_g8": ("tiny_nchw_f32_2x32x16x16_g8",),
+    "rows_f16_4096x1024": ("rows_f16_4096x1024",),
+    "rows_f16_8192x768": ("rows_f16_8192x768",),
+    "nhwc_f16_1x128x1024x2048_g16": ("nhwc_f16_1x128x1024x2048_g16",),
+    "nchw_f32_112x64x512x512_g8": ("nchw_f32_112x64x512x512_g8",),
+    "rows_bf16_131072x4096": ("rows_bf16_131072x4096",),
+}
+DEFAULT = "rows_f16_4096x1024+8192x768"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target duration of the oracle CPU-baseline sample (0 disables it)")
+    ap.add_argument("--force-path", default=None, choices=[None, "generic", "rows", "slab"])
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the GroupNorm path here runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import normalization_gn_stats_amd as gn
+    from normalization_gn_stats_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    mask = gn.GN_GRAD_DX | gn.GN_GRAD_DGAMMA | gn.GN_GRAD_DBETA
+
+    # ---- inputs resident in HBM, outputs and workspaces preallocated ----------
+    shapes = []
+    for name in WORKLOADS[args.workload]:
+        wl = inputs.WORKLOADS[name]
+        log(f"generating {wl.name}")
+        d = inputs.make_inputs(wl, seed=0, device="cuda")
+        x, dy, gamma, beta = d["x"], d["dy"], d["gamma"], d["beta"]
+        code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
+        lay = gn.layout_of(x)
+        fws = gn.forward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, args.force_path)
+        bws = gn.backward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, mask, args.force_path)
+        sh = dict(wl=wl, x=x, dy=dy, gamma=gamma, beta=beta, y=torch.empty_like(x), dx=torch.empty_like(x),
+                  mean=torch.empty(wl.N * wl.G, device=dev), rstd=torch.empty(wl.N * wl.G, device=dev),
+                  dgamma=torch.empty(wl.C, device=dev), dbeta=torch.empty(wl.C, device=dev),
+                  fws=torch.empty(max(fws, 1), dtype=torch.uint8, device=dev),
+                  bws=torch.empty(max(bws, 1), dtype=torch.uint8, device=dev),
+                  fplan=gn.PlanInfo(), bplan=gn.PlanInfo())
+        shapes.append(sh)
+
+    def step(events=None, i=0):
+        for k, sh in enumerate(shapes):
+            wl = sh["wl"]
+            fe = be = None
+            if events is not None:
+                fe = (events[i][k][0][0].cuda_event, events[i][k][0][1].cuda_event)
+                be = (events[i][k][1][0].cuda_event, events[i][k][1][1].cuda_event)
+            gn.forward_into(sh["x"], sh["gamma"], sh["beta"], wl.G, wl.eps, sh["y"], sh["mean"], sh["rstd"],
+                            sh["fws"], force_path=args.force_path, info=sh["fplan"], events=fe, stream=sp)
+            gn.backward_into(sh["dy"], sh["x"], sh["mean"], sh["rstd"], sh["gamma"], wl.G, mask, sh["dx"],
+                             sh["dgamma"], sh["dbeta"], sh["bws"], force_path=args.force_path,
+                             info=sh["bplan"], events=be, stream=sp)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-step, per-shape, per-call (begin, end) events around each main kernel
+    K = args.steps
+    events = [[[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(2)]
+               for _ in shapes] for _ in range(K)]
+    for row in events:             # torch creates HIP events lazily at their first record
+        for per_shape in row:
+            for pair in per_shape:
+                for ev in pair:
+                    ev.record(stream)
+    torch.cuda.synchronize()
+
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events, i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    bytes_per_step = sum(sh["wl"].fwd_min_bytes() + sh["wl"].bwd_min_bytes() for sh in shapes)
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+
+    # ---- per-call kernel durations from the library-recorded events ----------
+    calls = []
+    for k, sh in enumerate(shapes):
+        wl = sh["wl"]
+        for c, (kind, nbytes, plan) in enumerate((
+                ("fwd", wl.fwd_min_bytes(), sh["fplan"]),
+                # the main backward kernel writes dx; dgamma/dbeta (2*C*4 bytes) are
+                # written by the small column-sum kernel when one follows
+                ("bwd", wl.bwd_min_bytes() - (2 * wl.C * 4 if sh["bplan"].kernels > 1 else 0), sh["bplan"]))):
+            durs = [events[i][k][c][0].elapsed_time(events[i][k][c][1]) for i in range(K)]
+            avg_ms = sum(durs) / len(durs)
+            calls.append(dict(shape=wl.name, call=kind, path=gn.PATH_NAMES[plan.path], kernels=plan.kernels,
+                              main_kernel_us=avg_ms * 1e3, main_kernel_bytes=nbytes,
+                              main_kernel_gbs=nbytes / (avg_ms * 1e-3) / 1e9))
+    dom = max(calls, key=lambda c: c["main_kernel_us"])
+    roofline = {"bound": "hbm", "achieved": round(dom["main_kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dom["main_kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": f"{dom['call']} {dom['path']} main kernel on {dom['shape']}",
+                "avg_us": round(dom["main_kernel_us"], 3), "algorithmic_bytes": dom["main_kernel_bytes"]}
+
+    # ---- oracle CPU baseline on a bounded sample -------------------------------
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(shapes, args.cpu_seconds, bytes_per_step)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shapes[0]["wl"].dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload,
+                   "shapes": [dict(N=s["wl"].N, C=s["wl"].C, H=s["wl"].H, W=s["wl"].W, G=s["wl"].G,
+                                   dtype=s["wl"].dtype, layout=s["wl"].layout) for s in shapes],
+                   "mask": "dx|dgamma|dbeta", "bytes_per_step": bytes_per_step,
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "us_per_call": {f"{c['call']}:{c['shape']}": round(c["main_kernel_us"], 3) for c in calls},
+        "calls": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in c.items()} for c in calls],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(shapes, seconds, bytes_per_step):
+    """The fp64 oracle (as it stands) on the same workload, repeated until about
+    `seconds` of CPU time; reported in the metric's unit (algorithmic GB/s)."""
+    import numpy as np
+
+    import oracle
+    from normalization_gn_stats_amd import inputs
+
+    log("cpu baseline: oracle on the host cores")
+    prepared = []
+    for sh in shapes:
+        wl = sh["wl"]
+        x = inputs.memory_image(sh["x"], wl.layout).to("cpu", dtype=__import__("torch").float64).numpy()
+        dy = inputs.memory_image(sh["dy"], wl.layout).to("cpu", dtype=__import__("torch").float64).numpy()
+        g = sh["gamma"].double().cpu().numpy()
+        b = sh["beta"].double().cpu().numpy()
+        prepared.append((wl, x, dy, g, b, float(np.float32(wl.eps))))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for wl, x, dy, g, b, eps in prepared:
+            oracle.forward(x, g, b, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
+            oracle.backward(dy, x, g, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 10000:
+            break
+    return {"value": round(bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full steps of the workload (fwd+bwd of every shape) in {el:.1f} s, fp64 C oracle, "
+                      f"OpenMP threads={oracle.num_threads()}, host cpus={os.cpu_count()}"}
+
+
+if __name__ == "__main__":
+    main()

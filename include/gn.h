@@ -1,0 +1,156 @@
+/*
+ * gn.h -- C ABI of the GroupNorm forward/backward library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Operation (POPCORNBENCH GroupNorm trace; baracuda-kernels GroupNorm backward
+ * plan; apex PR #2018).  A dense activation tensor has N samples, C channels
+ * and HW spatial positions (all spatial dimensions flattened).  The C channels
+ * form G groups of D = C/G consecutive channels; a slice (n, g) holds the
+ * M = D*HW elements of sample n in group g.
+ *
+ *   forward:  mean = average of the slice, var = biased variance (denominator
+ *             M), rstd = 1/sqrt(var + eps), xhat = (x - mean)*rstd,
+ *             y = gamma_c*xhat + beta_c.  mean and rstd are saved per slice.
+ *   backward: with the saved mean/rstd, per slice A = sum gamma_c*dy and
+ *             B = sum gamma_c*dy*xhat;  dx = rstd*(gamma_c*dy - A/M - xhat*B/M);
+ *             dgamma_c = sum over n, p of dy*xhat;  dbeta_c = sum over n, p of dy.
+ *
+ * Memory layout of x, y, dy, dx (dense, element (n, c, p)):
+ *   GN_NCHW: offset (n*C + c)*HW + p
+ *   GN_NHWC: offset (n*HW + p)*C + c          (PyTorch channels_last)
+ * Activations are float32, float16 or bfloat16 (IEEE binary16 / bfloat16
+ * bit patterns); y and dx take x's dtype, rounded to nearest even.  gamma,
+ * beta, dgamma, dbeta, mean and rstd are float32.  mean/rstd have N*G entries,
+ * slice (n, g) at index n*G + g.  All arithmetic inside is float32.
+ *
+ * Ownership: every pointer argument except `opts` is a DEVICE pointer owned by
+ * the caller; the library allocates and frees nothing.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL is the null stream) and the calls return
+ * before it completes.  The workspace is borrowed until that work ends.
+ *
+ * Determinism: every reduction runs in a fixed order and no float atomics are
+ * used, so repeated calls with the same inputs and options give bitwise equal
+ * results on the same device (baracuda-kernels GroupNorm backward plan,
+ * precision guarantee: fp32 math and accumulators, deterministic).
+ *
+ * Errors are detected on the host, before anything is enqueued, and reported
+ * by the return value; nothing is written to any output then.  A zero extent
+ * (N, C or HW equal to 0) is a successful no-op (baracuda-kernels plan: run
+ * returns early on a zero extent).
+ */
+#ifndef GN_MI355X_H
+#define GN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gn_status {
+    GN_OK = 0,
+    GN_ERR_INVALID = 1,      /* bad sizes, G not dividing C, NULL where required,
+                                affine pointers not all-or-none, bad mask */
+    GN_ERR_UNSUPPORTED = 2,  /* dtype or layout outside the enums, or a forced
+                                path that cannot serve these arguments */
+    GN_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the size query returned */
+    GN_ERR_HIP = 4           /* the HIP runtime refused a launch */
+} gn_status;
+
+typedef enum gn_dtype { GN_F32 = 0, GN_F16 = 1, GN_BF16 = 2 } gn_dtype;
+
+typedef enum gn_layout { GN_NCHW = 0, GN_NHWC = 1 } gn_layout;
+
+/* Output mask of gn_backward (ROCm/pytorch PR #3564 tests: output_mask
+ * selecting dgamma and dbeta, dbeta only, dgamma only). */
+enum { GN_GRAD_DX = 1, GN_GRAD_DGAMMA = 2, GN_GRAD_DBETA = 4 };
+
+/* Kernel families; GN_PATH_AUTO lets the planner choose. */
+typedef enum gn_path {
+    GN_PATH_AUTO = 0,
+    GN_PATH_GENERIC = 1,  /* any shape/alignment: partial sums, finalize, elementwise */
+    GN_PATH_ROWS = 2,     /* HW == 1: one wavefront per slice, slice kept in registers */
+    GN_PATH_SLAB = 3      /* cooperative capped grid over contiguous slabs with
+                             grid-stride overflow tiles (one-pass backward) */
+} gn_path;
+
+/* What a call ran (filled when gn_options.info is not NULL). */
+typedef struct gn_plan_info {
+    int32_t path;            /* gn_path actually used */
+    int32_t kernels;         /* kernel launches enqueued by the call */
+    int64_t grid;            /* workgroups of the main kernel */
+    int64_t tiles;           /* work tiles of the main kernel (slab path) */
+    int64_t resident_cap;    /* co-resident workgroup limit used for the cap */
+    int64_t team;            /* workgroups cooperating on one slab (slab path) */
+} gn_plan_info;
+
+/* Optional knobs (pass NULL for defaults). */
+typedef struct gn_options {
+    int32_t force_path;             /* gn_path; GN_PATH_AUTO = planner's choice */
+    int32_t max_resident_override;  /* > 0: cap the cooperative grid at this many
+                                       workgroups (forces overflow tiles) */
+    gn_plan_info* info;             /* host pointer, may be NULL */
+    void* event_begin;              /* hipEvent_t recorded on `stream` right before
+                                       the call's main kernel, or NULL */
+    void* event_end;                /* hipEvent_t recorded right after it, or NULL */
+} gn_options;
+
+/* Workspace bytes gn_forward needs for these arguments (0 is possible).
+ * Returns 0 as well for arguments gn_forward would reject. */
+size_t gn_forward_workspace_size(int64_t N, int64_t C, int64_t HW, int64_t G,
+                                 gn_dtype dtype, gn_layout layout,
+                                 const gn_options* opts);
+
+/*
+ * Forward.  x: input; gamma, beta: [C] float32, both NULL (no affine: gamma 1,
+ * beta 0) or both set; y: output (may be NULL to compute only the statistics);
+ * mean, rstd: [N*G] float32 outputs (required).  eps >= 0.
+ * workspace: 16-byte aligned device buffer of at least gn_forward_workspace_size() bytes
+ * (may be NULL when that size is 0); its content on entry is irrelevant.
+ */
+gn_status gn_forward(const void* x, const float* gamma, const float* beta,
+                     void* y, float* mean, float* rstd,
+                     int64_t N, int64_t C, int64_t HW, int64_t G, float eps,
+                     gn_dtype dtype, gn_layout layout,
+                     void* workspace, size_t ws_bytes, void* stream,
+                     const gn_options* opts);
+
+/* Workspace bytes gn_backward needs for these arguments and mask. */
+size_t gn_backward_workspace_size(int64_t N, int64_t C, int64_t HW, int64_t G,
+                                  gn_dtype dtype, gn_layout layout, int32_t mask,
+                                  const gn_options* opts);
+
+/*
+ * Backward.  dy, x: inputs in the same dtype/layout; mean, rstd: [N*G] saved
+ * statistics of the forward; gamma: [C] or NULL (gamma = 1).
+ * mask: OR of GN_GRAD_DX / GN_GRAD_DGAMMA / GN_GRAD_DBETA (non-zero); each
+ * selected output must be non-NULL: dx (x's shape and dtype), dgamma [C],
+ * dbeta [C] (float32).  dgamma/dbeta require gamma (affine all-or-none, as in
+ * the baracuda-kernels plan's argument check).
+ */
+gn_status gn_backward(const void* dy, const void* x,
+                      const float* mean, const float* rstd, const float* gamma,
+                      void* dx, float* dgamma, float* dbeta, int32_t mask,
+                      int64_t N, int64_t C, int64_t HW, int64_t G,
+                      gn_dtype dtype, gn_layout layout,
+                      void* workspace, size_t ws_bytes, void* stream,
+                      const gn_options* opts);
+
+/* The path gn_forward (backward = 0) or gn_backward (backward = 1) would take
+ * for these arguments, without enqueuing anything.  Returns a gn_path, or -1
+ * for arguments the call would reject. */
+int32_t gn_select_path(int32_t backward, int64_t N, int64_t C, int64_t HW, int64_t G,
+                       gn_dtype dtype, gn_layout layout, const gn_options* opts);
+
+/* Static description of a status code (never NULL). */
+const char* gn_status_string(gn_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t gn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GN_MI355X_H */

@@ -1,0 +1,178 @@
+"""GroupNorm forward/backward on AMD Instinct MI355X (gfx950).
+
+Thin binding over the C ABI of ``include/gn.h``: it checks and marshals
+arguments, allocates outputs and workspace with torch, and passes torch's
+current HIP stream.  Every step of the computation runs in the library's HIP
+kernels; there is no CPU or PyTorch fallback -- if the library is missing or
+refuses a call, these functions raise.
+
+Tensors: x, dy are (N, C, *spatial) and dense, either contiguous (NCHW) or
+channels_last (NHWC); float32, float16 or bfloat16.  gamma/beta are float32
+(C,).  mean/rstd come back as float32 (N, G).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from . import _lib
+from ._lib import (GN_BF16, GN_F16, GN_F32, GN_GRAD_DBETA, GN_GRAD_DGAMMA, GN_GRAD_DX, GN_NCHW, GN_NHWC,
+                   GN_PATH_AUTO, GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB, PATH_NAMES, GNError, PlanInfo)
+
+__all__ = ["forward", "backward", "forward_into", "backward_into", "forward_workspace_size",
+           "backward_workspace_size", "select_path", "layout_of", "GNError", "PlanInfo",
+           "GN_GRAD_DX", "GN_GRAD_DGAMMA", "GN_GRAD_DBETA", "GN_PATH_AUTO", "GN_PATH_GENERIC",
+           "GN_PATH_ROWS", "GN_PATH_SLAB", "PATH_NAMES"]
+
+_PATHS = {None: GN_PATH_AUTO, "auto": GN_PATH_AUTO, "generic": GN_PATH_GENERIC, "rows": GN_PATH_ROWS,
+          "slab": GN_PATH_SLAB}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: GN_F32, torch.float16: GN_F16, torch.bfloat16: GN_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+    return m[t.dtype]
+
+
+def layout_of(t) -> int:
+    """GN_NCHW if t is contiguous, GN_NHWC if it is dense channels_last."""
+    torch = _torch()
+    if t.dim() < 2:
+        raise ValueError("expected a tensor of shape (N, C, *spatial)")
+    if t.is_contiguous():
+        return GN_NCHW
+    if t.dim() == 4 and t.is_contiguous(memory_format=torch.channels_last):
+        return GN_NHWC
+    if t.dim() == 5 and t.is_contiguous(memory_format=torch.channels_last_3d):
+        return GN_NHWC
+    raise ValueError("tensor must be dense: contiguous (NCHW) or channels_last (NHWC)")
+
+
+def _dims(t):
+    N, C = t.shape[0], t.shape[1]
+    HW = math.prod(t.shape[2:]) if t.dim() > 2 else 1
+    return int(N), int(C), int(HW)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _opts(force_path, max_resident, info, events):
+    o = _lib.Options()
+    o.force_path = _PATHS[force_path] if not isinstance(force_path, int) else force_path
+    o.max_resident_override = int(max_resident or 0)
+    o.info = ctypes.pointer(info) if info is not None else None
+    if events is not None:
+        o.event_begin = ctypes.c_void_p(events[0])
+        o.event_end = ctypes.c_void_p(events[1])
+    return o
+
+
+def _check_f32_vec(t, C, name):
+    torch = _torch()
+    if t is None:
+        return
+    if t.dtype != torch.float32 or t.numel() != C or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {C} elements")
+
+
+def forward_workspace_size(N, C, HW, G, dtype_code, layout, force_path=None) -> int:
+    o = _opts(force_path, 0, None, None)
+    return int(_lib.lib().gn_forward_workspace_size(N, C, HW, G, dtype_code, layout, ctypes.byref(o)))
+
+
+def backward_workspace_size(N, C, HW, G, dtype_code, layout, mask, force_path=None) -> int:
+    o = _opts(force_path, 0, None, None)
+    return int(_lib.lib().gn_backward_workspace_size(N, C, HW, G, dtype_code, layout, mask, ctypes.byref(o)))
+
+
+def select_path(backward: bool, N, C, HW, G, dtype_code, layout, force_path=None) -> int:
+    o = _opts(force_path, 0, None, None)
+    return int(_lib.lib().gn_select_path(1 if backward else 0, N, C, HW, G, dtype_code, layout, ctypes.byref(o)))
+
+
+def forward_into(x, gamma, beta, num_groups, eps, y, mean, rstd, workspace, *, force_path=None,
+                 max_resident=0, info=None, events=None, stream=None):
+    """gn_forward on preallocated outputs; returns nothing, raises GNError."""
+    torch = _torch()
+    N, C, HW = _dims(x)
+    layout = layout_of(x)
+    _check_f32_vec(gamma, C, "gamma")
+    _check_f32_vec(beta, C, "beta")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    o = _opts(force_path, max_resident, info, events)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.lib().gn_forward(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), N, C, HW,
+                               int(num_groups), float(eps), _dtype_code(x), layout, _ptr(workspace), ws_bytes,
+                               ctypes.c_void_p(stream), ctypes.byref(o))
+    if st != 0:
+        raise GNError(st, "gn_forward")
+
+
+def forward(x, gamma, beta, num_groups: int, eps: float = 1e-5, *, compute_y: bool = True, force_path=None,
+            max_resident: int = 0, info: PlanInfo | None = None):
+    """Returns (y, mean, rstd); y is None when compute_y is False."""
+    torch = _torch()
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device")
+    N, C, HW = _dims(x)
+    layout = layout_of(x)
+    G = int(num_groups)
+    with torch.cuda.device(x.device):
+        y = torch.empty_like(x) if compute_y else None
+        mean = torch.empty(N * G, device=x.device, dtype=torch.float32)
+        rstd = torch.empty(N * G, device=x.device, dtype=torch.float32)
+        wsb = forward_workspace_size(N, C, HW, G, _dtype_code(x), layout, force_path)
+        ws = torch.empty(max(wsb, 1), device=x.device, dtype=torch.uint8)
+        forward_into(x, gamma, beta, G, eps, y, mean, rstd, ws, force_path=force_path,
+                     max_resident=max_resident, info=info)
+    return y, mean.view(N, G), rstd.view(N, G)
+
+
+def backward_into(dy, x, mean, rstd, gamma, num_groups, mask, dx, dgamma, dbeta, workspace, *,
+                  force_path=None, max_resident=0, info=None, events=None, stream=None):
+    """gn_backward on preallocated outputs; returns nothing, raises GNError."""
+    torch = _torch()
+    N, C, HW = _dims(x)
+    layout = layout_of(x)
+    if tuple(dy.shape) != tuple(x.shape) or dy.dtype != x.dtype or layout_of(dy) != layout:
+        raise ValueError("dy must match x in shape, dtype and layout")
+    _check_f32_vec(gamma, C, "gamma")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    o = _opts(force_path, max_resident, info, events)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.lib().gn_backward(_ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd), _ptr(gamma), _ptr(dx), _ptr(dgamma),
+                                _ptr(dbeta), int(mask), N, C, HW, int(num_groups), _dtype_code(x), layout,
+                                _ptr(workspace), ws_bytes, ctypes.c_void_p(stream), ctypes.byref(o))
+    if st != 0:
+        raise GNError(st, "gn_backward")
+
+
+def backward(dy, x, mean, rstd, gamma, num_groups: int, mask: int = GN_GRAD_DX | GN_GRAD_DGAMMA | GN_GRAD_DBETA,
+             *, force_path=None, max_resident: int = 0, info: PlanInfo | None = None):
+    """Returns (dx, dgamma, dbeta), each None when not selected by mask."""
+    torch = _torch()
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device")
+    N, C, HW = _dims(x)
+    layout = layout_of(x)
+    G = int(num_groups)
+    with torch.cuda.device(x.device):
+        dx = torch.empty_like(x) if mask & GN_GRAD_DX else None
+        dgamma = torch.empty(C, device=x.device, dtype=torch.float32) if mask & GN_GRAD_DGAMMA else None
+        dbeta = torch.empty(C, device=x.device, dtype=torch.float32) if mask & GN_GRAD_DBETA else None
+        wsb = backward_workspace_size(N, C, HW, G, _dtype_code(x), layout, mask, force_path)
+        ws = torch.empty(max(wsb, 1), device=x.device, dtype=torch.uint8)
+        backward_into(dy, x, mean.reshape(-1), rstd.reshape(-1), gamma, G, mask, dx, dgamma, dbeta, ws,
+                      force_path=force_path, max_resident=max_resident, info=info)
+    return dx, dgamma, dbeta

@@ -1,0 +1,237 @@
+// gn_api.cpp -- the C ABI declared in include/gn.h: argument validation (the
+// checks of the baracuda-kernels GroupNorm backward plan: non-negative sizes,
+// G > 0 dividing C, supported dtype, affine all-or-none, workspace at least
+// the queried size, zero extent is a successful no-op), path selection and
+// dispatch to the kernel launchers.
+#include <math.h>
+#include <mutex>
+
+#include "gn_internal.hpp"
+
+namespace gn {
+
+namespace {
+DeviceInfo g_dev[64];
+bool g_dev_ok[64];
+std::mutex g_dev_mu;
+}  // namespace
+
+const DeviceInfo& device_info() {
+    static DeviceInfo fallback{-1, 256, 0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return fallback;
+    }
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (!g_dev_ok[dev]) {
+        DeviceInfo d{dev, 256, 0};
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            d.cu_count = v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess)
+            d.coop_supported = v;
+        (void)hipGetLastError();
+        g_dev[dev] = d;
+        g_dev_ok[dev] = true;
+    }
+    return g_dev[dev];
+}
+
+hipError_t record(hipEvent_t ev, hipStream_t s) {
+    if (!ev) return hipSuccess;
+    return hipEventRecord(ev, s);
+}
+
+}  // namespace gn
+
+using gn::Problem;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape/dtype/layout checks shared by every entry point.
+gn_status make_problem(int64_t N, int64_t C, int64_t HW, int64_t G, gn_dtype dtype, gn_layout layout,
+                       Problem* p) {
+    if (dtype != GN_F32 && dtype != GN_F16 && dtype != GN_BF16) return GN_ERR_UNSUPPORTED;
+    if (layout != GN_NCHW && layout != GN_NHWC) return GN_ERR_UNSUPPORTED;
+    if (N < 0 || C < 0 || HW < 0 || G <= 0) return GN_ERR_INVALID;
+    if (C > 0 && C % G != 0) return GN_ERR_INVALID;
+    if (C == 0 && G > 0) { /* zero extent: G is irrelevant */ }
+    // 64-bit element count must not overflow
+    if (N > 0 && C > 0 && HW > 0) {
+        const double e = (double)N * (double)C * (double)HW;
+        if (e > 9.0e18) return GN_ERR_INVALID;
+    }
+    p->N = N; p->C = C; p->HW = HW; p->G = G;
+    p->D = G > 0 ? C / G : 0;
+    p->M = p->D * HW;
+    p->S = N * G;
+    p->E = N * C * HW;
+    p->dtype = dtype;
+    p->layout = layout;
+    p->elem_bytes = dtype == GN_F32 ? 4 : 2;
+    return GN_OK;
+}
+
+bool zero_extent(const Problem& p) { return p.N == 0 || p.C == 0 || p.HW == 0; }
+
+int32_t forced(const gn_options* o) { return o ? o->force_path : GN_PATH_AUTO; }
+
+// Path for these shapes assuming 16-byte aligned pointers; -1 if the forced
+// path cannot serve them.
+int32_t plan(const Problem& p, bool backward, const gn_options* opts) {
+    (void)backward;
+    const int32_t f = forced(opts);
+    if (f == GN_PATH_GENERIC) return GN_PATH_GENERIC;
+    if (f == GN_PATH_ROWS) return gn::rows_ok(p) ? GN_PATH_ROWS : -1;
+    if (f == GN_PATH_SLAB) return -1;   // not built in this library version
+    if (f != GN_PATH_AUTO) return -1;
+    if (gn::rows_ok(p)) return GN_PATH_ROWS;
+    return GN_PATH_GENERIC;
+}
+
+size_t fwd_ws(const Problem& p, int32_t path) {
+    switch (path) {
+        case GN_PATH_ROWS: return gn::rows_fwd_ws(p);
+        default: return gn::generic_fwd_ws(p);
+    }
+}
+
+size_t bwd_ws(const Problem& p, int32_t mask, int32_t path) {
+    switch (path) {
+        case GN_PATH_ROWS: return gn::rows_bwd_ws(p, mask);
+        default: return gn::generic_bwd_ws(p, mask);
+    }
+}
+
+gn::Launch make_launch(void* ws, size_t ws_bytes, void* stream, const gn_options* opts) {
+    gn::Launch l;
+    l.stream = (hipStream_t)stream;
+    l.ws = ws;
+    l.ws_bytes = ws_bytes;
+    l.ev_begin = opts ? (hipEvent_t)opts->event_begin : nullptr;
+    l.ev_end = opts ? (hipEvent_t)opts->event_end : nullptr;
+    l.max_resident_override = opts ? opts->max_resident_override : 0;
+    l.info = opts ? opts->info : nullptr;
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gn_forward_workspace_size(int64_t N, int64_t C, int64_t HW, int64_t G, gn_dtype dtype,
+                                 gn_layout layout, const gn_options* opts) {
+    Problem p;
+    if (make_problem(N, C, HW, G, dtype, layout, &p) != GN_OK || zero_extent(p)) return 0;
+    const int32_t path = plan(p, false, opts);
+    if (path < 0) return 0;
+    // the generic path is the fallback for unaligned pointers: cover it too
+    size_t a = fwd_ws(p, path), b = gn::generic_fwd_ws(p);
+    return a > b ? a : b;
+}
+
+size_t gn_backward_workspace_size(int64_t N, int64_t C, int64_t HW, int64_t G, gn_dtype dtype,
+                                  gn_layout layout, int32_t mask, const gn_options* opts) {
+    Problem p;
+    if (make_problem(N, C, HW, G, dtype, layout, &p) != GN_OK || zero_extent(p)) return 0;
+    if (mask <= 0 || mask > 7) return 0;
+    const int32_t path = plan(p, true, opts);
+    if (path < 0) return 0;
+    size_t a = bwd_ws(p, mask, path), b = gn::generic_bwd_ws(p, mask);
+    return a > b ? a : b;
+}
+
+int32_t gn_select_path(int32_t backward, int64_t N, int64_t C, int64_t HW, int64_t G, gn_dtype dtype,
+                       gn_layout layout, const gn_options* opts) {
+    Problem p;
+    if (make_problem(N, C, HW, G, dtype, layout, &p) != GN_OK) return -1;
+    return plan(p, backward != 0, opts);
+}
+
+gn_status gn_forward(const void* x, const float* gamma, const float* beta, void* y, float* mean, float* rstd,
+                     int64_t N, int64_t C, int64_t HW, int64_t G, float eps, gn_dtype dtype, gn_layout layout,
+                     void* workspace, size_t ws_bytes, void* stream, const gn_options* opts) {
+    Problem p;
+    gn_status st = make_problem(N, C, HW, G, dtype, layout, &p);
+    if (st != GN_OK) return st;
+    if (!(eps >= 0.f) || isinf(eps)) return GN_ERR_INVALID;
+    if ((gamma == nullptr) != (beta == nullptr)) return GN_ERR_INVALID;
+    if (zero_extent(p)) {
+        if (opts && opts->info) *opts->info = gn_plan_info{GN_PATH_AUTO, 0, 0, 0, 0, 0};
+        return GN_OK;
+    }
+    if (x == nullptr || mean == nullptr || rstd == nullptr) return GN_ERR_INVALID;
+    int32_t path = plan(p, false, opts);
+    if (path < 0) return GN_ERR_UNSUPPORTED;
+    if (path != GN_PATH_GENERIC) {
+        const bool al = aligned16(x) && (y == nullptr || aligned16(y)) && aligned16(gamma) && aligned16(beta);
+        if (!al) {
+            if (forced(opts) != GN_PATH_AUTO) return GN_ERR_UNSUPPORTED;
+            path = GN_PATH_GENERIC;
+        }
+    }
+    const size_t need = fwd_ws(p, path);
+    if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
+    gn::FwdArgs a{x, gamma, beta, y, mean, rstd, eps};
+    gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
+    if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
+    hipError_t e = path == GN_PATH_ROWS ? gn::rows_fwd(p, a, l) : gn::generic_fwd(p, a, l);
+    return e == hipSuccess ? GN_OK : GN_ERR_HIP;
+}
+
+gn_status gn_backward(const void* dy, const void* x, const float* mean, const float* rstd, const float* gamma,
+                      void* dx, float* dgamma, float* dbeta, int32_t mask, int64_t N, int64_t C, int64_t HW,
+                      int64_t G, gn_dtype dtype, gn_layout layout, void* workspace, size_t ws_bytes,
+                      void* stream, const gn_options* opts) {
+    Problem p;
+    gn_status st = make_problem(N, C, HW, G, dtype, layout, &p);
+    if (st != GN_OK) return st;
+    if (mask <= 0 || mask > 7) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DX) && dx == nullptr) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DGAMMA) && dgamma == nullptr) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DBETA) && dbeta == nullptr) return GN_ERR_INVALID;
+    if ((mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) && gamma == nullptr) return GN_ERR_INVALID;
+    if (zero_extent(p)) {
+        if (opts && opts->info) *opts->info = gn_plan_info{GN_PATH_AUTO, 0, 0, 0, 0, 0};
+        return GN_OK;
+    }
+    if (dy == nullptr || x == nullptr || mean == nullptr || rstd == nullptr) return GN_ERR_INVALID;
+    int32_t path = plan(p, true, opts);
+    if (path < 0) return GN_ERR_UNSUPPORTED;
+    if (path != GN_PATH_GENERIC) {
+        const bool al = aligned16(dy) && aligned16(x) && aligned16(gamma) &&
+                        (!(mask & GN_GRAD_DX) || aligned16(dx));
+        if (!al) {
+            if (forced(opts) != GN_PATH_AUTO) return GN_ERR_UNSUPPORTED;
+            path = GN_PATH_GENERIC;
+        }
+    }
+    const size_t need = bwd_ws(p, mask, path);
+    if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
+    gn::BwdArgs a{dy, x, mean, rstd, gamma,
+                  (mask & GN_GRAD_DX) ? dx : nullptr,
+                  (mask & GN_GRAD_DGAMMA) ? dgamma : nullptr,
+                  (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask};
+    gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
+    if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
+    hipError_t e = path == GN_PATH_ROWS ? gn::rows_bwd(p, a, l) : gn::generic_bwd(p, a, l);
+    return e == hipSuccess ? GN_OK : GN_ERR_HIP;
+}
+
+const char* gn_status_string(gn_status s) {
+    switch (s) {
+        case GN_OK: return "ok";
+        case GN_ERR_INVALID: return "invalid argument";
+        case GN_ERR_UNSUPPORTED: return "unsupported dtype, layout or forced path";
+        case GN_ERR_WORKSPACE: return "workspace too small";
+        case GN_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t gn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,235 @@
+// gn_device.hpp -- device helpers shared by the GroupNorm kernels (gfx950, wave64).
+//
+// * 16-byte vector IO of float32 / float16 / bfloat16 activations with
+//   conversion to float32 and back (round to nearest even, the hardware
+//   v_cvt_pk_* conversions);
+// * wavefront and workgroup sums in a fixed order (bitwise reproducible);
+// * mean/M2 statistics merged with Chan, Golub and LeVeque's pairwise update
+//   ("Algorithms for computing the sample variance", 1983), operands always
+//   taken in a canonical order so that every lane agrees bitwise;
+// * an arrival counter barrier for co-resident workgroups with agent-scope
+//   release/acquire, bounded so that no wave can spin forever.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gn {
+
+constexpr int kWave = 64;
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef float f8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef __bf16 b8v __attribute__((ext_vector_type(8)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// element traits: V elements per 16-byte vector
+// ---------------------------------------------------------------------------
+template <typename T> struct Vec;
+
+template <> struct Vec<float> {
+    static constexpr int V = 4;
+    __device__ static inline void load(const float* p, float (&o)[4]) {
+        f4v v = *reinterpret_cast<const f4v*>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    __device__ static inline void unpack(const u4v& raw, float (&o)[4]) {
+        f4v v = __builtin_bit_cast(f4v, raw);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    __device__ static inline u4v pack(const float (&o)[4]) {
+        f4v v = {o[0], o[1], o[2], o[3]};
+        return __builtin_bit_cast(u4v, v);
+    }
+    __device__ static inline float to_f(float v) { return v; }
+    __device__ static inline float from_f(float v) { return v; }
+};
+
+template <> struct Vec<_Float16> {
+    static constexpr int V = 8;
+    __device__ static inline void unpack(const u4v& raw, float (&o)[8]) {
+        f8v f = __builtin_convertvector(__builtin_bit_cast(h8v, raw), f8v);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = f[k];
+    }
+    __device__ static inline u4v pack(const float (&o)[8]) {
+        f8v f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = o[k];
+        return __builtin_bit_cast(u4v, __builtin_convertvector(f, h8v));
+    }
+    __device__ static inline float to_f(_Float16 v) { return (float)v; }
+    __device__ static inline _Float16 from_f(float v) { return (_Float16)v; }
+};
+
+template <> struct Vec<__bf16> {
+    static constexpr int V = 8;
+    __device__ static inline void unpack(const u4v& raw, float (&o)[8]) {
+        f8v f = __builtin_convertvector(__builtin_bit_cast(b8v, raw), f8v);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = f[k];
+    }
+    __device__ static inline u4v pack(const float (&o)[8]) {
+        f8v f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = o[k];
+        return __builtin_bit_cast(u4v, __builtin_convertvector(f, b8v));
+    }
+    __device__ static inline float to_f(__bf16 v) { return (float)v; }
+    __device__ static inline __bf16 from_f(float v) { return (__bf16)v; }
+};
+
+__device__ inline u4v ld16(const void* p) { return *reinterpret_cast<const u4v*>(p); }
+__device__ inline void st16(void* p, const u4v& v) { *reinterpret_cast<u4v*>(p) = v; }
+// Streaming store for outputs that are not read again by the kernel.
+__device__ inline void st16_nt(void* p, const u4v& v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u4v*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// fixed-order reductions
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+    return __builtin_bit_cast(float,
+        __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float readlane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the 64 lanes; every lane receives the same bits.  Steps: lane
+// pairs, quads, half-rows and rows through DPP (each step adds a lane and its
+// mirror, which is commutative and hence identical on both), then the four
+// row sums combined as (r0 + r1) + (r2 + r3).
+__device__ inline float wave_sum(float v) {
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);  // row_half_mirror
+    v += dpp_f<0x140>(v);  // row_mirror
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+// Sum over lanes that are congruent modulo `stride` (stride a power of two,
+// 1..32): lanes l, l+stride, l+2*stride, ... all receive the same bits.
+__device__ inline float wave_sum_strided(float v, int stride) {
+    for (int off = stride; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Workgroup sum of NV values per thread; `lds` holds NWAVES*NV floats.  All
+// threads receive the same bits.  Contains __syncthreads (call uniformly).
+template <int NV, int NWAVES>
+__device__ inline void block_sum(float (&v)[NV], float* lds) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = wave_sum(v[k]);
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) lds[wave * NV + k] = v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        float s = lds[k];
+#pragma unroll
+        for (int w = 1; w < NWAVES; ++w) s += lds[w * NV + k];
+        v[k] = s;
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// (count, mean, M2) statistics
+// ---------------------------------------------------------------------------
+struct Stat {
+    float n;     // element count (exact: counts stay far below 2^24 per merge operand
+                 // only where noted; the merge uses the ratio, so large counts are fine)
+    float mean;
+    float m2;    // sum of squared deviations from mean
+};
+
+__device__ inline Stat stat_empty() { return Stat{0.f, 0.f, 0.f}; }
+
+// Chan et al. pairwise merge; a is the "left" operand.
+__device__ inline Stat stat_merge(const Stat& a, const Stat& b) {
+    const float n = a.n + b.n;
+    if (b.n == 0.f) return a;
+    if (a.n == 0.f) return b;
+    const float fb = b.n / n;
+    const float delta = b.mean - a.mean;
+    Stat r;
+    r.n = n;
+    r.mean = fmaf(delta, fb, a.mean);
+    r.m2 = a.m2 + b.m2 + delta * delta * (a.n * fb);
+    return r;
+}
+
+__device__ inline Stat shfl_xor_stat(const Stat& s, int off) {
+    return Stat{__shfl_xor(s.n, off, kWave), __shfl_xor(s.mean, off, kWave), __shfl_xor(s.m2, off, kWave)};
+}
+
+// Butterfly merge over lanes congruent modulo `stride` (power of two).  The
+// lower lane is always the left operand, so partners compute identical bits.
+__device__ inline Stat wave_merge_strided(Stat s, int stride) {
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int off = stride; off < kWave; off <<= 1) {
+        const Stat o = shfl_xor_stat(s, off);
+        s = (lane & off) ? stat_merge(o, s) : stat_merge(s, o);
+    }
+    return s;
+}
+
+// Exact two-pass statistics of K values held in registers, `valid` of which
+// count (the first `valid` ones).
+template <int K>
+__device__ inline Stat stat_of(const float (&v)[K], int valid) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) s += (k < valid) ? v[k] : 0.f;
+    if (valid <= 0) return stat_empty();
+    const float n = (float)valid;
+    const float m = s / n;
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float d = v[k] - m;
+        q += (k < valid) ? d * d : 0.f;
+    }
+    return Stat{n, m, q};
+}
+
+// ---------------------------------------------------------------------------
+// barrier among co-resident workgroups
+// ---------------------------------------------------------------------------
+// Spin limit: far above any legitimate wait (the longest waits are a few
+// milliseconds); on expiry the wave stops waiting and raises *err so that the
+// host can report a broken co-residency assumption instead of hanging.
+constexpr uint32_t kSpinLimit = 1u << 26;
+
+// Every thread of the workgroup calls this.  Publishes the workgroup's prior
+// global writes (agent-scope release), adds one arrival to *ctr and waits
+// until *ctr reaches `target`; afterwards the writes of every arrived
+// workgroup are visible (agent-scope acquire).
+__device__ inline void group_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t spins = 0;
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > kSpinLimit) {
+                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+}  // namespace gn

@@ -1,0 +1,82 @@
+// gn_internal.hpp -- host-side interfaces between the C ABI (gn_api.cpp) and
+// the kernel launchers of each path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gn.h"
+
+namespace gn {
+
+// One GroupNorm problem, validated by the C ABI.
+struct Problem {
+    int64_t N, C, HW, G;
+    int64_t D;       // channels per group, C/G
+    int64_t M;       // elements per slice, D*HW
+    int64_t S;       // slices, N*G
+    int64_t E;       // elements, N*C*HW
+    gn_dtype dtype;
+    gn_layout layout;
+    int elem_bytes;  // 4 or 2
+};
+
+struct FwdArgs {
+    const void* x;
+    const float* gamma;  // NULL => 1
+    const float* beta;   // NULL => 0
+    void* y;             // NULL => statistics only
+    float* mean;
+    float* rstd;
+    float eps;
+};
+
+struct BwdArgs {
+    const void* dy;
+    const void* x;
+    const float* mean;
+    const float* rstd;
+    const float* gamma;  // NULL => 1
+    void* dx;            // NULL unless GN_GRAD_DX
+    float* dgamma;       // NULL unless GN_GRAD_DGAMMA
+    float* dbeta;        // NULL unless GN_GRAD_DBETA
+    int32_t mask;
+};
+
+// Launch context handed to every launcher.
+struct Launch {
+    hipStream_t stream;
+    void* ws;              // device workspace (may be NULL when its size is 0)
+    size_t ws_bytes;
+    hipEvent_t ev_begin;   // recorded around the main kernel when not NULL
+    hipEvent_t ev_end;
+    int32_t max_resident_override;
+    gn_plan_info* info;    // may be NULL
+};
+
+// Device facts used by the planner (queried once per device).
+struct DeviceInfo {
+    int device;
+    int cu_count;
+    int coop_supported;
+};
+const DeviceInfo& device_info();
+
+// Records ev (if any) on the stream; returns hipSuccess or the error.
+hipError_t record(hipEvent_t ev, hipStream_t s);
+
+// ---- generic path: any shape, any alignment --------------------------------
+size_t generic_fwd_ws(const Problem& p);
+size_t generic_bwd_ws(const Problem& p, int32_t mask);
+hipError_t generic_fwd(const Problem& p, const FwdArgs& a, const Launch& l);
+hipError_t generic_bwd(const Problem& p, const BwdArgs& a, const Launch& l);
+
+// ---- rows path: HW == 1, one wavefront per slice ----------------------------
+bool rows_ok(const Problem& p);   // shape condition (alignment checked separately)
+size_t rows_fwd_ws(const Problem& p);
+size_t rows_bwd_ws(const Problem& p, int32_t mask);
+hipError_t rows_fwd(const Problem& p, const FwdArgs& a, const Launch& l);
+hipError_t rows_bwd(const Problem& p, const BwdArgs& a, const Launch& l);
+
+}  // namespace gn

@@ -1,0 +1,134 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/gn.h
+declares, and rejects bad arguments before enqueuing anything.  None of these
+calls reaches the GPU (validation returns first), so they run without one.
+
+The rejected cases follow the argument checks of the baracuda-kernels
+GroupNorm backward plan (non-negative sizes, G > 0 dividing C, supported
+dtype, affine parameters all-or-none, workspace at least the queried size,
+zero extent is a successful no-op) and the output mask of ROCm/pytorch
+PR #3564's tests.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from normalization_gn_stats_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gn.h")
+
+F32, F16, BF16 = _lib.GN_F32, _lib.GN_F16, _lib.GN_BF16
+NCHW, NHWC = _lib.GN_NCHW, _lib.GN_NHWC
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every case below is rejected on the host
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built")
+    return _lib.lib()
+
+
+def header_symbols():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(gn_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_header_declares_the_binding_list():
+    assert header_symbols() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    defined = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for s in header_symbols():
+        assert s in defined, s
+        assert getattr(L, s) is not None
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.gn_status_string(s)
+    assert L.gn_version() >= 100
+
+
+def fwd(L, x=FAKE, g=None, b=None, y=FAKE, m=FAKE, r=FAKE, N=2, C=8, HW=4, G=2, eps=1e-5, dt=F32, lay=NCHW,
+        ws=None, wsb=0):
+    return L.gn_forward(x, g, b, y, m, r, N, C, HW, G, eps, dt, lay, ws, wsb, None, None)
+
+
+def bwd(L, dy=FAKE, x=FAKE, m=FAKE, r=FAKE, g=FAKE, dx=FAKE, dg=FAKE, db=FAKE, mask=7, N=2, C=8, HW=4, G=2,
+        dt=F32, lay=NCHW, ws=None, wsb=0):
+    return L.gn_backward(dy, x, m, r, g, dx, dg, db, mask, N, C, HW, G, dt, lay, ws, wsb, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), _lib.GN_ERR_INVALID),
+    (dict(C=-8), _lib.GN_ERR_INVALID),
+    (dict(HW=-4), _lib.GN_ERR_INVALID),
+    (dict(G=0), _lib.GN_ERR_INVALID),
+    (dict(G=3), _lib.GN_ERR_INVALID),           # 3 does not divide 8
+    (dict(dt=7), _lib.GN_ERR_UNSUPPORTED),
+    (dict(lay=5), _lib.GN_ERR_UNSUPPORTED),
+    (dict(g=FAKE), _lib.GN_ERR_INVALID),        # gamma without beta
+    (dict(b=FAKE), _lib.GN_ERR_INVALID),        # beta without gamma
+    (dict(x=None), _lib.GN_ERR_INVALID),
+    (dict(m=None), _lib.GN_ERR_INVALID),
+    (dict(eps=-1.0), _lib.GN_ERR_INVALID),
+    (dict(eps=float("nan")), _lib.GN_ERR_INVALID),
+    (dict(N=1 << 40, C=1 << 20, HW=1 << 20, G=1), _lib.GN_ERR_INVALID),   # element count overflows
+])
+def test_forward_rejects(L, kw, status):
+    assert fwd(L, **kw) == status
+
+
+def test_forward_workspace_too_small(L):
+    need = L.gn_forward_workspace_size(2, 8, 4, 2, F32, NCHW, None)
+    assert need > 0
+    assert fwd(L, ws=FAKE, wsb=need - 1) == _lib.GN_ERR_WORKSPACE
+    assert fwd(L, ws=None, wsb=0) == _lib.GN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=0), _lib.GN_ERR_INVALID),
+    (dict(mask=8), _lib.GN_ERR_INVALID),
+    (dict(dx=None), _lib.GN_ERR_INVALID),
+    (dict(dg=None), _lib.GN_ERR_INVALID),
+    (dict(db=None), _lib.GN_ERR_INVALID),
+    (dict(g=None), _lib.GN_ERR_INVALID),             # dgamma/dbeta need gamma
+    (dict(g=None, mask=1, dg=None, db=None, dx=FAKE, ws=FAKE, wsb=0), _lib.GN_ERR_WORKSPACE),
+    (dict(dy=None), _lib.GN_ERR_INVALID),
+    (dict(G=5), _lib.GN_ERR_INVALID),
+    (dict(dt=3), _lib.GN_ERR_UNSUPPORTED),
+])
+def test_backward_rejects(L, kw, status):
+    assert bwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(C=0), dict(HW=0)])
+def test_zero_extent_is_a_noop(L, kw):
+    # outputs are NULL-free fakes: a no-op must not touch them (and reach no GPU)
+    assert fwd(L, **kw) == _lib.GN_OK
+    assert bwd(L, **kw) == _lib.GN_OK
+    assert L.gn_forward_workspace_size(kw.get("N", 2), kw.get("C", 8), kw.get("HW", 4), 2, F32, NCHW, None) == 0
+
+
+def test_path_selection(L):
+    sel = lambda bw, N, C, HW, G, dt, lay, force=0: L.gn_select_path(
+        bw, N, C, HW, G, dt, lay, ctypes.byref(_lib.Options(force, 0, None, None, None)))
+    assert sel(0, 4096, 1024, 1, 1, F16, NCHW) == _lib.GN_PATH_ROWS
+    assert sel(1, 131072, 4096, 1, 1, BF16, NCHW) == _lib.GN_PATH_ROWS
+    assert sel(0, 4, 36, 1, 1, F16, NCHW) == _lib.GN_PATH_GENERIC          # 36 not a multiple of 8
+    assert sel(0, 4, 36, 1, 1, F16, NCHW, _lib.GN_PATH_ROWS) == -1         # forced path cannot serve
+    assert sel(0, 2, 8, 4, 2, F32, NCHW, _lib.GN_PATH_GENERIC) == _lib.GN_PATH_GENERIC
+    assert sel(0, 2, 8, 4, 3, F32, NCHW) == -1
+
+
+def test_workspace_sizes_cover_every_mask(L):
+    for mask in range(1, 8):
+        n = L.gn_backward_workspace_size(4096, 1024, 1, 1, F16, NCHW, mask, None)
+        assert n >= 0
+    assert L.gn_backward_workspace_size(4096, 1024, 1, 1, F16, NCHW, 0, None) == 0

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kT) void gen_ab_partial(const T* __restrict__ dy, c
         const int64_t o = slice_elem(i, n, g, C, HW, D, layout, &c);
         const float gd = ldf(dy, o) * (gamma ? gamma[c] : 1.f);
         acc[0] += gd;
-        acc[1] += gd * ((ldf(x, o) - mu) * r);
+        acc[1] = fmaf(gd, (ldf(x, o) - mu) * r, acc[1]);
     }
     __shared__ float lds[kNW * 2];
     block_sum<2, kNW>(acc, lds);
@@ -168,6 +168,9 @@ __global__ __launch_bounds__(kT) void gen_dx(const T* __restrict__ dy, const T* 
                                              const float* __restrict__ gamma, const float2* __restrict__ ab,
                                              T* __restrict__ dx, int64_t E, int64_t C, int64_t HW, int64_t G,
                                              int64_t D, int64_t M, int layout) {
+    // gamma*dy is rounded exactly as in the partial sums, so that it cancels A/M
+    // exactly where the slice makes dx vanish (one element per slice)
+#pragma clang fp contract(off)
     const int64_t stride = (int64_t)gridDim.x * kT;
     const float invM = 1.0f / (float)M;
     for (int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x; e < E; e += stride) {

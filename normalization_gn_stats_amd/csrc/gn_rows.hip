@@ -156,16 +156,20 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
             }
         }
         if (!want_dx) continue;
-        const float A = wave_sum(a) * invD;
-        const float B = wave_sum(bb) * invD;
+        {
+            // gamma*dy stays the rounded product that entered A
+#pragma clang fp contract(off)
+            const float A = wave_sum(a) * invD;
+            const float B = wave_sum(bb) * invD;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int vi = j * kWave + lane;
-            if (vi >= nvec) continue;
-            float o[V];
+            for (int j = 0; j < NV; ++j) {
+                const int vi = j * kWave + lane;
+                if (vi >= nvec) continue;
+                float o[V];
 #pragma unroll
-            for (int k = 0; k < V; ++k) o[k] = r * (dv[j][k] - A - xv[j][k] * B);
-            st16(dx + base + (int64_t)vi * V, Vec<T>::pack(o));
+                for (int k = 0; k < V; ++k) o[k] = r * ((dv[j][k] - A) - xv[j][k] * B);
+                st16(dx + base + (int64_t)vi * V, Vec<T>::pack(o));
+            }
         }
     }
     if (!want_params) return;

@@ -136,9 +136,12 @@ def test_bitwise_deterministic(wl, force):
     data = inputs.make_inputs(wl, seed=1)
     a = run_gpu(wl, data, force_path=force)
     b = run_gpu(wl, data, force_path=force)
+    def bits(t):
+        flat = inputs.memory_image(t, wl.layout) if t.dim() == 4 else t.reshape(-1)
+        return flat.contiguous().view(torch.uint8)
+
     for k in ("y", "mean", "rstd", "dx", "dgamma", "dbeta"):
-        assert torch.equal(a[k].view(torch.uint8) if a[k].dtype != torch.float32 else a[k],
-                           b[k].view(torch.uint8) if b[k].dtype != torch.float32 else b[k]), k
+        assert torch.equal(bits(a[k]), bits(b[k])), k
 
 
 @pytest.mark.parametrize("wl", [inputs.ROWS_A, inputs.ROWS_B], ids=lambda w: w.name)

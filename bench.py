@@ -56,6 +56,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the oracle CPU-baseline sample (0 disables it)")
     ap.add_argument("--force-path", default=None, choices=[None, "generic", "rows", "slab"])
+    ap.add_argument("--mode", default="auto", choices=["auto", "graph", "eager"],
+                    help="graph: the timed steps run as one captured HIP graph (no host in the loop)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -96,26 +98,72 @@ def main():
                   fplan=gn.PlanInfo(), bplan=gn.PlanInfo())
         shapes.append(sh)
 
-    def step(events=None, i=0):
-        for k, sh in enumerate(shapes):
-            wl = sh["wl"]
-            fe = be = None
-            if events is not None:
-                fe = (events[i][k][0][0].cuda_event, events[i][k][0][1].cuda_event)
-                be = (events[i][k][1][0].cuda_event, events[i][k][1][1].cuda_event)
-            gn.forward_into(sh["x"], sh["gamma"], sh["beta"], wl.G, wl.eps, sh["y"], sh["mean"], sh["rstd"],
-                            sh["fws"], force_path=args.force_path, info=sh["fplan"], events=fe, stream=sp)
-            gn.backward_into(sh["dy"], sh["x"], sh["mean"], sh["rstd"], sh["gamma"], wl.G, mask, sh["dx"],
-                             sh["dgamma"], sh["dbeta"], sh["bws"], force_path=args.force_path,
-                             info=sh["bplan"], events=be, stream=sp)
+    # Pre-marshalled C-ABI calls (the binding's checks ran once above, through
+    # the size queries); a call costs one ctypes dispatch.
+    L = gn._lib.lib()
+    import ctypes
+
+    def calls_for(sh, stream_handle, evs):
+        wl = sh["wl"]
+        code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
+        lay = gn.layout_of(sh["x"])
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        out = []
+        for kind in ("fwd", "bwd"):
+            o = gn._lib.Options()
+            o.force_path = {None: 0, "generic": 1, "rows": 2, "slab": 3}[args.force_path]
+            o.info = ctypes.pointer(sh["fplan" if kind == "fwd" else "bplan"])
+            if evs is not None:
+                b, e = evs[0 if kind == "fwd" else 1]
+                o.event_begin = ctypes.c_void_p(b.cuda_event)
+                o.event_end = ctypes.c_void_p(e.cuda_event)
+            if kind == "fwd":
+                a = (P(sh["x"]), P(sh["gamma"]), P(sh["beta"]), P(sh["y"]), P(sh["mean"]), P(sh["rstd"]),
+                     wl.N, wl.C, wl.HW, wl.G, ctypes.c_float(wl.eps), code, lay, P(sh["fws"]),
+                     sh["fws"].numel(), ctypes.c_void_p(stream_handle), ctypes.byref(o))
+                out.append((L.gn_forward, a, o))
+            else:
+                a = (P(sh["dy"]), P(sh["x"]), P(sh["mean"]), P(sh["rstd"]), P(sh["gamma"]), P(sh["dx"]),
+                     P(sh["dgamma"]), P(sh["dbeta"]), mask, wl.N, wl.C, wl.HW, wl.G, code, lay, P(sh["bws"]),
+                     sh["bws"].numel(), ctypes.c_void_p(stream_handle), ctypes.byref(o))
+                out.append((L.gn_backward, a, o))
+        return out
+
+    def run(call_list):
+        for fn, a, _o in call_list:
+            st = fn(*a)
+            if st != 0:
+                raise gn.GNError(st, fn.__name__)
+
+    plain = [c for sh in shapes for c in calls_for(sh, sp, None)]
 
     log(f"warmup {args.warmup} steps")
+    t_w0 = time.perf_counter()
     for _ in range(args.warmup):
-        step()
+        run(plain)
     torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t_w0) * 1e3 / max(args.warmup, 1)
 
-    # per-step, per-shape, per-call (begin, end) events around each main kernel
     K = args.steps
+    mode = args.mode
+    if mode == "auto":
+        mode = "graph" if warm_ms < 2.0 else "eager"
+
+    # ---- timed region: exactly K steps between two synchronisations ----------
+    graph = None
+    if mode == "graph":
+        # the K steps captured into one HIP graph, so that no host work sits
+        # between the kernels of these microsecond-scale calls
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+            h = torch.cuda.current_stream().cuda_stream
+            for i in range(K):
+                for sh in shapes:
+                    run(calls_for(sh, h, None))
+        graph.replay()             # first replay uploads the graph
+        torch.cuda.synchronize()
+
+    # per-step, per-shape (fwd, bwd) x (begin, end) events around each main kernel
     events = [[[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(2)]
                for _ in shapes] for _ in range(K)]
     for row in events:             # torch creates HIP events lazily at their first record
@@ -124,15 +172,35 @@ def main():
                 for ev in pair:
                     ev.record(stream)
     torch.cuda.synchronize()
+    evcalls = [[c for k, sh in enumerate(shapes) for c in calls_for(sh, sp, events[i][k])] for i in range(K)]
 
-    log(f"timing {K} steps")
+    log(f"timing {K} steps ({mode})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        step(events, i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for cl in evcalls:
+            run(cl)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
+
+    if graph is not None:
+        # Kernel durations: the same K steps issued eagerly with the library's
+        # events around each main kernel, queued behind a GPU spin so that the
+        # kernels run back to back and each event pair brackets its kernel only.
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        torch.cuda._sleep(1_000_000)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cycles_per_ms = 1_000_000 / max(c0.elapsed_time(c1), 1e-3)
+        host_ms = warm_ms * K * 3 + 20.0
+        torch.cuda._sleep(int(cycles_per_ms * host_ms))
+        for cl in evcalls:
+            run(cl)
+        torch.cuda.synchronize()
 
     bytes_per_step = sum(sh["wl"].fwd_min_bytes() + sh["wl"].bwd_min_bytes() for sh in shapes)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
@@ -155,7 +223,10 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(dom["main_kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dom["main_kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": f"{dom['call']} {dom['path']} main kernel on {dom['shape']}",
-                "avg_us": round(dom["main_kernel_us"], 3), "algorithmic_bytes": dom["main_kernel_bytes"]}
+                "avg_us": round(dom["main_kernel_us"], 3), "algorithmic_bytes": dom["main_kernel_bytes"],
+                "timing": ("HIP events recorded by the library on the call's stream around the main kernel, "
+                           + ("K eager steps queued behind a GPU spin after the graph-timed region"
+                              if mode == "graph" else "over the timed region"))}
 
     # ---- oracle CPU baseline on a bounded sample -------------------------------
     cpu = None
@@ -175,7 +246,7 @@ def main():
         "vs_baseline": None,
         "dtype": shapes[0]["wl"].dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload,
+        "config": {"workload": args.workload, "launch": mode,
                    "shapes": [dict(N=s["wl"].N, C=s["wl"].C, H=s["wl"].H, W=s["wl"].W, G=s["wl"].G,
                                    dtype=s["wl"].dtype, layout=s["wl"].layout) for s in shapes],
                    "mask": "dx|dgamma|dbeta", "bytes_per_step": bytes_per_step,

@@ -40,6 +40,10 @@ const DeviceInfo& device_info() {
 
 hipError_t record(hipEvent_t ev, hipStream_t s) {
     if (!ev) return hipSuccess;
+    // under stream capture the event becomes a timing node of the graph
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive)
+        return hipEventRecordWithFlags(ev, s, hipEventRecordExternal);
     return hipEventRecord(ev, s);
 }
 

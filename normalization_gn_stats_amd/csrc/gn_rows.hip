@@ -29,24 +29,47 @@ constexpr int kNW = kT / kWave;
 template <typename T, int NV>
 __global__ __launch_bounds__(kT) void rows_fwd_k(const T* __restrict__ x, const float* __restrict__ gamma,
                                                  const float* __restrict__ beta, T* __restrict__ y,
-                                                 float* __restrict__ mean, float* __restrict__ rstd, int64_t S,
+                                                 float* __restrict__ mean, float* __restrict__ rstd, int64_t N,
                                                  int64_t G, int64_t C, int D, float eps) {
     constexpr int V = Vec<T>::V;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t s = (int64_t)blockIdx.x * kNW + threadIdx.x / kWave;
-    if (s >= S) return;
-    const int64_t n = s / G, g = s - n * G;
+    // grid: x = blocks of kNW samples, y = group; the wave index is uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t n = (int64_t)blockIdx.x * kNW + wave;
+    const int64_t g = blockIdx.y;
+    if (n >= N) return;
+    const int64_t s = n * G + g;
     const int64_t base = n * C + g * D;
     const int nvec = D / V;
+    // Loads are branch-free: a lane past the end of the slice reads the last
+    // vector again (always in bounds) and its values are dropped afterwards,
+    // so every load of the wave issues back to back.
     float v[NV][V];
+    u4v raw[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const int vi = j * kWave + lane;
-        if (vi < nvec) {
-            Vec<T>::unpack(ld16(x + base + (int64_t)vi * V), v[j]);
-        } else {
+        const int vi = min(j * kWave + lane, nvec - 1);
+        raw[j] = ld16(x + base + (int64_t)vi * V);
+    }
+    // affine parameters of the lane's columns, fetched while x is in flight
+    float ga[NV][V], be[NV][V];
 #pragma unroll
-            for (int k = 0; k < V; ++k) v[j][k] = 0.f;
+    for (int j = 0; j < NV; ++j) {
+        const int c0 = (int)(g * D) + min(j * kWave + lane, nvec - 1) * V;
+#pragma unroll
+        for (int k = 0; k < V; k += 4) {
+            const float4 q = gamma ? *reinterpret_cast<const float4*>(gamma + c0 + k) : make_float4(1.f, 1.f, 1.f, 1.f);
+            const float4 t = beta ? *reinterpret_cast<const float4*>(beta + c0 + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+            ga[j][k] = q.x; ga[j][k + 1] = q.y; ga[j][k + 2] = q.z; ga[j][k + 3] = q.w;
+            be[j][k] = t.x; be[j][k + 1] = t.y; be[j][k + 2] = t.z; be[j][k + 3] = t.w;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        Vec<T>::unpack(raw[j], v[j]);
+        if (j * kWave + lane >= nvec) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) v[j][k] = 0.f;   // not part of the slice
         }
     }
     float sum = 0.f;
@@ -79,95 +102,153 @@ __global__ __launch_bounds__(kT) void rows_fwd_k(const T* __restrict__ x, const 
     for (int j = 0; j < NV; ++j) {
         const int vi = j * kWave + lane;
         if (vi >= nvec) continue;
-        const int c0 = (int)(g * D) + vi * V;
         float o[V];
 #pragma unroll
-        for (int k = 0; k < V; k += 4) {
-            float4 ga = gamma ? *reinterpret_cast<const float4*>(gamma + c0 + k) : make_float4(1.f, 1.f, 1.f, 1.f);
-            float4 be = beta ? *reinterpret_cast<const float4*>(beta + c0 + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-            o[k + 0] = fmaf(v[j][k + 0] - mu, r * ga.x, be.x);
-            o[k + 1] = fmaf(v[j][k + 1] - mu, r * ga.y, be.y);
-            o[k + 2] = fmaf(v[j][k + 2] - mu, r * ga.z, be.z);
-            o[k + 3] = fmaf(v[j][k + 3] - mu, r * ga.w, be.w);
-        }
+        for (int k = 0; k < V; ++k) o[k] = fmaf(v[j][k] - mu, r * ga[j][k], be[j][k]);
         st16(y + base + (int64_t)vi * V, Vec<T>::pack(o));
     }
 }
 
 // part: [G][NB][D] float2 (sum dy, sum dy*xhat) -- one row per workgroup.
-template <typename T, int NV>
+// Wave wi of group g handles samples n = wi + j*W (W waves per group), RB of
+// them per batch: the batch's x and dy are all loaded before any is used, so
+// a wave has RB slices in flight instead of walking them one round trip at a
+// time.
+template <typename T, int NV, int RB>
 __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const T* __restrict__ x,
                                                  const float* __restrict__ mean, const float* __restrict__ rstd,
                                                  const float* __restrict__ gamma, T* __restrict__ dx,
                                                  float2* __restrict__ part, int64_t N, int64_t G, int64_t C,
                                                  int D, int NB, int want_dx, int want_params) {
     constexpr int V = Vec<T>::V;
-    extern __shared__ float2 lds_cols[];   // [D] when want_params
+    constexpr bool kHoistGamma = NV * V <= 16;   // gamma of the lane's columns kept in registers
+    extern __shared__ float2 lds_cols[];         // [D] when want_params
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int64_t g = blockIdx.x / NB;
-    const int b = blockIdx.x - (int)(g * NB);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t g = blockIdx.y;   // grid: x = NB workgroups per group, y = group
+    const int b = blockIdx.x;
     const int64_t W = (int64_t)NB * kNW;
+    const int64_t wi = (int64_t)b * kNW + wave;
     const int nvec = D / V;
     const float invD = 1.0f / (float)D;
+    const float* gcol = gamma ? gamma + g * D : nullptr;
+
+    float gam[kHoistGamma ? NV : 1][kHoistGamma ? V : 1];
+    // gamma of the V columns of vector j (registers, or float4 loads that hit L1/L2)
+    auto gamma_vec = [&](int j, int vi, float (&gv)[V]) {
+        if constexpr (kHoistGamma) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) gv[k] = gam[j][k];
+        } else {
+            const int vc = min(vi, nvec - 1);
+#pragma unroll
+            for (int k = 0; k < V; k += 4) {
+                float4 q = gcol ? *reinterpret_cast<const float4*>(gcol + vc * V + k) : make_float4(1.f, 1.f, 1.f, 1.f);
+                gv[k] = q.x; gv[k + 1] = q.y; gv[k + 2] = q.z; gv[k + 3] = q.w;
+            }
+        }
+    };
+
     float cs1[NV][V], cs2[NV][V];
 #pragma unroll
     for (int j = 0; j < NV; ++j)
 #pragma unroll
         for (int k = 0; k < V; ++k) { cs1[j][k] = 0.f; cs2[j][k] = 0.f; }
 
-    for (int64_t n = (int64_t)b * kNW + wave; n < N; n += W) {
-        const int64_t s = n * G + g;
-        const int64_t base = n * C + g * D;
-        float xv[NV][V], dv[NV][V];
+    bool first = true;
+    for (int64_t n0 = wi; n0 < N; n0 += (int64_t)RB * W) {
+        // Branch-free loads of the whole batch: rows past N re-read row N-1 and
+        // lanes past the slice re-read its last vector; both are dropped below.
+        u4v rx[RB][NV], rd[RB][NV];
+        float mu[RB], rs[RB];
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int vi = j * kWave + lane;
-            if (vi < nvec) {
-                Vec<T>::unpack(ld16(x + base + (int64_t)vi * V), xv[j]);
-                Vec<T>::unpack(ld16(dy + base + (int64_t)vi * V), dv[j]);
-            } else {
+        for (int r = 0; r < RB; ++r) {
+            const int64_t n = min(n0 + r * W, N - 1);
+            const int64_t base = n * C + g * D;
 #pragma unroll
-                for (int k = 0; k < V; ++k) { xv[j][k] = 0.f; dv[j][k] = 0.f; }
+            for (int j = 0; j < NV; ++j) {
+                const int vi = min(j * kWave + lane, nvec - 1);
+                rx[r][j] = ld16(x + base + (int64_t)vi * V);
+                rd[r][j] = ld16(dy + base + (int64_t)vi * V);
             }
+            mu[r] = mean[n * G + g];
+            rs[r] = rstd[n * G + g];
         }
-        const float mu = mean[s], r = rstd[s];
-        float a = 0.f, bb = 0.f;
+        if constexpr (kHoistGamma) {
+            if (first) {   // issued after the first batch's activations
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int vi = j * kWave + lane;
-            if (vi >= nvec) continue;
-            const int c0 = (int)(g * D) + vi * V;
+                for (int j = 0; j < NV; ++j) {
+                    const int vc = min(j * kWave + lane, nvec - 1);
 #pragma unroll
-            for (int k = 0; k < V; k += 4) {
-                float4 ga = gamma ? *reinterpret_cast<const float4*>(gamma + c0 + k) : make_float4(1.f, 1.f, 1.f, 1.f);
-                const float gk[4] = {ga.x, ga.y, ga.z, ga.w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float xh = (xv[j][k + u] - mu) * r;
-                    const float gd = dv[j][k + u] * gk[u];
-                    a += gd;
-                    bb = fmaf(gd, xh, bb);
-                    xv[j][k + u] = xh;            // keep xhat
-                    cs1[j][k + u] += dv[j][k + u];
-                    cs2[j][k + u] = fmaf(dv[j][k + u], xh, cs2[j][k + u]);
-                    dv[j][k + u] = gd;            // keep gamma*dy
+                    for (int k = 0; k < V; k += 4) {
+                        float4 q = gcol ? *reinterpret_cast<const float4*>(gcol + vc * V + k)
+                                        : make_float4(1.f, 1.f, 1.f, 1.f);
+                        gam[j][k] = q.x; gam[j][k + 1] = q.y; gam[j][k + 2] = q.z; gam[j][k + 3] = q.w;
+                    }
                 }
             }
         }
-        if (!want_dx) continue;
-        {
-            // gamma*dy stays the rounded product that entered A
-#pragma clang fp contract(off)
-            const float A = wave_sum(a) * invD;
-            const float B = wave_sum(bb) * invD;
+        first = false;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (n0 + r * W >= N) {   // uniform: a row past the end contributes nothing
+#pragma unroll
+                for (int j = 0; j < NV; ++j) { rx[r][j] = u4v{0u, 0u, 0u, 0u}; rd[r][j] = u4v{0u, 0u, 0u, 0u}; }
+            }
+        }
+        // per-slice sums A, B and the running column sums
+        float a[RB], bb[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            a[r] = 0.f;
+            bb[r] = 0.f;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int vi = j * kWave + lane;
                 if (vi >= nvec) continue;
-                float o[V];
+                float xv[V], dv[V], gv[V];
+                Vec<T>::unpack(rx[r][j], xv);
+                Vec<T>::unpack(rd[r][j], dv);
+                gamma_vec(j, vi, gv);
 #pragma unroll
-                for (int k = 0; k < V; ++k) o[k] = r * ((dv[j][k] - A) - xv[j][k] * B);
+                for (int k = 0; k < V; ++k) {
+                    const float xh = (xv[k] - mu[r]) * rs[r];
+                    const float gd = dv[k] * gv[k];
+                    a[r] += gd;
+                    bb[r] = fmaf(gd, xh, bb[r]);
+                    cs1[j][k] += dv[k];
+                    cs2[j][k] = fmaf(dv[k], xh, cs2[j][k]);
+                }
+            }
+        }
+        if (!want_dx) continue;
+        float A[RB], B[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            A[r] = wave_sum(a[r]) * invD;
+            B[r] = wave_sum(bb[r]) * invD;
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t n = n0 + r * W;
+            if (n >= N) continue;
+            const int64_t base = n * C + g * D;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                // gamma*dy rounded as it entered A, so that equal terms cancel exactly
+#pragma clang fp contract(off)
+                const int vi = j * kWave + lane;
+                if (vi >= nvec) continue;
+                float xv[V], dv[V], gv[V], o[V];
+                Vec<T>::unpack(rx[r][j], xv);
+                Vec<T>::unpack(rd[r][j], dv);
+                gamma_vec(j, vi, gv);
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float xh = (xv[k] - mu[r]) * rs[r];
+                    const float gd = dv[k] * gv[k];
+                    o[k] = rs[r] * ((gd - A[r]) - xh * B[r]);
+                }
                 st16(dx + base + (int64_t)vi * V, Vec<T>::pack(o));
             }
         }
@@ -195,37 +276,40 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
     for (int c = threadIdx.x; c < D; c += kT) dst[c] = lds_cols[c];
 }
 
-// dbeta[g*D + c] = sum_b part[g][b][c].x, dgamma likewise with .y, b in order.
-// Workgroup = 64 channels x 4 row lanes; each row lane sums rows rl, rl+4, ...
-// then the four lanes are added in order.
+// dbeta[g*D + c] = sum_b part[g][b][c].x, dgamma likewise with .y, b in
+// order.  A workgroup covers kColPairs pairs of channels (one float4 of
+// partials per row) with kRowLanes lanes over the partial rows: lane rl sums
+// rows rl, rl + kRowLanes, ... and the lanes are then added in lane order.
+constexpr int kColPairs = 8;
+constexpr int kRowLanes = kT / kColPairs;
+
 __global__ __launch_bounds__(kT) void rows_colsum_k(const float2* __restrict__ part, int NB, int D,
                                                     float* __restrict__ dgamma, float* __restrict__ dbeta) {
-    const int cb = blockIdx.x;
+    const int cp = threadIdx.x % kColPairs;
+    const int rl = threadIdx.x / kColPairs;
     const int g = blockIdx.y;
-    const int cl = threadIdx.x & 63;
-    const int rl = threadIdx.x >> 6;
-    const int c = cb * 64 + cl;
-    float s1 = 0.f, s2 = 0.f;
-    if (c < D) {
-        const float2* src = part + (int64_t)g * NB * D + c;
+    const int c0 = (blockIdx.x * kColPairs + cp) * 2;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c0 < D) {
+        const float2* src = part + (int64_t)g * NB * D + c0;
 #pragma unroll 8
-        for (int b = rl; b < NB; b += 4) {
-            const float2 q = src[(int64_t)b * D];
-            s1 += q.x;
-            s2 += q.y;
+        for (int b = rl; b < NB; b += kRowLanes) {
+            const float4 q = *reinterpret_cast<const float4*>(src + (int64_t)b * D);
+            acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
         }
     }
-    __shared__ float2 red[kT];
-    red[threadIdx.x] = make_float2(s1, s2);
+    __shared__ float4 red[kT];
+    red[threadIdx.x] = acc;
     __syncthreads();
-    if (rl == 0 && c < D) {
-        float2 t = red[cl];
-        for (int k = 1; k < 4; ++k) {
-            t.x += red[k * 64 + cl].x;
-            t.y += red[k * 64 + cl].y;
+    if (rl == 0 && c0 < D) {
+        float4 t = red[cp];
+        for (int k = 1; k < kRowLanes; ++k) {
+            const float4 q = red[k * kColPairs + cp];
+            t.x += q.x; t.y += q.y; t.z += q.z; t.w += q.w;
         }
-        if (dbeta) dbeta[(int64_t)g * D + c] = t.x;
-        if (dgamma) dgamma[(int64_t)g * D + c] = t.y;
+        const int64_t o = (int64_t)g * D + c0;
+        if (dbeta) { dbeta[o] = t.x; dbeta[o + 1] = t.z; }
+        if (dgamma) { dgamma[o] = t.y; dgamma[o + 1] = t.w; }
     }
 }
 
@@ -253,38 +337,39 @@ int rows_nb(const Problem& p) {
 
 template <typename T, int NV>
 hipError_t fwd_nv(const Problem& p, const FwdArgs& a, const Launch& l) {
-    const unsigned grid = (unsigned)((p.S + kNW - 1) / kNW);
+    const unsigned grid = (unsigned)((p.N + kNW - 1) / kNW);
     hipError_t e;
     if ((e = record(l.ev_begin, l.stream))) return e;
-    hipLaunchKernelGGL((rows_fwd_k<T, NV>), dim3(grid), dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta,
-                       (T*)a.y, a.mean, a.rstd, p.S, p.G, p.C, (int)p.D, a.eps);
+    hipLaunchKernelGGL((rows_fwd_k<T, NV>), dim3(grid, (unsigned)p.G), dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta,
+                       (T*)a.y, a.mean, a.rstd, p.N, p.G, p.C, (int)p.D, a.eps);
     if ((e = hipGetLastError())) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
     if (l.info) {
         l.info->path = GN_PATH_ROWS;
         l.info->kernels = 1;
-        l.info->grid = grid;
+        l.info->grid = (int64_t)grid * p.G;
     }
     return hipSuccess;
 }
 
 template <typename T, int NV>
 hipError_t bwd_nv(const Problem& p, const BwdArgs& a, const Launch& l) {
+    constexpr int RB = NV <= 2 ? 4 : NV <= 4 ? 2 : 1;   // slices per wave in flight
     const int NB = rows_nb(p);
     const bool params = (a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) != 0;
-    const unsigned grid = (unsigned)(p.G * NB);
+    const unsigned grid = (unsigned)NB;
     const size_t lds = params ? (size_t)p.D * sizeof(float2) : 0;
     float2* part = (float2*)l.ws;
     hipError_t e;
     if ((e = record(l.ev_begin, l.stream))) return e;
-    hipLaunchKernelGGL((rows_bwd_k<T, NV>), dim3(grid), dim3(kT), lds, l.stream, (const T*)a.dy, (const T*)a.x,
+    hipLaunchKernelGGL((rows_bwd_k<T, NV, RB>), dim3(grid, (unsigned)p.G), dim3(kT), lds, l.stream, (const T*)a.dy, (const T*)a.x,
                        a.mean, a.rstd, a.gamma, (T*)a.dx, part, p.N, p.G, p.C, (int)p.D, NB,
                        (a.mask & GN_GRAD_DX) ? 1 : 0, params ? 1 : 0);
     if ((e = hipGetLastError())) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
     int kernels = 1;
     if (params) {
-        hipLaunchKernelGGL(rows_colsum_k, dim3((unsigned)((p.D + 63) / 64), (unsigned)p.G), dim3(kT), 0,
+        hipLaunchKernelGGL(rows_colsum_k, dim3((unsigned)((p.D + 2 * kColPairs - 1) / (2 * kColPairs)), (unsigned)p.G), dim3(kT), 0,
                            l.stream, part, NB, (int)p.D, (a.mask & GN_GRAD_DGAMMA) ? a.dgamma : nullptr,
                            (a.mask & GN_GRAD_DBETA) ? a.dbeta : nullptr);
         if ((e = hipGetLastError())) return e;
@@ -293,7 +378,7 @@ hipError_t bwd_nv(const Problem& p, const BwdArgs& a, const Launch& l) {
     if (l.info) {
         l.info->path = GN_PATH_ROWS;
         l.info->kernels = kernels;
-        l.info->grid = grid;
+        l.info->grid = (int64_t)grid * p.G;
     }
     return hipSuccess;
 }

@@ -1,0 +1,57 @@
+"""The C-ABI calls captured into a HIP graph (as the benchmark runs them):
+every replay, with eager work and synchronisations in between, must give
+bitwise the eager results."""
+import pytest
+import torch
+
+import normalization_gn_stats_amd as gn
+from normalization_gn_stats_amd import inputs
+from gpu_harness import ALL, say
+
+pytestmark = pytest.mark.gpu
+W = inputs.Workload
+
+
+@pytest.mark.parametrize("wl,force", [
+    (W("graph_rows_f16", 512, 1024, 1, 1, 1, "f16", "nchw"), None),
+    (W("graph_gen_bf16", 2, 16, 20, 21, 4, "bf16", "nhwc"), "generic"),
+    (inputs.TINY, None),
+], ids=lambda v: getattr(v, "name", str(v)))
+def test_graph_replays_match_eager(wl, force):
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    say(f"[graph] {wl.name}")
+    dev = torch.device("cuda", 0)
+    d = {k: v.to(dev) for k, v in inputs.make_inputs(wl, seed=4).items()}
+    N, C, HW, G = wl.N, wl.C, wl.HW, wl.G
+    code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
+    lay = gn.layout_of(d["x"])
+    fws = torch.empty(max(gn.forward_workspace_size(N, C, HW, G, code, lay, force), 1), dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(gn.backward_workspace_size(N, C, HW, G, code, lay, ALL, force), 1), dtype=torch.uint8,
+                      device=dev)
+    out = dict(y=torch.empty_like(d["x"]), mean=torch.empty(N * G, device=dev), rstd=torch.empty(N * G, device=dev),
+               dx=torch.empty_like(d["x"]), dgamma=torch.empty(C, device=dev), dbeta=torch.empty(C, device=dev))
+
+    def step(stream_handle):
+        gn.forward_into(d["x"], d["gamma"], d["beta"], G, wl.eps, out["y"], out["mean"], out["rstd"], fws,
+                        force_path=force, stream=stream_handle)
+        gn.backward_into(d["dy"], d["x"], out["mean"], out["rstd"], d["gamma"], G, ALL, out["dx"], out["dgamma"],
+                         out["dbeta"], bws, force_path=force, stream=stream_handle)
+
+    step(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        step(torch.cuda.current_stream().cuda_stream)
+    for rep in range(4):
+        for v in out.values():      # eager work between replays: poison every output
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            a = inputs.memory_image(out[k], wl.layout) if out[k].dim() == 4 else out[k]
+            b = inputs.memory_image(ref[k], wl.layout) if ref[k].dim() == 4 else ref[k]
+            assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), (rep, k)

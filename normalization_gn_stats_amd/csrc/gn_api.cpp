@@ -90,15 +90,17 @@ int32_t plan(const Problem& p, bool backward, const gn_options* opts) {
     const int32_t f = forced(opts);
     if (f == GN_PATH_GENERIC) return GN_PATH_GENERIC;
     if (f == GN_PATH_ROWS) return gn::rows_ok(p) ? GN_PATH_ROWS : -1;
-    if (f == GN_PATH_SLAB) return -1;   // not built in this library version
+    if (f == GN_PATH_SLAB) return gn::slab_ok(p) ? GN_PATH_SLAB : -1;
     if (f != GN_PATH_AUTO) return -1;
     if (gn::rows_ok(p)) return GN_PATH_ROWS;
+    if (gn::slab_ok(p)) return GN_PATH_SLAB;
     return GN_PATH_GENERIC;
 }
 
 size_t fwd_ws(const Problem& p, int32_t path) {
     switch (path) {
         case GN_PATH_ROWS: return gn::rows_fwd_ws(p);
+        case GN_PATH_SLAB: return gn::slab_fwd_ws(p);
         default: return gn::generic_fwd_ws(p);
     }
 }
@@ -106,6 +108,7 @@ size_t fwd_ws(const Problem& p, int32_t path) {
 size_t bwd_ws(const Problem& p, int32_t mask, int32_t path) {
     switch (path) {
         case GN_PATH_ROWS: return gn::rows_bwd_ws(p, mask);
+        case GN_PATH_SLAB: return gn::slab_bwd_ws(p, mask);
         default: return gn::generic_bwd_ws(p, mask);
     }
 }
@@ -182,7 +185,9 @@ gn_status gn_forward(const void* x, const float* gamma, const float* beta, void*
     gn::FwdArgs a{x, gamma, beta, y, mean, rstd, eps};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
-    hipError_t e = path == GN_PATH_ROWS ? gn::rows_fwd(p, a, l) : gn::generic_fwd(p, a, l);
+    hipError_t e = path == GN_PATH_ROWS ? gn::rows_fwd(p, a, l)
+                 : path == GN_PATH_SLAB ? gn::slab_fwd(p, a, l)
+                                        : gn::generic_fwd(p, a, l);
     return e == hipSuccess ? GN_OK : GN_ERR_HIP;
 }
 
@@ -221,7 +226,9 @@ gn_status gn_backward(const void* dy, const void* x, const float* mean, const fl
                   (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
-    hipError_t e = path == GN_PATH_ROWS ? gn::rows_bwd(p, a, l) : gn::generic_bwd(p, a, l);
+    hipError_t e = path == GN_PATH_ROWS ? gn::rows_bwd(p, a, l)
+                 : path == GN_PATH_SLAB ? gn::slab_bwd(p, a, l)
+                                        : gn::generic_bwd(p, a, l);
     return e == hipSuccess ? GN_OK : GN_ERR_HIP;
 }
 

@@ -7,8 +7,9 @@
 // * mean/M2 statistics merged with Chan, Golub and LeVeque's pairwise update
 //   ("Algorithms for computing the sample variance", 1983), operands always
 //   taken in a canonical order so that every lane agrees bitwise;
-// * an arrival counter barrier for co-resident workgroups with agent-scope
-//   release/acquire, bounded so that no wave can spin forever.
+// * an arrival-counter barrier for co-resident workgroups whose exchanged
+//   values travel through agent-scope atomics (no whole-L2 write-back or
+//   invalidate), bounded so that no wave can spin forever.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -202,20 +203,54 @@ __device__ inline Stat stat_of(const float (&v)[K], int valid) {
     return Stat{n, m, q};
 }
 
-// ---------------------------------------------------------------------------
-// barrier among co-resident workgroups
-// ---------------------------------------------------------------------------
-// Spin limit: far above any legitimate wait (the longest waits are a few
-// milliseconds); on expiry the wave stops waiting and raises *err so that the
-// host can report a broken co-residency assumption instead of hanging.
-constexpr uint32_t kSpinLimit = 1u << 26;
+// Spin limit of the barriers: far above any legitimate wait (the longest are a
+// few milliseconds); on expiry the wave stops waiting and raises *err, so that
+// a broken co-residency assumption shows as an error flag instead of a hang.
+constexpr uint32_t kSpinLimit = 1u << 25;
 
-// Every thread of the workgroup calls this.  Publishes the workgroup's prior
-// global writes (agent-scope release), adds one arrival to *ctr and waits
-// until *ctr reaches `target`; afterwards the writes of every arrived
-// workgroup are visible (agent-scope acquire).
-__device__ inline void group_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// ---------------------------------------------------------------------------
+// exchange between the workgroups of one launch without cache maintenance
+// ---------------------------------------------------------------------------
+// gfx950 has one L2 per XCD and these L2s are not coherent with each other, so
+// an agent-scope release/acquire fence writes back and invalidates the whole
+// L2 of the XCD (buffer_wbl2 / buffer_inv).  A kernel that synchronises a team
+// of workgroups once per slab would pay that for every workgroup at every
+// slab.  Instead the few values that cross workgroups (partial sums, the slab
+// statistics) are written and read with agent-scope relaxed atomics, which the
+// hardware performs at the device coherence point (sc1), and the barrier only
+// waits for the wave's own stores to complete before it signals arrival.
+__device__ inline void xstore(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float xload(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void xstore2(float2* p, float2 v) {
+    xstore(&p->x, v.x);
+    xstore(&p->y, v.y);
+}
+__device__ inline float2 xload2(const float2* p) { return make_float2(xload(&p->x), xload(&p->y)); }
+__device__ inline void xstore_stat(float4* p, const Stat& s) {
+    xstore(&p->x, s.n);
+    xstore(&p->y, s.mean);
+    xstore(&p->z, s.m2);
+}
+__device__ inline Stat xload_stat(const float4* p) { return Stat{xload(&p->x), xload(&p->y), xload(&p->z)}; }
+
+// Waits until every memory operation this wave issued has completed
+// (s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15) in the gfx9 encoding); the
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ inline void wait_own_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Barrier of `target` co-resident workgroups on counter *ctr (zero before the
+// launch).  Data published before it with xstore is visible to xload after it.
+// Every thread of the workgroup calls it.  Bounded like group_barrier.
+__device__ inline void team_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+    wait_own_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
         __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -229,7 +264,7 @@ __device__ inline void group_barrier(uint32_t* ctr, uint32_t target, uint32_t* e
         }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 }  // namespace gn

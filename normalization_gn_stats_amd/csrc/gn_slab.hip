@@ -1,0 +1,829 @@
+// gn_slab.hip -- GroupNorm forward and one-pass backward as cooperative
+// kernels over contiguous "slabs", with the grid capped at the number of
+// co-resident workgroups and overflow tiles handled by a grid-stride loop
+// (the design of apex PR #2018: the cooperative grid is capped at the
+// residency limit; resident blocks also process the extra activation tiles,
+// which join the same reductions in the same launch and are reloaded for the
+// dx store after the global reduction -- no fall back to a second pass).
+//
+// Slab: NHWC -> one sample n (HW pixels x C channels, all G groups
+// interleaved, 16 bytes = V channels of one group per chunk); NCHW -> one
+// slice (n, g), the contiguous D*HW elements of sample n in group g.
+//
+// A team of TW workgroups works on one slab at a time (teams walk slabs
+// k, k + nteams, ...).  Member m takes the slab's tiles m, m + TW, ... (phase
+// 1), keeps the last one in registers, and after the team barrier writes the
+// outputs of that tile from registers and of the earlier tiles by reloading
+// them in reverse order (the most recently read tiles first, the ones most
+// likely still in the Infinity Cache).
+//
+// Reductions (all in a fixed order, no float atomics):
+//  forward   per thread: exact two-pass (count, mean, M2) of each tile from
+//            registers, merged across tiles and threads with Chan et al.'s
+//            pairwise update;
+//  backward  per-(n, c) sums of dy and dy*xhat (xhat from the saved mean/rstd);
+//            per slice A = sum_c gamma_c*S1[n,c], B = sum_c gamma_c*S2[n,c]
+//            (the per-group reduction of the baracuda-kernels backward plan,
+//            regrouped by channel), dgamma_c = sum_n S2[n,c], dbeta_c = sum_n S1[n,c].
+#include "gn_device.hpp"
+#include "gn_internal.hpp"
+
+namespace gn {
+namespace {
+
+constexpr int kT = 256;
+constexpr int kNW = kT / kWave;
+
+struct SlabCfg {
+    int64_t N, C, HW, G, D;
+    int64_t n_slabs;   // NHWC: N, NCHW: N*G
+    int64_t tiles;     // tiles per slab
+    int64_t tpc;       // NCHW: tiles per channel plane
+    int32_t team;      // workgroups per team
+    int32_t nteams;
+    float eps;
+    int32_t want_dx;   // backward: write dx
+    float* dgamma;     // backward, one-slab case: written by the finalizers
+    float* dbeta;
+};
+
+// ============================================================================
+// NHWC
+// ============================================================================
+// Thread t owns chunk q = t % CPP of each pixel it visits (channels q*V ..
+// q*V+V-1, all in group q*V/D) and pixel t / CPP of each iteration; a tile is
+// R iterations, i.e. R*PPI consecutive pixels.
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void slab_nhwc_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                    const float* __restrict__ beta, T* __restrict__ y,
+                                                    float* mean, float* rstd, SlabCfg cfg, uint32_t* ctr,
+                                                    uint32_t* err, float4* part) {
+    constexpr int V = Vec<T>::V;
+    const int t = threadIdx.x;
+    const int CPP = (int)(cfg.C / V);
+    const int q = t % CPP;
+    const int pi = t / CPP;
+    const int PPI = kT / CPP;
+    const int64_t TP = (int64_t)PPI * R;
+    const int gq = (q * V) / (int)cfg.D;
+    const int team = blockIdx.x / cfg.team;
+    const int m = blockIdx.x - team * cfg.team;
+    const int G = (int)cfg.G;
+    __shared__ Stat sst[kT];
+
+    for (int64_t sb = team; sb < cfg.n_slabs; sb += cfg.nteams) {
+        const int64_t n = sb;
+        const T* xs = x + n * cfg.HW * cfg.C + q * V;
+        u4v reg[R];
+        Stat st = stat_empty();
+        int64_t last = -1;
+        // ---- phase 1: statistics of every tile of this member ----
+        for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
+            const int64_t p0 = tile * TP + pi;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int64_t p = min(p0 + (int64_t)j * PPI, cfg.HW - 1);   // in bounds; dropped below if past HW
+                reg[j] = ld16(xs + p * cfg.C);
+            }
+            float s = 0.f;
+            int cnt = 0;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                if (p0 + (int64_t)j * PPI < cfg.HW) {
+                    float v[V];
+                    Vec<T>::unpack(reg[j], v);
+#pragma unroll
+                    for (int k = 0; k < V; ++k) s += v[k];
+                    cnt += V;
+                }
+            }
+            if (cnt > 0) {
+                const float mt = s / (float)cnt;
+                float m2 = 0.f;
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    if (p0 + (int64_t)j * PPI < cfg.HW) {
+                        float v[V];
+                        Vec<T>::unpack(reg[j], v);
+#pragma unroll
+                        for (int k = 0; k < V; ++k) {
+                            const float d = v[k] - mt;
+                            m2 = fmaf(d, d, m2);
+                        }
+                    }
+                }
+                st = stat_merge(st, Stat{(float)cnt, mt, m2});
+            }
+            last = tile;
+        }
+        // ---- per-group merge inside the workgroup, in thread order ----
+        sst[t] = st;
+        __syncthreads();
+        const int qpg = (int)cfg.D / V;   // chunks per group
+        for (int g = t; g < G; g += kT) {
+            // the group's threads u = i*CPP + qq, visited in increasing u
+            Stat a = stat_empty();
+            for (int i = 0; i < PPI; ++i)
+                for (int qq = g * qpg; qq < (g + 1) * qpg; ++qq) a = stat_merge(a, sst[i * CPP + qq]);
+            xstore_stat(&part[(sb * cfg.team + m) * G + g], a);
+        }
+        __syncthreads();
+        team_barrier(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
+
+        // ---- distributed finalize: member m owns groups m, m + team, ... ----
+        for (int g = m; g < G; g += cfg.team) {
+            Stat a = stat_empty();
+            for (int i = t; i < cfg.team; i += kT) a = stat_merge(a, xload_stat(&part[(sb * cfg.team + i) * G + g]));
+            sst[t] = a;
+            __syncthreads();
+            for (int stride = kT / 2; stride > 0; stride >>= 1) {
+                if (t < stride) sst[t] = stat_merge(sst[t], sst[t + stride]);
+                __syncthreads();
+            }
+            if (t == 0) {
+                const Stat f = sst[0];
+                float var = f.m2 / (float)(cfg.D * cfg.HW);
+                var = var > 0.f ? var : 0.f;
+                xstore(&mean[n * G + g], f.mean);
+                xstore(&rstd[n * G + g], 1.0f / sqrtf(var + cfg.eps));
+            }
+            __syncthreads();
+        }
+        team_barrier(&ctr[sb * 2 + 1], (uint32_t)cfg.team, err);
+        if (y == nullptr) continue;
+
+        // ---- phase 2: normalize + affine; resident tile first, then reloads ----
+        const float mu = xload(&mean[n * G + gq]);
+        const float r = xload(&rstd[n * G + gq]);
+        float a[V], b[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int c = q * V + k;
+            a[k] = r * (gamma ? gamma[c] : 1.f);
+            b[k] = beta ? beta[c] : 0.f;
+        }
+        T* ys = y + n * cfg.HW * cfg.C + q * V;
+        for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
+            const int64_t p0 = tile * TP + pi;
+            if (tile != last) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int64_t p = min(p0 + (int64_t)j * PPI, cfg.HW - 1);
+                    reg[j] = ld16(xs + p * cfg.C);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int64_t p = p0 + (int64_t)j * PPI;
+                if (p < cfg.HW) {
+                    float v[V], o[V];
+                    Vec<T>::unpack(reg[j], v);
+#pragma unroll
+                    for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu, a[k], b[k]);
+                    st16(ys + p * cfg.C, Vec<T>::pack(o));
+                }
+            }
+        }
+    }
+}
+
+// part: [slab][member][C] float2 per-member channel sums; stot: [N][C] float2.
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, const T* __restrict__ x,
+                                                    const float* __restrict__ mean,
+                                                    const float* __restrict__ rstd,
+                                                    const float* __restrict__ gamma, T* __restrict__ dx,
+                                                    SlabCfg cfg, uint32_t* ctr, uint32_t* err, float2* part,
+                                                    float2* stot) {
+    constexpr int V = Vec<T>::V;
+    const int t = threadIdx.x;
+    const int CPP = (int)(cfg.C / V);
+    const int q = t % CPP;
+    const int pi = t / CPP;
+    const int PPI = kT / CPP;
+    const int64_t TP = (int64_t)PPI * R;
+    const int gq = (q * V) / (int)cfg.D;
+    const int team = blockIdx.x / cfg.team;
+    const int m = blockIdx.x - team * cfg.team;
+    const int G = (int)cfg.G;
+    const int C = (int)cfg.C;
+    __shared__ float2 red[kT];
+    __shared__ float2 lds_ch[kT * 8];   // [thread][k] per-thread channel sums (V <= 8)
+
+    for (int64_t sb = team; sb < cfg.n_slabs; sb += cfg.nteams) {
+        const int64_t n = sb;
+        const int64_t off = n * cfg.HW * cfg.C + q * V;
+        const float mu = mean[n * G + gq];
+        const float r = rstd[n * G + gq];
+        u4v rx[R], rd[R];
+        float s1[V], s2[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
+        int64_t last = -1;
+        // ---- phase 1: per-channel sums over every tile of this member ----
+        for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
+            const int64_t p0 = tile * TP + pi;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int64_t p = min(p0 + (int64_t)j * PPI, cfg.HW - 1);
+                rx[j] = ld16(x + off + p * cfg.C);
+                rd[j] = ld16(dy + off + p * cfg.C);
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                if (p0 + (int64_t)j * PPI < cfg.HW) {
+                    float xv[V], dv[V];
+                    Vec<T>::unpack(rx[j], xv);
+                    Vec<T>::unpack(rd[j], dv);
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        s1[k] += dv[k];
+                        s2[k] = fmaf(dv[k], (xv[k] - mu) * r, s2[k]);
+                    }
+                }
+            }
+            last = tile;
+        }
+        // ---- per-channel sums of the workgroup, in thread order ----
+#pragma unroll
+        for (int k = 0; k < V; ++k) lds_ch[t * 8 + k] = make_float2(s1[k], s2[k]);
+        __syncthreads();
+        for (int c = t; c < C; c += kT) {
+            const int cq = c / V, ck = c - cq * V;
+            float2 acc = make_float2(0.f, 0.f);
+            for (int i = 0; i < PPI; ++i) {
+                const float2 v = lds_ch[(i * CPP + cq) * 8 + ck];
+                acc.x += v.x;
+                acc.y += v.y;
+            }
+            xstore2(&part[(sb * cfg.team + m) * C + c], acc);
+        }
+        __syncthreads();
+        team_barrier(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
+
+        // ---- distributed finalize: member m owns channels m, m + team, ... ----
+        for (int c = m; c < C; c += cfg.team) {
+            float2 acc = make_float2(0.f, 0.f);
+            for (int i = t; i < cfg.team; i += kT) {
+                const float2 v = xload2(&part[(sb * cfg.team + i) * C + c]);
+                acc.x += v.x;
+                acc.y += v.y;
+            }
+            red[t] = acc;
+            __syncthreads();
+            for (int stride = kT / 2; stride > 0; stride >>= 1) {
+                if (t < stride) {
+                    red[t].x += red[t + stride].x;
+                    red[t].y += red[t + stride].y;
+                }
+                __syncthreads();
+            }
+            if (t == 0) {
+                xstore2(&stot[n * C + c], red[0]);
+                if (cfg.dbeta) cfg.dbeta[c] = red[0].x;     // one-slab case: final already
+                if (cfg.dgamma) cfg.dgamma[c] = red[0].y;
+            }
+            __syncthreads();
+        }
+        if (!cfg.want_dx) continue;   // uniform over the grid: no member waits below
+        team_barrier(&ctr[sb * 2 + 1], (uint32_t)cfg.team, err);
+
+        // ---- phase 2: dx = rstd*(gamma_c*dy - A/M - xhat*B/M) ----
+        float A = 0.f, B = 0.f;
+        for (int c = gq * (int)cfg.D; c < (gq + 1) * (int)cfg.D; ++c) {
+            const float2 v = xload2(&stot[n * C + c]);
+            const float ga = gamma ? gamma[c] : 1.f;
+            A = fmaf(ga, v.x, A);
+            B = fmaf(ga, v.y, B);
+        }
+        const float invM = 1.0f / (float)(cfg.D * cfg.HW);
+        A *= invM;
+        B *= invM;
+        float ga[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) ga[k] = gamma ? gamma[q * V + k] : 1.f;
+        for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
+            const int64_t p0 = tile * TP + pi;
+            if (tile != last) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int64_t p = min(p0 + (int64_t)j * PPI, cfg.HW - 1);
+                    rx[j] = ld16(x + off + p * cfg.C);
+                    rd[j] = ld16(dy + off + p * cfg.C);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int64_t p = p0 + (int64_t)j * PPI;
+                if (p < cfg.HW) {
+#pragma clang fp contract(off)
+                    float xv[V], dv[V], o[V];
+                    Vec<T>::unpack(rx[j], xv);
+                    Vec<T>::unpack(rd[j], dv);
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        const float xh = (xv[k] - mu) * r;
+                        const float gd = dv[k] * ga[k];
+                        o[k] = r * ((gd - A) - xh * B);
+                    }
+                    st16(dx + off + p * cfg.C, Vec<T>::pack(o));
+                }
+            }
+        }
+    }
+}
+
+// ============================================================================
+// NCHW
+// ============================================================================
+// Slab (n, g) is D contiguous channel planes of HW elements.  Tiles never
+// straddle a plane: tile = (plane cl, k) covers elements [k*TE, (k+1)*TE) of
+// plane cl, TE = kT*R*V; chunk j of thread t is element k*TE + (j*kT + t)*V.
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                    const float* __restrict__ beta, T* __restrict__ y,
+                                                    float* mean, float* rstd, SlabCfg cfg, uint32_t* ctr,
+                                                    uint32_t* err, float4* part) {
+    constexpr int V = Vec<T>::V;
+    constexpr int64_t TE = (int64_t)kT * R * V;
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1), wave = t / kWave;
+    const int team = blockIdx.x / cfg.team;
+    const int m = blockIdx.x - team * cfg.team;
+    __shared__ Stat sst[kT];
+
+    for (int64_t sb = team; sb < cfg.n_slabs; sb += cfg.nteams) {
+        const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
+        const int64_t base = (n * cfg.C + g * cfg.D) * cfg.HW;
+        u4v reg[R];
+        int64_t last = -1;
+        for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
+            const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+            const T* src = x + base + cl * cfg.HW;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);
+                reg[j] = ld16(src + e);
+            }
+            float s = 0.f;
+            int cnt = 0;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
+                    float v[V];
+                    Vec<T>::unpack(reg[j], v);
+#pragma unroll
+                    for (int k = 0; k < V; ++k) s += v[k];
+                    cnt += V;
+                }
+            }
+            Stat st = stat_empty();
+            if (cnt > 0) {
+                const float mt = s / (float)cnt;
+                float m2 = 0.f;
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
+                        float v[V];
+                        Vec<T>::unpack(reg[j], v);
+#pragma unroll
+                        for (int k = 0; k < V; ++k) {
+                            const float d = v[k] - mt;
+                            m2 = fmaf(d, d, m2);
+                        }
+                    }
+                }
+                st = Stat{(float)cnt, mt, m2};
+            }
+            st = wave_merge_strided(st, 1);
+            if (lane == 0) sst[wave] = st;
+            __syncthreads();
+            if (t == 0) {
+                Stat a = sst[0];
+                for (int w = 1; w < kNW; ++w) a = stat_merge(a, sst[w]);
+                xstore_stat(&part[sb * cfg.tiles + tile], a);
+            }
+            __syncthreads();
+            last = tile;
+        }
+        team_barrier(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
+        // every member merges all tile statistics of the slab in the same order
+        Stat a = stat_empty();
+        for (int64_t i = t; i < cfg.tiles; i += kT) a = stat_merge(a, xload_stat(&part[sb * cfg.tiles + i]));
+        sst[t] = a;
+        __syncthreads();
+        for (int stride = kT / 2; stride > 0; stride >>= 1) {
+            if (t < stride) sst[t] = stat_merge(sst[t], sst[t + stride]);
+            __syncthreads();
+        }
+        const Stat f = sst[0];
+        __syncthreads();
+        float var = f.m2 / (float)(cfg.D * cfg.HW);
+        var = var > 0.f ? var : 0.f;
+        const float mu = f.mean;
+        const float r = 1.0f / sqrtf(var + cfg.eps);
+        if (m == 0 && t == 0) {
+            mean[sb] = mu;
+            rstd[sb] = r;
+        }
+        if (y == nullptr) continue;
+        for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
+            const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+            const int64_t c = g * cfg.D + cl;
+            const float a_c = r * (gamma ? gamma[c] : 1.f);
+            const float b_c = beta ? beta[c] : 0.f;
+            const T* src = x + base + cl * cfg.HW;
+            T* dst = y + base + cl * cfg.HW;
+            if (tile != last) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);
+                    reg[j] = ld16(src + e);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int64_t e = k0 + (int64_t)(j * kT + t) * V;
+                if (e < cfg.HW) {
+                    float v[V], o[V];
+                    Vec<T>::unpack(reg[j], v);
+#pragma unroll
+                    for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu, a_c, b_c);
+                    st16(dst + e, Vec<T>::pack(o));
+                }
+            }
+        }
+    }
+}
+
+// part: [slab][tile] float2 (sum dy, sum dy*xhat of the tile); stot: [N][C] float2.
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, const T* __restrict__ x,
+                                                    const float* __restrict__ mean,
+                                                    const float* __restrict__ rstd,
+                                                    const float* __restrict__ gamma, T* __restrict__ dx,
+                                                    SlabCfg cfg, uint32_t* ctr, uint32_t* err, float2* part,
+                                                    float2* stot) {
+    constexpr int V = Vec<T>::V;
+    constexpr int64_t TE = (int64_t)kT * R * V;
+    const int t = threadIdx.x;
+    const int team = blockIdx.x / cfg.team;
+    const int m = blockIdx.x - team * cfg.team;
+    __shared__ float lds[kNW * 2];
+    __shared__ float2 chan[kT];
+
+    for (int64_t sb = team; sb < cfg.n_slabs; sb += cfg.nteams) {
+        const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
+        const int64_t base = (n * cfg.C + g * cfg.D) * cfg.HW;
+        const float mu = mean[sb], r = rstd[sb];
+        u4v rx[R], rd[R];
+        int64_t last = -1;
+        for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
+            const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+            const int64_t pb = base + cl * cfg.HW;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);
+                rx[j] = ld16(x + pb + e);
+                rd[j] = ld16(dy + pb + e);
+            }
+            float acc[2] = {0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
+                    float xv[V], dv[V];
+                    Vec<T>::unpack(rx[j], xv);
+                    Vec<T>::unpack(rd[j], dv);
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        acc[0] += dv[k];
+                        acc[1] = fmaf(dv[k], (xv[k] - mu) * r, acc[1]);
+                    }
+                }
+            }
+            block_sum<2, kNW>(acc, lds);
+            if (t == 0) xstore2(&part[sb * cfg.tiles + tile], make_float2(acc[0], acc[1]));
+            last = tile;
+        }
+        team_barrier(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
+        // per-channel sums of the slab (tile order), then A and B (channel order)
+        for (int cl = t; cl < cfg.D; cl += kT) {
+            float2 s = make_float2(0.f, 0.f);
+            for (int64_t k = 0; k < cfg.tpc; ++k) {
+                const float2 v = xload2(&part[sb * cfg.tiles + cl * cfg.tpc + k]);
+                s.x += v.x;
+                s.y += v.y;
+            }
+            if (cl < kT) chan[cl] = s;
+            if (m == 0) stot[n * cfg.C + g * cfg.D + cl] = s;
+        }
+        __syncthreads();
+        float A = 0.f, B = 0.f;
+        if (cfg.D <= kT) {
+            for (int cl = 0; cl < cfg.D; ++cl) {
+                const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
+                A = fmaf(ga, chan[cl].x, A);
+                B = fmaf(ga, chan[cl].y, B);
+            }
+        } else {
+            // more channels than threads: recompute each channel's sum (same order)
+            for (int cl = 0; cl < cfg.D; ++cl) {
+                float2 s = make_float2(0.f, 0.f);
+                for (int64_t k = 0; k < cfg.tpc; ++k) {
+                    const float2 v = xload2(&part[sb * cfg.tiles + cl * cfg.tpc + k]);
+                    s.x += v.x;
+                    s.y += v.y;
+                }
+                const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
+                A = fmaf(ga, s.x, A);
+                B = fmaf(ga, s.y, B);
+            }
+        }
+        __syncthreads();
+        if (!cfg.want_dx) continue;
+        const float invM = 1.0f / (float)(cfg.D * cfg.HW);
+        A *= invM;
+        B *= invM;
+        for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
+            const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+            const int64_t pb = base + cl * cfg.HW;
+            const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
+            if (tile != last) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);
+                    rx[j] = ld16(x + pb + e);
+                    rd[j] = ld16(dy + pb + e);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int64_t e = k0 + (int64_t)(j * kT + t) * V;
+                if (e < cfg.HW) {
+#pragma clang fp contract(off)
+                    float xv[V], dv[V], o[V];
+                    Vec<T>::unpack(rx[j], xv);
+                    Vec<T>::unpack(rd[j], dv);
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        const float xh = (xv[k] - mu) * r;
+                        const float gd = dv[k] * ga;
+                        o[k] = r * ((gd - A) - xh * B);
+                    }
+                    st16(dx + pb + e, Vec<T>::pack(o));
+                }
+            }
+        }
+    }
+}
+
+// ---- helpers ---------------------------------------------------------------
+__global__ void clear_words(uint32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// dbeta_c = sum_n stot[n][c].x, dgamma_c = sum_n stot[n][c].y (n in order)
+__global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ stot, int64_t N, int64_t C,
+                                                    float* __restrict__ dgamma, float* __restrict__ dbeta) {
+    const int64_t c = (int64_t)blockIdx.x * kT + threadIdx.x;
+    if (c >= C) return;
+    float a = 0.f, b = 0.f;
+#pragma unroll 8
+    for (int64_t n = 0; n < N; ++n) {
+        const float2 v = stot[n * C + c];
+        a += v.x;
+        b += v.y;
+    }
+    if (dbeta) dbeta[c] = a;
+    if (dgamma) dgamma[c] = b;
+}
+
+// ---- planning --------------------------------------------------------------
+constexpr int kRF = 16;   // fwd chunks per thread per tile
+constexpr int kRB = 8;    // bwd chunks (of x and of dy) per thread per tile
+
+size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int vec_elems(const Problem& p) { return p.elem_bytes == 4 ? 4 : 8; }
+
+struct Plan {
+    SlabCfg cfg;
+    int64_t grid;
+    int64_t resident;
+    size_t off_ctr, off_err, off_part, off_stot, total;
+};
+
+int64_t tiles_per_slab(const Problem& p, int R, int64_t* tpc) {
+    const int V = vec_elems(p);
+    if (p.layout == GN_NHWC) {
+        const int CPP = (int)(p.C / V);
+        const int64_t TP = (int64_t)(kT / CPP) * R;
+        *tpc = 0;
+        return (p.HW + TP - 1) / TP;
+    }
+    const int64_t TE = (int64_t)kT * R * V;
+    *tpc = (p.HW + TE - 1) / TE;
+    return p.D * *tpc;
+}
+
+template <typename K>
+int64_t resident_cap(K kernel, int cu_count) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, (const void*)kernel, kT, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        blocks = 1;
+    }
+    return (int64_t)(blocks > 0 ? blocks : 1) * cu_count;
+}
+
+// Workspace layout, sized for the largest team (the slab's tile count), so
+// that the size does not depend on the device.
+Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
+    Plan pl{};
+    int64_t tpc = 0;
+    const int64_t tiles = tiles_per_slab(p, backward ? kRB : kRF, &tpc);
+    const int64_t n_slabs = p.layout == GN_NHWC ? p.N : p.S;
+    int64_t team = tiles < team_max ? tiles : team_max;
+    if (team < 1) team = 1;
+    pl.cfg.tiles = tiles;
+    pl.cfg.tpc = tpc;
+    pl.cfg.n_slabs = n_slabs;
+    size_t off = 256;            // [0, 256): error word
+    pl.off_err = 0;
+    pl.off_ctr = off;
+    off += al((size_t)n_slabs * 2 * sizeof(uint32_t));
+    pl.off_part = off;
+    size_t part;
+    if (p.layout == GN_NHWC)
+        part = backward ? (size_t)n_slabs * team * p.C * sizeof(float2) : (size_t)n_slabs * team * p.G * sizeof(float4);
+    else
+        part = backward ? (size_t)n_slabs * tiles * sizeof(float2) : (size_t)n_slabs * tiles * sizeof(float4);
+    off += al(part);
+    pl.off_stot = off;
+    if (backward) off += al((size_t)p.N * p.C * sizeof(float2));
+    pl.total = off;
+    pl.cfg.team = (int32_t)team;
+    return pl;
+}
+
+// Zeroes the error word and the arrival counters (one fill kernel: no
+// memset node, so the call stays safe to capture in a graph).
+hipError_t clear_sync_words(char* ws, const Plan& pl, hipStream_t s) {
+    const int64_t words = (int64_t)(pl.off_ctr / sizeof(uint32_t)) + pl.cfg.n_slabs * 2;
+    int64_t blocks = (words + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(clear_words, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)ws, words);
+    return hipGetLastError();
+}
+
+template <typename K>
+hipError_t launch_coop(K kernel, int64_t grid, void** args, hipStream_t s, bool coop) {
+    if (coop) return hipLaunchCooperativeKernel((const void*)kernel, dim3((unsigned)grid), dim3(kT), args, 0, s);
+    return hipLaunchKernel((const void*)kernel, dim3((unsigned)grid), dim3(kT), args, 0, s);
+}
+
+template <typename T>
+hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
+    const int cus = device_info().cu_count;
+    const bool nhwc = p.layout == GN_NHWC;
+    auto kn = slab_nhwc_fwd<T, kRF>;
+    auto kc = slab_nchw_fwd<T, kRF>;
+    int64_t cap = nhwc ? resident_cap(kn, cus) : resident_cap(kc, cus);
+    if (l.max_resident_override > 0 && l.max_resident_override < cap) cap = l.max_resident_override;
+    Plan pl = layout_ws(p, false, cap);
+    SlabCfg cfg = pl.cfg;
+    cfg.N = p.N; cfg.C = p.C; cfg.HW = p.HW; cfg.G = p.G; cfg.D = p.D; cfg.eps = a.eps;
+    cfg.want_dx = 0; cfg.dgamma = nullptr; cfg.dbeta = nullptr;
+    int64_t nteams = cap / cfg.team;
+    if (nteams > cfg.n_slabs) nteams = cfg.n_slabs;
+    if (nteams < 1) nteams = 1;
+    cfg.nteams = (int32_t)nteams;
+    const int64_t grid = nteams * cfg.team;
+    char* ws = (char*)l.ws;
+    uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
+    uint32_t* err = (uint32_t*)(ws + pl.off_err);
+    float4* part = (float4*)(ws + pl.off_part);
+    hipError_t e;
+    if ((e = clear_sync_words(ws, pl, l.stream))) return e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    const T* x = (const T*)a.x;
+    T* y = (T*)a.y;
+    const float* gamma = a.gamma;
+    const float* beta = a.beta;
+    float* mean = a.mean;
+    float* rstd = a.rstd;
+    void* args[] = {&x, &gamma, &beta, &y, &mean, &rstd, &cfg, &ctr, &err, &part};
+    const bool coop = cfg.team > 1;
+    e = nhwc ? launch_coop(kn, grid, args, l.stream, coop) : launch_coop(kc, grid, args, l.stream, coop);
+    if (e) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    if (l.info) {
+        l.info->path = GN_PATH_SLAB;
+        l.info->kernels = 2;
+        l.info->grid = grid;
+        l.info->tiles = cfg.tiles * cfg.n_slabs;
+        l.info->resident_cap = cap;
+        l.info->team = cfg.team;
+    }
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
+    const int cus = device_info().cu_count;
+    const bool nhwc = p.layout == GN_NHWC;
+    auto kn = slab_nhwc_bwd<T, kRB>;
+    auto kc = slab_nchw_bwd<T, kRB>;
+    int64_t cap = nhwc ? resident_cap(kn, cus) : resident_cap(kc, cus);
+    if (l.max_resident_override > 0 && l.max_resident_override < cap) cap = l.max_resident_override;
+    Plan pl = layout_ws(p, true, cap);
+    SlabCfg cfg = pl.cfg;
+    cfg.N = p.N; cfg.C = p.C; cfg.HW = p.HW; cfg.G = p.G; cfg.D = p.D; cfg.eps = 0.f;
+    cfg.want_dx = (a.mask & GN_GRAD_DX) ? 1 : 0;
+    const bool one_slab_params = nhwc && p.N == 1;
+    cfg.dgamma = one_slab_params ? a.dgamma : nullptr;
+    cfg.dbeta = one_slab_params ? a.dbeta : nullptr;
+    int64_t nteams = cap / cfg.team;
+    if (nteams > cfg.n_slabs) nteams = cfg.n_slabs;
+    if (nteams < 1) nteams = 1;
+    cfg.nteams = (int32_t)nteams;
+    const int64_t grid = nteams * cfg.team;
+    char* ws = (char*)l.ws;
+    uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
+    uint32_t* err = (uint32_t*)(ws + pl.off_err);
+    float2* part = (float2*)(ws + pl.off_part);
+    float2* stot = (float2*)(ws + pl.off_stot);
+    hipError_t e;
+    if ((e = clear_sync_words(ws, pl, l.stream))) return e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    const T* dy = (const T*)a.dy;
+    const T* x = (const T*)a.x;
+    const float* mean = a.mean;
+    const float* rstd = a.rstd;
+    const float* gamma = a.gamma;
+    T* dx = (T*)a.dx;
+    void* args[] = {&dy, &x, &mean, &rstd, &gamma, &dx, &cfg, &ctr, &err, &part, &stot};
+    const bool coop = cfg.team > 1;
+    e = nhwc ? launch_coop(kn, grid, args, l.stream, coop) : launch_coop(kc, grid, args, l.stream, coop);
+    if (e) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    int kernels = 2;
+    if ((a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) && !one_slab_params) {
+        hipLaunchKernelGGL(params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream, stot, p.N,
+                           p.C, a.dgamma, a.dbeta);
+        if ((e = hipGetLastError())) return e;
+        ++kernels;
+    }
+    if (l.info) {
+        l.info->path = GN_PATH_SLAB;
+        l.info->kernels = kernels;
+        l.info->grid = grid;
+        l.info->tiles = cfg.tiles * cfg.n_slabs;
+        l.info->resident_cap = cap;
+        l.info->team = cfg.team;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+bool slab_ok(const Problem& p) {
+    const int V = vec_elems(p);
+    if (p.layout == GN_NHWC) {
+        if (p.C % V != 0 || p.D % V != 0) return false;
+        const int64_t cpp = p.C / V;
+        if (cpp < 1 || cpp > kT || (kT % cpp) != 0) return false;   // chunks per pixel divide the workgroup
+        return p.HW >= 1;
+    }
+    if (p.HW % V != 0) return false;   // every channel plane starts 16-byte aligned
+    return p.HW >= V && p.D <= 4096;
+}
+
+size_t slab_fwd_ws(const Problem& p) {
+    int64_t tpc;
+    return layout_ws(p, false, tiles_per_slab(p, kRF, &tpc)).total;
+}
+
+size_t slab_bwd_ws(const Problem& p, int32_t) {
+    int64_t tpc;
+    return layout_ws(p, true, tiles_per_slab(p, kRB, &tpc)).total;
+}
+
+hipError_t slab_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {
+    switch (p.dtype) {
+        case GN_F32: return fwd_t<float>(p, a, l);
+        case GN_F16: return fwd_t<_Float16>(p, a, l);
+        default: return fwd_t<__bf16>(p, a, l);
+    }
+}
+
+hipError_t slab_bwd(const Problem& p, const BwdArgs& a, const Launch& l) {
+    switch (p.dtype) {
+        case GN_F32: return bwd_t<float>(p, a, l);
+        case GN_F16: return bwd_t<_Float16>(p, a, l);
+        default: return bwd_t<__bf16>(p, a, l);
+    }
+}
+
+}  // namespace gn

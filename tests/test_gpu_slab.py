@@ -1,0 +1,67 @@
+"""GPU parity of the slab path (cooperative capped grid, grid-stride overflow
+tiles, one-pass backward) against the fp64 oracle.
+
+The apex PR #2018 bug was overflow tiles missing from the first accumulation
+loop: dgamma/dbeta went wrong while dx stayed within tolerance.  Every case
+here runs with the natural residency cap and with small forced caps, so that
+most tiles are overflow tiles -- accumulated in phase 1 and reloaded for the
+outputs -- and checks dgamma/dbeta as well as y and dx.
+"""
+import pytest
+import torch
+
+import normalization_gn_stats_amd as gn
+from normalization_gn_stats_amd import inputs
+from gpu_harness import check_against_oracle, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+W = inputs.Workload
+
+CASES = [
+    # NHWC: chunks of 16 bytes never straddle a group; ragged last tile
+    W("slab_nhwc_f16_c64_g8", 2, 64, 37, 29, 8, "f16", "nhwc"),
+    W("slab_nhwc_f32_c32_g4", 3, 32, 50, 41, 4, "f32", "nhwc"),
+    W("slab_nhwc_bf16_c128_g16", 1, 128, 64, 130, 16, "bf16", "nhwc", affine="n01"),
+    W("slab_nhwc_f16_c512_g32", 2, 512, 9, 23, 32, "f16", "nhwc"),
+    W("slab_nhwc_f16_c8_g1", 2, 8, 31, 33, 1, "f16", "nhwc"),
+    # NCHW: tiles never straddle a channel plane; several tiles per plane
+    W("slab_nchw_f32_c16_g4", 2, 16, 64, 70, 4, "f32", "nchw"),
+    W("slab_nchw_f16_c8_g2", 2, 8, 256, 300, 2, "f16", "nchw"),
+    W("slab_nchw_bf16_c12_g3", 3, 12, 40, 52, 3, "bf16", "nchw"),
+    inputs.TINY,
+]
+
+
+@pytest.mark.parametrize("cap", [0, 1, 3, 8], ids=lambda c: f"cap{c}")
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_slab_parity(wl, cap):
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    say(f"[slab] {wl.name} cap={cap}")
+    data = inputs.make_inputs(wl, seed=2)
+    out = run_gpu(wl, data, force_path="slab", max_resident=cap)
+    fp, bp = out["fwd_plan"], out["bwd_plan"]
+    assert fp.path == gn.GN_PATH_SLAB and bp.path == gn.GN_PATH_SLAB
+    if cap:
+        assert fp.grid <= cap and bp.grid <= cap
+        assert bp.resident_cap == cap
+    check_against_oracle(wl, data, out)
+
+
+def test_overflow_tiles_exist_under_a_cap():
+    """With the cap below the tile count, members own several tiles."""
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    wl = W("slab_overflow_nhwc", 1, 128, 64, 130, 16, "f16", "nhwc", affine="n01")
+    data = inputs.make_inputs(wl, seed=6)
+    out = run_gpu(wl, data, force_path="slab", max_resident=8)
+    bp = out["bwd_plan"]
+    assert bp.tiles > bp.grid          # overflow tiles: more tiles than workgroups
+    assert bp.team == 8
+    check_against_oracle(wl, data, out)
+
+
+def test_auto_selects_slab():
+    assert gn.select_path(True, 1, 128, 1024 * 2048, 16, 1, gn._lib.GN_NHWC) == gn.GN_PATH_SLAB
+    assert gn.select_path(False, 112, 64, 512 * 512, 8, 0, gn._lib.GN_NCHW) == gn.GN_PATH_SLAB
+    assert gn.select_path(False, 2, 32, 256, 8, 0, gn._lib.GN_NCHW) == gn.GN_PATH_SLAB

@@ -43,6 +43,34 @@ WORKLOADS = {
 DEFAULT = "rows_f16_4096x1024+8192x768"
 
 
+def source_fingerprint() -> str:
+    """sha256 over the kernel sources (csrc/), to tell whether byte counters
+    recorded in profiles/traffic.json still describe the kernels built now."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(HERE, "normalization_gn_stats_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel_name, grid):
+    """HBM bytes per launch of this kernel from profiles/traffic.json (rocprofv3
+    FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when
+    missing or taken on different kernel sources."""
+    try:
+        t = json.load(open(os.path.join(HERE, "profiles", "traffic.json")))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_fingerprint") != source_fingerprint():
+        return None
+    e = t.get("kernels", {}).get(f"{workload}|{kernel_name}|{grid}")
+    if not e or e.get("read_bytes") is None or e.get("write_bytes") is None:
+        return None
+    return int(e["read_bytes"] + e["write_bytes"])
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -56,6 +84,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the oracle CPU-baseline sample (0 disables it)")
     ap.add_argument("--force-path", default=None, choices=[None, "generic", "rows", "slab"])
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB three times (a known-size "
+                         "kernel that scales the rocprofv3 byte counters)")
     ap.add_argument("--mode", default="auto", choices=["auto", "graph", "eager"],
                     help="graph: the timed steps run as one captured HIP graph (no host in the loop)")
     args = ap.parse_args()
@@ -216,17 +247,32 @@ def main():
                 ("bwd", wl.bwd_min_bytes() - (2 * wl.C * 4 if sh["bplan"].kernels > 1 else 0), sh["bplan"]))):
             durs = [events[i][k][c][0].elapsed_time(events[i][k][c][1]) for i in range(K)]
             avg_ms = sum(durs) / len(durs)
+            kname = {("rows", "fwd"): "rows_fwd_k", ("rows", "bwd"): "rows_bwd_k",
+                     ("slab", "fwd"): f"slab_{wl.layout}_fwd", ("slab", "bwd"): f"slab_{wl.layout}_bwd"
+                     }.get((gn.PATH_NAMES[plan.path], kind))
             calls.append(dict(shape=wl.name, call=kind, path=gn.PATH_NAMES[plan.path], kernels=plan.kernels,
+                              kernel=kname, grid=plan.grid,
                               main_kernel_us=avg_ms * 1e3, main_kernel_bytes=nbytes,
                               main_kernel_gbs=nbytes / (avg_ms * 1e-3) / 1e9))
     dom = max(calls, key=lambda c: c["main_kernel_us"])
+    traffic = recorded_traffic(args.workload, dom["kernel"], dom["grid"]) if dom["kernel"] else None
     roofline = {"bound": "hbm", "achieved": round(dom["main_kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dom["main_kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(dom["main_kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "traffic_over_algorithmic": (round(traffic / dom["main_kernel_bytes"], 3) if traffic else None),
                 "kernel": f"{dom['call']} {dom['path']} main kernel on {dom['shape']}",
                 "avg_us": round(dom["main_kernel_us"], 3), "algorithmic_bytes": dom["main_kernel_bytes"],
                 "timing": ("HIP events recorded by the library on the call's stream around the main kernel, "
                            + ("K eager steps queued behind a GPU spin after the graph-timed region"
                               if mode == "graph" else "over the timed region"))}
+
+    if args.copy_calibration_mib > 0:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- oracle CPU baseline on a bounded sample -------------------------------
     cpu = None

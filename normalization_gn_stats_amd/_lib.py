@@ -11,7 +11,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "lib", "libgn_mi355x.so")
+# GN_LIB_PATH selects another build of the same library (e.g. one compiled
+# with different tile constants); by default the in-tree build is used.
+LIB_PATH = os.environ.get("GN_LIB_PATH") or os.path.join(HERE, "lib", "libgn_mi355x.so")
 
 GN_OK, GN_ERR_INVALID, GN_ERR_UNSUPPORTED, GN_ERR_WORKSPACE, GN_ERR_HIP = range(5)
 GN_F32, GN_F16, GN_BF16 = range(3)

@@ -247,17 +247,22 @@ __device__ inline void wait_own_stores() {
 }
 
 // Barrier of `target` co-resident workgroups on counter *ctr (zero before the
-// launch).  Data published before it with xstore is visible to xload after it.
-// Every thread of the workgroup calls it.  Bounded like group_barrier.
-__device__ inline void team_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+// launch), in two halves so that loads for later work can be issued between
+// them: team_arrive publishes (waits for this workgroup's stores, then counts
+// one arrival), team_wait blocks until every member has arrived.  Data
+// published before the arrival with xstore is visible to xload after the wait.
+// Every thread of the workgroup calls both.
+__device__ inline void team_arrive(uint32_t* ctr) {
     wait_own_stores();
     __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void team_wait(uint32_t* ctr, uint32_t target, uint32_t* err) {
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t spins = 0;
         while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             __builtin_amdgcn_s_sleep(2);
-            if (++spins > kSpinLimit) {
+            if (++spins > kSpinLimit) {   // bounded: report instead of hanging
                 __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
@@ -265,6 +270,10 @@ __device__ inline void team_barrier(uint32_t* ctr, uint32_t target, uint32_t* er
     }
     __syncthreads();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ inline void team_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+    team_arrive(ctr);
+    team_wait(ctr, target, err);
 }
 
 }  // namespace gn

@@ -110,31 +110,39 @@ __global__ __launch_bounds__(kT) void rows_fwd_k(const T* __restrict__ x, const 
 }
 
 // part: [G][NB][D] float2 (sum dy, sum dy*xhat) -- one row per workgroup.
-// Wave wi of group g handles samples n = wi + j*W (W waves per group), RB of
-// them per batch: the batch's x and dy are all loaded before any is used, so
-// a wave has RB slices in flight instead of walking them one round trip at a
-// time.
-template <typename T, int NV, int RB>
+//
+// CS waves share a slice: wave w works on row slot w / CS and column part
+// w % CS, i.e. the 16-byte vectors [part*NV*64, (part+1)*NV*64) of the slice,
+// so that wide slices keep few registers per lane.  A workgroup takes blocks
+// of RPB = (4/CS)*RB consecutive samples (blocks b, b + NB, ...); all RB
+// slices of a wave in a block are loaded before any is used.  The per-slice
+// sums A and B are wave sums (CS = 1) or wave sums added in part order
+// through LDS (CS > 1).
+template <typename T, int NV, int RB, int CS>
 __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const T* __restrict__ x,
                                                  const float* __restrict__ mean, const float* __restrict__ rstd,
                                                  const float* __restrict__ gamma, T* __restrict__ dx,
                                                  float2* __restrict__ part, int64_t N, int64_t G, int64_t C,
                                                  int D, int NB, int want_dx, int want_params) {
     constexpr int V = Vec<T>::V;
+    constexpr int SLOTS = kNW / CS;
+    constexpr int RPB = SLOTS * RB;
     constexpr bool kHoistGamma = NV * V <= 16;   // gamma of the lane's columns kept in registers
     extern __shared__ float2 lds_cols[];         // [D] when want_params
+    __shared__ float2 red[RB][kNW];              // per-wave (a, b) of each slice of the block
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int slot = wave / CS;
+    const int cpart = wave - slot * CS;
     const int64_t g = blockIdx.y;   // grid: x = NB workgroups per group, y = group
     const int b = blockIdx.x;
-    const int64_t W = (int64_t)NB * kNW;
-    const int64_t wi = (int64_t)b * kNW + wave;
     const int nvec = D / V;
+    const int vbase = cpart * NV * kWave;
     const float invD = 1.0f / (float)D;
     const float* gcol = gamma ? gamma + g * D : nullptr;
 
     float gam[kHoistGamma ? NV : 1][kHoistGamma ? V : 1];
-    // gamma of the V columns of vector j (registers, or float4 loads that hit L1/L2)
+    // gamma of the V columns of vector vi (registers, or float4 loads that hit L1/L2)
     auto gamma_vec = [&](int j, int vi, float (&gv)[V]) {
         if constexpr (kHoistGamma) {
 #pragma unroll
@@ -156,18 +164,18 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
         for (int k = 0; k < V; ++k) { cs1[j][k] = 0.f; cs2[j][k] = 0.f; }
 
     bool first = true;
-    for (int64_t n0 = wi; n0 < N; n0 += (int64_t)RB * W) {
-        // Branch-free loads of the whole batch: rows past N re-read row N-1 and
-        // lanes past the slice re-read its last vector; both are dropped below.
+    for (int64_t blk = b; blk * RPB < N; blk += NB) {   // uniform over the workgroup
+        // Branch-free loads of the block: rows past N re-read row N-1 and
+        // vectors past the slice re-read its last vector; both are dropped below.
         u4v rx[RB][NV], rd[RB][NV];
         float mu[RB], rs[RB];
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const int64_t n = min(n0 + r * W, N - 1);
+            const int64_t n = min(blk * RPB + r * SLOTS + slot, N - 1);
             const int64_t base = n * C + g * D;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                const int vi = min(j * kWave + lane, nvec - 1);
+                const int vi = min(vbase + j * kWave + lane, nvec - 1);
                 rx[r][j] = ld16(x + base + (int64_t)vi * V);
                 rd[r][j] = ld16(dy + base + (int64_t)vi * V);
             }
@@ -175,10 +183,10 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
             rs[r] = rstd[n * G + g];
         }
         if constexpr (kHoistGamma) {
-            if (first) {   // issued after the first batch's activations
+            if (first) {   // issued after the first block's activations
 #pragma unroll
                 for (int j = 0; j < NV; ++j) {
-                    const int vc = min(j * kWave + lane, nvec - 1);
+                    const int vc = min(vbase + j * kWave + lane, nvec - 1);
 #pragma unroll
                     for (int k = 0; k < V; k += 4) {
                         float4 q = gcol ? *reinterpret_cast<const float4*>(gcol + vc * V + k)
@@ -191,12 +199,12 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
         first = false;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            if (n0 + r * W >= N) {   // uniform: a row past the end contributes nothing
+            if (blk * RPB + r * SLOTS + slot >= N) {   // uniform per wave: contributes nothing
 #pragma unroll
                 for (int j = 0; j < NV; ++j) { rx[r][j] = u4v{0u, 0u, 0u, 0u}; rd[r][j] = u4v{0u, 0u, 0u, 0u}; }
             }
         }
-        // per-slice sums A, B and the running column sums
+        // per-slice partial sums of this wave and the running column sums
         float a[RB], bb[RB];
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
             bb[r] = 0.f;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                const int vi = j * kWave + lane;
+                const int vi = vbase + j * kWave + lane;
                 if (vi >= nvec) continue;
                 float xv[V], dv[V], gv[V];
                 Vec<T>::unpack(rx[r][j], xv);
@@ -221,23 +229,47 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
                 }
             }
         }
-        if (!want_dx) continue;
+        if (!want_dx) continue;   // kernel argument: uniform
         float A[RB], B[RB];
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            A[r] = wave_sum(a[r]) * invD;
-            B[r] = wave_sum(bb[r]) * invD;
+            A[r] = wave_sum(a[r]);
+            B[r] = wave_sum(bb[r]);
+        }
+        if constexpr (CS > 1) {
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < RB; ++r) red[r][wave] = make_float2(A[r], B[r]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                float2 t = red[r][slot * CS];
+#pragma unroll
+                for (int p = 1; p < CS; ++p) {
+                    t.x += red[r][slot * CS + p].x;
+                    t.y += red[r][slot * CS + p].y;
+                }
+                A[r] = t.x;
+                B[r] = t.y;
+            }
+            __syncthreads();
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const int64_t n = n0 + r * W;
+            A[r] *= invD;
+            B[r] *= invD;
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t n = blk * RPB + r * SLOTS + slot;
             if (n >= N) continue;
             const int64_t base = n * C + g * D;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 // gamma*dy rounded as it entered A, so that equal terms cancel exactly
 #pragma clang fp contract(off)
-                const int vi = j * kWave + lane;
+                const int vi = vbase + j * kWave + lane;
                 if (vi >= nvec) continue;
                 float xv[V], dv[V], gv[V], o[V];
                 Vec<T>::unpack(rx[r][j], xv);
@@ -254,16 +286,17 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
         }
     }
     if (!want_params) return;
-    // waves add their column sums into LDS in wave order
-    for (int w = 0; w < kNW; ++w) {
-        if (wave == w) {
+    // column sums of the row slots added into LDS in slot order (the parts of
+    // one slot cover disjoint columns)
+    for (int sl = 0; sl < SLOTS; ++sl) {
+        if (slot == sl) {
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                const int vi = j * kWave + lane;
+                const int vi = vbase + j * kWave + lane;
                 if (vi >= nvec) continue;
 #pragma unroll
                 for (int k = 0; k < V; ++k) {
-                    float2 c = w == 0 ? make_float2(0.f, 0.f) : lds_cols[vi * V + k];
+                    float2 c = sl == 0 ? make_float2(0.f, 0.f) : lds_cols[vi * V + k];
                     c.x += cs1[j][k];
                     c.y += cs2[j][k];
                     lds_cols[vi * V + k] = c;
@@ -313,8 +346,15 @@ __global__ __launch_bounds__(kT) void rows_colsum_k(const float2* __restrict__ p
     }
 }
 
-constexpr int kMaxNV = 8;
+#ifndef GN_ROWS_BWD_TARGET_WG
+#define GN_ROWS_BWD_TARGET_WG 512
+#endif
+#ifndef GN_ROWS_BWD_RB
+#define GN_ROWS_BWD_RB 4
+#endif
 
+// 16-byte vectors per lane of the forward (one wave per slice): 1, 2, 4, 8, or
+// 0 when the slice does not fit.
 int nv_for(const Problem& p) {
     const int V = p.elem_bytes == 4 ? 4 : 8;
     const int64_t nvec = p.D / V;
@@ -322,15 +362,33 @@ int nv_for(const Problem& p) {
     return nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 8 ? 8 : 0;
 }
 
+// Backward split: CS waves per slice (1, 2, 4) and NV vectors per lane, the
+// fewest waves that keep NV <= 2; wider slices go to CS = 4 with NV 4 or 8.
+struct BwdShape { int cs, nv, rb; };
+BwdShape bwd_shape(const Problem& p) {
+    const int V = p.elem_bytes == 4 ? 4 : 8;
+    const int64_t nvec = p.D / V;
+    for (int cs : {1, 2, 4}) {
+        const int64_t nv = (nvec + cs * kWave - 1) / (cs * kWave);
+        if (nv <= 2) return BwdShape{cs, nv <= 1 ? 1 : 2, GN_ROWS_BWD_RB};
+    }
+    const int64_t nv = (nvec + 4 * kWave - 1) / (4 * kWave);
+    if (nv <= 4) return BwdShape{4, 4, 2};
+    if (nv <= 8) return BwdShape{4, 8, 1};
+    return BwdShape{0, 0, 0};
+}
+
 // Workgroups per group in the backward: about two per compute unit of an
-// MI355X (256 CUs) in total, and at least ~4 slices per wave.  A constant, so
+// MI355X (256 CUs) in total, fewer when the samples run out.  A constant, so
 // that the workspace size does not depend on the device queried.
-constexpr int64_t kBwdTargetWG = 512;
+constexpr int64_t kBwdTargetWG = GN_ROWS_BWD_TARGET_WG;
 
 int rows_nb(const Problem& p) {
+    const BwdShape sh = bwd_shape(p);
+    const int64_t rpb = (int64_t)(kNW / (sh.cs > 0 ? sh.cs : 1)) * (sh.rb > 0 ? sh.rb : 1);
     int64_t target = kBwdTargetWG / (p.G < 1 ? 1 : p.G);
     if (target < 1) target = 1;
-    int64_t need = (p.N + kNW * 4 - 1) / (kNW * 4);
+    int64_t need = (p.N + rpb - 1) / rpb;
     if (need < 1) need = 1;
     return (int)(need < target ? need : target);
 }
@@ -352,9 +410,8 @@ hipError_t fwd_nv(const Problem& p, const FwdArgs& a, const Launch& l) {
     return hipSuccess;
 }
 
-template <typename T, int NV>
-hipError_t bwd_nv(const Problem& p, const BwdArgs& a, const Launch& l) {
-    constexpr int RB = NV <= 2 ? 4 : NV <= 4 ? 2 : 1;   // slices per wave in flight
+template <typename T, int NV, int RB, int CS>
+hipError_t bwd_launch(const Problem& p, const BwdArgs& a, const Launch& l) {
     const int NB = rows_nb(p);
     const bool params = (a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) != 0;
     const unsigned grid = (unsigned)NB;
@@ -362,9 +419,9 @@ hipError_t bwd_nv(const Problem& p, const BwdArgs& a, const Launch& l) {
     float2* part = (float2*)l.ws;
     hipError_t e;
     if ((e = record(l.ev_begin, l.stream))) return e;
-    hipLaunchKernelGGL((rows_bwd_k<T, NV, RB>), dim3(grid, (unsigned)p.G), dim3(kT), lds, l.stream, (const T*)a.dy, (const T*)a.x,
-                       a.mean, a.rstd, a.gamma, (T*)a.dx, part, p.N, p.G, p.C, (int)p.D, NB,
-                       (a.mask & GN_GRAD_DX) ? 1 : 0, params ? 1 : 0);
+    hipLaunchKernelGGL((rows_bwd_k<T, NV, RB, CS>), dim3(grid, (unsigned)p.G), dim3(kT), lds, l.stream,
+                       (const T*)a.dy, (const T*)a.x, a.mean, a.rstd, a.gamma, (T*)a.dx, part, p.N, p.G, p.C,
+                       (int)p.D, NB, (a.mask & GN_GRAD_DX) ? 1 : 0, params ? 1 : 0);
     if ((e = hipGetLastError())) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
     int kernels = 1;
@@ -395,11 +452,17 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
 
 template <typename T>
 hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
-    switch (nv_for(p)) {
-        case 1: return bwd_nv<T, 1>(p, a, l);
-        case 2: return bwd_nv<T, 2>(p, a, l);
-        case 4: return bwd_nv<T, 4>(p, a, l);
-        default: return bwd_nv<T, 8>(p, a, l);
+    constexpr int RBS = GN_ROWS_BWD_RB;
+    const BwdShape sh = bwd_shape(p);
+    switch (sh.cs * 100 + sh.nv) {
+        case 101: return bwd_launch<T, 1, RBS, 1>(p, a, l);
+        case 102: return bwd_launch<T, 2, RBS, 1>(p, a, l);
+        case 201: return bwd_launch<T, 1, RBS, 2>(p, a, l);
+        case 202: return bwd_launch<T, 2, RBS, 2>(p, a, l);
+        case 401: return bwd_launch<T, 1, RBS, 4>(p, a, l);
+        case 402: return bwd_launch<T, 2, RBS, 4>(p, a, l);
+        case 404: return bwd_launch<T, 4, 2, 4>(p, a, l);
+        default: return bwd_launch<T, 8, 1, 4>(p, a, l);
     }
 }
 
@@ -409,8 +472,7 @@ bool rows_ok(const Problem& p) {
     if (p.HW != 1) return false;
     const int V = p.elem_bytes == 4 ? 4 : 8;
     if (p.D % V != 0 || p.C % V != 0) return false;   // every slice starts 16-byte aligned
-    if (nv_for(p) == 0) return false;                 // slice fits the register budget
-    (void)kMaxNV;
+    if (nv_for(p) == 0 || bwd_shape(p).cs == 0) return false;   // slice fits the register budget
     return true;
 }
 

@@ -39,6 +39,7 @@ struct SlabCfg {
     int64_t n_slabs;   // NHWC: N, NCHW: N*G
     int64_t tiles;     // tiles per slab
     int64_t tpc;       // NCHW: tiles per channel plane
+    int64_t pstride;   // NCHW: partial slots per slab (tiles rounded up to whole 128-byte lines)
     int32_t team;      // workgroups per team
     int32_t nteams;
     float eps;
@@ -339,124 +340,297 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
 // Slab (n, g) is D contiguous channel planes of HW elements.  Tiles never
 // straddle a plane: tile = (plane cl, k) covers elements [k*TE, (k+1)*TE) of
 // plane cl, TE = kT*R*V; chunk j of thread t is element k*TE + (j*kT + t)*V.
+//
+// Between arriving at a slab's barrier and waiting on it, a member issues the
+// loads of its first tile of the team's next slab, so that HBM keeps streaming
+// while the team synchronises (prefetch into a second register tile).
+template <typename T, int R>
+__device__ inline void nchw_load_tile(const T* __restrict__ src, const SlabCfg& cfg, int64_t sb, int64_t tile,
+                                      u4v (&dst)[R]) {
+    constexpr int V = Vec<T>::V;
+    constexpr int64_t TE = (int64_t)kT * R * V;
+    const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
+    const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+    const T* p = src + (n * cfg.C + g * cfg.D + cl) * cfg.HW;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t e = min(k0 + (int64_t)(j * kT + (int)threadIdx.x) * V, cfg.HW - V);   // in bounds
+        dst[j] = ld16(p + e);
+    }
+}
+
+// Phase 1 of the forward for slab sb: statistics of member m's tiles, one
+// (count, mean, M2) partial per tile -- an exact two-pass over the tile in
+// registers: workgroup sum -> tile mean -> workgroup sum of squared
+// deviations.  The last tile stays in buf; its channel's gamma/beta are
+// fetched here so that phase 2 does not wait for them.  Returns the last tile
+// index (-1 if the member has none).
+template <typename T, int R>
+__device__ inline int64_t nchw_fwd_phase1(const T* __restrict__ x, const float* __restrict__ gamma,
+                                          const float* __restrict__ beta, const SlabCfg& cfg, int64_t sb, int m,
+                                          u4v (&buf)[R], float2& gb, float4* part, float* lds) {
+    constexpr int V = Vec<T>::V;
+    constexpr int64_t TE = (int64_t)kT * R * V;
+    const int t = threadIdx.x;
+    int64_t last = -1;
+    for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
+        const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+        nchw_load_tile<T, R>(x, cfg, sb, tile, buf);
+        const int64_t c = (sb - (sb / cfg.G) * cfg.G) * cfg.D + cl;
+        gb = make_float2(gamma ? gamma[c] : 1.f, beta ? beta[c] : 0.f);
+        const int64_t rem = cfg.HW - k0;
+        const float cnt = (float)(rem < TE ? rem : TE);   // elements of this tile
+        float acc[1] = {0.f};
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
+                float v[V];
+                Vec<T>::unpack(buf[j], v);
+#pragma unroll
+                for (int k = 0; k < V; ++k) acc[0] += v[k];
+            }
+        }
+        block_sum<1, kNW>(acc, lds);
+        const float mt = acc[0] / cnt;
+        float q[1] = {0.f};
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
+                float v[V];
+                Vec<T>::unpack(buf[j], v);
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float d = v[k] - mt;
+                    q[0] = fmaf(d, d, q[0]);
+                }
+            }
+        }
+        block_sum<1, kNW>(q, lds);
+        if (t == 0) xstore_stat(&part[sb * cfg.pstride + tile], Stat{cnt, mt, q[0]});
+        last = tile;
+    }
+    return last;
+}
+
+// Phase 2 of the forward for slab sb: every member combines all tile
+// partials in the same order -- slab mean = sum(n_i*mean_i)/sum(n_i), then
+// M2 = sum(M2_i + n_i*(mean_i - mean)^2) (the parallel form of Chan et al.'s
+// update), each a fixed-order workgroup sum -- then writes y for its tiles
+// (the last one from buf, the earlier ones reloaded in reverse order).
+template <typename T, int R>
+__device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __restrict__ gamma,
+                                       const float* __restrict__ beta, T* __restrict__ y, float* mean,
+                                       float* rstd, const SlabCfg& cfg, int64_t sb, int m, int64_t last,
+                                       u4v (&buf)[R], float2 gb, const float4* part, float* lds) {
+    constexpr int V = Vec<T>::V;
+    constexpr int64_t TE = (int64_t)kT * R * V;
+    const int t = threadIdx.x;
+    const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
+    // Plain (L2-cacheable) loads: this slab's partial block was written once,
+    // through to the coherence point, before the barrier, and it shares no
+    // 128-byte line with other slabs, so no XCD can hold a stale copy; the
+    // first member of an XCD to read a line brings it into that XCD's L2.
+    float sums[2] = {0.f, 0.f};   // sum n_i*mean_i, sum n_i
+    for (int64_t i = t; i < cfg.tiles; i += kT) {
+        const float4 v = part[sb * cfg.pstride + i];
+        sums[0] = fmaf(v.x, v.y, sums[0]);
+        sums[1] += v.x;
+    }
+    block_sum<2, kNW>(sums, lds);
+    const float mu = sums[0] / sums[1];
+    float m2[1] = {0.f};
+    for (int64_t i = t; i < cfg.tiles; i += kT) {
+        const float4 v = part[sb * cfg.pstride + i];
+        const float d = v.y - mu;
+        m2[0] += fmaf(v.x * d, d, v.z);
+    }
+    block_sum<1, kNW>(m2, lds);
+    float var = m2[0] / (float)(cfg.D * cfg.HW);
+    var = var > 0.f ? var : 0.f;
+    const float r = 1.0f / sqrtf(var + cfg.eps);
+    if (m == 0 && t == 0) {
+        mean[sb] = mu;
+        rstd[sb] = r;
+    }
+    if (y == nullptr) return;
+    const int64_t base = (n * cfg.C + g * cfg.D) * cfg.HW;
+    for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
+        const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+        float2 p = gb;
+        if (tile != last) {
+            nchw_load_tile<T, R>(x, cfg, sb, tile, buf);
+            const int64_t c = g * cfg.D + cl;
+            p = make_float2(gamma ? gamma[c] : 1.f, beta ? beta[c] : 0.f);
+        }
+        const float a_c = r * p.x;
+        const float b_c = p.y;
+        T* dst = y + base + cl * cfg.HW;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int64_t e = k0 + (int64_t)(j * kT + t) * V;
+            if (e < cfg.HW) {
+                float v[V], o[V];
+                Vec<T>::unpack(buf[j], v);
+#pragma unroll
+                for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu, a_c, b_c);
+                st16(dst + e, Vec<T>::pack(o));
+            }
+        }
+    }
+}
+
+// Two slabs in flight per team: after arriving at slab s's barrier a member
+// runs phase 1 of the team's next slab (into the second register tile) and
+// arrives there too, and only then waits on s -- the barrier latency of s is
+// covered by the next slab's loads.
 template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
                                                     const float* __restrict__ beta, T* __restrict__ y,
                                                     float* mean, float* rstd, SlabCfg cfg, uint32_t* ctr,
                                                     uint32_t* err, float4* part) {
+    const int team = blockIdx.x / cfg.team;
+    const int m = blockIdx.x - team * cfg.team;
+    __shared__ float lds[kNW * 2];
+    u4v cur[R], nxt[R];
+    float2 gcur = make_float2(1.f, 0.f), gnxt = gcur;
+    int64_t sb = team;
+    if (sb >= cfg.n_slabs) return;   // uniform over the team
+    int64_t last = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, sb, m, cur, gcur, part, lds);
+    team_arrive(&ctr[sb * 2 + 0]);
+    while (true) {
+        const int64_t nsb = sb + cfg.nteams;
+        int64_t nlast = -1;
+        if (nsb < cfg.n_slabs) {
+            nlast = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, nsb, m, nxt, gnxt, part, lds);
+            team_arrive(&ctr[nsb * 2 + 0]);
+        }
+        team_wait(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
+        nchw_fwd_phase2<T, R>(x, gamma, beta, y, mean, rstd, cfg, sb, m, last, cur, gcur, part, lds);
+        if (nsb >= cfg.n_slabs) break;
+#pragma unroll
+        for (int j = 0; j < R; ++j) cur[j] = nxt[j];
+        gcur = gnxt;
+        last = nlast;
+        sb = nsb;
+    }
+}
+
+// Phase 1 of the backward for slab sb: per-tile sums of dy and dy*xhat; the
+// last tile of x and dy stays in bx, bd.
+template <typename T, int R>
+__device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __restrict__ x,
+                                          const float* __restrict__ mean, const float* __restrict__ rstd,
+                                          const SlabCfg& cfg, int64_t sb, int m, u4v (&bx)[R], u4v (&bd)[R],
+                                          float2* part, float* lds) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
     const int t = threadIdx.x;
-    const int lane = t & (kWave - 1), wave = t / kWave;
-    const int team = blockIdx.x / cfg.team;
-    const int m = blockIdx.x - team * cfg.team;
-    __shared__ Stat sst[kT];
+    const float mu = mean[sb], r = rstd[sb];
+    int64_t last = -1;
+    for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
+        const int64_t k0 = (tile - (tile / cfg.tpc) * cfg.tpc) * TE;
+        nchw_load_tile<T, R>(x, cfg, sb, tile, bx);
+        nchw_load_tile<T, R>(dy, cfg, sb, tile, bd);
+        float acc[2] = {0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
+                float xv[V], dv[V];
+                Vec<T>::unpack(bx[j], xv);
+                Vec<T>::unpack(bd[j], dv);
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    acc[0] += dv[k];
+                    acc[1] = fmaf(dv[k], (xv[k] - mu) * r, acc[1]);
+                }
+            }
+        }
+        block_sum<2, kNW>(acc, lds);
+        if (t == 0) xstore2(&part[sb * cfg.pstride + tile], make_float2(acc[0], acc[1]));
+        last = tile;
+    }
+    return last;
+}
 
-    for (int64_t sb = team; sb < cfg.n_slabs; sb += cfg.nteams) {
-        const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
-        const int64_t base = (n * cfg.C + g * cfg.D) * cfg.HW;
-        u4v reg[R];
-        int64_t last = -1;
-        for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
-            const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
-            const T* src = x + base + cl * cfg.HW;
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);
-                reg[j] = ld16(src + e);
-            }
-            float s = 0.f;
-            int cnt = 0;
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
-                    float v[V];
-                    Vec<T>::unpack(reg[j], v);
-#pragma unroll
-                    for (int k = 0; k < V; ++k) s += v[k];
-                    cnt += V;
-                }
-            }
-            Stat st = stat_empty();
-            if (cnt > 0) {
-                const float mt = s / (float)cnt;
-                float m2 = 0.f;
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
-                        float v[V];
-                        Vec<T>::unpack(reg[j], v);
-#pragma unroll
-                        for (int k = 0; k < V; ++k) {
-                            const float d = v[k] - mt;
-                            m2 = fmaf(d, d, m2);
-                        }
-                    }
-                }
-                st = Stat{(float)cnt, mt, m2};
-            }
-            st = wave_merge_strided(st, 1);
-            if (lane == 0) sst[wave] = st;
-            __syncthreads();
-            if (t == 0) {
-                Stat a = sst[0];
-                for (int w = 1; w < kNW; ++w) a = stat_merge(a, sst[w]);
-                xstore_stat(&part[sb * cfg.tiles + tile], a);
-            }
-            __syncthreads();
-            last = tile;
-        }
-        team_barrier(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
-        // every member merges all tile statistics of the slab in the same order
-        Stat a = stat_empty();
-        for (int64_t i = t; i < cfg.tiles; i += kT) a = stat_merge(a, xload_stat(&part[sb * cfg.tiles + i]));
-        sst[t] = a;
+constexpr int kStage = 1024;   // tile partials staged in LDS per step of the channel sums
+
+// Phase 2 of the backward for slab sb: per-channel sums of the slab (each in
+// tile order, partials staged through LDS), A and B (channel order), then dx
+// for the member's tiles (last from registers, the others reloaded).
+template <typename T, int R>
+__device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __restrict__ x,
+                                       const float* __restrict__ mean, const float* __restrict__ rstd,
+                                       const float* __restrict__ gamma, T* __restrict__ dx, const SlabCfg& cfg,
+                                       int64_t sb, int m, int64_t last, u4v (&bx)[R], u4v (&bd)[R],
+                                       const float2* part, float2* stot, float2* stage, float2* chan) {
+    constexpr int V = Vec<T>::V;
+    constexpr int64_t TE = (int64_t)kT * R * V;
+    const int t = threadIdx.x;
+    const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
+    const float mu = mean[sb], r = rstd[sb];
+    // channel sums: tiles cl*tpc .. cl*tpc+tpc-1 belong to channel cl
+    float2 run = make_float2(0.f, 0.f);   // thread cl's running sum (cl < D <= kT)
+    for (int64_t s0 = 0; s0 < cfg.tiles; s0 += kStage) {
+        const int64_t cnt = cfg.tiles - s0 < kStage ? cfg.tiles - s0 : kStage;
+        // plain loads of this slab's partial block: see nchw_fwd_phase2
+        for (int64_t i = t; i < cnt; i += kT) stage[i] = part[sb * cfg.pstride + s0 + i];
         __syncthreads();
-        for (int stride = kT / 2; stride > 0; stride >>= 1) {
-            if (t < stride) sst[t] = stat_merge(sst[t], sst[t + stride]);
-            __syncthreads();
-        }
-        const Stat f = sst[0];
-        __syncthreads();
-        float var = f.m2 / (float)(cfg.D * cfg.HW);
-        var = var > 0.f ? var : 0.f;
-        const float mu = f.mean;
-        const float r = 1.0f / sqrtf(var + cfg.eps);
-        if (m == 0 && t == 0) {
-            mean[sb] = mu;
-            rstd[sb] = r;
-        }
-        if (y == nullptr) continue;
-        for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
-            const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
-            const int64_t c = g * cfg.D + cl;
-            const float a_c = r * (gamma ? gamma[c] : 1.f);
-            const float b_c = beta ? beta[c] : 0.f;
-            const T* src = x + base + cl * cfg.HW;
-            T* dst = y + base + cl * cfg.HW;
-            if (tile != last) {
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);
-                    reg[j] = ld16(src + e);
-                }
+        if (t < cfg.D) {
+            const int64_t lo = (int64_t)t * cfg.tpc, hi = lo + cfg.tpc;
+            for (int64_t i = lo > s0 ? lo : s0; i < hi && i < s0 + cnt; ++i) {
+                run.x += stage[i - s0].x;
+                run.y += stage[i - s0].y;
             }
+        }
+        __syncthreads();
+    }
+    if (t < cfg.D) {
+        chan[t] = run;
+        if (m == 0) stot[n * cfg.C + g * cfg.D + t] = run;
+    }
+    __syncthreads();
+    float A = 0.f, B = 0.f;
+    for (int cl = 0; cl < cfg.D; ++cl) {
+        const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
+        A = fmaf(ga, chan[cl].x, A);
+        B = fmaf(ga, chan[cl].y, B);
+    }
+    __syncthreads();
+    if (!cfg.want_dx) return;
+    const float invM = 1.0f / (float)(cfg.D * cfg.HW);
+    A *= invM;
+    B *= invM;
+    const int64_t base = (n * cfg.C + g * cfg.D) * cfg.HW;
+    for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
+        const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+        const int64_t pb = base + cl * cfg.HW;
+        const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
+        if (tile != last) {
+            nchw_load_tile<T, R>(x, cfg, sb, tile, bx);
+            nchw_load_tile<T, R>(dy, cfg, sb, tile, bd);
+        }
 #pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const int64_t e = k0 + (int64_t)(j * kT + t) * V;
-                if (e < cfg.HW) {
-                    float v[V], o[V];
-                    Vec<T>::unpack(reg[j], v);
+        for (int j = 0; j < R; ++j) {
+            const int64_t e = k0 + (int64_t)(j * kT + t) * V;
+            if (e < cfg.HW) {
+#pragma clang fp contract(off)
+                float xv[V], dv[V], o[V];
+                Vec<T>::unpack(bx[j], xv);
+                Vec<T>::unpack(bd[j], dv);
 #pragma unroll
-                    for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu, a_c, b_c);
-                    st16(dst + e, Vec<T>::pack(o));
+                for (int k = 0; k < V; ++k) {
+                    const float xh = (xv[k] - mu) * r;
+                    const float gd = dv[k] * ga;
+                    o[k] = r * ((gd - A) - xh * B);
                 }
+                st16(dx + pb + e, Vec<T>::pack(o));
             }
         }
     }
 }
 
 // part: [slab][tile] float2 (sum dy, sum dy*xhat of the tile); stot: [N][C] float2.
+// Same two-slab pipeline as the forward.  Requires D <= kT (checked on the host).
 template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, const T* __restrict__ x,
                                                     const float* __restrict__ mean,
@@ -464,116 +638,30 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
                                                     const float* __restrict__ gamma, T* __restrict__ dx,
                                                     SlabCfg cfg, uint32_t* ctr, uint32_t* err, float2* part,
                                                     float2* stot) {
-    constexpr int V = Vec<T>::V;
-    constexpr int64_t TE = (int64_t)kT * R * V;
-    const int t = threadIdx.x;
     const int team = blockIdx.x / cfg.team;
     const int m = blockIdx.x - team * cfg.team;
     __shared__ float lds[kNW * 2];
     __shared__ float2 chan[kT];
-
-    for (int64_t sb = team; sb < cfg.n_slabs; sb += cfg.nteams) {
-        const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
-        const int64_t base = (n * cfg.C + g * cfg.D) * cfg.HW;
-        const float mu = mean[sb], r = rstd[sb];
-        u4v rx[R], rd[R];
-        int64_t last = -1;
-        for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
-            const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
-            const int64_t pb = base + cl * cfg.HW;
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);
-                rx[j] = ld16(x + pb + e);
-                rd[j] = ld16(dy + pb + e);
-            }
-            float acc[2] = {0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
-                    float xv[V], dv[V];
-                    Vec<T>::unpack(rx[j], xv);
-                    Vec<T>::unpack(rd[j], dv);
-#pragma unroll
-                    for (int k = 0; k < V; ++k) {
-                        acc[0] += dv[k];
-                        acc[1] = fmaf(dv[k], (xv[k] - mu) * r, acc[1]);
-                    }
-                }
-            }
-            block_sum<2, kNW>(acc, lds);
-            if (t == 0) xstore2(&part[sb * cfg.tiles + tile], make_float2(acc[0], acc[1]));
-            last = tile;
+    __shared__ float2 stage[kStage];
+    u4v cx[R], cd[R], nx[R], nd[R];
+    int64_t sb = team;
+    if (sb >= cfg.n_slabs) return;   // uniform over the team
+    int64_t last = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, sb, m, cx, cd, part, lds);
+    team_arrive(&ctr[sb * 2 + 0]);
+    while (true) {
+        const int64_t nsb = sb + cfg.nteams;
+        int64_t nlast = -1;
+        if (nsb < cfg.n_slabs) {
+            nlast = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, nsb, m, nx, nd, part, lds);
+            team_arrive(&ctr[nsb * 2 + 0]);
         }
-        team_barrier(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
-        // per-channel sums of the slab (tile order), then A and B (channel order)
-        for (int cl = t; cl < cfg.D; cl += kT) {
-            float2 s = make_float2(0.f, 0.f);
-            for (int64_t k = 0; k < cfg.tpc; ++k) {
-                const float2 v = xload2(&part[sb * cfg.tiles + cl * cfg.tpc + k]);
-                s.x += v.x;
-                s.y += v.y;
-            }
-            if (cl < kT) chan[cl] = s;
-            if (m == 0) stot[n * cfg.C + g * cfg.D + cl] = s;
-        }
-        __syncthreads();
-        float A = 0.f, B = 0.f;
-        if (cfg.D <= kT) {
-            for (int cl = 0; cl < cfg.D; ++cl) {
-                const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
-                A = fmaf(ga, chan[cl].x, A);
-                B = fmaf(ga, chan[cl].y, B);
-            }
-        } else {
-            // more channels than threads: recompute each channel's sum (same order)
-            for (int cl = 0; cl < cfg.D; ++cl) {
-                float2 s = make_float2(0.f, 0.f);
-                for (int64_t k = 0; k < cfg.tpc; ++k) {
-                    const float2 v = xload2(&part[sb * cfg.tiles + cl * cfg.tpc + k]);
-                    s.x += v.x;
-                    s.y += v.y;
-                }
-                const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
-                A = fmaf(ga, s.x, A);
-                B = fmaf(ga, s.y, B);
-            }
-        }
-        __syncthreads();
-        if (!cfg.want_dx) continue;
-        const float invM = 1.0f / (float)(cfg.D * cfg.HW);
-        A *= invM;
-        B *= invM;
-        for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
-            const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
-            const int64_t pb = base + cl * cfg.HW;
-            const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
-            if (tile != last) {
+        team_wait(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
+        nchw_bwd_phase2<T, R>(dy, x, mean, rstd, gamma, dx, cfg, sb, m, last, cx, cd, part, stot, stage, chan);
+        if (nsb >= cfg.n_slabs) break;
 #pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);
-                    rx[j] = ld16(x + pb + e);
-                    rd[j] = ld16(dy + pb + e);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const int64_t e = k0 + (int64_t)(j * kT + t) * V;
-                if (e < cfg.HW) {
-#pragma clang fp contract(off)
-                    float xv[V], dv[V], o[V];
-                    Vec<T>::unpack(rx[j], xv);
-                    Vec<T>::unpack(rd[j], dv);
-#pragma unroll
-                    for (int k = 0; k < V; ++k) {
-                        const float xh = (xv[k] - mu) * r;
-                        const float gd = dv[k] * ga;
-                        o[k] = r * ((gd - A) - xh * B);
-                    }
-                    st16(dx + pb + e, Vec<T>::pack(o));
-                }
-            }
-        }
+        for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }
+        last = nlast;
+        sb = nsb;
     }
 }
 
@@ -600,8 +688,23 @@ __global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ s
 }
 
 // ---- planning --------------------------------------------------------------
-constexpr int kRF = 16;   // fwd chunks per thread per tile
-constexpr int kRB = 8;    // bwd chunks (of x and of dy) per thread per tile
+// 16-byte chunks per thread per tile (of x, and of dy in the backward)
+#ifndef GN_SLAB_NHWC_RF
+#define GN_SLAB_NHWC_RF 16
+#endif
+#ifndef GN_SLAB_NHWC_RB
+#define GN_SLAB_NHWC_RB 8
+#endif
+#ifndef GN_SLAB_NCHW_RF
+#define GN_SLAB_NCHW_RF 32
+#endif
+#ifndef GN_SLAB_NCHW_RB
+#define GN_SLAB_NCHW_RB 16
+#endif
+int tile_chunks(const Problem& p, bool backward) {
+    if (p.layout == GN_NHWC) return backward ? GN_SLAB_NHWC_RB : GN_SLAB_NHWC_RF;
+    return backward ? GN_SLAB_NCHW_RB : GN_SLAB_NCHW_RF;
+}
 
 size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -642,12 +745,13 @@ int64_t resident_cap(K kernel, int cu_count) {
 Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
     Plan pl{};
     int64_t tpc = 0;
-    const int64_t tiles = tiles_per_slab(p, backward ? kRB : kRF, &tpc);
+    const int64_t tiles = tiles_per_slab(p, tile_chunks(p, backward), &tpc);
     const int64_t n_slabs = p.layout == GN_NHWC ? p.N : p.S;
     int64_t team = tiles < team_max ? tiles : team_max;
     if (team < 1) team = 1;
     pl.cfg.tiles = tiles;
     pl.cfg.tpc = tpc;
+    pl.cfg.pstride = (tiles + 15) / 16 * 16;   // 16 slots: whole 128-byte lines for float4 and float2
     pl.cfg.n_slabs = n_slabs;
     size_t off = 256;            // [0, 256): error word
     pl.off_err = 0;
@@ -658,7 +762,8 @@ Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
     if (p.layout == GN_NHWC)
         part = backward ? (size_t)n_slabs * team * p.C * sizeof(float2) : (size_t)n_slabs * team * p.G * sizeof(float4);
     else
-        part = backward ? (size_t)n_slabs * tiles * sizeof(float2) : (size_t)n_slabs * tiles * sizeof(float4);
+        part = backward ? (size_t)n_slabs * pl.cfg.pstride * sizeof(float2)
+                        : (size_t)n_slabs * pl.cfg.pstride * sizeof(float4);
     off += al(part);
     pl.off_stot = off;
     if (backward) off += al((size_t)p.N * p.C * sizeof(float2));
@@ -687,8 +792,8 @@ template <typename T>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
-    auto kn = slab_nhwc_fwd<T, kRF>;
-    auto kc = slab_nchw_fwd<T, kRF>;
+    auto kn = slab_nhwc_fwd<T, GN_SLAB_NHWC_RF>;
+    auto kc = slab_nchw_fwd<T, GN_SLAB_NCHW_RF>;
     int64_t cap = nhwc ? resident_cap(kn, cus) : resident_cap(kc, cus);
     if (l.max_resident_override > 0 && l.max_resident_override < cap) cap = l.max_resident_override;
     Plan pl = layout_ws(p, false, cap);
@@ -733,8 +838,8 @@ template <typename T>
 hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
-    auto kn = slab_nhwc_bwd<T, kRB>;
-    auto kc = slab_nchw_bwd<T, kRB>;
+    auto kn = slab_nhwc_bwd<T, GN_SLAB_NHWC_RB>;
+    auto kc = slab_nchw_bwd<T, GN_SLAB_NCHW_RB>;
     int64_t cap = nhwc ? resident_cap(kn, cus) : resident_cap(kc, cus);
     if (l.max_resident_override > 0 && l.max_resident_override < cap) cap = l.max_resident_override;
     Plan pl = layout_ws(p, true, cap);
@@ -797,17 +902,17 @@ bool slab_ok(const Problem& p) {
         return p.HW >= 1;
     }
     if (p.HW % V != 0) return false;   // every channel plane starts 16-byte aligned
-    return p.HW >= V && p.D <= 4096;
+    return p.HW >= V && p.D <= kT;      // channel sums of a slab: one thread per channel
 }
 
 size_t slab_fwd_ws(const Problem& p) {
     int64_t tpc;
-    return layout_ws(p, false, tiles_per_slab(p, kRF, &tpc)).total;
+    return layout_ws(p, false, tiles_per_slab(p, tile_chunks(p, false), &tpc)).total;
 }
 
 size_t slab_bwd_ws(const Problem& p, int32_t) {
     int64_t tpc;
-    return layout_ws(p, true, tiles_per_slab(p, kRB, &tpc)).total;
+    return layout_ws(p, true, tiles_per_slab(p, tile_chunks(p, true), &tpc)).total;
 }
 
 hipError_t slab_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {

@@ -65,3 +65,35 @@ def test_auto_selects_slab():
     assert gn.select_path(True, 1, 128, 1024 * 2048, 16, 1, gn._lib.GN_NHWC) == gn.GN_PATH_SLAB
     assert gn.select_path(False, 112, 64, 512 * 512, 8, 0, gn._lib.GN_NCHW) == gn.GN_PATH_SLAB
     assert gn.select_path(False, 2, 32, 256, 8, 0, gn._lib.GN_NCHW) == gn.GN_PATH_SLAB
+
+
+@pytest.mark.parametrize("wl", [W("reuse_nchw_f32", 3, 16, 64, 70, 4, "f32", "nchw"),
+                                W("reuse_nhwc_f16", 2, 64, 37, 29, 8, "f16", "nhwc"),
+                                W("reuse_rows_bf16", 300, 2048, 1, 1, 2, "bf16", "nchw")],
+                         ids=lambda w: w.name)
+def test_same_workspace_new_inputs(wl):
+    """Back-to-back calls through the same buffers and workspace with different
+    inputs: no call may see values (partial sums, counters) of the previous
+    one -- identical inputs would hide that, so each call draws new ones."""
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    dev = torch.device("cuda", 0)
+    first = inputs.make_inputs(wl, seed=10)
+    bufs = {k: v.to(dev) for k, v in first.items()}
+    N, C, HW, G = wl.N, wl.C, wl.HW, wl.G
+    code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
+    lay = gn.layout_of(bufs["x"])
+    fws = torch.empty(gn.forward_workspace_size(N, C, HW, G, code, lay) + 1, dtype=torch.uint8, device=dev)
+    bws = torch.empty(gn.backward_workspace_size(N, C, HW, G, code, lay, 7) + 1, dtype=torch.uint8, device=dev)
+    out = dict(y=torch.empty_like(bufs["x"]), mean=torch.empty(N * G, device=dev), rstd=torch.empty(N * G, device=dev),
+               dx=torch.empty_like(bufs["x"]), dgamma=torch.empty(C, device=dev), dbeta=torch.empty(C, device=dev))
+    for seed in (11, 12, 13):
+        data = inputs.make_inputs(wl, seed=seed)
+        for k in bufs:
+            bufs[k].copy_(data[k])
+        say(f"[reuse] {wl.name} seed={seed}")
+        gn.forward_into(bufs["x"], bufs["gamma"], bufs["beta"], G, wl.eps, out["y"], out["mean"], out["rstd"], fws)
+        gn.backward_into(bufs["dy"], bufs["x"], out["mean"], out["rstd"], bufs["gamma"], G, 7, out["dx"],
+                         out["dgamma"], out["dbeta"], bws)
+        torch.cuda.synchronize()
+        check_against_oracle(wl, data, out)

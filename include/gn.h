@@ -71,8 +71,12 @@ typedef enum gn_path {
     GN_PATH_AUTO = 0,
     GN_PATH_GENERIC = 1,  /* any shape/alignment: partial sums, finalize, elementwise */
     GN_PATH_ROWS = 2,     /* HW == 1: one wavefront per slice, slice kept in registers */
-    GN_PATH_SLAB = 3      /* cooperative capped grid over contiguous slabs with
+    GN_PATH_SLAB = 3,     /* cooperative capped grid over contiguous slabs with
                              grid-stride overflow tiles (one-pass backward) */
+    GN_PATH_STREAM = 4    /* NHWC: a few launches of one tile per workgroup
+                             (statistics, fixed-order combine, outputs); the
+                             planner's choice when a sample has more tiles than
+                             the co-resident grid holds */
 } gn_path;
 
 /* What a call ran (filled when gn_options.info is not NULL). */
@@ -92,8 +96,10 @@ typedef struct gn_options {
                                        workgroups (forces overflow tiles) */
     gn_plan_info* info;             /* host pointer, may be NULL */
     void* event_begin;              /* hipEvent_t recorded on `stream` right before
-                                       the call's main kernel, or NULL */
-    void* event_end;                /* hipEvent_t recorded right after it, or NULL */
+                                       the call's main kernel (GN_PATH_STREAM:
+                                       before its first kernel), or NULL */
+    void* event_end;                /* hipEvent_t recorded right after it
+                                       (GN_PATH_STREAM: after its last), or NULL */
 } gn_options;
 
 /* Workspace bytes gn_forward needs for these arguments (0 is possible).

@@ -17,15 +17,16 @@ import math
 
 from . import _lib
 from ._lib import (GN_BF16, GN_F16, GN_F32, GN_GRAD_DBETA, GN_GRAD_DGAMMA, GN_GRAD_DX, GN_NCHW, GN_NHWC,
-                   GN_PATH_AUTO, GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB, PATH_NAMES, GNError, PlanInfo)
+                   GN_PATH_AUTO, GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB, GN_PATH_STREAM, PATH_NAMES, GNError,
+                   PlanInfo)
 
 __all__ = ["forward", "backward", "forward_into", "backward_into", "forward_workspace_size",
            "backward_workspace_size", "select_path", "layout_of", "GNError", "PlanInfo",
            "GN_GRAD_DX", "GN_GRAD_DGAMMA", "GN_GRAD_DBETA", "GN_PATH_AUTO", "GN_PATH_GENERIC",
-           "GN_PATH_ROWS", "GN_PATH_SLAB", "PATH_NAMES"]
+           "GN_PATH_ROWS", "GN_PATH_SLAB", "GN_PATH_STREAM", "PATH_NAMES"]
 
 _PATHS = {None: GN_PATH_AUTO, "auto": GN_PATH_AUTO, "generic": GN_PATH_GENERIC, "rows": GN_PATH_ROWS,
-          "slab": GN_PATH_SLAB}
+          "slab": GN_PATH_SLAB, "stream": GN_PATH_STREAM}
 
 
 def _torch():

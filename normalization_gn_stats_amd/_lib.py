@@ -19,8 +19,9 @@ GN_OK, GN_ERR_INVALID, GN_ERR_UNSUPPORTED, GN_ERR_WORKSPACE, GN_ERR_HIP = range(
 GN_F32, GN_F16, GN_BF16 = range(3)
 GN_NCHW, GN_NHWC = range(2)
 GN_GRAD_DX, GN_GRAD_DGAMMA, GN_GRAD_DBETA = 1, 2, 4
-GN_PATH_AUTO, GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB = range(4)
-PATH_NAMES = {GN_PATH_AUTO: "auto", GN_PATH_GENERIC: "generic", GN_PATH_ROWS: "rows", GN_PATH_SLAB: "slab"}
+GN_PATH_AUTO, GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB, GN_PATH_STREAM = range(5)
+PATH_NAMES = {GN_PATH_AUTO: "auto", GN_PATH_GENERIC: "generic", GN_PATH_ROWS: "rows", GN_PATH_SLAB: "slab",
+              GN_PATH_STREAM: "stream"}
 
 # every symbol include/gn.h declares
 EXPORTED = ("gn_forward_workspace_size", "gn_forward", "gn_backward_workspace_size", "gn_backward",

@@ -86,13 +86,15 @@ int32_t forced(const gn_options* o) { return o ? o->force_path : GN_PATH_AUTO; }
 // Path for these shapes assuming 16-byte aligned pointers; -1 if the forced
 // path cannot serve them.
 int32_t plan(const Problem& p, bool backward, const gn_options* opts) {
-    (void)backward;
     const int32_t f = forced(opts);
     if (f == GN_PATH_GENERIC) return GN_PATH_GENERIC;
     if (f == GN_PATH_ROWS) return gn::rows_ok(p) ? GN_PATH_ROWS : -1;
     if (f == GN_PATH_SLAB) return gn::slab_ok(p) ? GN_PATH_SLAB : -1;
+    if (f == GN_PATH_STREAM) return gn::stream_ok(p) ? GN_PATH_STREAM : -1;
     if (f != GN_PATH_AUTO) return -1;
     if (gn::rows_ok(p)) return GN_PATH_ROWS;
+    // an NHWC sample too large for the co-resident grid streams instead
+    if (gn::stream_ok(p) && !gn::slab_resident(p, backward)) return GN_PATH_STREAM;
     if (gn::slab_ok(p)) return GN_PATH_SLAB;
     return GN_PATH_GENERIC;
 }
@@ -101,6 +103,7 @@ size_t fwd_ws(const Problem& p, int32_t path) {
     switch (path) {
         case GN_PATH_ROWS: return gn::rows_fwd_ws(p);
         case GN_PATH_SLAB: return gn::slab_fwd_ws(p);
+        case GN_PATH_STREAM: return gn::stream_fwd_ws(p);
         default: return gn::generic_fwd_ws(p);
     }
 }
@@ -109,6 +112,7 @@ size_t bwd_ws(const Problem& p, int32_t mask, int32_t path) {
     switch (path) {
         case GN_PATH_ROWS: return gn::rows_bwd_ws(p, mask);
         case GN_PATH_SLAB: return gn::slab_bwd_ws(p, mask);
+        case GN_PATH_STREAM: return gn::stream_bwd_ws(p, mask);
         default: return gn::generic_bwd_ws(p, mask);
     }
 }
@@ -187,6 +191,7 @@ gn_status gn_forward(const void* x, const float* gamma, const float* beta, void*
     if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
     hipError_t e = path == GN_PATH_ROWS ? gn::rows_fwd(p, a, l)
                  : path == GN_PATH_SLAB ? gn::slab_fwd(p, a, l)
+                 : path == GN_PATH_STREAM ? gn::stream_fwd(p, a, l)
                                         : gn::generic_fwd(p, a, l);
     return e == hipSuccess ? GN_OK : GN_ERR_HIP;
 }
@@ -228,6 +233,7 @@ gn_status gn_backward(const void* dy, const void* x, const float* mean, const fl
     if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
     hipError_t e = path == GN_PATH_ROWS ? gn::rows_bwd(p, a, l)
                  : path == GN_PATH_SLAB ? gn::slab_bwd(p, a, l)
+                 : path == GN_PATH_STREAM ? gn::stream_bwd(p, a, l)
                                         : gn::generic_bwd(p, a, l);
     return e == hipSuccess ? GN_OK : GN_ERR_HIP;
 }

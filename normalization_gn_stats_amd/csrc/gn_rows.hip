@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_k(const T* __restrict__ x, const 
         float o[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) o[k] = fmaf(v[j][k] - mu, r * ga[j][k], be[j][k]);
-        st16(y + base + (int64_t)vi * V, Vec<T>::pack(o));
+        st16_nt(y + base + (int64_t)vi * V, Vec<T>::pack(o));
     }
 }
 
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
                     const float gd = dv[k] * gv[k];
                     o[k] = rs[r] * ((gd - A[r]) - xh * B[r]);
                 }
-                st16(dx + base + (int64_t)vi * V, Vec<T>::pack(o));
+                st16_nt(dx + base + (int64_t)vi * V, Vec<T>::pack(o));
             }
         }
     }

@@ -54,11 +54,54 @@ struct SlabCfg {
 // Thread t owns chunk q = t % CPP of each pixel it visits (channels q*V ..
 // q*V+V-1, all in group q*V/D) and pixel t / CPP of each iteration; a tile is
 // R iterations, i.e. R*PPI consecutive pixels.
+//
+// Tiles are handed out dynamically (an atomic tile counter per slab), so that
+// faster workgroups take more of them -- the barrier then waits for less.  The
+// partial statistics are kept per tile and merged in tile order, so the result
+// does not depend on which workgroup took which tile.  Each member keeps its
+// last tile in registers and flags it resident; after the barriers, phase 2
+// hands out the remaining tiles from a second counter, in reverse order.
+//
+// Sync words per slab: [0] barrier 1, [1] barrier 2, [2] phase-1 tile counter,
+// [3] phase-2 tile counter; res[slab][tile] = 1 for resident tiles.
+
+// Takes the next tile of a counter (thread 0 draws, the workgroup shares it).
+__device__ inline int64_t grab_tile(uint32_t* counter, int* s_slot) {
+    if (threadIdx.x == 0) *s_slot = (int)__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t tile = *s_slot;
+    __syncthreads();
+    return tile;
+}
+
+// Phase-2 tiles: the second counter runs over all tiles in reverse order
+// (most recently read first); resident tiles (flag set in phase 1, before the
+// barriers) are skipped.  Returns -1 when the counter is exhausted.  The flags
+// are read with plain loads: written once, through to the coherence point,
+// before the first barrier and not read by anyone before it.
+__device__ inline int64_t grab_phase2_tile(uint32_t* counter, const uint32_t* res, int64_t tiles, int* s_slot) {
+    while (true) {
+        const int64_t k = grab_tile(counter, s_slot);
+        if (k >= tiles) return -1;
+        const int64_t tile = tiles - 1 - k;
+        if (!res[tile]) return tile;
+    }
+}
+
+template <typename T, int R>
+__device__ inline void nhwc_load(const T* __restrict__ src, int64_t HW, int64_t C, int64_t p0, int PPI, u4v (&dst)[R]) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t p = min(p0 + (int64_t)j * PPI, HW - 1);   // in bounds; dropped by the caller if past HW
+        dst[j] = ld16_nt(src + p * C);
+    }
+}
+
 template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nhwc_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
                                                     const float* __restrict__ beta, T* __restrict__ y,
                                                     float* mean, float* rstd, SlabCfg cfg, uint32_t* ctr,
-                                                    uint32_t* err, float4* part) {
+                                                    uint32_t* err, float4* part, uint32_t* res) {
     constexpr int V = Vec<T>::V;
     const int t = threadIdx.x;
     const int CPP = (int)(cfg.C / V);
@@ -67,37 +110,42 @@ __global__ __launch_bounds__(kT) void slab_nhwc_fwd(const T* __restrict__ x, con
     const int PPI = kT / CPP;
     const int64_t TP = (int64_t)PPI * R;
     const int gq = (q * V) / (int)cfg.D;
+    const int qpg = (int)cfg.D / V;   // chunks per group
     const int team = blockIdx.x / cfg.team;
     const int m = blockIdx.x - team * cfg.team;
     const int G = (int)cfg.G;
     __shared__ Stat sst[kT];
+    __shared__ float lds[kNW * 2];
+    __shared__ int s_tile;
 
     for (int64_t sb = team; sb < cfg.n_slabs; sb += cfg.nteams) {
         const int64_t n = sb;
+        uint32_t* sw = ctr + sb * 4;
+        const uint32_t* rs_flags = res + sb * cfg.tiles;
         const T* xs = x + n * cfg.HW * cfg.C + q * V;
-        u4v reg[R];
-        Stat st = stat_empty();
+        u4v cur[R], nxt[R];
         int64_t last = -1;
-        // ---- phase 1: statistics of every tile of this member ----
-        for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
+        // ---- phase 1: statistics of every tile this member takes; the next
+        // tile is drawn and its loads issued before the current one is used ----
+        int64_t tile = grab_tile(&sw[2], &s_tile);
+        if (tile < cfg.tiles) nhwc_load<T, R>(xs, cfg.HW, cfg.C, tile * TP + pi, PPI, cur);
+        while (tile < cfg.tiles) {
+            const int64_t ntile = grab_tile(&sw[2], &s_tile);
+            if (ntile < cfg.tiles) nhwc_load<T, R>(xs, cfg.HW, cfg.C, ntile * TP + pi, PPI, nxt);
             const int64_t p0 = tile * TP + pi;
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const int64_t p = min(p0 + (int64_t)j * PPI, cfg.HW - 1);   // in bounds; dropped below if past HW
-                reg[j] = ld16(xs + p * cfg.C);
-            }
             float s = 0.f;
             int cnt = 0;
 #pragma unroll
             for (int j = 0; j < R; ++j) {
                 if (p0 + (int64_t)j * PPI < cfg.HW) {
                     float v[V];
-                    Vec<T>::unpack(reg[j], v);
+                    Vec<T>::unpack(cur[j], v);
 #pragma unroll
                     for (int k = 0; k < V; ++k) s += v[k];
                     cnt += V;
                 }
             }
+            Stat st = stat_empty();
             if (cnt > 0) {
                 const float mt = s / (float)cnt;
                 float m2 = 0.f;
@@ -105,7 +153,7 @@ __global__ __launch_bounds__(kT) void slab_nhwc_fwd(const T* __restrict__ x, con
                 for (int j = 0; j < R; ++j) {
                     if (p0 + (int64_t)j * PPI < cfg.HW) {
                         float v[V];
-                        Vec<T>::unpack(reg[j], v);
+                        Vec<T>::unpack(cur[j], v);
 #pragma unroll
                         for (int k = 0; k < V; ++k) {
                             const float d = v[k] - mt;
@@ -113,47 +161,63 @@ __global__ __launch_bounds__(kT) void slab_nhwc_fwd(const T* __restrict__ x, con
                         }
                     }
                 }
-                st = stat_merge(st, Stat{(float)cnt, mt, m2});
+                st = Stat{(float)cnt, mt, m2};
             }
+            // per-group statistics of the tile: the group's threads, in thread order
+            sst[t] = st;
+            __syncthreads();
+            for (int g = t; g < G; g += kT) {
+                Stat a = stat_empty();
+                for (int i = 0; i < PPI; ++i)
+                    for (int qq = g * qpg; qq < (g + 1) * qpg; ++qq) a = stat_merge(a, sst[i * CPP + qq]);
+                xstore_stat(&part[(sb * G + g) * cfg.pstride + tile], a);
+            }
+            __syncthreads();
             last = tile;
+            if (ntile >= cfg.tiles) break;   // cur keeps the last tile
+#pragma unroll
+            for (int j = 0; j < R; ++j) cur[j] = nxt[j];
+            tile = ntile;
         }
-        // ---- per-group merge inside the workgroup, in thread order ----
-        sst[t] = st;
-        __syncthreads();
-        const int qpg = (int)cfg.D / V;   // chunks per group
-        for (int g = t; g < G; g += kT) {
-            // the group's threads u = i*CPP + qq, visited in increasing u
-            Stat a = stat_empty();
-            for (int i = 0; i < PPI; ++i)
-                for (int qq = g * qpg; qq < (g + 1) * qpg; ++qq) a = stat_merge(a, sst[i * CPP + qq]);
-            xstore_stat(&part[(sb * cfg.team + m) * G + g], a);
-        }
-        __syncthreads();
-        team_barrier(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
+        if (last >= 0 && t == 0) __hip_atomic_store(&res[sb * cfg.tiles + last], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        team_barrier(&sw[0], (uint32_t)cfg.team, err);
 
         // ---- distributed finalize: member m owns groups m, m + team, ... ----
+        // tile partials merged in tile order: mean = sum(n_i*mean_i)/sum(n_i),
+        // M2 = sum(M2_i + n_i*(mean_i - mean)^2), each a fixed-order workgroup
+        // sum.  Plain loads: each (slab, group) block of partials is written
+        // once before the barrier, through to the coherence point, and padded
+        // to whole 128-byte lines, so no XCD holds a stale copy.
         for (int g = m; g < G; g += cfg.team) {
-            Stat a = stat_empty();
-            for (int i = t; i < cfg.team; i += kT) a = stat_merge(a, xload_stat(&part[(sb * cfg.team + i) * G + g]));
-            sst[t] = a;
-            __syncthreads();
-            for (int stride = kT / 2; stride > 0; stride >>= 1) {
-                if (t < stride) sst[t] = stat_merge(sst[t], sst[t + stride]);
-                __syncthreads();
+            const float4* pg = part + (sb * G + g) * cfg.pstride;
+            float sums[2] = {0.f, 0.f};
+            for (int64_t i = t; i < cfg.tiles; i += kT) {
+                const float4 v = pg[i];
+                sums[0] = fmaf(v.x, v.y, sums[0]);
+                sums[1] += v.x;
             }
+            block_sum<2, kNW>(sums, lds);
+            const float mu = sums[0] / sums[1];
+            float m2[1] = {0.f};
+            for (int64_t i = t; i < cfg.tiles; i += kT) {
+                const float4 v = pg[i];
+                const float d = v.y - mu;
+                m2[0] += fmaf(v.x * d, d, v.z);
+            }
+            block_sum<1, kNW>(m2, lds);
             if (t == 0) {
-                const Stat f = sst[0];
-                float var = f.m2 / (float)(cfg.D * cfg.HW);
+                float var = m2[0] / (float)(cfg.D * cfg.HW);
                 var = var > 0.f ? var : 0.f;
-                xstore(&mean[n * G + g], f.mean);
+                xstore(&mean[n * G + g], mu);
                 xstore(&rstd[n * G + g], 1.0f / sqrtf(var + cfg.eps));
             }
-            __syncthreads();
         }
-        team_barrier(&ctr[sb * 2 + 1], (uint32_t)cfg.team, err);
+        team_barrier(&sw[1], (uint32_t)cfg.team, err);
         if (y == nullptr) continue;
 
-        // ---- phase 2: normalize + affine; resident tile first, then reloads ----
+        // ---- phase 2: normalize + affine; the resident tile, then tiles
+        // drawn in reverse order (next tile's loads issued before the current
+        // one is written); streaming stores for y ----
         const float mu = xload(&mean[n * G + gq]);
         const float r = xload(&rstd[n * G + gq]);
         float a[V], b[V];
@@ -164,38 +228,42 @@ __global__ __launch_bounds__(kT) void slab_nhwc_fwd(const T* __restrict__ x, con
             b[k] = beta ? beta[c] : 0.f;
         }
         T* ys = y + n * cfg.HW * cfg.C + q * V;
-        for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
+        tile = last;
+        if (tile < 0) {
+            tile = grab_phase2_tile(&sw[3], rs_flags, cfg.tiles, &s_tile);
+            if (tile >= 0) nhwc_load<T, R>(xs, cfg.HW, cfg.C, tile * TP + pi, PPI, cur);
+        }
+        while (tile >= 0) {
+            const int64_t ntile = grab_phase2_tile(&sw[3], rs_flags, cfg.tiles, &s_tile);
+            if (ntile >= 0) nhwc_load<T, R>(xs, cfg.HW, cfg.C, ntile * TP + pi, PPI, nxt);
             const int64_t p0 = tile * TP + pi;
-            if (tile != last) {
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    const int64_t p = min(p0 + (int64_t)j * PPI, cfg.HW - 1);
-                    reg[j] = ld16(xs + p * cfg.C);
-                }
-            }
 #pragma unroll
             for (int j = 0; j < R; ++j) {
                 const int64_t p = p0 + (int64_t)j * PPI;
                 if (p < cfg.HW) {
                     float v[V], o[V];
-                    Vec<T>::unpack(reg[j], v);
+                    Vec<T>::unpack(cur[j], v);
 #pragma unroll
                     for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu, a[k], b[k]);
-                    st16(ys + p * cfg.C, Vec<T>::pack(o));
+                    st16_nt(ys + p * cfg.C, Vec<T>::pack(o));
                 }
             }
+            if (ntile < 0) break;
+#pragma unroll
+            for (int j = 0; j < R; ++j) cur[j] = nxt[j];
+            tile = ntile;
         }
     }
 }
 
-// part: [slab][member][C] float2 per-member channel sums; stot: [N][C] float2.
+// part: [slab][C][pstride] float2 per-tile channel sums; stot: [N][C] float2.
 template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, const T* __restrict__ x,
                                                     const float* __restrict__ mean,
                                                     const float* __restrict__ rstd,
                                                     const float* __restrict__ gamma, T* __restrict__ dx,
                                                     SlabCfg cfg, uint32_t* ctr, uint32_t* err, float2* part,
-                                                    float2* stot) {
+                                                    float2* stot, uint32_t* res) {
     constexpr int V = Vec<T>::V;
     const int t = threadIdx.x;
     const int CPP = (int)(cfg.C / V);
@@ -208,34 +276,41 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
     const int m = blockIdx.x - team * cfg.team;
     const int G = (int)cfg.G;
     const int C = (int)cfg.C;
-    __shared__ float2 red[kT];
+    __shared__ float lds[kNW * 2];
     __shared__ float2 lds_ch[kT * 8];   // [thread][k] per-thread channel sums (V <= 8)
+    __shared__ int s_tile;
 
     for (int64_t sb = team; sb < cfg.n_slabs; sb += cfg.nteams) {
         const int64_t n = sb;
+        uint32_t* sw = ctr + sb * 4;
+        const uint32_t* rs_flags = res + sb * cfg.tiles;
         const int64_t off = n * cfg.HW * cfg.C + q * V;
         const float mu = mean[n * G + gq];
         const float r = rstd[n * G + gq];
-        u4v rx[R], rd[R];
-        float s1[V], s2[V];
-#pragma unroll
-        for (int k = 0; k < V; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
+        u4v cx[R], cd[R], nx[R], nd[R];
         int64_t last = -1;
-        // ---- phase 1: per-channel sums over every tile of this member ----
-        for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
-            const int64_t p0 = tile * TP + pi;
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const int64_t p = min(p0 + (int64_t)j * PPI, cfg.HW - 1);
-                rx[j] = ld16(x + off + p * cfg.C);
-                rd[j] = ld16(dy + off + p * cfg.C);
+        // ---- phase 1: per-tile channel sums of every tile this member takes ----
+        int64_t tile = grab_tile(&sw[2], &s_tile);
+        if (tile < cfg.tiles) {
+            nhwc_load<T, R>(x + off, cfg.HW, cfg.C, tile * TP + pi, PPI, cx);
+            nhwc_load<T, R>(dy + off, cfg.HW, cfg.C, tile * TP + pi, PPI, cd);
+        }
+        while (tile < cfg.tiles) {
+            const int64_t ntile = grab_tile(&sw[2], &s_tile);
+            if (ntile < cfg.tiles) {
+                nhwc_load<T, R>(x + off, cfg.HW, cfg.C, ntile * TP + pi, PPI, nx);
+                nhwc_load<T, R>(dy + off, cfg.HW, cfg.C, ntile * TP + pi, PPI, nd);
             }
+            const int64_t p0 = tile * TP + pi;
+            float s1[V], s2[V];
+#pragma unroll
+            for (int k = 0; k < V; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
 #pragma unroll
             for (int j = 0; j < R; ++j) {
                 if (p0 + (int64_t)j * PPI < cfg.HW) {
                     float xv[V], dv[V];
-                    Vec<T>::unpack(rx[j], xv);
-                    Vec<T>::unpack(rd[j], dv);
+                    Vec<T>::unpack(cx[j], xv);
+                    Vec<T>::unpack(cd[j], dv);
 #pragma unroll
                     for (int k = 0; k < V; ++k) {
                         s1[k] += dv[k];
@@ -243,51 +318,48 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
                     }
                 }
             }
-            last = tile;
-        }
-        // ---- per-channel sums of the workgroup, in thread order ----
 #pragma unroll
-        for (int k = 0; k < V; ++k) lds_ch[t * 8 + k] = make_float2(s1[k], s2[k]);
-        __syncthreads();
-        for (int c = t; c < C; c += kT) {
-            const int cq = c / V, ck = c - cq * V;
-            float2 acc = make_float2(0.f, 0.f);
-            for (int i = 0; i < PPI; ++i) {
-                const float2 v = lds_ch[(i * CPP + cq) * 8 + ck];
-                acc.x += v.x;
-                acc.y += v.y;
-            }
-            xstore2(&part[(sb * cfg.team + m) * C + c], acc);
-        }
-        __syncthreads();
-        team_barrier(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
-
-        // ---- distributed finalize: member m owns channels m, m + team, ... ----
-        for (int c = m; c < C; c += cfg.team) {
-            float2 acc = make_float2(0.f, 0.f);
-            for (int i = t; i < cfg.team; i += kT) {
-                const float2 v = xload2(&part[(sb * cfg.team + i) * C + c]);
-                acc.x += v.x;
-                acc.y += v.y;
-            }
-            red[t] = acc;
+            for (int k = 0; k < V; ++k) lds_ch[t * 8 + k] = make_float2(s1[k], s2[k]);
             __syncthreads();
-            for (int stride = kT / 2; stride > 0; stride >>= 1) {
-                if (t < stride) {
-                    red[t].x += red[t + stride].x;
-                    red[t].y += red[t + stride].y;
+            for (int c = t; c < C; c += kT) {
+                const int cq = c / V, ck = c - cq * V;
+                float2 acc = make_float2(0.f, 0.f);
+                for (int i = 0; i < PPI; ++i) {
+                    const float2 v = lds_ch[(i * CPP + cq) * 8 + ck];
+                    acc.x += v.x;
+                    acc.y += v.y;
                 }
-                __syncthreads();
-            }
-            if (t == 0) {
-                xstore2(&stot[n * C + c], red[0]);
-                if (cfg.dbeta) cfg.dbeta[c] = red[0].x;     // one-slab case: final already
-                if (cfg.dgamma) cfg.dgamma[c] = red[0].y;
+                xstore2(&part[(sb * C + c) * cfg.pstride + tile], acc);
             }
             __syncthreads();
+            last = tile;
+            if (ntile >= cfg.tiles) break;   // cx, cd keep the last tile
+#pragma unroll
+            for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }
+            tile = ntile;
+        }
+        if (last >= 0 && t == 0) __hip_atomic_store(&res[sb * cfg.tiles + last], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        team_barrier(&sw[0], (uint32_t)cfg.team, err);
+
+        // ---- distributed finalize: member m owns channels m, m + team, ...
+        // (plain loads of the tile partials: see slab_nhwc_fwd) ----
+        for (int c = m; c < C; c += cfg.team) {
+            const float2* pc = part + (sb * C + c) * cfg.pstride;
+            float acc[2] = {0.f, 0.f};
+            for (int64_t i = t; i < cfg.tiles; i += kT) {
+                const float2 v = pc[i];
+                acc[0] += v.x;
+                acc[1] += v.y;
+            }
+            block_sum<2, kNW>(acc, lds);
+            if (t == 0) {
+                xstore2(&stot[n * C + c], make_float2(acc[0], acc[1]));
+                if (cfg.dbeta) cfg.dbeta[c] = acc[0];     // one-slab case: final already
+                if (cfg.dgamma) cfg.dgamma[c] = acc[1];
+            }
         }
         if (!cfg.want_dx) continue;   // uniform over the grid: no member waits below
-        team_barrier(&ctr[sb * 2 + 1], (uint32_t)cfg.team, err);
+        team_barrier(&sw[1], (uint32_t)cfg.team, err);
 
         // ---- phase 2: dx = rstd*(gamma_c*dy - A/M - xhat*B/M) ----
         float A = 0.f, B = 0.f;
@@ -303,33 +375,42 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
         float ga[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) ga[k] = gamma ? gamma[q * V + k] : 1.f;
-        for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
-            const int64_t p0 = tile * TP + pi;
-            if (tile != last) {
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    const int64_t p = min(p0 + (int64_t)j * PPI, cfg.HW - 1);
-                    rx[j] = ld16(x + off + p * cfg.C);
-                    rd[j] = ld16(dy + off + p * cfg.C);
-                }
+        tile = last;
+        if (tile < 0) {
+            tile = grab_phase2_tile(&sw[3], rs_flags, cfg.tiles, &s_tile);
+            if (tile >= 0) {
+                nhwc_load<T, R>(x + off, cfg.HW, cfg.C, tile * TP + pi, PPI, cx);
+                nhwc_load<T, R>(dy + off, cfg.HW, cfg.C, tile * TP + pi, PPI, cd);
             }
+        }
+        while (tile >= 0) {
+            const int64_t ntile = grab_phase2_tile(&sw[3], rs_flags, cfg.tiles, &s_tile);
+            if (ntile >= 0) {
+                nhwc_load<T, R>(x + off, cfg.HW, cfg.C, ntile * TP + pi, PPI, nx);
+                nhwc_load<T, R>(dy + off, cfg.HW, cfg.C, ntile * TP + pi, PPI, nd);
+            }
+            const int64_t p0 = tile * TP + pi;
 #pragma unroll
             for (int j = 0; j < R; ++j) {
                 const int64_t p = p0 + (int64_t)j * PPI;
                 if (p < cfg.HW) {
 #pragma clang fp contract(off)
                     float xv[V], dv[V], o[V];
-                    Vec<T>::unpack(rx[j], xv);
-                    Vec<T>::unpack(rd[j], dv);
+                    Vec<T>::unpack(cx[j], xv);
+                    Vec<T>::unpack(cd[j], dv);
 #pragma unroll
                     for (int k = 0; k < V; ++k) {
                         const float xh = (xv[k] - mu) * r;
                         const float gd = dv[k] * ga[k];
                         o[k] = r * ((gd - A) - xh * B);
                     }
-                    st16(dx + off + p * cfg.C, Vec<T>::pack(o));
+                    st16_nt(dx + off + p * cfg.C, Vec<T>::pack(o));
                 }
             }
+            if (ntile < 0) break;
+#pragma unroll
+            for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }
+            tile = ntile;
         }
     }
 }
@@ -344,7 +425,9 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
 // Between arriving at a slab's barrier and waiting on it, a member issues the
 // loads of its first tile of the team's next slab, so that HBM keeps streaming
 // while the team synchronises (prefetch into a second register tile).
-template <typename T, int R>
+// NT: non-temporal loads (the backward's measured choice; the forward runs
+// faster with plain loads and stores).
+template <typename T, int R, bool NT>
 __device__ inline void nchw_load_tile(const T* __restrict__ src, const SlabCfg& cfg, int64_t sb, int64_t tile,
                                       u4v (&dst)[R]) {
     constexpr int V = Vec<T>::V;
@@ -355,7 +438,7 @@ __device__ inline void nchw_load_tile(const T* __restrict__ src, const SlabCfg& 
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int64_t e = min(k0 + (int64_t)(j * kT + (int)threadIdx.x) * V, cfg.HW - V);   // in bounds
-        dst[j] = ld16(p + e);
+        dst[j] = NT ? ld16_nt(p + e) : ld16(p + e);
     }
 }
 
@@ -375,7 +458,7 @@ __device__ inline int64_t nchw_fwd_phase1(const T* __restrict__ x, const float* 
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
         const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
-        nchw_load_tile<T, R>(x, cfg, sb, tile, buf);
+        nchw_load_tile<T, R, false>(x, cfg, sb, tile, buf);
         const int64_t c = (sb - (sb / cfg.G) * cfg.G) * cfg.D + cl;
         gb = make_float2(gamma ? gamma[c] : 1.f, beta ? beta[c] : 0.f);
         const int64_t rem = cfg.HW - k0;
@@ -458,7 +541,7 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
         const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
         float2 p = gb;
         if (tile != last) {
-            nchw_load_tile<T, R>(x, cfg, sb, tile, buf);
+            nchw_load_tile<T, R, false>(x, cfg, sb, tile, buf);
             const int64_t c = g * cfg.D + cl;
             p = make_float2(gamma ? gamma[c] : 1.f, beta ? beta[c] : 0.f);
         }
@@ -487,7 +570,7 @@ template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
                                                     const float* __restrict__ beta, T* __restrict__ y,
                                                     float* mean, float* rstd, SlabCfg cfg, uint32_t* ctr,
-                                                    uint32_t* err, float4* part) {
+                                                    uint32_t* err, float4* part, uint32_t* /*res: NHWC only*/) {
     const int team = blockIdx.x / cfg.team;
     const int m = blockIdx.x - team * cfg.team;
     __shared__ float lds[kNW * 2];
@@ -496,15 +579,15 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
     int64_t sb = team;
     if (sb >= cfg.n_slabs) return;   // uniform over the team
     int64_t last = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, sb, m, cur, gcur, part, lds);
-    team_arrive(&ctr[sb * 2 + 0]);
+    team_arrive(&ctr[sb * 4 + 0]);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
         int64_t nlast = -1;
         if (nsb < cfg.n_slabs) {
             nlast = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, nsb, m, nxt, gnxt, part, lds);
-            team_arrive(&ctr[nsb * 2 + 0]);
+            team_arrive(&ctr[nsb * 4 + 0]);
         }
-        team_wait(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
+        team_wait(&ctr[sb * 4 + 0], (uint32_t)cfg.team, err);
         nchw_fwd_phase2<T, R>(x, gamma, beta, y, mean, rstd, cfg, sb, m, last, cur, gcur, part, lds);
         if (nsb >= cfg.n_slabs) break;
 #pragma unroll
@@ -529,8 +612,8 @@ __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __r
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
         const int64_t k0 = (tile - (tile / cfg.tpc) * cfg.tpc) * TE;
-        nchw_load_tile<T, R>(x, cfg, sb, tile, bx);
-        nchw_load_tile<T, R>(dy, cfg, sb, tile, bd);
+        nchw_load_tile<T, R, true>(x, cfg, sb, tile, bx);
+        nchw_load_tile<T, R, true>(dy, cfg, sb, tile, bd);
         float acc[2] = {0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < R; ++j) {
@@ -606,8 +689,8 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
         const int64_t pb = base + cl * cfg.HW;
         const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
         if (tile != last) {
-            nchw_load_tile<T, R>(x, cfg, sb, tile, bx);
-            nchw_load_tile<T, R>(dy, cfg, sb, tile, bd);
+            nchw_load_tile<T, R, true>(x, cfg, sb, tile, bx);
+            nchw_load_tile<T, R, true>(dy, cfg, sb, tile, bd);
         }
 #pragma unroll
         for (int j = 0; j < R; ++j) {
@@ -623,7 +706,7 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
                     const float gd = dv[k] * ga;
                     o[k] = r * ((gd - A) - xh * B);
                 }
-                st16(dx + pb + e, Vec<T>::pack(o));
+                st16_nt(dx + pb + e, Vec<T>::pack(o));
             }
         }
     }
@@ -637,7 +720,7 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
                                                     const float* __restrict__ rstd,
                                                     const float* __restrict__ gamma, T* __restrict__ dx,
                                                     SlabCfg cfg, uint32_t* ctr, uint32_t* err, float2* part,
-                                                    float2* stot) {
+                                                    float2* stot, uint32_t* /*res: NHWC only*/) {
     const int team = blockIdx.x / cfg.team;
     const int m = blockIdx.x - team * cfg.team;
     __shared__ float lds[kNW * 2];
@@ -647,15 +730,15 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
     int64_t sb = team;
     if (sb >= cfg.n_slabs) return;   // uniform over the team
     int64_t last = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, sb, m, cx, cd, part, lds);
-    team_arrive(&ctr[sb * 2 + 0]);
+    team_arrive(&ctr[sb * 4 + 0]);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
         int64_t nlast = -1;
         if (nsb < cfg.n_slabs) {
             nlast = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, nsb, m, nx, nd, part, lds);
-            team_arrive(&ctr[nsb * 2 + 0]);
+            team_arrive(&ctr[nsb * 4 + 0]);
         }
-        team_wait(&ctr[sb * 2 + 0], (uint32_t)cfg.team, err);
+        team_wait(&ctr[sb * 4 + 0], (uint32_t)cfg.team, err);
         nchw_bwd_phase2<T, R>(dy, x, mean, rstd, gamma, dx, cfg, sb, m, last, cx, cd, part, stot, stage, chan);
         if (nsb >= cfg.n_slabs) break;
 #pragma unroll
@@ -714,7 +797,7 @@ struct Plan {
     SlabCfg cfg;
     int64_t grid;
     int64_t resident;
-    size_t off_ctr, off_err, off_part, off_stot, total;
+    size_t off_ctr, off_err, off_res, off_part, off_stot, total;
 };
 
 int64_t tiles_per_slab(const Problem& p, int R, int64_t* tpc) {
@@ -755,12 +838,15 @@ Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
     pl.cfg.n_slabs = n_slabs;
     size_t off = 256;            // [0, 256): error word
     pl.off_err = 0;
-    pl.off_ctr = off;
-    off += al((size_t)n_slabs * 2 * sizeof(uint32_t));
-    pl.off_part = off;
+    pl.off_ctr = off;            // 4 sync words per slab
+    off += al((size_t)n_slabs * 4 * sizeof(uint32_t));
+    pl.off_res = off;            // NHWC: resident flag per tile
+    if (p.layout == GN_NHWC) off += al((size_t)n_slabs * tiles * sizeof(uint32_t));
+    pl.off_part = off;           // everything before this offset is cleared each call
     size_t part;
     if (p.layout == GN_NHWC)
-        part = backward ? (size_t)n_slabs * team * p.C * sizeof(float2) : (size_t)n_slabs * team * p.G * sizeof(float4);
+        part = backward ? (size_t)n_slabs * p.C * pl.cfg.pstride * sizeof(float2)
+                        : (size_t)n_slabs * p.G * pl.cfg.pstride * sizeof(float4);
     else
         part = backward ? (size_t)n_slabs * pl.cfg.pstride * sizeof(float2)
                         : (size_t)n_slabs * pl.cfg.pstride * sizeof(float4);
@@ -772,10 +858,10 @@ Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
     return pl;
 }
 
-// Zeroes the error word and the arrival counters (one fill kernel: no
-// memset node, so the call stays safe to capture in a graph).
+// Zeroes the error word, the sync words and the resident flags (one fill
+// kernel: no memset node, so the call stays safe to capture in a graph).
 hipError_t clear_sync_words(char* ws, const Plan& pl, hipStream_t s) {
-    const int64_t words = (int64_t)(pl.off_ctr / sizeof(uint32_t)) + pl.cfg.n_slabs * 2;
+    const int64_t words = (int64_t)(pl.off_part / sizeof(uint32_t));
     int64_t blocks = (words + 255) / 256;
     if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL(clear_words, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)ws, words);
@@ -809,6 +895,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
     uint32_t* err = (uint32_t*)(ws + pl.off_err);
     float4* part = (float4*)(ws + pl.off_part);
+    uint32_t* res = (uint32_t*)(ws + pl.off_res);
     hipError_t e;
     if ((e = clear_sync_words(ws, pl, l.stream))) return e;
     if ((e = record(l.ev_begin, l.stream))) return e;
@@ -818,7 +905,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     const float* beta = a.beta;
     float* mean = a.mean;
     float* rstd = a.rstd;
-    void* args[] = {&x, &gamma, &beta, &y, &mean, &rstd, &cfg, &ctr, &err, &part};
+    void* args[] = {&x, &gamma, &beta, &y, &mean, &rstd, &cfg, &ctr, &err, &part, &res};
     const bool coop = cfg.team > 1;
     e = nhwc ? launch_coop(kn, grid, args, l.stream, coop) : launch_coop(kc, grid, args, l.stream, coop);
     if (e) return e;
@@ -859,6 +946,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     uint32_t* err = (uint32_t*)(ws + pl.off_err);
     float2* part = (float2*)(ws + pl.off_part);
     float2* stot = (float2*)(ws + pl.off_stot);
+    uint32_t* res = (uint32_t*)(ws + pl.off_res);
     hipError_t e;
     if ((e = clear_sync_words(ws, pl, l.stream))) return e;
     if ((e = record(l.ev_begin, l.stream))) return e;
@@ -868,7 +956,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     const float* rstd = a.rstd;
     const float* gamma = a.gamma;
     T* dx = (T*)a.dx;
-    void* args[] = {&dy, &x, &mean, &rstd, &gamma, &dx, &cfg, &ctr, &err, &part, &stot};
+    void* args[] = {&dy, &x, &mean, &rstd, &gamma, &dx, &cfg, &ctr, &err, &part, &stot, &res};
     const bool coop = cfg.team > 1;
     e = nhwc ? launch_coop(kn, grid, args, l.stream, coop) : launch_coop(kc, grid, args, l.stream, coop);
     if (e) return e;
@@ -903,6 +991,15 @@ bool slab_ok(const Problem& p) {
     }
     if (p.HW % V != 0) return false;   // every channel plane starts 16-byte aligned
     return p.HW >= V && p.D <= kT;      // channel sums of a slab: one thread per channel
+}
+
+// True when one slab's tiles do not outnumber the workgroups an MI355X keeps
+// resident (256 CUs x 4), i.e. the cooperative grid can hold the whole slab in
+// registers; a fixed figure, so that the choice does not depend on the device.
+bool slab_resident(const Problem& p, bool backward) {
+    constexpr int64_t kResidentTiles = 1024;
+    int64_t tpc;
+    return tiles_per_slab(p, tile_chunks(p, backward), &tpc) <= kResidentTiles;
 }
 
 size_t slab_fwd_ws(const Problem& p) {

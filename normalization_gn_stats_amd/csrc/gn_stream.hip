@@ -1,0 +1,605 @@
+// gn_stream.hip -- NHWC GroupNorm as a few streaming launches, one tile per
+// workgroup, for images whose tiles far outnumber the workgroups an MI355X can
+// keep resident.
+//
+// In NHWC every group of a sample is spread over the whole image (16 bytes =
+// V channels of one group per pixel), so the slab of one statistic is the
+// whole sample.  When that slab exceeds what the co-resident grid can hold in
+// registers, a cooperative one-pass kernel re-reads most tiles anyway and
+// pays a per-tile hand-out and barrier cost on top; launching one workgroup
+// per tile lets the hardware dispatcher balance the load instead.
+//
+//   forward   1. per tile: (count, mean, M2) of each group, exact two-pass per
+//               thread from registers, merged across the tile's threads
+//               (Chan et al.'s pairwise update, fixed tree order)
+//             2. per slice: the tile partials in a fixed order -> mean, rstd
+//               (sum n_i*mean_i, then sum M2_i + n_i*(mean_i - mean)^2)
+//             3. per tile: y = (x - mean)*(rstd*gamma_c) + beta_c
+//   backward  1. per tile: per-channel sums of dy and dy*xhat (xhat from the
+//               saved mean/rstd)
+//             2. per (n, c): those sums over the tiles, in two fixed-order
+//               levels -> S1[n,c], S2[n,c]
+//             3. per slice: A/M = sum_c gamma_c*S1/M, B/M = sum_c gamma_c*S2/M;
+//               dbeta_c = sum_n S1[n,c], dgamma_c = sum_n S2[n,c]
+//             4. per tile: dx = rstd*(gamma_c*dy - A/M - xhat*B/M)
+// (POPCORNBENCH GroupNorm trace: statistics pass, then normalize-and-affine
+// pass; baracuda-kernels GroupNorm backward plan: per-group reductions, then
+// the elementwise dx.)  All reductions run in a fixed order, so the results
+// are bitwise reproducible.  Activations are read with non-temporal loads and
+// outputs written with non-temporal stores: nothing is read twice within the
+// caches' reach.
+#include "gn_device.hpp"
+#include "gn_internal.hpp"
+
+namespace gn {
+namespace {
+
+constexpr int kT = 256;
+constexpr int kNW = kT / kWave;
+
+// 16-byte chunks per thread per tile (of x, and of dy in the backward), per
+// kernel, as measured on the 1x128x1024x2048 fp16 image: 16 for the two
+// reductions and the forward's output pass, 4 for dx.
+#ifndef GN_STREAM_R_STATS
+#define GN_STREAM_R_STATS 16
+#endif
+#ifndef GN_STREAM_R_APPLY
+#define GN_STREAM_R_APPLY 16
+#endif
+#ifndef GN_STREAM_R_SUMS
+#define GN_STREAM_R_SUMS 16
+#endif
+#ifndef GN_STREAM_R_DX
+#define GN_STREAM_R_DX 4
+#endif
+
+struct StreamCfg {
+    int64_t N, C, HW, G, D;
+    int64_t tiles;   // tiles per sample of the reduction kernel (partials per sample)
+    int64_t otiles;  // tiles per sample of the output kernel
+    float eps;
+};
+
+int vec_elems(const Problem& p) { return p.elem_bytes == 4 ? 4 : 8; }
+
+// Thread t owns chunk q = t % CPP of each pixel it visits (channels q*V ..
+// q*V+V-1, all in group q*V/D) and pixel t / CPP of each of the tile's R
+// iterations; a tile is R*PPI consecutive pixels of one sample.
+struct TileGeom {
+    int V, CPP, q, pi, PPI;
+    int64_t TP;
+};
+
+template <typename T, int R>
+__device__ inline TileGeom tile_geom(int64_t C) {
+    TileGeom g;
+    g.V = Vec<T>::V;
+    g.CPP = (int)(C / g.V);
+    g.q = threadIdx.x % g.CPP;
+    g.pi = threadIdx.x / g.CPP;
+    g.PPI = kT / g.CPP;
+    g.TP = (int64_t)g.PPI * R;
+    return g;
+}
+
+// R chunks of one tile; pixels past HW are clamped onto the last pixel (in
+// bounds, no branch around the loads) and dropped by the caller.
+template <typename T, int R>
+__device__ inline void load_tile(const T* __restrict__ src, int64_t HW, int64_t C, int64_t p0, int PPI,
+                                 u4v (&dst)[R]) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t p = min(p0 + (int64_t)j * PPI, HW - 1);
+        dst[j] = ld16_nt(src + p * C);
+    }
+}
+
+// V per-channel parameters from c0 (a multiple of 4; p 16-byte aligned), or
+// `dflt` when p is NULL: float4 loads.
+template <int V>
+__device__ inline void load_params(const float* __restrict__ p, int64_t c0, float dflt, float (&o)[V]) {
+    if (!p) {
+#pragma unroll
+        for (int k = 0; k < V; ++k) o[k] = dflt;
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < V; k += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(p + c0 + k);
+        o[k] = q.x; o[k + 1] = q.y; o[k + 2] = q.z; o[k + 3] = q.w;
+    }
+}
+
+// ---- forward ----------------------------------------------------------------
+// grid (tiles, N); part: [N*G][tiles] float4 (count, mean, M2, -)
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void fwd_tile_stats(const T* __restrict__ x, StreamCfg cfg,
+                                                     float4* __restrict__ part) {
+    const TileGeom tg = tile_geom<T, R>(cfg.C);
+    constexpr int V = Vec<T>::V;
+    const int t = threadIdx.x;
+    const int64_t tile = blockIdx.x, n = blockIdx.y;
+    __shared__ Stat sst[kT];
+    u4v reg[R];
+    const int64_t p0 = tile * tg.TP + tg.pi;
+    load_tile<T, R>(x + n * cfg.HW * cfg.C + tg.q * V, cfg.HW, cfg.C, p0, tg.PPI, reg);
+    float s = 0.f;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (p0 + (int64_t)j * tg.PPI < cfg.HW) {
+            float v[V];
+            Vec<T>::unpack(reg[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) s += v[k];
+            cnt += V;
+        }
+    }
+    Stat st = stat_empty();
+    if (cnt > 0) {
+        const float mt = s / (float)cnt;
+        float m2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            if (p0 + (int64_t)j * tg.PPI < cfg.HW) {
+                float v[V];
+                Vec<T>::unpack(reg[j], v);
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float d = v[k] - mt;
+                    m2 = fmaf(d, d, m2);
+                }
+            }
+        }
+        st = Stat{(float)cnt, mt, m2};
+    }
+    // merge tree: first over the pixel rows of each chunk, then over the
+    // chunks of each group (row 0 only)
+    sst[t] = st;
+    __syncthreads();
+    for (int h = tg.PPI / 2; h > 0; h /= 2) {
+        if (tg.pi < h) sst[t] = stat_merge(sst[t], sst[t + h * tg.CPP]);
+        __syncthreads();
+    }
+    const int qpg = (int)cfg.D / V;   // any count: the tree skips missing partners
+    int top = 1;
+    while (top < qpg) top *= 2;
+    for (int h = top / 2; h > 0; h /= 2) {
+        if (t < tg.CPP && (t % qpg) < h && (t % qpg) + h < qpg) sst[t] = stat_merge(sst[t], sst[t + h]);
+        __syncthreads();
+    }
+    for (int g = t; g < (int)cfg.G; g += kT) {
+        const Stat a = sst[g * qpg];
+        part[(n * cfg.G + g) * cfg.tiles + tile] = make_float4(a.n, a.mean, a.m2, 0.f);
+    }
+}
+
+// one workgroup of kFinT threads per slice (blockIdx.x = n*G + g).  Each pass
+// loads kFinB partials per thread at once (independent loads), so a slice of
+// many thousand tiles costs a few load round trips, not one per tile.
+constexpr int kFinT = 1024, kFinNW = kFinT / kWave, kFinB = 8;
+__global__ __launch_bounds__(kFinT) void fwd_finalize(const float4* __restrict__ part, StreamCfg cfg,
+                                                      float* __restrict__ mean, float* __restrict__ rstd) {
+    __shared__ float lds[kFinNW * 2];
+    const int64_t sg = blockIdx.x;
+    const float4* pg = part + sg * cfg.tiles;
+    const int t = threadIdx.x;
+    float sums[2] = {0.f, 0.f};
+    for (int64_t base = 0; base < cfg.tiles; base += (int64_t)kFinT * kFinB) {
+        float4 v[kFinB];
+#pragma unroll
+        for (int j = 0; j < kFinB; ++j) {
+            const int64_t i = base + (int64_t)j * kFinT + t;
+            v[j] = i < cfg.tiles ? pg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < kFinB; ++j) {
+            sums[0] = fmaf(v[j].x, v[j].y, sums[0]);
+            sums[1] += v[j].x;
+        }
+    }
+    block_sum<2, kFinNW>(sums, lds);
+    const float mu = sums[0] / sums[1];
+    float m2[1] = {0.f};
+    for (int64_t base = 0; base < cfg.tiles; base += (int64_t)kFinT * kFinB) {
+        float4 v[kFinB];
+#pragma unroll
+        for (int j = 0; j < kFinB; ++j) {
+            const int64_t i = base + (int64_t)j * kFinT + t;
+            v[j] = i < cfg.tiles ? pg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < kFinB; ++j) {
+            const float d = v[j].y - mu;
+            m2[0] += fmaf(v[j].x * d, d, v[j].z);
+        }
+    }
+    block_sum<1, kFinNW>(m2, lds);
+    if (t == 0) {
+        float var = m2[0] / (float)(cfg.D * cfg.HW);
+        var = var > 0.f ? var : 0.f;
+        mean[sg] = mu;
+        rstd[sg] = 1.0f / sqrtf(var + cfg.eps);
+    }
+}
+
+// grid (otiles, N)
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void fwd_apply(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                const float* __restrict__ beta, T* __restrict__ y,
+                                                const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                StreamCfg cfg) {
+    const TileGeom tg = tile_geom<T, R>(cfg.C);
+    constexpr int V = Vec<T>::V;
+    const int gq = (tg.q * V) / (int)cfg.D;
+    const int64_t tile = blockIdx.x, n = blockIdx.y;
+    const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
+    u4v reg[R];
+    const int64_t p0 = tile * tg.TP + tg.pi;
+    load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, reg);
+    const float mu = mean[n * cfg.G + gq];
+    const float r = rstd[n * cfg.G + gq];
+    float a[V], b[V];
+    load_params<V>(gamma, tg.q * V, 1.f, a);
+    load_params<V>(beta, tg.q * V, 0.f, b);
+#pragma unroll
+    for (int k = 0; k < V; ++k) a[k] *= r;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t p = p0 + (int64_t)j * tg.PPI;
+        if (p < cfg.HW) {
+            float v[V], o[V];
+            Vec<T>::unpack(reg[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu, a[k], b[k]);
+            st16_nt(y + off + p * cfg.C, Vec<T>::pack(o));
+        }
+    }
+}
+
+// ---- backward ---------------------------------------------------------------
+// grid (tiles, N); part: [N][tiles][C] float2 (sum dy, sum dy*xhat)
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void bwd_tile_sums(const T* __restrict__ dy, const T* __restrict__ x,
+                                                    const float* __restrict__ mean,
+                                                    const float* __restrict__ rstd, StreamCfg cfg,
+                                                    float2* __restrict__ part) {
+    const TileGeom tg = tile_geom<T, R>(cfg.C);
+    constexpr int V = Vec<T>::V;
+    const int t = threadIdx.x;
+    const int gq = (tg.q * V) / (int)cfg.D;
+    const int64_t tile = blockIdx.x, n = blockIdx.y;
+    const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
+    __shared__ float2 lds[kT * 8];   // [thread][k], V <= 8
+    u4v rx[R], rd[R];
+    const int64_t p0 = tile * tg.TP + tg.pi;
+    load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, rx);
+    load_tile<T, R>(dy + off, cfg.HW, cfg.C, p0, tg.PPI, rd);
+    const float mu = mean[n * cfg.G + gq];
+    const float r = rstd[n * cfg.G + gq];
+    float s1[V], s2[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (p0 + (int64_t)j * tg.PPI < cfg.HW) {
+            float xv[V], dv[V];
+            Vec<T>::unpack(rx[j], xv);
+            Vec<T>::unpack(rd[j], dv);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                s1[k] += dv[k];
+                s2[k] = fmaf(dv[k], (xv[k] - mu) * r, s2[k]);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k) lds[t * V + k] = make_float2(s1[k], s2[k]);
+    __syncthreads();
+    // tree over the pixel rows of each chunk
+    for (int h = tg.PPI / 2; h > 0; h /= 2) {
+        if (tg.pi < h) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float2 u = lds[(t + h * tg.CPP) * V + k];
+                float2 w = lds[t * V + k];
+                w.x += u.x;
+                w.y += u.y;
+                lds[t * V + k] = w;
+            }
+        }
+        __syncthreads();
+    }
+    // row 0 holds the tile's channel sums, channel c at lds[c]
+    float2* dst = part + (n * cfg.tiles + tile) * cfg.C;
+    for (int c = t; c < (int)cfg.C; c += kT) dst[c] = lds[c];
+}
+
+// Column sums of src [N][rows][C] float2 over row ranges of `per` rows:
+// dst [N][chunks][C].  grid (ceil(C/(2*kColPairs)), chunks, N).  Each thread
+// sums two adjacent channels (one float4) over its row lane in row order; the
+// row lanes are then added in lane order.
+constexpr int kColPairs = 8;
+constexpr int kRowLanes = kT / kColPairs;
+__global__ __launch_bounds__(kT) void col_sums(const float2* __restrict__ src, int64_t rows, int64_t C,
+                                               int64_t per, float2* __restrict__ dst) {
+    const int cp = threadIdx.x % kColPairs;
+    const int rl = threadIdx.x / kColPairs;
+    const int64_t c0 = ((int64_t)blockIdx.x * kColPairs + cp) * 2;
+    const int64_t chunk = blockIdx.y, n = blockIdx.z;
+    const int64_t r0 = chunk * per;
+    const int64_t r1 = min(r0 + per, rows);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c0 < C) {
+        const float2* s = src + n * rows * C + c0;
+#pragma unroll 4
+        for (int64_t b = r0 + rl; b < r1; b += kRowLanes) {
+            const float4 q = *reinterpret_cast<const float4*>(s + b * C);
+            acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
+        }
+    }
+    __shared__ float4 red[kT];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (rl == 0 && c0 < C) {
+        float4 tot = red[cp];
+        for (int k = 1; k < kRowLanes; ++k) {
+            const float4 q = red[k * kColPairs + cp];
+            tot.x += q.x; tot.y += q.y; tot.z += q.z; tot.w += q.w;
+        }
+        *reinterpret_cast<float4*>(dst + (n * gridDim.y + chunk) * C + c0) = tot;
+    }
+}
+
+// grid (G, N): ab[n*G + g] = (A/M, B/M); with one sample, dbeta/dgamma too
+__global__ __launch_bounds__(kT) void bwd_group_ab(const float2* __restrict__ stot, const float* __restrict__ gamma,
+                                                   StreamCfg cfg, float2* __restrict__ ab,
+                                                   float* __restrict__ dgamma, float* __restrict__ dbeta) {
+    __shared__ float lds[kNW * 2];
+    const int64_t g = blockIdx.x, n = blockIdx.y;
+    float acc[2] = {0.f, 0.f};
+    for (int64_t c = g * cfg.D + threadIdx.x; c < (g + 1) * cfg.D; c += kT) {
+        const float2 v = stot[n * cfg.C + c];
+        const float ga = gamma ? gamma[c] : 1.f;
+        acc[0] = fmaf(ga, v.x, acc[0]);
+        acc[1] = fmaf(ga, v.y, acc[1]);
+        if (cfg.N == 1) {
+            if (dbeta) dbeta[c] = v.x;
+            if (dgamma) dgamma[c] = v.y;
+        }
+    }
+    block_sum<2, kNW>(acc, lds);
+    if (threadIdx.x == 0) {
+        const float invM = 1.0f / (float)(cfg.D * cfg.HW);
+        ab[n * cfg.G + g] = make_float2(acc[0] * invM, acc[1] * invM);
+    }
+}
+
+// dgamma/dbeta as sums over the samples, in sample order
+__global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ stot, int64_t N, int64_t C,
+                                                    float* __restrict__ dgamma, float* __restrict__ dbeta) {
+    const int64_t c = (int64_t)blockIdx.x * kT + threadIdx.x;
+    if (c >= C) return;
+    float a = 0.f, b = 0.f;
+#pragma unroll 8
+    for (int64_t n = 0; n < N; ++n) {
+        const float2 v = stot[n * C + c];
+        a += v.x;
+        b += v.y;
+    }
+    if (dbeta) dbeta[c] = a;
+    if (dgamma) dgamma[c] = b;
+}
+
+// grid (otiles, N)
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void bwd_dx(const T* __restrict__ dy, const T* __restrict__ x,
+                                             const float* __restrict__ mean, const float* __restrict__ rstd,
+                                             const float* __restrict__ gamma, const float2* __restrict__ ab,
+                                             T* __restrict__ dx, StreamCfg cfg) {
+    const TileGeom tg = tile_geom<T, R>(cfg.C);
+    constexpr int V = Vec<T>::V;
+    const int gq = (tg.q * V) / (int)cfg.D;
+    const int64_t tile = blockIdx.x, n = blockIdx.y;
+    const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
+    u4v rx[R], rd[R];
+    const int64_t p0 = tile * tg.TP + tg.pi;
+    load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, rx);
+    load_tile<T, R>(dy + off, cfg.HW, cfg.C, p0, tg.PPI, rd);
+    const float mu = mean[n * cfg.G + gq];
+    const float r = rstd[n * cfg.G + gq];
+    const float2 AB = ab[n * cfg.G + gq];
+    float ga[V];
+    load_params<V>(gamma, tg.q * V, 1.f, ga);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t p = p0 + (int64_t)j * tg.PPI;
+        if (p < cfg.HW) {
+#pragma clang fp contract(off)
+            float xv[V], dv[V], o[V];
+            Vec<T>::unpack(rx[j], xv);
+            Vec<T>::unpack(rd[j], dv);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float xh = (xv[k] - mu) * r;
+                const float gd = dv[k] * ga[k];
+                o[k] = r * ((gd - AB.x) - xh * AB.y);
+            }
+            st16_nt(dx + off + p * cfg.C, Vec<T>::pack(o));
+        }
+    }
+}
+
+// ---- planning ---------------------------------------------------------------
+// (events, when given, bracket all kernels of a call)
+size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int64_t tiles_of(const Problem& p, int R) {
+    const int CPP = (int)(p.C / vec_elems(p));
+    const int64_t TP = (int64_t)(kT / CPP) * R;
+    return (p.HW + TP - 1) / TP;
+}
+
+StreamCfg make_cfg(const Problem& p, int R, int RO, float eps) {
+    StreamCfg c;
+    c.N = p.N; c.C = p.C; c.HW = p.HW; c.G = p.G; c.D = p.D;
+    c.tiles = tiles_of(p, R);
+    c.otiles = tiles_of(p, RO);
+    c.eps = eps;
+    return c;
+}
+
+// Backward workspace: tile sums [N][tiles][C], chunk sums [N][chunks][C]
+// (when there is more than one chunk), per-(n, c) totals [N][C] and (A/M,
+// B/M) [N*G], all float2.
+constexpr int64_t kRowsPerChunk = 64;
+
+struct BwdPlan {
+    int64_t tiles, chunks;
+    size_t off_part, off_chunk, off_stot, off_ab, total;
+};
+
+BwdPlan bwd_plan(const Problem& p) {
+    BwdPlan b{};
+    b.tiles = tiles_of(p, GN_STREAM_R_SUMS);
+    b.chunks = (b.tiles + kRowsPerChunk - 1) / kRowsPerChunk;
+    size_t off = 0;
+    b.off_part = off;
+    off += al((size_t)p.N * b.tiles * p.C * sizeof(float2));
+    b.off_chunk = off;
+    if (b.chunks > 1) off += al((size_t)p.N * b.chunks * p.C * sizeof(float2));
+    b.off_stot = off;
+    off += al((size_t)p.N * p.C * sizeof(float2));
+    b.off_ab = off;
+    off += al((size_t)p.N * p.G * sizeof(float2));
+    b.total = off;
+    return b;
+}
+
+template <typename T>
+hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
+    constexpr int R = GN_STREAM_R_STATS, RO = GN_STREAM_R_APPLY;
+    const StreamCfg cfg = make_cfg(p, R, RO, a.eps);
+    float4* part = (float4*)l.ws;
+    const dim3 grid((unsigned)cfg.tiles, (unsigned)p.N), ogrid((unsigned)cfg.otiles, (unsigned)p.N);
+    hipError_t e = record(l.ev_begin, l.stream);
+    if (e) return e;
+    hipLaunchKernelGGL((fwd_tile_stats<T, R>), grid, dim3(kT), 0, l.stream, (const T*)a.x, cfg, part);
+    hipLaunchKernelGGL(fwd_finalize, dim3((unsigned)(p.N * p.G)), dim3(kFinT), 0, l.stream, part, cfg, a.mean, a.rstd);
+    if ((e = hipGetLastError())) return e;
+    int kernels = 2;
+    if (a.y) {
+        hipLaunchKernelGGL((fwd_apply<T, RO>), ogrid, dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta, (T*)a.y,
+                           a.mean, a.rstd, cfg);
+        if ((e = hipGetLastError())) return e;
+        ++kernels;
+    }
+    if ((e = record(l.ev_end, l.stream))) return e;
+    if (l.info) {
+        l.info->path = GN_PATH_STREAM;
+        l.info->kernels = kernels;
+        l.info->grid = cfg.tiles * p.N;
+        l.info->tiles = cfg.tiles * p.N;
+    }
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
+    constexpr int R = GN_STREAM_R_SUMS, RO = GN_STREAM_R_DX;
+    const StreamCfg cfg = make_cfg(p, R, RO, 0.f);
+    const BwdPlan b = bwd_plan(p);
+    char* ws = (char*)l.ws;
+    float2* part = (float2*)(ws + b.off_part);
+    float2* chunk = (float2*)(ws + b.off_chunk);
+    float2* stot = (float2*)(ws + b.off_stot);
+    float2* ab = (float2*)(ws + b.off_ab);
+    float* dg = (a.mask & GN_GRAD_DGAMMA) ? a.dgamma : nullptr;
+    float* db = (a.mask & GN_GRAD_DBETA) ? a.dbeta : nullptr;
+    const bool want_dx = (a.mask & GN_GRAD_DX) != 0;
+    const dim3 grid((unsigned)cfg.tiles, (unsigned)p.N), ogrid((unsigned)cfg.otiles, (unsigned)p.N);
+    const unsigned cblocks = (unsigned)((p.C + 2 * kColPairs - 1) / (2 * kColPairs));
+    int kernels = 0;
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL((bwd_tile_sums<T, R>), grid, dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean,
+                       a.rstd, cfg, part);
+    ++kernels;
+    if (b.chunks > 1) {
+        hipLaunchKernelGGL(col_sums, dim3(cblocks, (unsigned)b.chunks, (unsigned)p.N), dim3(kT), 0, l.stream,
+                           (const float2*)part, b.tiles, p.C, kRowsPerChunk, chunk);
+        hipLaunchKernelGGL(col_sums, dim3(cblocks, 1, (unsigned)p.N), dim3(kT), 0, l.stream, (const float2*)chunk,
+                           b.chunks, p.C, b.chunks, stot);
+        kernels += 2;
+    } else {
+        hipLaunchKernelGGL(col_sums, dim3(cblocks, 1, (unsigned)p.N), dim3(kT), 0, l.stream, (const float2*)part,
+                           b.tiles, p.C, b.tiles, stot);
+        ++kernels;
+    }
+    if ((e = hipGetLastError())) return e;
+    if (want_dx || p.N == 1) {
+        hipLaunchKernelGGL(bwd_group_ab, dim3((unsigned)p.G, (unsigned)p.N), dim3(kT), 0, l.stream,
+                           (const float2*)stot, a.gamma, cfg, ab, dg, db);
+        ++kernels;
+    }
+    if (p.N > 1 && (dg || db)) {
+        hipLaunchKernelGGL(params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream,
+                           (const float2*)stot, p.N, p.C, dg, db);
+        ++kernels;
+    }
+    if ((e = hipGetLastError())) return e;
+    if (want_dx) {
+        hipLaunchKernelGGL((bwd_dx<T, RO>), ogrid, dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean,
+                           a.rstd, a.gamma, (const float2*)ab, (T*)a.dx, cfg);
+        ++kernels;
+        if ((e = hipGetLastError())) return e;
+    }
+    if ((e = record(l.ev_end, l.stream))) return e;
+    if (l.info) {
+        l.info->path = GN_PATH_STREAM;
+        l.info->kernels = kernels;
+        l.info->grid = cfg.tiles * p.N;
+        l.info->tiles = cfg.tiles * p.N;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+// Same shape condition as the NHWC slab kernels: 16-byte chunks never straddle
+// a group and the chunks of one pixel divide the workgroup.
+bool stream_ok(const Problem& p) {
+    if (p.layout != GN_NHWC || p.HW < 1) return false;
+    const int V = vec_elems(p);
+    if (p.C % V != 0 || p.D % V != 0) return false;
+    const int64_t cpp = p.C / V;
+    if (cpp < 1 || cpp > kT || (kT % cpp) != 0) return false;
+    // grid limits: samples and column-sum chunks on grid y (at most 65535)
+    if (p.N > 65535) return false;
+    const int64_t chunks = (tiles_of(p, GN_STREAM_R_SUMS) + kRowsPerChunk - 1) / kRowsPerChunk;
+    return chunks <= 65535 && tiles_of(p, 1) <= INT32_MAX;   // grid x: tiles of the smallest size
+}
+
+size_t stream_fwd_ws(const Problem& p) {
+    return al((size_t)p.N * p.G * tiles_of(p, GN_STREAM_R_STATS) * sizeof(float4));
+}
+
+size_t stream_bwd_ws(const Problem& p, int32_t) { return bwd_plan(p).total; }
+
+hipError_t stream_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {
+    switch (p.dtype) {
+        case GN_F32: return fwd_t<float>(p, a, l);
+        case GN_F16: return fwd_t<_Float16>(p, a, l);
+        default: return fwd_t<__bf16>(p, a, l);
+    }
+}
+
+hipError_t stream_bwd(const Problem& p, const BwdArgs& a, const Launch& l) {
+    switch (p.dtype) {
+        case GN_F32: return bwd_t<float>(p, a, l);
+        case GN_F16: return bwd_t<_Float16>(p, a, l);
+        default: return bwd_t<__bf16>(p, a, l);
+    }
+}
+
+}  // namespace gn

@@ -61,7 +61,7 @@ def _full_compare(wl, expect_path):
 @pytest.mark.timeout(900)
 def test_full_nhwc_image():
     _need_gpu()
-    _full_compare(inputs.NHWC_IMG, gn.GN_PATH_SLAB)
+    _full_compare(inputs.NHWC_IMG, gn.GN_PATH_STREAM)
 
 
 @pytest.mark.timeout(900)

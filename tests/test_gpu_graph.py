@@ -16,6 +16,8 @@ W = inputs.Workload
     (W("graph_rows_f16", 512, 1024, 1, 1, 1, "f16", "nchw"), None),
     (W("graph_gen_bf16", 2, 16, 20, 21, 4, "bf16", "nhwc"), "generic"),
     (inputs.TINY, None),
+    (W("graph_slab_nhwc_f16", 2, 64, 37, 29, 8, "f16", "nhwc"), "slab"),
+    (W("graph_stream_nhwc_f16", 2, 64, 130, 131, 8, "f16", "nhwc"), "stream"),
 ], ids=lambda v: getattr(v, "name", str(v)))
 def test_graph_replays_match_eager(wl, force):
     if not torch.cuda.is_available():

@@ -62,7 +62,7 @@ def test_overflow_tiles_exist_under_a_cap():
 
 
 def test_auto_selects_slab():
-    assert gn.select_path(True, 1, 128, 1024 * 2048, 16, 1, gn._lib.GN_NHWC) == gn.GN_PATH_SLAB
+    assert gn.select_path(True, 1, 128, 64 * 130, 16, 1, gn._lib.GN_NHWC) == gn.GN_PATH_SLAB
     assert gn.select_path(False, 112, 64, 512 * 512, 8, 0, gn._lib.GN_NCHW) == gn.GN_PATH_SLAB
     assert gn.select_path(False, 2, 32, 256, 8, 0, gn._lib.GN_NCHW) == gn.GN_PATH_SLAB
 

@@ -1,0 +1,89 @@
+"""GPU parity of the stream path (NHWC as a few launches of one tile per
+workgroup) against the fp64 oracle.
+
+Cases cover every activation dtype, one and several samples (dgamma/dbeta
+written by the per-group kernel or summed over the samples), a tile count
+past one column-sum chunk (the two-level channel reduction), groups of
+several 16-byte chunks (the merge tree across chunks), ragged last tiles and
+every output mask.
+"""
+import pytest
+import torch
+
+import normalization_gn_stats_amd as gn
+from normalization_gn_stats_amd import inputs
+from gpu_harness import ALL, check_against_oracle, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+W = inputs.Workload
+
+CASES = [
+    W("stream_nhwc_f16_c64_g8", 2, 64, 37, 29, 8, "f16", "nhwc"),
+    W("stream_nhwc_f32_c32_g4", 3, 32, 50, 41, 4, "f32", "nhwc"),
+    W("stream_nhwc_bf16_c128_g16", 1, 128, 64, 130, 16, "bf16", "nhwc", affine="n01"),
+    W("stream_nhwc_f16_c512_g32", 2, 512, 9, 23, 32, "f16", "nhwc"),
+    W("stream_nhwc_f16_c8_g1", 2, 8, 31, 33, 1, "f16", "nhwc"),
+    # 4 chunks per group (two merge levels across chunks); one pixel per
+    # iteration (256 chunks per pixel: no merge over pixel rows)
+    W("stream_nhwc_f16_c64_g2", 2, 64, 33, 35, 2, "f16", "nhwc"),
+    W("stream_nhwc_f16_c2048_g8", 1, 2048, 5, 9, 8, "f16", "nhwc"),
+    # more than 64 backward tiles per sample: two column-sum levels
+    W("stream_nhwc_f16_c64_twolevel", 2, 64, 130, 131, 8, "f16", "nhwc"),
+    W("stream_nhwc_f32_c16_twolevel", 1, 16, 200, 181, 2, "f32", "nhwc"),
+]
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+
+
+def _servable(wl):
+    p = gn.select_path(False, wl.N, wl.C, wl.HW, wl.G, {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype],
+                       gn._lib.GN_NHWC, "stream")
+    return p == gn.GN_PATH_STREAM
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_stream_parity(wl):
+    _need_gpu()
+    if not _servable(wl):
+        pytest.skip("shape outside the stream path (chunks per pixel must divide the workgroup)")
+    say(f"[stream] {wl.name}")
+    data = inputs.make_inputs(wl, seed=3)
+    out = run_gpu(wl, data, force_path="stream")
+    assert out["fwd_plan"].path == gn.GN_PATH_STREAM and out["bwd_plan"].path == gn.GN_PATH_STREAM
+    check_against_oracle(wl, data, out)
+
+
+MASKS = [gn.GN_GRAD_DX, gn.GN_GRAD_DGAMMA, gn.GN_GRAD_DBETA, gn.GN_GRAD_DGAMMA | gn.GN_GRAD_DBETA,
+         gn.GN_GRAD_DX | gn.GN_GRAD_DBETA, ALL]
+
+
+@pytest.mark.parametrize("mask", MASKS)
+@pytest.mark.parametrize("wl", [W("stream_mask_n1", 1, 64, 40, 41, 8, "f16", "nhwc"),
+                                W("stream_mask_n3", 3, 32, 30, 31, 4, "bf16", "nhwc")], ids=lambda w: w.name)
+def test_stream_output_mask(wl, mask):
+    _need_gpu()
+    say(f"[stream-mask] {wl.name} mask={mask}")
+    data = inputs.make_inputs(wl, seed=5)
+    out = run_gpu(wl, data, force_path="stream", mask=mask)
+    assert out["bwd_plan"].path == gn.GN_PATH_STREAM
+    check_against_oracle(wl, data, out, mask=mask)
+    if not mask & gn.GN_GRAD_DGAMMA:
+        assert out["dgamma"] is None
+    if not mask & gn.GN_GRAD_DBETA:
+        assert out["dbeta"] is None
+
+
+def test_stream_bitwise_deterministic():
+    _need_gpu()
+    wl = W("stream_det", 2, 64, 130, 131, 8, "bf16", "nhwc")
+    data = inputs.make_inputs(wl, seed=7)
+    a = run_gpu(wl, data, force_path="stream")
+    b = run_gpu(wl, data, force_path="stream")
+    for k in ("y", "mean", "rstd", "dx", "dgamma", "dbeta"):
+        ta, tb = a[k], b[k]
+        if ta.dim() == 4:
+            ta, tb = inputs.memory_image(ta, wl.layout), inputs.memory_image(tb, wl.layout)
+        assert torch.equal(ta.contiguous().view(torch.uint8), tb.contiguous().view(torch.uint8)), k

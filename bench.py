@@ -71,6 +71,44 @@ def recorded_traffic(workload, kernel_name, grid):
     return int(e["read_bytes"] + e["write_bytes"])
 
 
+class TimingEvents:
+    """HIP events for kernel timing, created with hipEventDisableSystemFence:
+    recording them performs no system-scope fence (no cache write-back and
+    invalidation around the timed kernel), which on MI355X keeps the event
+    pair of a microsecond-scale kernel within about a microsecond of the
+    kernel's own duration (plain events read 1.5-2 us high)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch already loaded
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        st = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {st}")
+        self.made.append(e)
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        st = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(a), self.ct.c_void_p(b))
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {st}")
+        return ms.value
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -83,7 +121,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the oracle CPU-baseline sample (0 disables it)")
-    ap.add_argument("--force-path", default=None, choices=[None, "generic", "rows", "slab"])
+    ap.add_argument("--force-path", default=None, choices=[None, "generic", "rows", "slab", "stream"])
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times (a known-size "
                          "kernel that scales the rocprofv3 byte counters)")
@@ -142,12 +180,12 @@ def main():
         out = []
         for kind in ("fwd", "bwd"):
             o = gn._lib.Options()
-            o.force_path = {None: 0, "generic": 1, "rows": 2, "slab": 3}[args.force_path]
+            o.force_path = {None: 0, "generic": 1, "rows": 2, "slab": 3, "stream": 4}[args.force_path]
             o.info = ctypes.pointer(sh["fplan" if kind == "fwd" else "bplan"])
             if evs is not None:
                 b, e = evs[0 if kind == "fwd" else 1]
-                o.event_begin = ctypes.c_void_p(b.cuda_event)
-                o.event_end = ctypes.c_void_p(e.cuda_event)
+                o.event_begin = ctypes.c_void_p(b)
+                o.event_end = ctypes.c_void_p(e)
             if kind == "fwd":
                 a = (P(sh["x"]), P(sh["gamma"]), P(sh["beta"]), P(sh["y"]), P(sh["mean"]), P(sh["rstd"]),
                      wl.N, wl.C, wl.HW, wl.G, ctypes.c_float(wl.eps), code, lay, P(sh["fws"]),
@@ -195,14 +233,8 @@ def main():
         torch.cuda.synchronize()
 
     # per-step, per-shape (fwd, bwd) x (begin, end) events around each main kernel
-    events = [[[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(2)]
-               for _ in shapes] for _ in range(K)]
-    for row in events:             # torch creates HIP events lazily at their first record
-        for per_shape in row:
-            for pair in per_shape:
-                for ev in pair:
-                    ev.record(stream)
-    torch.cuda.synchronize()
+    tev = TimingEvents()
+    events = [[[[tev.new() for _ in range(2)] for _ in range(2)] for _ in shapes] for _ in range(K)]
     evcalls = [[c for k, sh in enumerate(shapes) for c in calls_for(sh, sp, events[i][k])] for i in range(K)]
 
     log(f"timing {K} steps ({mode})")
@@ -240,29 +272,41 @@ def main():
     calls = []
     for k, sh in enumerate(shapes):
         wl = sh["wl"]
-        for c, (kind, nbytes, plan) in enumerate((
-                ("fwd", wl.fwd_min_bytes(), sh["fplan"]),
+        for c, (kind, plan) in enumerate((("fwd", sh["fplan"]), ("bwd", sh["bplan"]))):
+            path = gn.PATH_NAMES[plan.path]
+            if path == "stream":
+                # the stream path's events bracket all kernels of the call: the
+                # call's algorithmic bytes over the call's time
+                nbytes = wl.fwd_min_bytes() if kind == "fwd" else wl.bwd_min_bytes()
+            elif kind == "fwd":
+                nbytes = wl.fwd_min_bytes()
+            else:
                 # the main backward kernel writes dx; dgamma/dbeta (2*C*4 bytes) are
                 # written by the small column-sum kernel when one follows
-                ("bwd", wl.bwd_min_bytes() - (2 * wl.C * 4 if sh["bplan"].kernels > 1 else 0), sh["bplan"]))):
-            durs = [events[i][k][c][0].elapsed_time(events[i][k][c][1]) for i in range(K)]
+                nbytes = wl.bwd_min_bytes() - (2 * wl.C * 4 if plan.kernels > 1 else 0)
+            durs = [tev.elapsed_ms(events[i][k][c][0], events[i][k][c][1]) for i in range(K)]
             avg_ms = sum(durs) / len(durs)
             kname = {("rows", "fwd"): "rows_fwd_k", ("rows", "bwd"): "rows_bwd_k",
-                     ("slab", "fwd"): f"slab_{wl.layout}_fwd", ("slab", "bwd"): f"slab_{wl.layout}_bwd"
-                     }.get((gn.PATH_NAMES[plan.path], kind))
-            calls.append(dict(shape=wl.name, call=kind, path=gn.PATH_NAMES[plan.path], kernels=plan.kernels,
-                              kernel=kname, grid=plan.grid,
+                     ("slab", "fwd"): f"slab_{wl.layout}_fwd", ("slab", "bwd"): f"slab_{wl.layout}_bwd",
+                     ("stream", "fwd"): "stream_fwd_call", ("stream", "bwd"): "stream_bwd_call",
+                     }.get((path, kind))
+            calls.append(dict(shape=wl.name, call=kind, path=path, kernels=plan.kernels,
+                              kernel=kname, grid=plan.grid if path != "stream" else "call",
                               main_kernel_us=avg_ms * 1e3, main_kernel_bytes=nbytes,
                               main_kernel_gbs=nbytes / (avg_ms * 1e-3) / 1e9))
+    tev.close()
     dom = max(calls, key=lambda c: c["main_kernel_us"])
     traffic = recorded_traffic(args.workload, dom["kernel"], dom["grid"]) if dom["kernel"] else None
     roofline = {"bound": "hbm", "achieved": round(dom["main_kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dom["main_kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "traffic_over_algorithmic": (round(traffic / dom["main_kernel_bytes"], 3) if traffic else None),
-                "kernel": f"{dom['call']} {dom['path']} main kernel on {dom['shape']}",
+                "kernel": (f"{dom['call']} {dom['path']} " + ("call (all its kernels)" if dom["path"] == "stream"
+                                                                  else "main kernel") + f" on {dom['shape']}"),
                 "avg_us": round(dom["main_kernel_us"], 3), "algorithmic_bytes": dom["main_kernel_bytes"],
-                "timing": ("HIP events recorded by the library on the call's stream around the main kernel, "
+                "timing": ("HIP events (created without the system-scope fence) recorded by the library on "
+                           "the call's stream around the main kernel "
+                           "(stream path: around all kernels of the call), "
                            + ("K eager steps queued behind a GPU spin after the graph-timed region"
                               if mode == "graph" else "over the timed region"))}
 

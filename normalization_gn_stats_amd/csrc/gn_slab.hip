@@ -442,7 +442,8 @@ __device__ inline void nchw_load_tile(const T* __restrict__ src, const SlabCfg& 
     }
 }
 
-// Phase 1 of the forward for slab sb: statistics of member m's tiles, one
+// Phase 1 of the forward for slab sb: statistics of member m's tiles (the
+// first one already in buf when `preloaded`), one
 // (count, mean, M2) partial per tile -- an exact two-pass over the tile in
 // registers: workgroup sum -> tile mean -> workgroup sum of squared
 // deviations.  The last tile stays in buf; its channel's gamma/beta are
@@ -451,14 +452,14 @@ __device__ inline void nchw_load_tile(const T* __restrict__ src, const SlabCfg& 
 template <typename T, int R>
 __device__ inline int64_t nchw_fwd_phase1(const T* __restrict__ x, const float* __restrict__ gamma,
                                           const float* __restrict__ beta, const SlabCfg& cfg, int64_t sb, int m,
-                                          u4v (&buf)[R], float2& gb, float4* part, float* lds) {
+                                          u4v (&buf)[R], float2& gb, float4* part, float* lds, bool preloaded) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
     const int t = threadIdx.x;
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
         const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
-        nchw_load_tile<T, R, false>(x, cfg, sb, tile, buf);
+        if (!(preloaded && tile == m)) nchw_load_tile<T, R, false>(x, cfg, sb, tile, buf);
         const int64_t c = (sb - (sb / cfg.G) * cfg.G) * cfg.D + cl;
         gb = make_float2(gamma ? gamma[c] : 1.f, beta ? beta[c] : 0.f);
         const int64_t rem = cfg.HW - k0;
@@ -564,8 +565,13 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
 
 // Two slabs in flight per team: after arriving at slab s's barrier a member
 // runs phase 1 of the team's next slab (into the second register tile) and
-// arrives there too, and only then waits on s -- the barrier latency of s is
-// covered by the next slab's loads.
+// arrives there too, and only then waits on s -- slab s's barrier has had a
+// whole phase of slack, and the y stores of s are issued right before the
+// loads of the slab after, so that the two streams overlap in the memory
+// system.  (A wave's memory operations complete in issue order -- one
+// counter for loads and stores -- so every dependent load also waits for the
+// bulk traffic issued before it; of the orders measured, this one is the
+// fastest for the forward.)
 template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
                                                     const float* __restrict__ beta, T* __restrict__ y,
@@ -578,18 +584,19 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
     float2 gcur = make_float2(1.f, 0.f), gnxt = gcur;
     int64_t sb = team;
     if (sb >= cfg.n_slabs) return;   // uniform over the team
-    int64_t last = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, sb, m, cur, gcur, part, lds);
+    int64_t last = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, sb, m, cur, gcur, part, lds, false);
     team_arrive(&ctr[sb * 4 + 0]);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
+        const bool more = nsb < cfg.n_slabs;   // uniform over the team
         int64_t nlast = -1;
-        if (nsb < cfg.n_slabs) {
-            nlast = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, nsb, m, nxt, gnxt, part, lds);
+        if (more) {
+            nlast = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, nsb, m, nxt, gnxt, part, lds, false);
             team_arrive(&ctr[nsb * 4 + 0]);
         }
         team_wait(&ctr[sb * 4 + 0], (uint32_t)cfg.team, err);
         nchw_fwd_phase2<T, R>(x, gamma, beta, y, mean, rstd, cfg, sb, m, last, cur, gcur, part, lds);
-        if (nsb >= cfg.n_slabs) break;
+        if (!more) break;
 #pragma unroll
         for (int j = 0; j < R; ++j) cur[j] = nxt[j];
         gcur = gnxt;
@@ -598,13 +605,14 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
     }
 }
 
-// Phase 1 of the backward for slab sb: per-tile sums of dy and dy*xhat; the
-// last tile of x and dy stays in bx, bd.
+// Phase 1 of the backward for slab sb: per-tile sums of dy and dy*xhat (the
+// member's first tile already in bx, bd when `preloaded`); the last tile of x
+// and dy stays in bx, bd.
 template <typename T, int R>
 __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __restrict__ x,
                                           const float* __restrict__ mean, const float* __restrict__ rstd,
                                           const SlabCfg& cfg, int64_t sb, int m, u4v (&bx)[R], u4v (&bd)[R],
-                                          float2* part, float* lds) {
+                                          float2* part, float* lds, bool preloaded) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
     const int t = threadIdx.x;
@@ -612,8 +620,10 @@ __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __r
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
         const int64_t k0 = (tile - (tile / cfg.tpc) * cfg.tpc) * TE;
-        nchw_load_tile<T, R, true>(x, cfg, sb, tile, bx);
-        nchw_load_tile<T, R, true>(dy, cfg, sb, tile, bd);
+        if (!(preloaded && tile == m)) {
+            nchw_load_tile<T, R, true>(x, cfg, sb, tile, bx);
+            nchw_load_tile<T, R, true>(dy, cfg, sb, tile, bd);
+        }
         float acc[2] = {0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < R; ++j) {
@@ -713,7 +723,11 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
 }
 
 // part: [slab][tile] float2 (sum dy, sum dy*xhat of the tile); stot: [N][C] float2.
-// Same two-slab pipeline as the forward.  Requires D <= kT (checked on the host).
+// Two slabs in flight as in the forward, in the order measured fastest for
+// the backward: the loads of the next slab's first tile are issued before
+// the wait on slab s's barrier, so that they stream during the wait and
+// during the dx stores of s; the next slab's sums then start from registers.
+// Requires D <= kT (checked on the host).
 template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, const T* __restrict__ x,
                                                     const float* __restrict__ mean,
@@ -729,18 +743,20 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
     u4v cx[R], cd[R], nx[R], nd[R];
     int64_t sb = team;
     if (sb >= cfg.n_slabs) return;   // uniform over the team
-    int64_t last = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, sb, m, cx, cd, part, lds);
+    int64_t last = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, sb, m, cx, cd, part, lds, false);
     team_arrive(&ctr[sb * 4 + 0]);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
-        int64_t nlast = -1;
-        if (nsb < cfg.n_slabs) {
-            nlast = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, nsb, m, nx, nd, part, lds);
-            team_arrive(&ctr[nsb * 4 + 0]);
+        const bool more = nsb < cfg.n_slabs;   // uniform over the team
+        if (more && m < cfg.tiles) {
+            nchw_load_tile<T, R, true>(x, cfg, nsb, m, nx);
+            nchw_load_tile<T, R, true>(dy, cfg, nsb, m, nd);
         }
         team_wait(&ctr[sb * 4 + 0], (uint32_t)cfg.team, err);
         nchw_bwd_phase2<T, R>(dy, x, mean, rstd, gamma, dx, cfg, sb, m, last, cx, cd, part, stot, stage, chan);
-        if (nsb >= cfg.n_slabs) break;
+        if (!more) break;
+        const int64_t nlast = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, nsb, m, nx, nd, part, lds, true);
+        team_arrive(&ctr[nsb * 4 + 0]);
 #pragma unroll
         for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }
         last = nlast;

@@ -41,6 +41,10 @@ SMALL = [
     (W("rows_g4_f16_300x512", 300, 512, 1, 1, 4, "f16", "nhwc"), None, gn.GN_PATH_ROWS),
     (W("rows_g8_bf16_2100x256", 2100, 256, 1, 1, 8, "bf16", "nchw"), None, gn.GN_PATH_ROWS),
     (W("rows_f16_odd_c_20x36", 20, 36, 1, 1, 1, "f16", "nchw"), None, gn.GN_PATH_GENERIC),
+    # enough slices per group that the forward's waves walk several slices each
+    (W("rows_walk_f16_20000x64", 20000, 64, 1, 1, 1, "f16", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_walk_f32_9001x2048", 9001, 2048, 1, 1, 1, "f32", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_walk_bf16_g4_6000x1024", 6000, 1024, 1, 1, 4, "bf16", "nhwc"), None, gn.GN_PATH_ROWS),
     # degenerate shapes
     (W("deg_m1_f32", 5, 6, 1, 1, 6, "f32", "nchw"), None, None),         # one element per slice
     (W("deg_instance_f16", 2, 8, 5, 5, 8, "f16", "nchw"), None, None),   # G = C

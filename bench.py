@@ -39,6 +39,7 @@ WORKLOADS = {
     "nhwc_f16_1x128x1024x2048_g16": ("nhwc_f16_1x128x1024x2048_g16",),
     "nchw_f32_112x64x512x512_g8": ("nchw_f32_112x64x512x512_g8",),
     "rows_bf16_131072x4096": ("rows_bf16_131072x4096",),
+    "rows_f16_131072x64": ("rows_f16_131072x64",),
 }
 DEFAULT = "rows_f16_4096x1024+8192x768"
 

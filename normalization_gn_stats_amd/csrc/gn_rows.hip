@@ -8,6 +8,9 @@
 // taken from the registers (an exact two-pass variance at one read of x), and
 // y = (x - mean)*(rstd*gamma_c) + beta_c is written with 16-byte stores.
 //
+// Slices of at most 32 16-byte vectors (e.g. 64 fp16 channels) share a
+// wavefront instead: LPR lanes per slice, segmented shuffle sums.
+//
 // Backward: waves are assigned per group g and walk samples n = w, w + W, ...
 // For each slice: xhat = (x - mean)*rstd from the saved statistics,
 // A = sum gamma_c*dy, B = sum gamma_c*dy*xhat (wave sums), dx =
@@ -203,6 +206,197 @@ __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, co
         }
 #pragma unroll
         for (int j = 0; j < NV; ++j) cur[j] = nxt[j];
+    }
+}
+
+// ---- narrow slices: several slices per wavefront ----------------------------
+// A slice of at most 32 16-byte vectors takes LPR lanes (the power of two at
+// or above its vector count), so a wave holds RPW = 64/LPR slices at a time
+// instead of leaving most of its lanes idle; each lane loads RB such row sets
+// up front.  Slice sums are butterfly shuffles within the LPR lanes of a
+// slice (partners add the same two values, so every lane of the slice ends
+// with the same bits).  Same arithmetic as the one-wave-per-slice kernels.
+template <int LPR>
+__device__ inline float seg_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+template <int V>
+__device__ inline void load_vec_params(const float* __restrict__ p, int64_t c0, float dflt, float (&o)[V]) {
+#pragma unroll
+    for (int k = 0; k < V; k += 4) {
+        const float4 q = p ? *reinterpret_cast<const float4*>(p + c0 + k) : make_float4(dflt, dflt, dflt, dflt);
+        o[k] = q.x; o[k + 1] = q.y; o[k + 2] = q.z; o[k + 3] = q.w;
+    }
+}
+
+// grid: x = blocks of kNW*RPW*RB samples, y = group
+template <typename T, int LPR, int RB>
+__global__ __launch_bounds__(kT) void rows_fwd_narrow_k(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                        const float* __restrict__ beta, T* __restrict__ y,
+                                                        float* __restrict__ mean, float* __restrict__ rstd,
+                                                        int64_t N, int64_t G, int64_t C, int D, float eps) {
+    constexpr int V = Vec<T>::V;
+    constexpr int RPW = kWave / LPR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int vi = lane % LPR;   // vector within the slice
+    const int rl = lane / LPR;   // slice within the row set
+    const int64_t g = blockIdx.y;
+    const int nvec = D / V;
+    const bool act = vi < nvec;
+    const int vc = min(vi, nvec - 1);   // branch-free loads: idle lanes re-read the last vector
+    const int64_t n0 = ((int64_t)blockIdx.x * kNW + wave) * (RPW * RB);
+    u4v raw[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int64_t n = min(n0 + r * RPW + rl, N - 1);   // rows past N re-read row N-1
+        raw[r] = ld16(x + n * C + g * D + (int64_t)vc * V);
+    }
+    float ga[V], be[V];
+    load_vec_params<V>(gamma, g * D + (int64_t)vc * V, 1.f, ga);
+    load_vec_params<V>(beta, g * D + (int64_t)vc * V, 0.f, be);
+    const float invD = 1.0f / (float)D;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int64_t n = n0 + r * RPW + rl;
+        float v[V];
+        Vec<T>::unpack(raw[r], v);
+        float sum = 0.f;
+        if (act) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) sum += v[k];
+        }
+        const float mu = seg_sum<LPR>(sum) * invD;
+        float q = 0.f;
+        if (act) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float d = v[k] - mu;
+                q = fmaf(d, d, q);
+            }
+        }
+        float var = seg_sum<LPR>(q) * invD;
+        var = var > 0.f ? var : 0.f;
+        const float rs = 1.0f / sqrtf(var + eps);
+        if (n < N) {
+            if (vi == 0) {
+                mean[n * G + g] = mu;
+                rstd[n * G + g] = rs;
+            }
+            if (y != nullptr && act) {
+                float o[V];
+#pragma unroll
+                for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu, rs * ga[k], be[k]);
+                st16_nt(y + n * C + g * D + (int64_t)vi * V, Vec<T>::pack(o));
+            }
+        }
+    }
+}
+
+// grid: x = NB workgroups per group, y = group; part as for rows_bwd_k.  A
+// workgroup takes blocks of RPB = kNW*RPW*RB samples (blocks b, b + NB, ...).
+template <typename T, int LPR, int RB>
+__global__ __launch_bounds__(kT) void rows_bwd_narrow_k(const T* __restrict__ dy, const T* __restrict__ x,
+                                                        const float* __restrict__ mean,
+                                                        const float* __restrict__ rstd,
+                                                        const float* __restrict__ gamma, T* __restrict__ dx,
+                                                        float2* __restrict__ part, int64_t N, int64_t G, int64_t C,
+                                                        int D, int NB, int want_dx, int want_params) {
+    constexpr int V = Vec<T>::V;
+    constexpr int RPW = kWave / LPR;
+    constexpr int RPB = kNW * RPW * RB;
+    __shared__ float2 red_cols[kNW][32 * 8];   // per-wave column sums (D <= 32 vectors of <= 8)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int vi = lane % LPR;
+    const int rl = lane / LPR;
+    const int64_t g = blockIdx.y;
+    const int b = blockIdx.x;
+    const int nvec = D / V;
+    const bool act = vi < nvec;
+    const int vc = min(vi, nvec - 1);
+    const float invD = 1.0f / (float)D;
+    float gam[V];
+    load_vec_params<V>(gamma, g * D + (int64_t)vc * V, 1.f, gam);
+    float cs1[V], cs2[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) { cs1[k] = 0.f; cs2[k] = 0.f; }
+    for (int64_t blk = b; blk * RPB < N; blk += NB) {   // uniform over the workgroup
+        const int64_t n0 = blk * RPB + (int64_t)wave * (RPW * RB);
+        u4v rx[RB], rd[RB];
+        float mu[RB], rs[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t n = min(n0 + r * RPW + rl, N - 1);   // rows past N re-read row N-1
+            const int64_t off = n * C + g * D + (int64_t)vc * V;
+            rx[r] = ld16(x + off);
+            rd[r] = ld16(dy + off);
+            mu[r] = mean[n * G + g];
+            rs[r] = rstd[n * G + g];
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t n = n0 + r * RPW + rl;
+            const bool valid = act && n < N;
+            float xv[V], dv[V];
+            Vec<T>::unpack(rx[r], xv);
+            Vec<T>::unpack(rd[r], dv);
+            float a = 0.f, bb = 0.f;
+            if (valid) {
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float xh = (xv[k] - mu[r]) * rs[r];
+                    const float gd = dv[k] * gam[k];
+                    a += gd;
+                    bb = fmaf(gd, xh, bb);
+                    cs1[k] += dv[k];
+                    cs2[k] = fmaf(dv[k], xh, cs2[k]);
+                }
+            }
+            const float A = seg_sum<LPR>(a) * invD;
+            const float B = seg_sum<LPR>(bb) * invD;
+            if (want_dx && valid) {
+                // gamma*dy rounded as it entered A, so that equal terms cancel exactly
+#pragma clang fp contract(off)
+                float o[V];
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float xh = (xv[k] - mu[r]) * rs[r];
+                    const float gd = dv[k] * gam[k];
+                    o[k] = rs[r] * ((gd - A) - xh * B);
+                }
+                st16_nt(dx + n * C + g * D + (int64_t)vi * V, Vec<T>::pack(o));
+            }
+        }
+    }
+    if (!want_params) return;
+    // column sums: the wave's row sets (lanes of equal vi) by butterfly, then
+    // the waves in wave order through LDS
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+#pragma unroll
+        for (int m = LPR; m < kWave; m <<= 1) {
+            cs1[k] += __shfl_xor(cs1[k], m, kWave);
+            cs2[k] += __shfl_xor(cs2[k], m, kWave);
+        }
+    }
+    if (lane < LPR && act) {
+#pragma unroll
+        for (int k = 0; k < V; ++k) red_cols[wave][vi * V + k] = make_float2(cs1[k], cs2[k]);
+    }
+    __syncthreads();
+    float2* dst = part + ((int64_t)g * NB + b) * D;
+    for (int c = threadIdx.x; c < D; c += kT) {
+        float2 t = red_cols[0][c];
+#pragma unroll
+        for (int w = 1; w < kNW; ++w) {
+            t.x += red_cols[w][c].x;
+            t.y += red_cols[w][c].y;
+        }
+        dst[c] = t;
     }
 }
 
@@ -493,6 +687,82 @@ int rows_nb(const Problem& p) {
     return (int)(need < target ? need : target);
 }
 
+#ifndef GN_ROWS_NARROW_RBF
+#define GN_ROWS_NARROW_RBF 2   // row sets per lane in the narrow forward
+#endif
+#ifndef GN_ROWS_NARROW_RBB
+#define GN_ROWS_NARROW_RBB 8   // row sets per lane in the narrow backward
+#endif
+
+// Lanes per slice of the narrow kernels (1 .. 32), or 0 when the slice takes
+// more than 32 vectors (one or more waves per slice instead).
+int narrow_lpr(const Problem& p) {
+    const int V = p.elem_bytes == 4 ? 4 : 8;
+    const int64_t nvec = p.D / V;
+    if (nvec > 32) return 0;
+    int lpr = 1;
+    while (lpr < nvec) lpr *= 2;
+    return lpr;
+}
+
+int narrow_nb(const Problem& p) {
+    const int lpr = narrow_lpr(p);
+    const int64_t rpb = (int64_t)kNW * (kWave / lpr) * GN_ROWS_NARROW_RBB;
+    int64_t target = kBwdTargetWG / (p.G < 1 ? 1 : p.G);
+    if (target < 1) target = 1;
+    int64_t need = (p.N + rpb - 1) / rpb;
+    if (need < 1) need = 1;
+    return (int)(need < target ? need : target);
+}
+
+template <typename T, int LPR>
+hipError_t fwd_narrow(const Problem& p, const FwdArgs& a, const Launch& l) {
+    constexpr int RB = GN_ROWS_NARROW_RBF;
+    constexpr int64_t rows_per_wg = (int64_t)kNW * (kWave / LPR) * RB;
+    const unsigned grid = (unsigned)((p.N + rows_per_wg - 1) / rows_per_wg);
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL((rows_fwd_narrow_k<T, LPR, RB>), dim3(grid, (unsigned)p.G), dim3(kT), 0, l.stream,
+                       (const T*)a.x, a.gamma, a.beta, (T*)a.y, a.mean, a.rstd, p.N, p.G, p.C, (int)p.D, a.eps);
+    if ((e = hipGetLastError())) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    if (l.info) {
+        l.info->path = GN_PATH_ROWS;
+        l.info->kernels = 1;
+        l.info->grid = (int64_t)grid * p.G;
+    }
+    return hipSuccess;
+}
+
+template <typename T, int LPR>
+hipError_t bwd_narrow(const Problem& p, const BwdArgs& a, const Launch& l) {
+    constexpr int RB = GN_ROWS_NARROW_RBB;
+    const int NB = narrow_nb(p);
+    const bool params = (a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) != 0;
+    float2* part = (float2*)l.ws;
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL((rows_bwd_narrow_k<T, LPR, RB>), dim3((unsigned)NB, (unsigned)p.G), dim3(kT), 0, l.stream,
+                       (const T*)a.dy, (const T*)a.x, a.mean, a.rstd, a.gamma, (T*)a.dx, part, p.N, p.G, p.C,
+                       (int)p.D, NB, (a.mask & GN_GRAD_DX) ? 1 : 0, params ? 1 : 0);
+    if ((e = hipGetLastError())) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    int kernels = 1;
+    if (params) {
+        hipLaunchKernelGGL(rows_colsum_k, dim3((unsigned)((p.D + 2 * kColPairs - 1) / (2 * kColPairs)), (unsigned)p.G),
+                           dim3(kT), 0, l.stream, part, NB, (int)p.D, (a.mask & GN_GRAD_DGAMMA) ? a.dgamma : nullptr,
+                           (a.mask & GN_GRAD_DBETA) ? a.dbeta : nullptr);
+        if ((e = hipGetLastError())) return e;
+        ++kernels;
+    }
+    if (l.info) {
+        l.info->path = GN_PATH_ROWS;
+        l.info->kernels = kernels;
+        l.info->grid = (int64_t)NB * p.G;
+    }
+    return hipSuccess;
+}
+
 template <typename T, int NV>
 hipError_t fwd_nv(const Problem& p, const FwdArgs& a, const Launch& l) {
     unsigned grid = (unsigned)((p.N + kNW - 1) / kNW);
@@ -562,6 +832,15 @@ hipError_t bwd_launch(const Problem& p, const BwdArgs& a, const Launch& l) {
 
 template <typename T>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
+    switch (narrow_lpr(p)) {
+        case 1: return fwd_narrow<T, 1>(p, a, l);
+        case 2: return fwd_narrow<T, 2>(p, a, l);
+        case 4: return fwd_narrow<T, 4>(p, a, l);
+        case 8: return fwd_narrow<T, 8>(p, a, l);
+        case 16: return fwd_narrow<T, 16>(p, a, l);
+        case 32: return fwd_narrow<T, 32>(p, a, l);
+        default: break;
+    }
     switch (nv_for(p)) {
         case 1: return fwd_nv<T, 1>(p, a, l);
         case 2: return fwd_nv<T, 2>(p, a, l);
@@ -572,6 +851,15 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
 
 template <typename T>
 hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
+    switch (narrow_lpr(p)) {
+        case 1: return bwd_narrow<T, 1>(p, a, l);
+        case 2: return bwd_narrow<T, 2>(p, a, l);
+        case 4: return bwd_narrow<T, 4>(p, a, l);
+        case 8: return bwd_narrow<T, 8>(p, a, l);
+        case 16: return bwd_narrow<T, 16>(p, a, l);
+        case 32: return bwd_narrow<T, 32>(p, a, l);
+        default: break;
+    }
     constexpr int RBS = GN_ROWS_BWD_RB;
     const BwdShape sh = bwd_shape(p);
     switch (sh.cs * 100 + sh.nv) {
@@ -600,7 +888,7 @@ size_t rows_fwd_ws(const Problem&) { return 0; }
 
 size_t rows_bwd_ws(const Problem& p, int32_t mask) {
     if (!(mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA))) return 0;
-    return (size_t)p.G * rows_nb(p) * p.D * sizeof(float2);
+    return (size_t)p.G * (narrow_lpr(p) ? narrow_nb(p) : rows_nb(p)) * p.D * sizeof(float2);
 }
 
 hipError_t rows_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {

@@ -80,8 +80,10 @@ ROWS_B = Workload("rows_f16_8192x768", 8192, 768, 1, 1, 1, "f16", "nchw")
 NHWC_IMG = Workload("nhwc_f16_1x128x1024x2048_g16", 1, 128, 1024, 2048, 16, "f16", "nhwc", affine="n01")
 NCHW_BIG = Workload("nchw_f32_112x64x512x512_g8", 112, 64, 512, 512, 8, "f32", "nchw")
 ROWS_BIG = Workload("rows_bf16_131072x4096", 131072, 4096, 1, 1, 1, "bf16", "nchw")
+# Narrow rows with many of them (the "huge M" LayerNorm shape of the same table).
+ROWS_NARROW = Workload("rows_f16_131072x64", 131072, 64, 1, 1, 1, "f16", "nchw")
 
-WORKLOADS = {w.name: w for w in (TINY, ROWS_A, ROWS_B, NHWC_IMG, NCHW_BIG, ROWS_BIG)}
+WORKLOADS = {w.name: w for w in (TINY, ROWS_A, ROWS_B, NHWC_IMG, NCHW_BIG, ROWS_BIG, ROWS_NARROW)}
 
 
 def make_inputs(wl: Workload, seed: int = 0, device: str = "cpu"):

@@ -18,6 +18,7 @@ W = inputs.Workload
     (inputs.TINY, None),
     (W("graph_slab_nhwc_f16", 2, 64, 37, 29, 8, "f16", "nhwc"), "slab"),
     (W("graph_stream_nhwc_f16", 2, 64, 130, 131, 8, "f16", "nhwc"), "stream"),
+    (W("graph_rows_narrow_f16", 3000, 64, 1, 1, 1, "f16", "nchw"), None),
 ], ids=lambda v: getattr(v, "name", str(v)))
 def test_graph_replays_match_eager(wl, force):
     if not torch.cuda.is_available():

@@ -42,9 +42,17 @@ SMALL = [
     (W("rows_g8_bf16_2100x256", 2100, 256, 1, 1, 8, "bf16", "nchw"), None, gn.GN_PATH_ROWS),
     (W("rows_f16_odd_c_20x36", 20, 36, 1, 1, 1, "f16", "nchw"), None, gn.GN_PATH_GENERIC),
     # enough slices per group that the forward's waves walk several slices each
-    (W("rows_walk_f16_20000x64", 20000, 64, 1, 1, 1, "f16", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_walk_f16_20000x512", 20000, 512, 1, 1, 1, "f16", "nchw"), None, gn.GN_PATH_ROWS),
     (W("rows_walk_f32_9001x2048", 9001, 2048, 1, 1, 1, "f32", "nchw"), None, gn.GN_PATH_ROWS),
-    (W("rows_walk_bf16_g4_6000x1024", 6000, 1024, 1, 1, 4, "bf16", "nhwc"), None, gn.GN_PATH_ROWS),
+    (W("rows_walk_bf16_g4_6000x4096", 6000, 4096, 1, 1, 4, "bf16", "nhwc"), None, gn.GN_PATH_ROWS),
+    # narrow slices (at most 32 vectors): several slices per wavefront, from
+    # 64 slices per wave (one vector each) to 2 (32 vectors each), with idle
+    # lanes (6 vectors on 8 lanes) and ragged last row sets
+    (W("rows_narrow_f16_131072x64", 131072, 64, 1, 1, 1, "f16", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_narrow_f32_5003x4", 5003, 4, 1, 1, 1, "f32", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_narrow_bf16_g2_777x96", 777, 96, 1, 1, 2, "bf16", "nhwc"), None, gn.GN_PATH_ROWS),
+    (W("rows_narrow_f32_1001x128", 1001, 128, 1, 1, 1, "f32", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_narrow_f16_g4_3000x256", 3000, 256, 1, 1, 4, "f16", "nchw"), None, gn.GN_PATH_ROWS),
     # degenerate shapes
     (W("deg_m1_f32", 5, 6, 1, 1, 6, "f32", "nchw"), None, None),         # one element per slice
     (W("deg_instance_f16", 2, 8, 5, 5, 8, "f16", "nchw"), None, None),   # G = C
@@ -72,6 +80,7 @@ MASKS = [gn.GN_GRAD_DX, gn.GN_GRAD_DGAMMA, gn.GN_GRAD_DBETA, gn.GN_GRAD_DGAMMA |
 
 @pytest.mark.parametrize("mask", MASKS)
 @pytest.mark.parametrize("wl", [W("mask_rows_f16", 96, 1024, 1, 1, 1, "f16", "nchw"),
+                                W("mask_rows_narrow_bf16", 900, 64, 1, 1, 2, "bf16", "nchw"),
                                 W("mask_gen_f32", 2, 12, 9, 10, 3, "f32", "nhwc")], ids=lambda w: w.name)
 def test_output_mask(wl, mask):
     _need_gpu()

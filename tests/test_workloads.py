@@ -23,7 +23,8 @@ def test_nchw_workload_is_the_popcornbench_problem():
 
 def test_row_workloads_are_the_rocm_table_shapes():
     g = GOLD["rocm_pytorch_3564_shapes"]
-    for w, key in ((inputs.ROWS_A, "tile256_large"), (inputs.ROWS_B, "gpt2_style"), (inputs.ROWS_BIG, "llm_hidden_4096")):
+    for w, key in ((inputs.ROWS_A, "tile256_large"), (inputs.ROWS_B, "gpt2_style"), (inputs.ROWS_BIG, "llm_hidden_4096"),
+                   (inputs.ROWS_NARROW, "two_pass_huge_M")):
         assert (w.N, w.C, w.dtype, w.G, w.HW) == (g[key]["rows"], g[key]["cols"], g[key]["dtype"], 1, 1)
 
 

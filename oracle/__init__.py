@@ -9,7 +9,9 @@ Definition followed (see the header of ``gn_oracle.c`` for the citations):
 forward = per-(n, group) mean and biased variance, x_hat = (x - mean) /
 sqrt(var + eps), y = gamma_c * x_hat + beta_c; backward = dbeta, dgamma column
 sums, per-slice A = sum(gamma*dy), B = sum(gamma*dy*x_hat), and
-dx = rstd * (gamma*dy - A/M - x_hat*B/M).
+dx = rstd * (gamma*dy - A/M - x_hat*B/M).  RMSNorm over rows (``rms_forward``,
+``rms_backward``): r = 1/sqrt(mean(x^2) + eps), y = gamma_c * x * r,
+dx = r * (gamma*dy - x_hat * sum(gamma*dy*x_hat)/D), dgamma = sum dy*x_hat.
 """
 from __future__ import annotations
 
@@ -53,6 +55,10 @@ def _load(path: str) -> ctypes.CDLL:
     lib.gno_forward.restype = i
     lib.gno_backward.argtypes = [i64, i64, i64, i64, i, p, p, p, d, p, p, p, p, p, p]
     lib.gno_backward.restype = i
+    lib.gno_rms_forward.argtypes = [i64, i64, i64, p, p, d, p, p]
+    lib.gno_rms_forward.restype = i
+    lib.gno_rms_backward.argtypes = [i64, i64, i64, p, p, p, d, p, p, p]
+    lib.gno_rms_backward.restype = i
     lib.gno_num_threads.restype = i
     lib.gno_set_num_threads.argtypes = [i]
     _libs[path] = lib
@@ -128,6 +134,46 @@ def backward(dy, x, gamma, N: int, C: int, HW: int, G: int, eps: float,
     if rc != 0:
         raise ValueError("oracle backward: invalid arguments")
     return dx, dgamma, dbeta, mean, rstd
+
+
+def rms_forward(x, gamma, N: int, C: int, G: int, eps: float, want_y: bool = True, mutant: int = 0):
+    """RMSNorm over rows of D = C/G channels of an [N, C] tensor.
+    Returns (y or None, rstd[N*G]) as float64 numpy arrays."""
+    lib = _load(LIB_MUT if mutant else LIB)
+    if mutant:
+        ctypes.c_int.in_dll(lib, "gno_mutation").value = mutant
+    x = _f64(x)
+    g = _f64(gamma)
+    assert x.size == N * C
+    y = np.empty(N * C, np.float64) if want_y else None
+    rstd = np.empty(N * G, np.float64)
+    rc = lib.gno_rms_forward(N, C, G, _ptr(x), _ptr(g), float(eps), _ptr(y), _ptr(rstd))
+    if mutant:
+        ctypes.c_int.in_dll(lib, "gno_mutation").value = 0
+    if rc != 0:
+        raise ValueError("oracle rms forward: invalid arguments")
+    return y, rstd
+
+
+def rms_backward(dy, x, gamma, N: int, C: int, G: int, eps: float, want_dx: bool = True,
+                 want_dgamma: bool = True, mutant: int = 0):
+    """Returns (dx or None, dgamma or None, rstd) as float64 numpy arrays."""
+    lib = _load(LIB_MUT if mutant else LIB)
+    if mutant:
+        ctypes.c_int.in_dll(lib, "gno_mutation").value = mutant
+    dy = _f64(dy)
+    x = _f64(x)
+    g = _f64(gamma)
+    assert x.size == N * C and dy.size == x.size
+    dx = np.empty(N * C, np.float64) if want_dx else None
+    dgamma = np.empty(C, np.float64) if want_dgamma else None
+    rstd = np.empty(N * G, np.float64)
+    rc = lib.gno_rms_backward(N, C, G, _ptr(dy), _ptr(x), _ptr(g), float(eps), _ptr(dx), _ptr(dgamma), _ptr(rstd))
+    if mutant:
+        ctypes.c_int.in_dll(lib, "gno_mutation").value = 0
+    if rc != 0:
+        raise ValueError("oracle rms backward: invalid arguments")
+    return dx, dgamma, rstd
 
 
 def num_threads() -> int:

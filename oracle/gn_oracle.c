@@ -214,6 +214,91 @@ int gno_backward(int64_t N, int64_t C, int64_t HW, int64_t G, int layout,
     return 0;
 }
 
+/*
+ * RMSNorm over rows.  ROCm/pytorch PR #3564 benchmarks an rms_norm operator
+ * next to layer_norm (its summary table) and checks its gamma backward and
+ * autograd against a CPU reference (its test list), but prints no formula.
+ * Reading: PyTorch's rms_norm -- the root mean square over the normalised
+ * (last) dimension, no mean subtracted, a weight and no bias.  Rows are the
+ * D = C/G consecutive channels (n, g) of an [N, C] tensor (G = 1: one row per
+ * sample, as in that table):
+ *     r    = 1 / sqrt((1/D) * sum x^2 + eps)
+ *     xhat = x * r
+ *     y    = gamma_c * xhat
+ * backward (the derivative of sum(y * dy) with respect to x and gamma):
+ *     per row: B = sum gamma_c * dy * xhat
+ *     dx = r * (gamma_c * dy - xhat * B/D)
+ *     dgamma_c = sum over n of dy * xhat
+ * rstd holds r per row at index n*G + g.  gamma may be NULL (= 1).
+ */
+static double rms_row_r(int64_t C, int64_t G, const double* x, int64_t n, int64_t g, double eps) {
+    const int64_t D = C / G;
+    double ss = 0.0;
+    if (MUT(8)) { /* mutant 8: mean subtracted (a LayerNorm variance) */
+        double s = 0.0;
+        for (int64_t c = g * D; c < (g + 1) * D; ++c) s += x[n * C + c];
+        const double mu = s / (double)D;
+        for (int64_t c = g * D; c < (g + 1) * D; ++c) ss += (x[n * C + c] - mu) * (x[n * C + c] - mu);
+    } else {
+        for (int64_t c = g * D; c < (g + 1) * D; ++c) ss += x[n * C + c] * x[n * C + c];
+    }
+    const double ms = ss / (double)D;
+    return MUT(9) ? 1.0 / sqrt(ms) + 0.0 * eps : 1.0 / sqrt(ms + eps); /* mutant 9: eps dropped */
+}
+
+int gno_rms_forward(int64_t N, int64_t C, int64_t G, const double* x, const double* gamma, double eps,
+                    double* y, double* rstd) {
+    if (N < 0 || C < 0 || G <= 0 || C % G != 0) return 1;
+    const int64_t D = C / G;
+    const int64_t S = N * G;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t s = 0; s < S; ++s) {
+        const int64_t n = s / G, g = s % G;
+        const double r = rms_row_r(C, G, x, n, g, eps);
+        rstd[s] = r;
+        if (y == NULL) continue;
+        for (int64_t c = g * D; c < (g + 1) * D; ++c)
+            y[n * C + c] = (gamma ? gamma[c] : 1.0) * (x[n * C + c] * r);
+    }
+    return 0;
+}
+
+int gno_rms_backward(int64_t N, int64_t C, int64_t G, const double* dy, const double* x, const double* gamma,
+                     double eps, double* dx, double* dgamma, double* rstd) {
+    if (N < 0 || C < 0 || G <= 0 || C % G != 0) return 1;
+    const int64_t D = C / G;
+    const int64_t S = N * G;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t s = 0; s < S; ++s) {
+        const int64_t n = s / G, g = s % G;
+        const double r = rms_row_r(C, G, x, n, g, eps);
+        if (rstd) rstd[s] = r;
+        if (dx == NULL) continue;
+        double B = 0.0;
+        for (int64_t c = g * D; c < (g + 1) * D; ++c)
+            B += (gamma ? gamma[c] : 1.0) * dy[n * C + c] * (x[n * C + c] * r);
+        for (int64_t c = g * D; c < (g + 1) * D; ++c) {
+            const double ga = gamma ? gamma[c] : 1.0;
+            const double xhat = x[n * C + c] * r;
+            dx[n * C + c] = MUT(10) ? r * ga * dy[n * C + c]                       /* mutant 10: B term dropped */
+                                    : r * (ga * dy[n * C + c] - xhat * B / (double)D);
+        }
+    }
+    if (dgamma != NULL) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t c = 0; c < C; ++c) {
+            const int64_t g = c / D;
+            double sg = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double r = rms_row_r(C, G, x, n, g, eps);
+                sg += MUT(11) ? dy[n * C + c] * x[n * C + c] : dy[n * C + c] * (x[n * C + c] * r); /* mutant 11: raw x */
+            }
+            dgamma[c] = sg;
+        }
+    }
+    return 0;
+}
+
 /* Threads OpenMP will use for the parallel loops above (1 without OpenMP). */
 int gno_num_threads(void) {
 #ifdef _OPENMP

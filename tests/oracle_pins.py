@@ -13,6 +13,9 @@ the oracle disagrees with the fact.  The facts:
 * closed-form invariants: with gamma = 1, beta = 0 every slice of y has mean 0
   and variance var/(var + eps); dbeta_c is the column sum of dy; per slice
   sum(dx) = 0 and sum(dx * xhat) = rstd * B * eps / (var + eps);
+* RMSNorm over rows: a hand-worked row, torch's float64 rms_norm with
+  autograd, and its invariants (mean square of y, dx orthogonal to x at
+  eps = 0, scale invariance, groups as independent rows);
 * structure: NCHW and NHWC images of one logical tensor give the same logical
   outputs; permuting positions inside a slice permutes y and dx alike; with
   eps = 0, scaling x leaves y unchanged; a one-element slice gives y = beta and
@@ -299,9 +302,82 @@ def pin_structure(mutant=0):
     _assert_close(dxc, expect.reshape(-1), 1e-10, 1e-10, "constant slice dx")
 
 
+# ----------------------------------------------------------------------------
+# RMSNorm over rows
+# ----------------------------------------------------------------------------
+def pin_rms_hand(mutant=0):
+    """Row [3, 4], gamma [2, 0.5], eps 0: mean square 12.5, r = 1/sqrt(12.5);
+    y = [6r, 2r]; with dy = [1, 0]: B = 6r, dx = [r*(2 - 9r^2), -12r^3]
+    (= [32r/25, -24r/25], the derivative of L = 2*x0*r worked by hand), and
+    dgamma = [3r, 0]."""
+    x = [3.0, 4.0]
+    g = [2.0, 0.5]
+    r = 1.0 / math.sqrt(12.5)
+    y, rs = oracle.rms_forward(x, g, 1, 2, 1, 0.0, mutant=mutant)
+    _assert_close(rs, [r], 1e-15, 0, "rms hand r")
+    _assert_close(y, [6 * r, 2 * r], 1e-15, 0, "rms hand y")
+    dx, dg, _ = oracle.rms_backward([1.0, 0.0], x, g, 1, 2, 1, 0.0, mutant=mutant)
+    _assert_close(dx, [32 * r / 25, -24 * r / 25], 1e-14, 1e-15, "rms hand dx")
+    _assert_close(dg, [3 * r, 0.0], 1e-15, 1e-15, "rms hand dgamma")
+
+
+def pin_torch_rms_norm(mutant=0):
+    """torch's float64 CPU rms_norm with autograd (the operator itself)."""
+    for k, (N, C, eps, scale) in enumerate([(9, 40, 1e-5, 1.0), (5, 8, 1e-6, 0.01), (3, 256, 1e-5, 3.0)]):
+        r = _rng(300 + k)
+        x = r.standard_normal((N, C)) * scale + 0.3
+        dy = r.standard_normal((N, C))
+        gamma = r.standard_normal(C)
+        xt = torch.tensor(x, requires_grad=True)
+        gt = torch.tensor(gamma, requires_grad=True)
+        yt = F.rms_norm(xt, (C,), gt, eps)
+        yt.backward(torch.tensor(dy))
+        y, _ = oracle.rms_forward(x.reshape(-1), gamma, N, C, 1, eps, mutant=mutant)
+        dx, dg, _ = oracle.rms_backward(dy.reshape(-1), x.reshape(-1), gamma, N, C, 1, eps, mutant=mutant)
+        _assert_close(y, yt.detach().numpy().reshape(-1), 1e-12, 1e-12, f"rms_norm y {k}")
+        _assert_close(dx, xt.grad.numpy().reshape(-1), 1e-10, 1e-11, f"rms_norm dx {k}")
+        _assert_close(dg, gt.grad.numpy(), 1e-10, 1e-11, f"rms_norm dgamma {k}")
+
+
+def pin_rms_invariants(mutant=0):
+    """gamma = 1: each row of y has mean square ms/(ms + eps); at eps = 0 each
+    row's dx is orthogonal to x (sum dx*x = r*sum(dy*x)*eps/(ms + eps)) and y
+    is unchanged by scaling x; rows of D = C/G channels with G > 1 are the
+    G = 1 operator on each group's columns."""
+    N, C, G = 6, 24, 3
+    D = C // G
+    r = _rng(17)
+    x = r.standard_normal((N, C)) * 2 + 1
+    dy = r.standard_normal((N, C))
+    eps = 0.05
+    y, rs = oracle.rms_forward(x.reshape(-1), None, N, C, 1, eps, mutant=mutant)
+    ms = (x ** 2).mean(axis=1)
+    _assert_close((y.reshape(N, C) ** 2).mean(axis=1), ms / (ms + eps), 1e-12, 1e-14, "rms mean square of y")
+    dx, _, _ = oracle.rms_backward(dy.reshape(-1), x.reshape(-1), None, N, C, 1, eps, mutant=mutant)
+    lhs = (dx.reshape(N, C) * x).sum(axis=1)
+    rhs = rs * (dy * x).sum(axis=1) * eps / (ms + eps)
+    _assert_close(lhs, rhs, 1e-10, 1e-12, "rms sum dx*x")
+    y0, _ = oracle.rms_forward(x.reshape(-1), None, N, C, 1, 0.0, mutant=mutant)
+    y1, _ = oracle.rms_forward((x * 37.5).reshape(-1), None, N, C, 1, 0.0, mutant=mutant)
+    _assert_close(y1, y0, 1e-13, 1e-14, "rms scale invariance")
+    gamma = r.standard_normal(C)
+    yg, rg = oracle.rms_forward(x.reshape(-1), gamma, N, C, G, eps, mutant=mutant)
+    dxg, dgg, _ = oracle.rms_backward(dy.reshape(-1), x.reshape(-1), gamma, N, C, G, eps, mutant=mutant)
+    for g in range(G):
+        cs = slice(g * D, (g + 1) * D)
+        xs = np.ascontiguousarray(x[:, cs])
+        ys, rss = oracle.rms_forward(xs.reshape(-1), gamma[cs], N, D, 1, eps, mutant=mutant)
+        dxs, dgs, _ = oracle.rms_backward(np.ascontiguousarray(dy[:, cs]).reshape(-1), xs.reshape(-1), gamma[cs],
+                                          N, D, 1, eps, mutant=mutant)
+        _assert_close(yg.reshape(N, C)[:, cs].reshape(-1), ys, 1e-14, 0, f"rms groups y {g}")
+        _assert_close(rg.reshape(N, G)[:, g], rss, 1e-15, 0, f"rms groups r {g}")
+        _assert_close(dxg.reshape(N, C)[:, cs].reshape(-1), dxs, 1e-13, 1e-15, f"rms groups dx {g}")
+        _assert_close(dgg[cs], dgs, 1e-13, 1e-15, f"rms groups dgamma {g}")
+
+
 ALL_PINS = [pin_hand_slice, pin_hand_textbook, pin_hand_nhwc_two_groups, pin_finite_differences,
             pin_torch_group_norm, pin_torch_layer_norm, pin_torch_instance_norm, pin_invariants,
-            pin_structure]
+            pin_structure, pin_rms_hand, pin_torch_rms_norm, pin_rms_invariants]
 
 # planted mistakes compiled into the oracle's mutant build (see gn_oracle.c)
 MUTANTS = {
@@ -312,4 +388,8 @@ MUTANTS = {
     5: "B term dropped from dx",
     6: "sign of the B term in dx",
     7: "dgamma summed with raw x instead of xhat",
+    8: "RMSNorm with the mean subtracted",
+    9: "eps dropped from the RMSNorm r",
+    10: "B term dropped from the RMSNorm dx",
+    11: "RMSNorm dgamma summed with raw x",
 }

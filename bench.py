@@ -40,6 +40,10 @@ WORKLOADS = {
     "nchw_f32_112x64x512x512_g8": ("nchw_f32_112x64x512x512_g8",),
     "rows_bf16_131072x4096": ("rows_bf16_131072x4096",),
     "rows_f16_131072x64": ("rows_f16_131072x64",),
+    # RMSNorm over rows (gn_rms_forward / gn_rms_backward)
+    "rms_f16_4096x1024": ("rms_f16_4096x1024",),
+    "rms_bf16_131072x4096": ("rms_bf16_131072x4096",),
+    "rms_f16_131072x64": ("rms_f16_131072x64",),
 }
 DEFAULT = "rows_f16_4096x1024+8192x768"
 
@@ -119,7 +123,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS),
+                    help="rms_* workloads run RMSNorm over rows (gn_rms_forward / gn_rms_backward)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the oracle CPU-baseline sample (0 disables it)")
     ap.add_argument("--force-path", default=None, choices=[None, "generic", "rows", "slab", "stream"])
@@ -148,6 +153,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     mask = gn.GN_GRAD_DX | gn.GN_GRAD_DGAMMA | gn.GN_GRAD_DBETA
+    rms_mask = gn.GN_GRAD_DX | gn.GN_GRAD_DGAMMA
 
     # ---- inputs resident in HBM, outputs and workspaces preallocated ----------
     shapes = []
@@ -157,9 +163,15 @@ def main():
         d = inputs.make_inputs(wl, seed=0, device="cuda")
         x, dy, gamma, beta = d["x"], d["dy"], d["gamma"], d["beta"]
         code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
-        lay = gn.layout_of(x)
-        fws = gn.forward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, args.force_path)
-        bws = gn.backward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, mask, args.force_path)
+        if wl.op == "rms":   # [N, C] rows
+            x, dy = x.reshape(wl.N, wl.C), dy.reshape(wl.N, wl.C)
+            lay = gn.GN_NCHW
+            fws = gn.rms_forward_workspace_size(wl.N, wl.C, wl.G, code, args.force_path)
+            bws = gn.rms_backward_workspace_size(wl.N, wl.C, wl.G, code, rms_mask, args.force_path)
+        else:
+            lay = gn.layout_of(x)
+            fws = gn.forward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, args.force_path)
+            bws = gn.backward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, mask, args.force_path)
         sh = dict(wl=wl, x=x, dy=dy, gamma=gamma, beta=beta, y=torch.empty_like(x), dx=torch.empty_like(x),
                   mean=torch.empty(wl.N * wl.G, device=dev), rstd=torch.empty(wl.N * wl.G, device=dev),
                   dgamma=torch.empty(wl.C, device=dev), dbeta=torch.empty(wl.C, device=dev),
@@ -176,7 +188,7 @@ def main():
     def calls_for(sh, stream_handle, evs):
         wl = sh["wl"]
         code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
-        lay = gn.layout_of(sh["x"])
+        lay = gn.layout_of(sh["x"]) if wl.op != "rms" else gn.GN_NCHW
         P = lambda t: ctypes.c_void_p(t.data_ptr())
         out = []
         for kind in ("fwd", "bwd"):
@@ -187,7 +199,16 @@ def main():
                 b, e = evs[0 if kind == "fwd" else 1]
                 o.event_begin = ctypes.c_void_p(b)
                 o.event_end = ctypes.c_void_p(e)
-            if kind == "fwd":
+            if wl.op == "rms" and kind == "fwd":
+                a = (P(sh["x"]), P(sh["gamma"]), P(sh["y"]), P(sh["rstd"]), wl.N, wl.C, wl.G, ctypes.c_float(wl.eps),
+                     code, P(sh["fws"]), sh["fws"].numel(), ctypes.c_void_p(stream_handle), ctypes.byref(o))
+                out.append((L.gn_rms_forward, a, o))
+            elif wl.op == "rms":
+                a = (P(sh["dy"]), P(sh["x"]), P(sh["rstd"]), P(sh["gamma"]), P(sh["dx"]), P(sh["dgamma"]), rms_mask,
+                     wl.N, wl.C, wl.G, code, P(sh["bws"]), sh["bws"].numel(), ctypes.c_void_p(stream_handle),
+                     ctypes.byref(o))
+                out.append((L.gn_rms_backward, a, o))
+            elif kind == "fwd":
                 a = (P(sh["x"]), P(sh["gamma"]), P(sh["beta"]), P(sh["y"]), P(sh["mean"]), P(sh["rstd"]),
                      wl.N, wl.C, wl.HW, wl.G, ctypes.c_float(wl.eps), code, lay, P(sh["fws"]),
                      sh["fws"].numel(), ctypes.c_void_p(stream_handle), ctypes.byref(o))
@@ -287,9 +308,13 @@ def main():
                 nbytes = wl.bwd_min_bytes() - (2 * wl.C * 4 if plan.kernels > 1 else 0)
             durs = [tev.elapsed_ms(events[i][k][c][0], events[i][k][c][1]) for i in range(K)]
             avg_ms = sum(durs) / len(durs)
-            kname = {("rows", "fwd"): "rows_fwd_k", ("rows", "bwd"): "rows_bwd_k",
-                     ("slab", "fwd"): f"slab_{wl.layout}_fwd", ("slab", "bwd"): f"slab_{wl.layout}_bwd",
-                     ("stream", "fwd"): "stream_fwd_call", ("stream", "bwd"): "stream_bwd_call",
+            # kernels that can be the call's main kernel (the rows path picks one of
+            # several by the slice width and count; the grid tells them apart in
+            # the recorded counters)
+            kname = {("rows", "fwd"): ("rows_fwd_k", "rows_fwd_lds_k", "rows_fwd_narrow_k"),
+                     ("rows", "bwd"): ("rows_bwd_k", "rows_bwd_narrow_k"),
+                     ("slab", "fwd"): (f"slab_{wl.layout}_fwd",), ("slab", "bwd"): (f"slab_{wl.layout}_bwd",),
+                     ("stream", "fwd"): ("stream_fwd_call",), ("stream", "bwd"): ("stream_bwd_call",),
                      }.get((path, kind))
             calls.append(dict(shape=wl.name, call=kind, path=path, kernels=plan.kernels,
                               kernel=kname, grid=plan.grid if path != "stream" else "call",
@@ -297,7 +322,12 @@ def main():
                               main_kernel_gbs=nbytes / (avg_ms * 1e-3) / 1e9))
     tev.close()
     dom = max(calls, key=lambda c: c["main_kernel_us"])
-    traffic = recorded_traffic(args.workload, dom["kernel"], dom["grid"]) if dom["kernel"] else None
+    traffic = None
+    for kn in dom["kernel"] or ():
+        traffic = recorded_traffic(args.workload, kn, dom["grid"])
+        if traffic is not None:
+            dom["kernel"] = kn
+            break
     roofline = {"bound": "hbm", "achieved": round(dom["main_kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dom["main_kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
@@ -340,7 +370,9 @@ def main():
         "config": {"workload": args.workload, "launch": mode,
                    "shapes": [dict(N=s["wl"].N, C=s["wl"].C, H=s["wl"].H, W=s["wl"].W, G=s["wl"].G,
                                    dtype=s["wl"].dtype, layout=s["wl"].layout) for s in shapes],
-                   "mask": "dx|dgamma|dbeta", "bytes_per_step": bytes_per_step,
+                   "op": shapes[0]["wl"].op,
+                   "mask": "dx|dgamma" if shapes[0]["wl"].op == "rms" else "dx|dgamma|dbeta",
+                   "bytes_per_step": bytes_per_step,
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "us_per_call": {f"{c['call']}:{c['shape']}": round(c["main_kernel_us"], 3) for c in calls},
         "calls": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in c.items()} for c in calls],
@@ -371,6 +403,10 @@ def cpu_baseline(shapes, seconds, bytes_per_step):
     t0 = time.perf_counter()
     while True:
         for wl, x, dy, g, b, eps in prepared:
+            if wl.op == "rms":
+                oracle.rms_forward(x, g, wl.N, wl.C, wl.G, eps)
+                oracle.rms_backward(dy, x, g, wl.N, wl.C, wl.G, eps)
+                continue
             oracle.forward(x, g, b, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
             oracle.backward(dy, x, g, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
         reps += 1

@@ -149,6 +149,46 @@ gn_status gn_backward(const void* dy, const void* x,
 int32_t gn_select_path(int32_t backward, int64_t N, int64_t C, int64_t HW, int64_t G,
                        gn_dtype dtype, gn_layout layout, const gn_options* opts);
 
+/*
+ * RMSNorm over rows (ROCm/pytorch PR #3564 benchmarks an rms_norm operator
+ * beside layer_norm; read as PyTorch's rms_norm).  x is a dense [N, C] row
+ * major tensor (one row per sample; no spatial extent); each row is split
+ * into G groups of D = C/G consecutive channels (G = 1: the whole row), and
+ * every (n, g) segment is normalised by its root mean square:
+ *     rstd = 1/sqrt((1/D) * sum x^2 + eps),   y = gamma_c * x * rstd
+ * backward, per segment B = sum gamma_c * dy * x * rstd:
+ *     dx = rstd * (gamma_c * dy - x * rstd * B/D),   dgamma_c = sum over n of dy * x * rstd
+ * rstd: [N*G] float32, segment (n, g) at n*G + g (saved by the forward, read
+ * by the backward).  gamma: [C] float32 or NULL (= 1); there is no bias.
+ * dtypes as for gn_forward; y, dx take x's dtype.  These calls run on the
+ * rows kernels only: they return GN_ERR_UNSUPPORTED when D or C is not a
+ * multiple of 4 (float32) / 8 (16-bit) elements, when D exceeds 2048
+ * (float32) / 4096 (16-bit) channels, when a pointer is not 16-byte aligned,
+ * or for a forced path other than GN_PATH_ROWS.  Pointers, streams,
+ * workspace, options and errors as for gn_forward / gn_backward.
+ */
+size_t gn_rms_forward_workspace_size(int64_t N, int64_t C, int64_t G, gn_dtype dtype,
+                                     const gn_options* opts);
+
+/* x, y: [N, C]; y may be NULL (rstd only); rstd required. eps >= 0. */
+gn_status gn_rms_forward(const void* x, const float* gamma, void* y, float* rstd,
+                         int64_t N, int64_t C, int64_t G, float eps, gn_dtype dtype,
+                         void* workspace, size_t ws_bytes, void* stream,
+                         const gn_options* opts);
+
+/* Workspace bytes gn_rms_backward needs for these arguments and mask. */
+size_t gn_rms_backward_workspace_size(int64_t N, int64_t C, int64_t G, gn_dtype dtype,
+                                      int32_t mask, const gn_options* opts);
+
+/* dy, x: [N, C]; rstd: [N*G] from gn_rms_forward; gamma: [C] or NULL.
+ * mask: GN_GRAD_DX and/or GN_GRAD_DGAMMA (GN_GRAD_DBETA is invalid: there is
+ * no bias); each selected output non-NULL; dgamma requires gamma. */
+gn_status gn_rms_backward(const void* dy, const void* x, const float* rstd, const float* gamma,
+                          void* dx, float* dgamma, int32_t mask,
+                          int64_t N, int64_t C, int64_t G, gn_dtype dtype,
+                          void* workspace, size_t ws_bytes, void* stream,
+                          const gn_options* opts);
+
 /* Static description of a status code (never NULL). */
 const char* gn_status_string(gn_status status);
 

@@ -22,6 +22,8 @@ from ._lib import (GN_BF16, GN_F16, GN_F32, GN_GRAD_DBETA, GN_GRAD_DGAMMA, GN_GR
 
 __all__ = ["forward", "backward", "forward_into", "backward_into", "forward_workspace_size",
            "backward_workspace_size", "select_path", "layout_of", "GNError", "PlanInfo",
+           "rms_forward", "rms_backward", "rms_forward_into", "rms_backward_into",
+           "rms_forward_workspace_size", "rms_backward_workspace_size",
            "GN_GRAD_DX", "GN_GRAD_DGAMMA", "GN_GRAD_DBETA", "GN_PATH_AUTO", "GN_PATH_GENERIC",
            "GN_PATH_ROWS", "GN_PATH_SLAB", "GN_PATH_STREAM", "PATH_NAMES"]
 
@@ -177,3 +179,91 @@ def backward(dy, x, mean, rstd, gamma, num_groups: int, mask: int = GN_GRAD_DX |
         backward_into(dy, x, mean.reshape(-1), rstd.reshape(-1), gamma, G, mask, dx, dgamma, dbeta, ws,
                       force_path=force_path, max_resident=max_resident, info=info)
     return dx, dgamma, dbeta
+
+
+# ---- RMSNorm over rows ([N, C] tensors; segments of C/G channels) ------------
+def _rows_dims(x):
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("RMSNorm takes a contiguous [N, C] tensor")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def rms_forward_workspace_size(N, C, G, dtype_code, force_path=None) -> int:
+    o = _opts(force_path, 0, None, None)
+    return int(_lib.lib().gn_rms_forward_workspace_size(N, C, G, dtype_code, ctypes.byref(o)))
+
+
+def rms_backward_workspace_size(N, C, G, dtype_code, mask, force_path=None) -> int:
+    o = _opts(force_path, 0, None, None)
+    return int(_lib.lib().gn_rms_backward_workspace_size(N, C, G, dtype_code, mask, ctypes.byref(o)))
+
+
+def rms_forward_into(x, gamma, num_groups, eps, y, rstd, workspace, *, force_path=None, info=None, events=None,
+                     stream=None):
+    """gn_rms_forward on preallocated outputs; returns nothing, raises GNError."""
+    torch = _torch()
+    N, C = _rows_dims(x)
+    _check_f32_vec(gamma, C, "gamma")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    o = _opts(force_path, 0, info, events)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.lib().gn_rms_forward(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), N, C, int(num_groups), float(eps),
+                                   _dtype_code(x), _ptr(workspace), ws_bytes, ctypes.c_void_p(stream),
+                                   ctypes.byref(o))
+    if st != 0:
+        raise GNError(st, "gn_rms_forward")
+
+
+def rms_forward(x, gamma, eps: float = 1e-6, num_groups: int = 1, *, compute_y: bool = True, force_path=None,
+                info: PlanInfo | None = None):
+    """RMSNorm of each (row, group) segment of an [N, C] tensor.  Returns
+    (y, rstd[N, G]); y is None when compute_y is False."""
+    torch = _torch()
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device")
+    N, C = _rows_dims(x)
+    G = int(num_groups)
+    with torch.cuda.device(x.device):
+        y = torch.empty_like(x) if compute_y else None
+        rstd = torch.empty(N * G, device=x.device, dtype=torch.float32)
+        wsb = rms_forward_workspace_size(N, C, G, _dtype_code(x), force_path)
+        ws = torch.empty(max(wsb, 1), device=x.device, dtype=torch.uint8)
+        rms_forward_into(x, gamma, G, eps, y, rstd, ws, force_path=force_path, info=info)
+    return y, rstd.view(N, G)
+
+
+def rms_backward_into(dy, x, rstd, gamma, num_groups, mask, dx, dgamma, workspace, *, force_path=None, info=None,
+                      events=None, stream=None):
+    """gn_rms_backward on preallocated outputs; returns nothing, raises GNError."""
+    torch = _torch()
+    N, C = _rows_dims(x)
+    if tuple(dy.shape) != tuple(x.shape) or dy.dtype != x.dtype or not dy.is_contiguous():
+        raise ValueError("dy must match x in shape and dtype")
+    _check_f32_vec(gamma, C, "gamma")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    o = _opts(force_path, 0, info, events)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.lib().gn_rms_backward(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(gamma), _ptr(dx), _ptr(dgamma), int(mask),
+                                    N, C, int(num_groups), _dtype_code(x), _ptr(workspace), ws_bytes,
+                                    ctypes.c_void_p(stream), ctypes.byref(o))
+    if st != 0:
+        raise GNError(st, "gn_rms_backward")
+
+
+def rms_backward(dy, x, rstd, gamma, num_groups: int = 1, mask: int = GN_GRAD_DX | GN_GRAD_DGAMMA, *,
+                 force_path=None, info: PlanInfo | None = None):
+    """Returns (dx, dgamma), each None when not selected by mask."""
+    torch = _torch()
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device")
+    N, C = _rows_dims(x)
+    G = int(num_groups)
+    with torch.cuda.device(x.device):
+        dx = torch.empty_like(x) if mask & GN_GRAD_DX else None
+        dgamma = torch.empty(C, device=x.device, dtype=torch.float32) if mask & GN_GRAD_DGAMMA else None
+        wsb = rms_backward_workspace_size(N, C, G, _dtype_code(x), mask, force_path)
+        ws = torch.empty(max(wsb, 1), device=x.device, dtype=torch.uint8)
+        rms_backward_into(dy, x, rstd.reshape(-1), gamma, G, mask, dx, dgamma, ws, force_path=force_path, info=info)
+    return dx, dgamma

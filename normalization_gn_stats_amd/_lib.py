@@ -25,7 +25,8 @@ PATH_NAMES = {GN_PATH_AUTO: "auto", GN_PATH_GENERIC: "generic", GN_PATH_ROWS: "r
 
 # every symbol include/gn.h declares
 EXPORTED = ("gn_forward_workspace_size", "gn_forward", "gn_backward_workspace_size", "gn_backward",
-            "gn_select_path", "gn_status_string", "gn_version")
+            "gn_select_path", "gn_status_string", "gn_version", "gn_rms_forward_workspace_size",
+            "gn_rms_forward", "gn_rms_backward_workspace_size", "gn_rms_backward")
 
 
 class PlanInfo(ctypes.Structure):
@@ -68,6 +69,14 @@ def lib() -> ctypes.CDLL:
     L.gn_backward.restype = i32
     L.gn_select_path.argtypes = [i32, i64, i64, i64, i64, i32, i32, op]
     L.gn_select_path.restype = i32
+    L.gn_rms_forward_workspace_size.argtypes = [i64, i64, i64, i32, op]
+    L.gn_rms_forward_workspace_size.restype = sz
+    L.gn_rms_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, f, i32, vp, sz, vp, op]
+    L.gn_rms_forward.restype = i32
+    L.gn_rms_backward_workspace_size.argtypes = [i64, i64, i64, i32, i32, op]
+    L.gn_rms_backward_workspace_size.restype = sz
+    L.gn_rms_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp, sz, vp, op]
+    L.gn_rms_backward.restype = i32
     L.gn_status_string.argtypes = [i32]
     L.gn_status_string.restype = ctypes.c_char_p
     L.gn_version.restype = i32

@@ -238,6 +238,81 @@ gn_status gn_backward(const void* dy, const void* x, const float* mean, const fl
     return e == hipSuccess ? GN_OK : GN_ERR_HIP;
 }
 
+// ---- RMSNorm over rows: the rows kernels with the mean taken as 0 ----------
+namespace {
+// Rows problem of an [N, C] tensor; GN_OK, or the status to return.
+gn_status rms_problem(int64_t N, int64_t C, int64_t G, gn_dtype dtype, const gn_options* opts, Problem* p) {
+    gn_status st = make_problem(N, C, 1, G, dtype, GN_NCHW, p);
+    if (st != GN_OK) return st;
+    const int32_t f = forced(opts);
+    if (f != GN_PATH_AUTO && f != GN_PATH_ROWS) return GN_ERR_UNSUPPORTED;
+    if (!zero_extent(*p) && !gn::rows_ok(*p)) return GN_ERR_UNSUPPORTED;
+    return GN_OK;
+}
+}  // namespace
+
+size_t gn_rms_forward_workspace_size(int64_t N, int64_t C, int64_t G, gn_dtype dtype, const gn_options* opts) {
+    Problem p;
+    if (rms_problem(N, C, G, dtype, opts, &p) != GN_OK || zero_extent(p)) return 0;
+    return gn::rows_fwd_ws(p);
+}
+
+gn_status gn_rms_forward(const void* x, const float* gamma, void* y, float* rstd, int64_t N, int64_t C, int64_t G,
+                         float eps, gn_dtype dtype, void* workspace, size_t ws_bytes, void* stream,
+                         const gn_options* opts) {
+    Problem p;
+    gn_status st = rms_problem(N, C, G, dtype, opts, &p);
+    if (st != GN_OK) return st;
+    if (!(eps >= 0.f) || isinf(eps)) return GN_ERR_INVALID;
+    if (zero_extent(p)) {
+        if (opts && opts->info) *opts->info = gn_plan_info{GN_PATH_AUTO, 0, 0, 0, 0, 0};
+        return GN_OK;
+    }
+    if (x == nullptr || rstd == nullptr) return GN_ERR_INVALID;
+    if (!aligned16(x) || (y != nullptr && !aligned16(y)) || !aligned16(gamma)) return GN_ERR_UNSUPPORTED;
+    const size_t need = gn::rows_fwd_ws(p);
+    if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
+    gn::FwdArgs a{x, gamma, nullptr, y, nullptr, rstd, eps, 1};
+    gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
+    if (l.info) *l.info = gn_plan_info{GN_PATH_ROWS, 0, 0, 0, 0, 0};
+    return gn::rows_fwd(p, a, l) == hipSuccess ? GN_OK : GN_ERR_HIP;
+}
+
+size_t gn_rms_backward_workspace_size(int64_t N, int64_t C, int64_t G, gn_dtype dtype, int32_t mask,
+                                      const gn_options* opts) {
+    Problem p;
+    if (rms_problem(N, C, G, dtype, opts, &p) != GN_OK || zero_extent(p)) return 0;
+    if (mask <= 0 || mask > (GN_GRAD_DX | GN_GRAD_DGAMMA)) return 0;
+    return gn::rows_bwd_ws(p, mask);
+}
+
+gn_status gn_rms_backward(const void* dy, const void* x, const float* rstd, const float* gamma, void* dx,
+                          float* dgamma, int32_t mask, int64_t N, int64_t C, int64_t G, gn_dtype dtype,
+                          void* workspace, size_t ws_bytes, void* stream, const gn_options* opts) {
+    Problem p;
+    gn_status st = rms_problem(N, C, G, dtype, opts, &p);
+    if (st != GN_OK) return st;
+    if (mask <= 0 || mask > (GN_GRAD_DX | GN_GRAD_DGAMMA)) return GN_ERR_INVALID;   // no dbeta: no bias
+    if ((mask & GN_GRAD_DX) && dx == nullptr) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DGAMMA) && (dgamma == nullptr || gamma == nullptr)) return GN_ERR_INVALID;
+    if (zero_extent(p)) {
+        if (opts && opts->info) *opts->info = gn_plan_info{GN_PATH_AUTO, 0, 0, 0, 0, 0};
+        return GN_OK;
+    }
+    if (dy == nullptr || x == nullptr || rstd == nullptr) return GN_ERR_INVALID;
+    if (!aligned16(dy) || !aligned16(x) || !aligned16(gamma) || ((mask & GN_GRAD_DX) && !aligned16(dx)))
+        return GN_ERR_UNSUPPORTED;
+    const size_t need = gn::rows_bwd_ws(p, mask);
+    if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
+    gn::BwdArgs a{dy, x, nullptr, rstd, gamma,
+                  (mask & GN_GRAD_DX) ? dx : nullptr,
+                  (mask & GN_GRAD_DGAMMA) ? dgamma : nullptr,
+                  nullptr, mask, 1};
+    gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
+    if (l.info) *l.info = gn_plan_info{GN_PATH_ROWS, 0, 0, 0, 0, 0};
+    return gn::rows_bwd(p, a, l) == hipSuccess ? GN_OK : GN_ERR_HIP;
+}
+
 const char* gn_status_string(gn_status s) {
     switch (s) {
         case GN_OK: return "ok";
@@ -249,6 +324,6 @@ const char* gn_status_string(gn_status s) {
     }
 }
 
-int32_t gn_version(void) { return 100; }
+int32_t gn_version(void) { return 200; }
 
 }  // extern "C"

@@ -27,9 +27,10 @@ struct FwdArgs {
     const float* gamma;  // NULL => 1
     const float* beta;   // NULL => 0
     void* y;             // NULL => statistics only
-    float* mean;
+    float* mean;         // NULL for RMSNorm
     float* rstd;
     float eps;
+    int32_t rms;         // RMSNorm over rows (rows path only): no mean, no beta
 };
 
 struct BwdArgs {
@@ -42,6 +43,7 @@ struct BwdArgs {
     float* dgamma;       // NULL unless GN_GRAD_DGAMMA
     float* dbeta;        // NULL unless GN_GRAD_DBETA
     int32_t mask;
+    int32_t rms;         // RMSNorm over rows (rows path only): mean unused, no mean term
 };
 
 // Launch context handed to every launcher.

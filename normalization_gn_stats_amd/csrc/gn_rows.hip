@@ -33,7 +33,7 @@ template <typename T, int NV>
 __global__ __launch_bounds__(kT) void rows_fwd_k(const T* __restrict__ x, const float* __restrict__ gamma,
                                                  const float* __restrict__ beta, T* __restrict__ y,
                                                  float* __restrict__ mean, float* __restrict__ rstd, int64_t N,
-                                                 int64_t G, int64_t C, int D, float eps) {
+                                                 int64_t G, int64_t C, int D, float eps, int rms) {
     constexpr int V = Vec<T>::V;
     const int lane = threadIdx.x & (kWave - 1);
     // grid: x = blocks of kNW samples, y = group; the wave index is uniform
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_k(const T* __restrict__ x, const 
 #pragma unroll
         for (int k = 0; k < V; ++k) sum += v[j][k];
     const float invD = 1.0f / (float)D;
-    const float mu = wave_sum(sum) * invD;
+    const float mu = rms ? 0.f : wave_sum(sum) * invD;   // RMSNorm: no mean
     float q = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_k(const T* __restrict__ x, const 
     var = var > 0.f ? var : 0.f;
     const float r = 1.0f / sqrtf(var + eps);
     if (lane == 0) {
-        mean[s] = mu;
+        if (mean) mean[s] = mu;
         rstd[s] = r;
     }
     if (y == nullptr) return;
@@ -126,7 +126,7 @@ template <typename T, int NV>
 __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, const float* __restrict__ gamma,
                                                      const float* __restrict__ beta, T* __restrict__ y,
                                                      float* __restrict__ mean, float* __restrict__ rstd, int64_t N,
-                                                     int64_t G, int64_t C, int D, float eps) {
+                                                     int64_t G, int64_t C, int D, float eps, int rms) {
     constexpr int V = Vec<T>::V;
     extern __shared__ float4 lds_par[];   // [D/4] gamma, then [D/4] beta
     float* sg = reinterpret_cast<float*>(lds_par);
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, co
         for (int j = 0; j < NV; ++j)
 #pragma unroll
             for (int k = 0; k < V; ++k) sum += v[j][k];
-        const float mu = wave_sum(sum) * invD;
+        const float mu = rms ? 0.f : wave_sum(sum) * invD;   // RMSNorm: no mean
         float q = 0.f;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, co
         const float r = 1.0f / sqrtf(var + eps);
         const int64_t sl = n * G + g;
         if (lane == 0) {
-            mean[sl] = mu;
+            if (mean) mean[sl] = mu;
             rstd[sl] = r;
         }
         if (y != nullptr) {
@@ -237,7 +237,7 @@ template <typename T, int LPR, int RB>
 __global__ __launch_bounds__(kT) void rows_fwd_narrow_k(const T* __restrict__ x, const float* __restrict__ gamma,
                                                         const float* __restrict__ beta, T* __restrict__ y,
                                                         float* __restrict__ mean, float* __restrict__ rstd,
-                                                        int64_t N, int64_t G, int64_t C, int D, float eps) {
+                                                        int64_t N, int64_t G, int64_t C, int D, float eps, int rms) {
     constexpr int V = Vec<T>::V;
     constexpr int RPW = kWave / LPR;
     const int lane = threadIdx.x & (kWave - 1);
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_narrow_k(const T* __restrict__ x,
 #pragma unroll
             for (int k = 0; k < V; ++k) sum += v[k];
         }
-        const float mu = seg_sum<LPR>(sum) * invD;
+        const float mu = rms ? 0.f : seg_sum<LPR>(sum) * invD;   // RMSNorm: no mean
         float q = 0.f;
         if (act) {
 #pragma unroll
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_narrow_k(const T* __restrict__ x,
         const float rs = 1.0f / sqrtf(var + eps);
         if (n < N) {
             if (vi == 0) {
-                mean[n * G + g] = mu;
+                if (mean) mean[n * G + g] = mu;
                 rstd[n * G + g] = rs;
             }
             if (y != nullptr && act) {
@@ -304,7 +304,8 @@ __global__ __launch_bounds__(kT) void rows_bwd_narrow_k(const T* __restrict__ dy
                                                         const float* __restrict__ rstd,
                                                         const float* __restrict__ gamma, T* __restrict__ dx,
                                                         float2* __restrict__ part, int64_t N, int64_t G, int64_t C,
-                                                        int D, int NB, int want_dx, int want_params) {
+                                                        int D, int NB, int want_dx, int want_params,
+                                                 int rms) {
     constexpr int V = Vec<T>::V;
     constexpr int RPW = kWave / LPR;
     constexpr int RPB = kNW * RPW * RB;
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(kT) void rows_bwd_narrow_k(const T* __restrict__ dy
             const int64_t off = n * C + g * D + (int64_t)vc * V;
             rx[r] = ld16(x + off);
             rd[r] = ld16(dy + off);
-            mu[r] = mean[n * G + g];
+            mu[r] = rms ? 0.f : mean[n * G + g];
             rs[r] = rstd[n * G + g];
         }
 #pragma unroll
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(kT) void rows_bwd_narrow_k(const T* __restrict__ dy
                     cs2[k] = fmaf(dv[k], xh, cs2[k]);
                 }
             }
-            const float A = seg_sum<LPR>(a) * invD;
+            const float A = rms ? 0.f : seg_sum<LPR>(a) * invD;   // RMSNorm: no mean term
             const float B = seg_sum<LPR>(bb) * invD;
             if (want_dx && valid) {
                 // gamma*dy rounded as it entered A, so that equal terms cancel exactly
@@ -414,7 +415,8 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
                                                  const float* __restrict__ mean, const float* __restrict__ rstd,
                                                  const float* __restrict__ gamma, T* __restrict__ dx,
                                                  float2* __restrict__ part, int64_t N, int64_t G, int64_t C,
-                                                 int D, int NB, int want_dx, int want_params) {
+                                                 int D, int NB, int want_dx, int want_params,
+                                                 int rms) {
     constexpr int V = Vec<T>::V;
     constexpr int SLOTS = kNW / CS;
     constexpr int RPB = SLOTS * RB;
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
                 rx[r][j] = ld16(x + base + (int64_t)vi * V);
                 rd[r][j] = ld16(dy + base + (int64_t)vi * V);
             }
-            mu[r] = mean[n * G + g];
+            mu[r] = rms ? 0.f : mean[n * G + g];
             rs[r] = rstd[n * G + g];
         }
         if constexpr (kHoistGamma) {
@@ -548,7 +550,7 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            A[r] *= invD;
+            A[r] = rms ? 0.f : A[r] * invD;   // RMSNorm: no mean term
             B[r] *= invD;
         }
 #pragma unroll
@@ -723,7 +725,7 @@ hipError_t fwd_narrow(const Problem& p, const FwdArgs& a, const Launch& l) {
     hipError_t e;
     if ((e = record(l.ev_begin, l.stream))) return e;
     hipLaunchKernelGGL((rows_fwd_narrow_k<T, LPR, RB>), dim3(grid, (unsigned)p.G), dim3(kT), 0, l.stream,
-                       (const T*)a.x, a.gamma, a.beta, (T*)a.y, a.mean, a.rstd, p.N, p.G, p.C, (int)p.D, a.eps);
+                       (const T*)a.x, a.gamma, a.beta, (T*)a.y, a.mean, a.rstd, p.N, p.G, p.C, (int)p.D, a.eps, a.rms);
     if ((e = hipGetLastError())) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
     if (l.info) {
@@ -744,7 +746,7 @@ hipError_t bwd_narrow(const Problem& p, const BwdArgs& a, const Launch& l) {
     if ((e = record(l.ev_begin, l.stream))) return e;
     hipLaunchKernelGGL((rows_bwd_narrow_k<T, LPR, RB>), dim3((unsigned)NB, (unsigned)p.G), dim3(kT), 0, l.stream,
                        (const T*)a.dy, (const T*)a.x, a.mean, a.rstd, a.gamma, (T*)a.dx, part, p.N, p.G, p.C,
-                       (int)p.D, NB, (a.mask & GN_GRAD_DX) ? 1 : 0, params ? 1 : 0);
+                       (int)p.D, NB, (a.mask & GN_GRAD_DX) ? 1 : 0, params ? 1 : 0, a.rms);
     if ((e = hipGetLastError())) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
     int kernels = 1;
@@ -785,10 +787,10 @@ hipError_t fwd_nv(const Problem& p, const FwdArgs& a, const Launch& l) {
     if (walk) {
         grid = (unsigned)(cap < 1 ? 1 : cap);
         hipLaunchKernelGGL((rows_fwd_lds_k<T, NV>), dim3(grid, (unsigned)p.G), dim3(kT), (size_t)p.D * 8, l.stream,
-                           (const T*)a.x, a.gamma, a.beta, (T*)a.y, a.mean, a.rstd, p.N, p.G, p.C, (int)p.D, a.eps);
+                           (const T*)a.x, a.gamma, a.beta, (T*)a.y, a.mean, a.rstd, p.N, p.G, p.C, (int)p.D, a.eps, a.rms);
     } else {
         hipLaunchKernelGGL((rows_fwd_k<T, NV>), dim3(grid, (unsigned)p.G), dim3(kT), 0, l.stream, (const T*)a.x,
-                           a.gamma, a.beta, (T*)a.y, a.mean, a.rstd, p.N, p.G, p.C, (int)p.D, a.eps);
+                           a.gamma, a.beta, (T*)a.y, a.mean, a.rstd, p.N, p.G, p.C, (int)p.D, a.eps, a.rms);
     }
     if ((e = hipGetLastError())) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
@@ -811,7 +813,7 @@ hipError_t bwd_launch(const Problem& p, const BwdArgs& a, const Launch& l) {
     if ((e = record(l.ev_begin, l.stream))) return e;
     hipLaunchKernelGGL((rows_bwd_k<T, NV, RB, CS>), dim3(grid, (unsigned)p.G), dim3(kT), lds, l.stream,
                        (const T*)a.dy, (const T*)a.x, a.mean, a.rstd, a.gamma, (T*)a.dx, part, p.N, p.G, p.C,
-                       (int)p.D, NB, (a.mask & GN_GRAD_DX) ? 1 : 0, params ? 1 : 0);
+                       (int)p.D, NB, (a.mask & GN_GRAD_DX) ? 1 : 0, params ? 1 : 0, a.rms);
     if ((e = hipGetLastError())) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
     int kernels = 1;

@@ -35,6 +35,7 @@ class Workload:
     layout: str         # "nchw" | "nhwc"
     affine: str = "n1"  # "n1": gamma ~ N(1, 0.1), beta ~ N(0, 0.1); "n01": both ~ N(0, 1)
     eps: float = 1e-5
+    op: str = "gn"          # "gn": GroupNorm; "rms": RMSNorm over rows (HW == 1, no beta)
 
     @property
     def HW(self) -> int:
@@ -54,17 +55,21 @@ class Workload:
 
     def fwd_min_bytes(self) -> int:
         """Algorithmic bytes of one forward: read x, write y, read gamma/beta,
-        write mean/rstd."""
+        write mean/rstd (RMSNorm: gamma only, rstd only)."""
+        if self.op == "rms":
+            return 2 * self.E * self.s + self.C * 4 + self.N * self.G * 4
         return 2 * self.E * self.s + 2 * self.C * 4 + 2 * self.N * self.G * 4
 
     def bwd_min_bytes(self, dx: bool = True, dparams: bool = True) -> int:
         """Algorithmic bytes of one backward: read dy, x, gamma, mean/rstd,
-        write dx (if asked) and dgamma/dbeta (if asked)."""
-        b = 2 * self.E * self.s + self.C * 4 + 2 * self.N * self.G * 4
+        write dx (if asked) and dgamma/dbeta (if asked); RMSNorm: rstd only
+        and dgamma only."""
+        nstat, nparam = (1, 1) if self.op == "rms" else (2, 2)
+        b = 2 * self.E * self.s + self.C * 4 + nstat * self.N * self.G * 4
         if dx:
             b += self.E * self.s
         if dparams:
-            b += 2 * self.C * 4
+            b += nparam * self.C * 4
         return b
 
     def scaled(self, **kw) -> "Workload":
@@ -83,7 +88,14 @@ ROWS_BIG = Workload("rows_bf16_131072x4096", 131072, 4096, 1, 1, 1, "bf16", "nch
 # Narrow rows with many of them (the "huge M" LayerNorm shape of the same table).
 ROWS_NARROW = Workload("rows_f16_131072x64", 131072, 64, 1, 1, 1, "f16", "nchw")
 
-WORKLOADS = {w.name: w for w in (TINY, ROWS_A, ROWS_B, NHWC_IMG, NCHW_BIG, ROWS_BIG, ROWS_NARROW)}
+# RMSNorm at the three rms_norm shapes of that table (eps 1e-6: the table
+# states none).
+RMS_A = Workload("rms_f16_4096x1024", 4096, 1024, 1, 1, 1, "f16", "nchw", eps=1e-6, op="rms")
+RMS_BIG = Workload("rms_bf16_131072x4096", 131072, 4096, 1, 1, 1, "bf16", "nchw", eps=1e-6, op="rms")
+RMS_NARROW = Workload("rms_f16_131072x64", 131072, 64, 1, 1, 1, "f16", "nchw", eps=1e-6, op="rms")
+
+WORKLOADS = {w.name: w for w in (TINY, ROWS_A, ROWS_B, NHWC_IMG, NCHW_BIG, ROWS_BIG, ROWS_NARROW,
+                                 RMS_A, RMS_BIG, RMS_NARROW)}
 
 
 def make_inputs(wl: Workload, seed: int = 0, device: str = "cpu"):

@@ -263,16 +263,18 @@ int gno_rms_forward(int64_t N, int64_t C, int64_t G, const double* x, const doub
     return 0;
 }
 
+/* rstd: [N*G], required (the per-row r, computed once and reused by the
+ * dgamma sums). */
 int gno_rms_backward(int64_t N, int64_t C, int64_t G, const double* dy, const double* x, const double* gamma,
                      double eps, double* dx, double* dgamma, double* rstd) {
-    if (N < 0 || C < 0 || G <= 0 || C % G != 0) return 1;
+    if (N < 0 || C < 0 || G <= 0 || C % G != 0 || rstd == NULL) return 1;
     const int64_t D = C / G;
     const int64_t S = N * G;
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t s = 0; s < S; ++s) {
         const int64_t n = s / G, g = s % G;
         const double r = rms_row_r(C, G, x, n, g, eps);
-        if (rstd) rstd[s] = r;
+        rstd[s] = r;
         if (dx == NULL) continue;
         double B = 0.0;
         for (int64_t c = g * D; c < (g + 1) * D; ++c)
@@ -290,7 +292,7 @@ int gno_rms_backward(int64_t N, int64_t C, int64_t G, const double* dy, const do
             const int64_t g = c / D;
             double sg = 0.0;
             for (int64_t n = 0; n < N; ++n) {
-                const double r = rms_row_r(C, G, x, n, g, eps);
+                const double r = rstd[n * G + g];
                 sg += MUT(11) ? dy[n * C + c] * x[n * C + c] : dy[n * C + c] * (x[n * C + c] * r); /* mutant 11: raw x */
             }
             dgamma[c] = sg;

@@ -97,3 +97,45 @@ def check_against_oracle(wl, data, out, mask=ALL):
         rel_l2(out["dgamma"].cpu().numpy(), rdg, f"{wl.name} dgamma")
     if mask & gn.GN_GRAD_DBETA:
         rel_l2(out["dbeta"].cpu().numpy(), rdb, f"{wl.name} dbeta")
+
+
+# ---- RMSNorm over rows --------------------------------------------------------
+RMS_ALL = gn.GN_GRAD_DX | gn.GN_GRAD_DGAMMA
+
+
+def rows2d(t: torch.Tensor) -> torch.Tensor:
+    """[N, C, 1, 1] (or [N, C]) workload tensor as a contiguous [N, C] tensor."""
+    return t.reshape(t.shape[0], t.shape[1]).contiguous()
+
+
+def run_rms_gpu(wl, data, mask=RMS_ALL, affine=True):
+    dev = torch.device("cuda", 0)
+    x = rows2d(data["x"]).to(dev)
+    dy = rows2d(data["dy"]).to(dev)
+    gamma = data["gamma"].to(dev) if affine else None
+    fi, bi = gn.PlanInfo(), gn.PlanInfo()
+    y, rstd = gn.rms_forward(x, gamma, wl.eps, wl.G, info=fi)
+    dx, dg = gn.rms_backward(dy, x, rstd, gamma, wl.G, mask, info=bi)
+    torch.cuda.synchronize()
+    return dict(y=y, rstd=rstd, dx=dx, dgamma=dg, fwd_plan=fi, bwd_plan=bi)
+
+
+def check_rms_against_oracle(wl, data, out, mask=RMS_ALL, affine=True):
+    rtol, atol = TOL[wl.dtype]
+    x64 = rows2d(data["x"]).double().cpu().numpy().reshape(-1)
+    dy64 = rows2d(data["dy"]).double().cpu().numpy().reshape(-1)
+    g64 = data["gamma"].double().cpu().numpy() if affine else None
+    eps = float(np.float32(wl.eps))
+    ry, rr = oracle.rms_forward(x64, g64, wl.N, wl.C, wl.G, eps)
+    close(out["y"].double().cpu().numpy(), ry, rtol, atol, f"{wl.name} rms y")
+    close(out["rstd"].double().cpu().numpy(), rr, *STAT_TOL, f"{wl.name} rms rstd")
+    rdx, rdg, _ = oracle.rms_backward(dy64, x64, g64, wl.N, wl.C, wl.G, eps, want_dx=bool(mask & gn.GN_GRAD_DX),
+                                      want_dgamma=bool(mask & gn.GN_GRAD_DGAMMA))
+    if mask & gn.GN_GRAD_DX:
+        close(out["dx"].double().cpu().numpy(), rdx, rtol, atol, f"{wl.name} rms dx")
+    else:
+        assert out["dx"] is None
+    if mask & gn.GN_GRAD_DGAMMA:
+        rel_l2(out["dgamma"].cpu().numpy(), rdg, f"{wl.name} rms dgamma")
+    else:
+        assert out["dgamma"] is None

@@ -140,3 +140,59 @@ def test_workspace_sizes_cover_every_mask(L):
         n = L.gn_backward_workspace_size(4096, 1024, 1, 1, F16, NCHW, mask, None)
         assert n >= 0
     assert L.gn_backward_workspace_size(4096, 1024, 1, 1, F16, NCHW, 0, None) == 0
+
+
+# ---- RMSNorm over rows -------------------------------------------------------
+def rfwd(L, x=FAKE, g=None, y=FAKE, r=FAKE, N=4, C=64, G=1, eps=1e-5, dt=F16, ws=None, wsb=0, opts=None):
+    return L.gn_rms_forward(x, g, y, r, N, C, G, eps, dt, ws, wsb, None, opts)
+
+
+def rbwd(L, dy=FAKE, x=FAKE, r=FAKE, g=FAKE, dx=FAKE, dg=FAKE, mask=3, N=4, C=64, G=1, dt=F16, ws=None, wsb=0,
+         opts=None):
+    return L.gn_rms_backward(dy, x, r, g, dx, dg, mask, N, C, G, dt, ws, wsb, None, opts)
+
+
+def _forced(path):
+    return ctypes.byref(_lib.Options(path, 0, None, None, None))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), _lib.GN_ERR_INVALID),
+    (dict(G=0), _lib.GN_ERR_INVALID),
+    (dict(G=3), _lib.GN_ERR_INVALID),                 # 3 does not divide 64
+    (dict(dt=7), _lib.GN_ERR_UNSUPPORTED),
+    (dict(x=None), _lib.GN_ERR_INVALID),
+    (dict(r=None), _lib.GN_ERR_INVALID),
+    (dict(eps=-1.0), _lib.GN_ERR_INVALID),
+    (dict(C=36), _lib.GN_ERR_UNSUPPORTED),            # not a multiple of 8 fp16 elements
+    (dict(C=8192), _lib.GN_ERR_UNSUPPORTED),          # wider than the rows kernels hold
+    (dict(x=ctypes.c_void_p(0x10004)), _lib.GN_ERR_UNSUPPORTED),   # not 16-byte aligned
+    (dict(opts=_forced(_lib.GN_PATH_SLAB)), _lib.GN_ERR_UNSUPPORTED),
+])
+def test_rms_forward_rejects(L, kw, status):
+    assert rfwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=0), _lib.GN_ERR_INVALID),
+    (dict(mask=_lib.GN_GRAD_DBETA), _lib.GN_ERR_INVALID),      # no bias
+    (dict(mask=7), _lib.GN_ERR_INVALID),
+    (dict(dx=None), _lib.GN_ERR_INVALID),
+    (dict(dg=None), _lib.GN_ERR_INVALID),
+    (dict(g=None), _lib.GN_ERR_INVALID),                       # dgamma needs gamma
+    (dict(dy=None), _lib.GN_ERR_INVALID),
+    (dict(r=None), _lib.GN_ERR_INVALID),
+    (dict(C=36), _lib.GN_ERR_UNSUPPORTED),
+    (dict(mask=_lib.GN_GRAD_DGAMMA, ws=FAKE, wsb=8), _lib.GN_ERR_WORKSPACE),
+])
+def test_rms_backward_rejects(L, kw, status):
+    assert rbwd(L, **kw) == status
+
+
+def test_rms_zero_extent_and_sizes(L):
+    assert rfwd(L, N=0) == _lib.GN_OK
+    assert rbwd(L, N=0) == _lib.GN_OK
+    assert L.gn_rms_forward_workspace_size(4096, 1024, 1, F16, None) == 0
+    assert L.gn_rms_backward_workspace_size(4096, 1024, 1, F16, _lib.GN_GRAD_DX, None) == 0
+    assert L.gn_rms_backward_workspace_size(4096, 1024, 1, F16, _lib.GN_GRAD_DGAMMA, None) > 0
+    assert L.gn_rms_backward_workspace_size(4096, 1024, 1, F16, _lib.GN_GRAD_DBETA, None) == 0

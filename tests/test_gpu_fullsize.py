@@ -3,6 +3,7 @@ bench.py times (automatic path choice, default options).
 
 * NHWC fp16 1x128x1024x2048, G=16 and rows bf16 131072x4096: every output
   against the fp64 oracle on the whole tensor.
+* RMSNorm bf16 131072x4096: every output against the fp64 oracle.
 * NCHW fp32 112x64x512x512, G=8 (7.5 GB per tensor): y, dx, mean and rstd of
   sampled slices, each the oracle's result on that slice alone (a slice is
   its own GroupNorm problem with one group); dgamma/dbeta of two whole groups,
@@ -18,7 +19,8 @@ import torch
 import normalization_gn_stats_amd as gn
 import oracle
 from normalization_gn_stats_amd import inputs
-from gpu_harness import ALL, PARAM_REL_L2, STAT_TOL, TOL, close, img64, rel_l2, run_gpu, say
+from gpu_harness import (ALL, PARAM_REL_L2, STAT_TOL, TOL, check_rms_against_oracle, close, img64, rel_l2,
+                         run_gpu, run_rms_gpu, say)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -109,6 +111,24 @@ def test_full_nchw_sampled():
         del xg, dyg
         gc.collect()
     say(f"[full] {wl.name}: sampled outputs within tolerance")
+    del data, out
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_full_rms_bf16_131072x4096():
+    """RMSNorm at the rms_llm shape of the ROCm/pytorch PR #3564 table, every
+    output against the fp64 oracle on the whole tensor."""
+    _need_gpu()
+    wl = inputs.ROWS_BIG.scaled(name="rms_bf16_131072x4096", eps=1e-6)
+    say(f"[full] {wl.name}: generating on the device")
+    data = inputs.make_inputs(wl, seed=0, device="cuda")
+    out = run_rms_gpu(wl, data)
+    assert out["fwd_plan"].path == gn.GN_PATH_ROWS and out["bwd_plan"].path == gn.GN_PATH_ROWS
+    say(f"[full] {wl.name}: oracle")
+    check_rms_against_oracle(wl, data, out)
+    say(f"[full] {wl.name}: all outputs within tolerance")
     del data, out
     gc.collect()
     torch.cuda.empty_cache()

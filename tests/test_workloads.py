@@ -28,6 +28,16 @@ def test_row_workloads_are_the_rocm_table_shapes():
         assert (w.N, w.C, w.dtype, w.G, w.HW) == (g[key]["rows"], g[key]["cols"], g[key]["dtype"], 1, 1)
 
 
+def test_rms_workloads_are_the_rocm_table_shapes():
+    g = GOLD["rocm_pytorch_3564_shapes"]
+    for w, key in ((inputs.RMS_A, "rms_tile256"), (inputs.RMS_BIG, "rms_llm"), (inputs.RMS_NARROW, "rms_two_pass")):
+        assert (w.N, w.C, w.dtype, w.G, w.HW, w.op) == (g[key]["rows"], g[key]["cols"], g[key]["dtype"], 1, 1, "rms")
+        assert g[key]["op"] == "rms_norm"
+    w = inputs.RMS_A
+    assert w.fwd_min_bytes() == 2 * w.E * 2 + w.C * 4 + w.N * 4
+    assert w.bwd_min_bytes() == 3 * w.E * 2 + w.C * 4 + w.N * 4 + w.C * 4
+
+
 def test_inputs_are_seeded_and_quantised():
     w = inputs.TINY
     a = inputs.make_inputs(w, seed=0)

@@ -1,0 +1,122 @@
+"""Tensors past 2^31 elements on every path: 64-bit offsets throughout.
+
+Each case has more than 2^31 elements per tensor, so that any 32-bit index in
+a kernel would wrap.  The oracle checks sampled slices -- those at the start,
+those whose offsets cross 2^31, and the last -- each on its own (a slice is
+its own GroupNorm problem with one group).  Where the oracle cannot run on the
+whole tensor, dbeta is checked by its closed form (the column sum of dy, here
+summed in float64 by torch on the device) and dgamma by the same sum of
+dy * xhat taken from the saved statistics.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import normalization_gn_stats_amd as gn
+import oracle
+from normalization_gn_stats_amd import inputs
+from gpu_harness import PARAM_REL_L2, STAT_TOL, TOL, close, rel_l2, run_gpu, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+W = inputs.Workload
+TWO31 = 1 << 31
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _check_slice(wl, data, out, n, g, eps, rtol, atol, tag):
+    """Slice (n, g) of a dense NCHW or NHWC tensor against the oracle."""
+    D = wl.C // wl.G
+    cs = slice(g * D, (g + 1) * D)
+    xs = data["x"][n:n + 1, cs].contiguous().double().cpu().numpy().reshape(-1)
+    dys = data["dy"][n:n + 1, cs].contiguous().double().cpu().numpy().reshape(-1)
+    gam = data["gamma"][cs].double().cpu().numpy()
+    bet = data["beta"][cs].double().cpu().numpy()
+    ry, rm, rr = oracle.forward(xs, gam, bet, 1, D, wl.HW, 1, eps)
+    close(out["y"][n:n + 1, cs].contiguous().double().cpu().numpy().reshape(-1), ry, rtol, atol, f"{tag} y ({n},{g})")
+    close([out["mean"].reshape(-1)[n * wl.G + g].item()], rm, *STAT_TOL, f"{tag} mean ({n},{g})")
+    close([out["rstd"].reshape(-1)[n * wl.G + g].item()], rr, *STAT_TOL, f"{tag} rstd ({n},{g})")
+    rdx, _, _, _, _ = oracle.backward(dys, xs, gam, 1, D, wl.HW, 1, eps, want_dgamma=False, want_dbeta=False)
+    close(out["dx"][n:n + 1, cs].contiguous().double().cpu().numpy().reshape(-1), rdx, rtol, atol,
+          f"{tag} dx ({n},{g})")
+
+
+def _check_params_by_definition(wl, data, out, tag):
+    """dbeta_c = sum of dy over (n, p); dgamma_c = sum of dy * xhat with the
+    saved statistics; float64 on the device, in chunks of samples."""
+    dev = data["x"].device
+    D = wl.C // wl.G
+    db = torch.zeros(wl.C, dtype=torch.float64, device=dev)
+    dg = torch.zeros(wl.C, dtype=torch.float64, device=dev)
+    mean = out["mean"].reshape(wl.N, wl.G).double()
+    rstd = out["rstd"].reshape(wl.N, wl.G).double()
+    step = max(1, (1 << 27) // (wl.C * wl.HW))
+    for n0 in range(0, wl.N, step):
+        n1 = min(wl.N, n0 + step)
+        x = data["x"][n0:n1].double().reshape(n1 - n0, wl.C, wl.HW)
+        dy = data["dy"][n0:n1].double().reshape(n1 - n0, wl.C, wl.HW)
+        mu = mean[n0:n1].repeat_interleave(D, dim=1).unsqueeze(-1)
+        rs = rstd[n0:n1].repeat_interleave(D, dim=1).unsqueeze(-1)
+        db += dy.sum(dim=(0, 2))
+        dg += (dy * (x - mu) * rs).sum(dim=(0, 2))
+        del x, dy, mu, rs
+    rel_l2(out["dbeta"].cpu().numpy(), db.cpu().numpy(), f"{tag} dbeta", PARAM_REL_L2)
+    rel_l2(out["dgamma"].cpu().numpy(), dg.cpu().numpy(), f"{tag} dgamma", PARAM_REL_L2)
+
+
+def _run_case(wl, force, expect, slices):
+    assert wl.E > TWO31
+    say(f"[max] {wl.name}: {wl.E} elements, generating on the device")
+    data = inputs.make_inputs(wl, seed=1, device="cuda")
+    out = run_gpu(wl, data, force_path=force)
+    assert out["fwd_plan"].path == expect and out["bwd_plan"].path == expect
+    rtol, atol = TOL[wl.dtype]
+    eps = float(np.float32(wl.eps))
+    for n, g in slices:
+        say(f"[max] {wl.name}: slice ({n}, {g})")
+        _check_slice(wl, data, out, n, g, eps, rtol, atol, wl.name)
+    say(f"[max] {wl.name}: dgamma / dbeta")
+    _check_params_by_definition(wl, data, out, wl.name)
+    say(f"[max] {wl.name}: within tolerance")
+    del data, out
+    _free()
+
+
+@pytest.mark.timeout(900)
+def test_max_rows_f16():
+    _need_gpu()
+    N = (TWO31 // 1024) + 3   # rows past element 2^31
+    wl = W("max_rows_f16", N, 1024, 1, 1, 1, "f16", "nchw")
+    mid = TWO31 // 1024
+    _run_case(wl, None, gn.GN_PATH_ROWS, [(0, 0), (mid - 1, 0), (mid, 0), (N - 1, 0)])
+
+
+@pytest.mark.timeout(900)
+def test_max_nhwc_stream_f16():
+    _need_gpu()
+    wl = W("max_nhwc_f16", 1, 64, 8193, 4096, 8, "f16", "nhwc")
+    _run_case(wl, None, gn.GN_PATH_STREAM, [(0, 0), (0, 7)])
+
+
+@pytest.mark.timeout(900)
+def test_max_nchw_slab_f32():
+    _need_gpu()
+    wl = W("max_nchw_f32", 129, 64, 512, 512, 8, "f32", "nchw")
+    _run_case(wl, None, gn.GN_PATH_SLAB, [(0, 0), (127, 7), (128, 0), (128, 7)])
+
+
+@pytest.mark.timeout(900)
+def test_max_generic_nhwc_bf16():
+    _need_gpu()
+    wl = W("max_generic_bf16", 2, 32, 8193, 4096, 4, "bf16", "nhwc")
+    _run_case(wl, "generic", gn.GN_PATH_GENERIC, [(0, 0), (1, 3)])

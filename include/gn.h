@@ -162,8 +162,8 @@ int32_t gn_select_path(int32_t backward, int64_t N, int64_t C, int64_t HW, int64
  * by the backward).  gamma: [C] float32 or NULL (= 1); there is no bias.
  * dtypes as for gn_forward; y, dx take x's dtype.  These calls run on the
  * rows kernels only: they return GN_ERR_UNSUPPORTED when D or C is not a
- * multiple of 4 (float32) / 8 (16-bit) elements, when D exceeds 2048
- * (float32) / 4096 (16-bit) channels, when a pointer is not 16-byte aligned,
+ * multiple of 4 (float32) / 8 (16-bit) elements, when D exceeds 8192
+ * (float32) / 16384 (16-bit) channels, when a pointer is not 16-byte aligned,
  * or for a forced path other than GN_PATH_ROWS.  Pointers, streams,
  * workspace, options and errors as for gn_forward / gn_backward.
  */

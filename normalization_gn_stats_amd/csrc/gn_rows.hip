@@ -112,6 +112,108 @@ __global__ __launch_bounds__(kT) void rows_fwd_k(const T* __restrict__ x, const 
     }
 }
 
+// Forward for wide slices (more than 64*8 16-byte vectors): CS waves share a
+// slice -- wave w works on slot w / CS and on the vectors [part*NV*64,
+// (part+1)*NV*64) of its slice, part = w % CS -- and the per-wave sums meet in
+// LDS, added in part order.  Same arithmetic as rows_fwd_k otherwise; gamma
+// and beta are fetched per vector in the output loop (from L1/L2) instead of
+// being held in registers.
+template <typename T, int NV, int CS>
+__global__ __launch_bounds__(kT) void rows_fwd_cs_k(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                    const float* __restrict__ beta, T* __restrict__ y,
+                                                    float* __restrict__ mean, float* __restrict__ rstd, int64_t N,
+                                                    int64_t G, int64_t C, int D, float eps, int rms) {
+    constexpr int V = Vec<T>::V;
+    constexpr int SLOTS = kNW / CS;
+    __shared__ float red[2][kNW];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int slot = wave / CS;
+    const int cpart = wave - slot * CS;
+    const int64_t n_raw = (int64_t)blockIdx.x * SLOTS + slot;
+    const bool live = n_raw < N;                       // uniform per wave
+    const int64_t n = live ? n_raw : N - 1;            // past N: re-read the last slice, write nothing
+    const int64_t g = blockIdx.y;
+    const int64_t s = n * G + g;
+    const int64_t base = n * C + g * D;
+    const int nvec = D / V;
+    const int vbase = cpart * NV * kWave;
+    float v[NV][V];
+    u4v raw[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int vi = min(vbase + j * kWave + lane, nvec - 1);   // branch-free: see rows_fwd_k
+        raw[j] = ld16(x + base + (int64_t)vi * V);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        Vec<T>::unpack(raw[j], v[j]);
+        if (vbase + j * kWave + lane >= nvec) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) v[j][k] = 0.f;   // not part of the slice
+        }
+    }
+    const float invD = 1.0f / (float)D;
+    float mu = 0.f;
+    if (!rms) {   // RMSNorm: no mean
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int k = 0; k < V; ++k) sum += v[j][k];
+        sum = wave_sum(sum);
+        if (lane == 0) red[0][wave] = sum;
+        __syncthreads();
+        float t = red[0][slot * CS];
+#pragma unroll
+        for (int q = 1; q < CS; ++q) t += red[0][slot * CS + q];
+        mu = t * invD;
+    }
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        if (vbase + j * kWave + lane < nvec) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float d = v[j][k] - mu;
+                q = fmaf(d, d, q);
+            }
+        }
+    }
+    q = wave_sum(q);
+    if (lane == 0) red[1][wave] = q;
+    __syncthreads();
+    float t = red[1][slot * CS];
+#pragma unroll
+    for (int k = 1; k < CS; ++k) t += red[1][slot * CS + k];
+    float var = t * invD;
+    var = var > 0.f ? var : 0.f;
+    const float r = 1.0f / sqrtf(var + eps);
+    if (!live) return;
+    if (cpart == 0 && lane == 0) {
+        if (mean) mean[s] = mu;
+        rstd[s] = r;
+    }
+    if (y == nullptr) return;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int vi = vbase + j * kWave + lane;
+        if (vi >= nvec) continue;
+        const int64_t c0 = g * D + (int64_t)vi * V;
+        float o[V];
+#pragma unroll
+        for (int k = 0; k < V; k += 4) {
+            const float4 ga = gamma ? *reinterpret_cast<const float4*>(gamma + c0 + k) : make_float4(1.f, 1.f, 1.f, 1.f);
+            const float4 be = beta ? *reinterpret_cast<const float4*>(beta + c0 + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+            o[k] = fmaf(v[j][k] - mu, r * ga.x, be.x);
+            o[k + 1] = fmaf(v[j][k + 1] - mu, r * ga.y, be.y);
+            o[k + 2] = fmaf(v[j][k + 2] - mu, r * ga.z, be.z);
+            o[k + 3] = fmaf(v[j][k + 3] - mu, r * ga.w, be.w);
+        }
+        st16_nt(y + base + (int64_t)vi * V, Vec<T>::pack(o));
+    }
+}
+
 // Forward for many slices per group: each wave walks slices n = w, w + W, ...
 // of group g (W waves per group), with the next slice's loads issued before
 // the current one is reduced and written.  gamma and beta of the group are
@@ -650,12 +752,21 @@ __global__ __launch_bounds__(kT) void rows_colsum_k(const float2* __restrict__ p
 #endif
 
 // 16-byte vectors per lane of the forward (one wave per slice): 1, 2, 4, 8, or
-// 0 when the slice does not fit.
+// 0 when the slice does not fit one wave.
 int nv_for(const Problem& p) {
     const int V = p.elem_bytes == 4 ? 4 : 8;
     const int64_t nvec = p.D / V;
     const int64_t nv = (nvec + kWave - 1) / kWave;
     return nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 8 ? 8 : 0;
+}
+
+// Vectors per lane of the forward with four waves per slice (slices wider
+// than one wave takes): 4, 8, or 0 when the slice does not fit four waves.
+int nv_cs4(const Problem& p) {
+    const int V = p.elem_bytes == 4 ? 4 : 8;
+    const int64_t nvec = p.D / V;
+    const int64_t nv = (nvec + 4 * kWave - 1) / (4 * kWave);
+    return nv <= 4 ? 4 : nv <= 8 ? 8 : 0;
 }
 
 // Backward split: CS waves per slice (1, 2, 4) and NV vectors per lane, the
@@ -832,8 +943,31 @@ hipError_t bwd_launch(const Problem& p, const BwdArgs& a, const Launch& l) {
     return hipSuccess;
 }
 
+template <typename T, int NV>
+hipError_t fwd_cs4(const Problem& p, const FwdArgs& a, const Launch& l) {
+    constexpr int CS = 4;
+    constexpr int SLOTS = kNW / CS;
+    const unsigned grid = (unsigned)((p.N + SLOTS - 1) / SLOTS);
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL((rows_fwd_cs_k<T, NV, CS>), dim3(grid, (unsigned)p.G), dim3(kT), 0, l.stream, (const T*)a.x,
+                       a.gamma, a.beta, (T*)a.y, a.mean, a.rstd, p.N, p.G, p.C, (int)p.D, a.eps, a.rms);
+    if ((e = hipGetLastError())) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    if (l.info) {
+        l.info->path = GN_PATH_ROWS;
+        l.info->kernels = 1;
+        l.info->grid = (int64_t)grid * p.G;
+    }
+    return hipSuccess;
+}
+
 template <typename T>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
+    if (nv_for(p) == 0) {   // wider than one wave: four waves per slice
+        if (nv_cs4(p) == 4) return fwd_cs4<T, 4>(p, a, l);
+        return fwd_cs4<T, 8>(p, a, l);
+    }
     switch (narrow_lpr(p)) {
         case 1: return fwd_narrow<T, 1>(p, a, l);
         case 2: return fwd_narrow<T, 2>(p, a, l);
@@ -882,7 +1016,7 @@ bool rows_ok(const Problem& p) {
     if (p.HW != 1) return false;
     const int V = p.elem_bytes == 4 ? 4 : 8;
     if (p.D % V != 0 || p.C % V != 0) return false;   // every slice starts 16-byte aligned
-    if (nv_for(p) == 0 || bwd_shape(p).cs == 0) return false;   // slice fits the register budget
+    if ((nv_for(p) == 0 && nv_cs4(p) == 0) || bwd_shape(p).cs == 0) return false;   // slice fits the register budget
     return true;
 }
 

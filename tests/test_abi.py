@@ -165,7 +165,7 @@ def _forced(path):
     (dict(r=None), _lib.GN_ERR_INVALID),
     (dict(eps=-1.0), _lib.GN_ERR_INVALID),
     (dict(C=36), _lib.GN_ERR_UNSUPPORTED),            # not a multiple of 8 fp16 elements
-    (dict(C=8192), _lib.GN_ERR_UNSUPPORTED),          # wider than the rows kernels hold
+    (dict(C=32768), _lib.GN_ERR_UNSUPPORTED),         # wider than the rows kernels hold
     (dict(x=ctypes.c_void_p(0x10004)), _lib.GN_ERR_UNSUPPORTED),   # not 16-byte aligned
     (dict(opts=_forced(_lib.GN_PATH_SLAB)), _lib.GN_ERR_UNSUPPORTED),
 ])

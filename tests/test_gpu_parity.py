@@ -45,6 +45,11 @@ SMALL = [
     (W("rows_walk_f16_20000x512", 20000, 512, 1, 1, 1, "f16", "nchw"), None, gn.GN_PATH_ROWS),
     (W("rows_walk_f32_9001x2048", 9001, 2048, 1, 1, 1, "f32", "nchw"), None, gn.GN_PATH_ROWS),
     (W("rows_walk_bf16_g4_6000x4096", 6000, 4096, 1, 1, 4, "bf16", "nhwc"), None, gn.GN_PATH_ROWS),
+    # wide slices (more vectors than one wave takes): four waves per slice
+    (W("rows_wide_bf16_300x8192", 300, 8192, 1, 1, 1, "bf16", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_wide_f16_129x16384", 129, 16384, 1, 1, 1, "f16", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_wide_f32_201x3072", 201, 3072, 1, 1, 1, "f32", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_wide_f32_g2_50x16384", 50, 16384, 1, 1, 2, "f32", "nhwc"), None, gn.GN_PATH_ROWS),
     # narrow slices (at most 32 vectors): several slices per wavefront, from
     # 64 slices per wave (one vector each) to 2 (32 vectors each), with idle
     # lanes (6 vectors on 8 lanes) and ragged last row sets

@@ -2,8 +2,9 @@
 the C ABI) against the fp64 oracle.
 
 RMSNorm runs on the rows kernels with the mean taken as 0: the cases cover
-each of their shapes -- one wave per slice, several waves per slice, the
-slice-walking forward, several narrow slices per wave -- every dtype, groups
+each of their shapes -- one wave per slice, several waves per slice (wide
+slices, forward and backward), the slice-walking forward, several narrow
+slices per wave -- every dtype, groups
 of channels (G > 1), no weight, every output mask, and the RMSNorm shapes of
 the ROCm/pytorch PR #3564 table at 4096 x 1024 fp16 and 131072 x 64 fp16 (the
 131072 x 4096 bf16 one is in the full-size tests).
@@ -30,6 +31,8 @@ CASES = [
     W("rms_narrow_bf16_g2_777x96", 777, 96, 1, 1, 2, "bf16", "nchw"),
     W("rms_g4_f16_300x512", 300, 512, 1, 1, 4, "f16", "nchw"),
     W("rms_g8_bf16_2100x256", 2100, 256, 1, 1, 8, "bf16", "nchw"),
+    W("rms_wide_bf16_301x8192", 301, 8192, 1, 1, 1, "bf16", "nchw"),
+    W("rms_wide_f32_77x6144", 77, 6144, 1, 1, 1, "f32", "nchw"),
 ]
 
 

@@ -800,9 +800,21 @@ __global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ s
 #ifndef GN_SLAB_NCHW_RB
 #define GN_SLAB_NCHW_RB 16
 #endif
+// NCHW: the tile (R 16-byte chunks per thread) is sized to the channel plane
+// -- the power of two at or above the plane's chunks per thread, at most
+// GN_SLAB_NCHW_RF / RB -- so that a small plane does not leave most of a
+// fixed-size tile empty.
+int nchw_r(const Problem& p, bool backward) {
+    const int64_t per_thread = (p.HW / (p.elem_bytes == 4 ? 4 : 8) + kT - 1) / kT;
+    const int rmax = backward ? GN_SLAB_NCHW_RB : GN_SLAB_NCHW_RF;
+    int r = 1;
+    while (r < per_thread && r < rmax) r *= 2;
+    return r;
+}
+
 int tile_chunks(const Problem& p, bool backward) {
     if (p.layout == GN_NHWC) return backward ? GN_SLAB_NHWC_RB : GN_SLAB_NHWC_RF;
-    return backward ? GN_SLAB_NCHW_RB : GN_SLAB_NCHW_RF;
+    return nchw_r(p, backward);
 }
 
 size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -891,11 +903,34 @@ hipError_t launch_coop(K kernel, int64_t grid, void** args, hipStream_t s, bool 
 }
 
 template <typename T>
+auto nchw_fwd_kernel(int R) -> decltype(&slab_nchw_fwd<T, GN_SLAB_NCHW_RF>) {
+    switch (R) {
+        case 1: return slab_nchw_fwd<T, 1>;
+        case 2: return slab_nchw_fwd<T, 2>;
+        case 4: return slab_nchw_fwd<T, 4>;
+        case 8: return slab_nchw_fwd<T, 8>;
+        case 16: return slab_nchw_fwd<T, 16>;
+        default: return slab_nchw_fwd<T, GN_SLAB_NCHW_RF>;
+    }
+}
+
+template <typename T>
+auto nchw_bwd_kernel(int R) -> decltype(&slab_nchw_bwd<T, GN_SLAB_NCHW_RB>) {
+    switch (R) {
+        case 1: return slab_nchw_bwd<T, 1>;
+        case 2: return slab_nchw_bwd<T, 2>;
+        case 4: return slab_nchw_bwd<T, 4>;
+        case 8: return slab_nchw_bwd<T, 8>;
+        default: return slab_nchw_bwd<T, GN_SLAB_NCHW_RB>;
+    }
+}
+
+template <typename T>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
     auto kn = slab_nhwc_fwd<T, GN_SLAB_NHWC_RF>;
-    auto kc = slab_nchw_fwd<T, GN_SLAB_NCHW_RF>;
+    auto kc = nchw_fwd_kernel<T>(nchw_r(p, false));
     int64_t cap = nhwc ? resident_cap(kn, cus) : resident_cap(kc, cus);
     if (l.max_resident_override > 0 && l.max_resident_override < cap) cap = l.max_resident_override;
     Plan pl = layout_ws(p, false, cap);
@@ -942,7 +977,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
     auto kn = slab_nhwc_bwd<T, GN_SLAB_NHWC_RB>;
-    auto kc = slab_nchw_bwd<T, GN_SLAB_NCHW_RB>;
+    auto kc = nchw_bwd_kernel<T>(nchw_r(p, true));
     int64_t cap = nhwc ? resident_cap(kn, cus) : resident_cap(kc, cus);
     if (l.max_resident_override > 0 && l.max_resident_override < cap) cap = l.max_resident_override;
     Plan pl = layout_ws(p, true, cap);

@@ -28,6 +28,8 @@ CASES = [
     W("slab_nchw_f32_c16_g4", 2, 16, 64, 70, 4, "f32", "nchw"),
     W("slab_nchw_f16_c8_g2", 2, 8, 256, 300, 2, "f16", "nchw"),
     W("slab_nchw_bf16_c12_g3", 3, 12, 40, 52, 3, "bf16", "nchw"),
+    # tiles sized to small channel planes (ten channels per group, 64x64)
+    W("slab_nchw_f16_c320_g32", 2, 320, 64, 64, 32, "f16", "nchw"),
     inputs.TINY,
 ]
 

@@ -76,7 +76,8 @@ typedef enum gn_path {
     GN_PATH_STREAM = 4    /* NHWC: a few launches of one tile per workgroup
                              (statistics, fixed-order combine, outputs); the
                              planner's choice when a sample has more tiles than
-                             the co-resident grid holds */
+                             the co-resident grid holds, or a channel count the
+                             slab kernels do not take */
 } gn_path;
 
 /* What a call ran (filled when gn_options.info is not NULL). */

@@ -93,8 +93,10 @@ int32_t plan(const Problem& p, bool backward, const gn_options* opts) {
     if (f == GN_PATH_STREAM) return gn::stream_ok(p) ? GN_PATH_STREAM : -1;
     if (f != GN_PATH_AUTO) return -1;
     if (gn::rows_ok(p)) return GN_PATH_ROWS;
-    // an NHWC sample too large for the co-resident grid streams instead
-    if (gn::stream_ok(p) && !gn::slab_resident(p, backward)) return GN_PATH_STREAM;
+    // NHWC: the cooperative slab kernels when a sample fits the co-resident
+    // grid; the stream kernels for larger samples and for channel counts the
+    // slab kernels do not take
+    if (gn::stream_ok(p) && (!gn::slab_ok(p) || !gn::slab_resident(p, backward))) return GN_PATH_STREAM;
     if (gn::slab_ok(p)) return GN_PATH_SLAB;
     return GN_PATH_GENERIC;
 }

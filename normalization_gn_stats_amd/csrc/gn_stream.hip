@@ -9,9 +9,8 @@
 // pays a per-tile hand-out and barrier cost on top; launching one workgroup
 // per tile lets the hardware dispatcher balance the load instead.
 //
-//   forward   1. per tile: (count, mean, M2) of each group, exact two-pass per
-//               thread from registers, merged across the tile's threads
-//               (Chan et al.'s pairwise update, fixed tree order)
+//   forward   1. per tile: (count, mean, M2) of each group, an exact two-pass
+//               over the tile from registers (fixed-order trees in LDS)
 //             2. per slice: the tile partials in a fixed order -> mean, rstd
 //               (sum n_i*mean_i, then sum M2_i + n_i*(mean_i - mean)^2)
 //             3. per tile: y = (x - mean)*(rstd*gamma_c) + beta_c
@@ -63,10 +62,15 @@ struct StreamCfg {
 int vec_elems(const Problem& p) { return p.elem_bytes == 4 ? 4 : 8; }
 
 // Thread t owns chunk q = t % CPP of each pixel it visits (channels q*V ..
-// q*V+V-1, all in group q*V/D) and pixel t / CPP of each of the tile's R
-// iterations; a tile is R*PPI consecutive pixels of one sample.
+// q*V+V-1, CPP = C/V chunks per pixel) and pixel row t / CPP of each of the
+// tile's R iterations; a tile is R*PPI consecutive pixels of one sample,
+// PPI = floor(kT / CPP).  When CPP does not divide kT, the last kT - PPI*CPP
+// threads are idle.  A chunk's channels may belong to two or more groups (D
+// need not be a multiple of V): every per-channel quantity looks up its own
+// channel's group.
 struct TileGeom {
     int V, CPP, q, pi, PPI;
+    bool active;
     int64_t TP;
 };
 
@@ -78,6 +82,7 @@ __device__ inline TileGeom tile_geom(int64_t C) {
     g.q = threadIdx.x % g.CPP;
     g.pi = threadIdx.x / g.CPP;
     g.PPI = kT / g.CPP;
+    g.active = g.pi < g.PPI;
     g.TP = (int64_t)g.PPI * R;
     return g;
 }
@@ -91,6 +96,103 @@ __device__ inline void load_tile(const T* __restrict__ src, int64_t HW, int64_t 
     for (int j = 0; j < R; ++j) {
         const int64_t p = min(p0 + (int64_t)j * PPI, HW - 1);
         dst[j] = ld16_nt(src + p * C);
+    }
+}
+
+__device__ inline void add_to(float& a, const float& b) { a += b; }
+__device__ inline void add_to(float2& a, const float2& b) {
+    a.x += b.x;
+    a.y += b.y;
+}
+
+// Fixed-order tree over the tile's PPI pixel rows of per-thread, per-channel
+// values s[t*V + k]; afterwards row 0 holds the tile's channel totals, the
+// value of channel c at s[c].  Every thread of the workgroup calls it.
+template <int V, typename S>
+__device__ inline void tree_rows(S* s, const TileGeom& tg) {
+    int top = 1;
+    while (top < tg.PPI) top *= 2;
+    for (int h = top / 2; h > 0; h /= 2) {
+        if (tg.active && tg.pi < h && tg.pi + h < tg.PPI) {
+            const int t = threadIdx.x;
+#pragma unroll
+            for (int k = 0; k < V; ++k) add_to(s[t * V + k], s[(t + h * tg.CPP) * V + k]);
+        }
+        __syncthreads();
+    }
+}
+
+// Fixed-order tree over consecutive segments of `seg` entries among the
+// first `count` entries of s (a group's channels, or its chunks); afterwards
+// s[g*seg] holds segment g's total.  Every thread calls it.
+__device__ inline void tree_groups(float* s, int count, int seg) {
+    int top = 1;
+    while (top < seg) top *= 2;
+    for (int h = top / 2; h > 0; h /= 2) {
+        for (int c = threadIdx.x; c < count; c += kT) {
+            const int l = c % seg;
+            if (l < h && l + h < seg) s[c] += s[c + h];
+        }
+        __syncthreads();
+    }
+}
+
+// Group totals of per-thread, per-channel values acc[k] over the tile: the
+// values go through the pixel-row tree and the per-group tree; afterwards
+// group g's total lies at s[group_slot(g)].  WHOLE (D % V == 0): each thread
+// first adds its V channels, all of one group, so the trees carry one value
+// per thread (the group's total then at s[g*D/V]); otherwise V values per
+// thread and a tree over each group's channels (total at s[g*D]).
+template <int V, bool WHOLE>
+__device__ inline void group_totals(float* s, const float (&acc)[V], const TileGeom& tg, int C, int D) {
+    const int t = threadIdx.x;
+    if constexpr (WHOLE) {
+        float a = 0.f;
+#pragma unroll
+        for (int k = 0; k < V; ++k) a += acc[k];
+        s[t] = a;
+        __syncthreads();
+        tree_rows<1>(s, tg);
+        tree_groups(s, tg.CPP, D / V);
+    } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) s[t * V + k] = acc[k];
+        __syncthreads();
+        tree_rows<V>(s, tg);
+        tree_groups(s, C, D);
+    }
+}
+
+template <int V, bool WHOLE>
+__device__ inline int group_slot(int g, int D) { return WHOLE ? g * (D / V) : g * D; }
+
+// Slice (n, g) of each of a thread's V channels q*V .. q*V+V-1.  WHOLE: the
+// groups are whole 16-byte chunks, so all V channels share one slice (one
+// division, one load per quantity); otherwise one per channel (32-bit
+// divisions: channels are below 2048).  A compile-time choice, so that
+// neither form has a branch around loads.
+template <int V, bool WHOLE>
+__device__ inline void channel_slices(int q, int D, int64_t n, int64_t G, int64_t (&s)[V]) {
+    if constexpr (WHOLE) {
+        const int64_t s0 = n * G + (q * V) / D;
+#pragma unroll
+        for (int k = 0; k < V; ++k) s[k] = s0;
+    } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) s[k] = n * G + (q * V + k) / D;
+    }
+}
+
+// Per-channel copies of a per-slice quantity.
+template <int V, bool WHOLE, typename S>
+__device__ inline void per_channel(const S* __restrict__ v, const int64_t (&s)[V], S (&o)[V]) {
+    if constexpr (WHOLE) {
+        const S a = v[s[0]];
+#pragma unroll
+        for (int k = 0; k < V; ++k) o[k] = a;
+    } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) o[k] = v[s[k]];
     }
 }
 
@@ -111,67 +213,61 @@ __device__ inline void load_params(const float* __restrict__ p, int64_t c0, floa
 }
 
 // ---- forward ----------------------------------------------------------------
-// grid (tiles, N); part: [N*G][tiles] float4 (count, mean, M2, -)
-template <typename T, int R>
+// grid (tiles, N); part: [N*G][tiles] float4 (count, mean, M2, -) of each
+// group over the tile -- an exact two-pass over the tile: per-channel sums ->
+// group sums -> the tile's group means, then per-channel sums of squared
+// deviations from them -> group M2, each reduction a fixed-order tree.
+constexpr int kMaxC = kT * 8;   // channels of a pixel (C/V <= kT chunks of at most 8)
+template <typename T, int R, bool WHOLE>
 __global__ __launch_bounds__(kT) void fwd_tile_stats(const T* __restrict__ x, StreamCfg cfg,
                                                      float4* __restrict__ part) {
     const TileGeom tg = tile_geom<T, R>(cfg.C);
     constexpr int V = Vec<T>::V;
     const int t = threadIdx.x;
+    const int C = (int)cfg.C, D = (int)cfg.D, G = (int)cfg.G;
     const int64_t tile = blockIdx.x, n = blockIdx.y;
-    __shared__ Stat sst[kT];
+    __shared__ float s[kT * 8];      // [thread][k], then channel totals at s[c]
+    __shared__ float gsum[kMaxC];    // group sums of pass 1 (G <= C)
     u4v reg[R];
     const int64_t p0 = tile * tg.TP + tg.pi;
     load_tile<T, R>(x + n * cfg.HW * cfg.C + tg.q * V, cfg.HW, cfg.C, p0, tg.PPI, reg);
-    float s = 0.f;
-    int cnt = 0;
+    float acc[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) acc[k] = 0.f;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        if (p0 + (int64_t)j * tg.PPI < cfg.HW) {
+        if (tg.active && p0 + (int64_t)j * tg.PPI < cfg.HW) {
             float v[V];
             Vec<T>::unpack(reg[j], v);
 #pragma unroll
-            for (int k = 0; k < V; ++k) s += v[k];
-            cnt += V;
+            for (int k = 0; k < V; ++k) acc[k] += v[k];
         }
     }
-    Stat st = stat_empty();
-    if (cnt > 0) {
-        const float mt = s / (float)cnt;
-        float m2 = 0.f;
+    group_totals<V, WHOLE>(s, acc, tg, C, D);
+    const int64_t rows = min(tg.TP, cfg.HW - tile * tg.TP);   // pixels of this tile
+    const float cnt = (float)(rows * D);                       // elements of a group in it
+    float mu[V];
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-            if (p0 + (int64_t)j * tg.PPI < cfg.HW) {
-                float v[V];
-                Vec<T>::unpack(reg[j], v);
+    for (int k = 0; k < V; ++k) mu[k] = s[group_slot<V, WHOLE>((tg.q * V + k) / D, D)] / cnt;
+    for (int g = t; g < G; g += kT) gsum[g] = s[group_slot<V, WHOLE>(g, D)];
+    __syncthreads();   // every read of pass 1's totals is done before s is reused
 #pragma unroll
-                for (int k = 0; k < V; ++k) {
-                    const float d = v[k] - mt;
-                    m2 = fmaf(d, d, m2);
-                }
+    for (int k = 0; k < V; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (tg.active && p0 + (int64_t)j * tg.PPI < cfg.HW) {
+            float v[V];
+            Vec<T>::unpack(reg[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float d = v[k] - mu[k];
+                acc[k] = fmaf(d, d, acc[k]);
             }
         }
-        st = Stat{(float)cnt, mt, m2};
     }
-    // merge tree: first over the pixel rows of each chunk, then over the
-    // chunks of each group (row 0 only)
-    sst[t] = st;
-    __syncthreads();
-    for (int h = tg.PPI / 2; h > 0; h /= 2) {
-        if (tg.pi < h) sst[t] = stat_merge(sst[t], sst[t + h * tg.CPP]);
-        __syncthreads();
-    }
-    const int qpg = (int)cfg.D / V;   // any count: the tree skips missing partners
-    int top = 1;
-    while (top < qpg) top *= 2;
-    for (int h = top / 2; h > 0; h /= 2) {
-        if (t < tg.CPP && (t % qpg) < h && (t % qpg) + h < qpg) sst[t] = stat_merge(sst[t], sst[t + h]);
-        __syncthreads();
-    }
-    for (int g = t; g < (int)cfg.G; g += kT) {
-        const Stat a = sst[g * qpg];
-        part[(n * cfg.G + g) * cfg.tiles + tile] = make_float4(a.n, a.mean, a.m2, 0.f);
-    }
+    group_totals<V, WHOLE>(s, acc, tg, C, D);
+    for (int g = t; g < G; g += kT)
+        part[(n * cfg.G + g) * cfg.tiles + tile] = make_float4(cnt, gsum[g] / cnt, s[group_slot<V, WHOLE>(g, D)], 0.f);
 }
 
 // one workgroup of kFinT threads per slice (blockIdx.x = n*G + g).  Each pass
@@ -224,26 +320,28 @@ __global__ __launch_bounds__(kFinT) void fwd_finalize(const float4* __restrict__
 }
 
 // grid (otiles, N)
-template <typename T, int R>
+template <typename T, int R, bool WHOLE>
 __global__ __launch_bounds__(kT) void fwd_apply(const T* __restrict__ x, const float* __restrict__ gamma,
                                                 const float* __restrict__ beta, T* __restrict__ y,
                                                 const float* __restrict__ mean, const float* __restrict__ rstd,
                                                 StreamCfg cfg) {
     const TileGeom tg = tile_geom<T, R>(cfg.C);
     constexpr int V = Vec<T>::V;
-    const int gq = (tg.q * V) / (int)cfg.D;
+    if (!tg.active) return;   // no barrier below
     const int64_t tile = blockIdx.x, n = blockIdx.y;
     const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
     u4v reg[R];
     const int64_t p0 = tile * tg.TP + tg.pi;
     load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, reg);
-    const float mu = mean[n * cfg.G + gq];
-    const float r = rstd[n * cfg.G + gq];
-    float a[V], b[V];
+    float mu[V], rs[V], a[V], b[V];
+    int64_t sl[V];
+    channel_slices<V, WHOLE>(tg.q, (int)cfg.D, n, cfg.G, sl);
+    per_channel<V, WHOLE>(mean, sl, mu);
+    per_channel<V, WHOLE>(rstd, sl, rs);
     load_params<V>(gamma, tg.q * V, 1.f, a);
     load_params<V>(beta, tg.q * V, 0.f, b);
 #pragma unroll
-    for (int k = 0; k < V; ++k) a[k] *= r;
+    for (int k = 0; k < V; ++k) a[k] *= rs[k];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int64_t p = p0 + (int64_t)j * tg.PPI;
@@ -251,7 +349,7 @@ __global__ __launch_bounds__(kT) void fwd_apply(const T* __restrict__ x, const f
             float v[V], o[V];
             Vec<T>::unpack(reg[j], v);
 #pragma unroll
-            for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu, a[k], b[k]);
+            for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu[k], a[k], b[k]);
             st16_nt(y + off + p * cfg.C, Vec<T>::pack(o));
         }
     }
@@ -259,7 +357,7 @@ __global__ __launch_bounds__(kT) void fwd_apply(const T* __restrict__ x, const f
 
 // ---- backward ---------------------------------------------------------------
 // grid (tiles, N); part: [N][tiles][C] float2 (sum dy, sum dy*xhat)
-template <typename T, int R>
+template <typename T, int R, bool WHOLE>
 __global__ __launch_bounds__(kT) void bwd_tile_sums(const T* __restrict__ dy, const T* __restrict__ x,
                                                     const float* __restrict__ mean,
                                                     const float* __restrict__ rstd, StreamCfg cfg,
@@ -267,7 +365,6 @@ __global__ __launch_bounds__(kT) void bwd_tile_sums(const T* __restrict__ dy, co
     const TileGeom tg = tile_geom<T, R>(cfg.C);
     constexpr int V = Vec<T>::V;
     const int t = threadIdx.x;
-    const int gq = (tg.q * V) / (int)cfg.D;
     const int64_t tile = blockIdx.x, n = blockIdx.y;
     const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
     __shared__ float2 lds[kT * 8];   // [thread][k], V <= 8
@@ -275,41 +372,31 @@ __global__ __launch_bounds__(kT) void bwd_tile_sums(const T* __restrict__ dy, co
     const int64_t p0 = tile * tg.TP + tg.pi;
     load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, rx);
     load_tile<T, R>(dy + off, cfg.HW, cfg.C, p0, tg.PPI, rd);
-    const float mu = mean[n * cfg.G + gq];
-    const float r = rstd[n * cfg.G + gq];
+    float mu[V], rs[V];
+    int64_t sl[V];
+    channel_slices<V, WHOLE>(tg.q, (int)cfg.D, n, cfg.G, sl);
+    per_channel<V, WHOLE>(mean, sl, mu);
+    per_channel<V, WHOLE>(rstd, sl, rs);
     float s1[V], s2[V];
 #pragma unroll
     for (int k = 0; k < V; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        if (p0 + (int64_t)j * tg.PPI < cfg.HW) {
+        if (tg.active && p0 + (int64_t)j * tg.PPI < cfg.HW) {
             float xv[V], dv[V];
             Vec<T>::unpack(rx[j], xv);
             Vec<T>::unpack(rd[j], dv);
 #pragma unroll
             for (int k = 0; k < V; ++k) {
                 s1[k] += dv[k];
-                s2[k] = fmaf(dv[k], (xv[k] - mu) * r, s2[k]);
+                s2[k] = fmaf(dv[k], (xv[k] - mu[k]) * rs[k], s2[k]);
             }
         }
     }
 #pragma unroll
     for (int k = 0; k < V; ++k) lds[t * V + k] = make_float2(s1[k], s2[k]);
     __syncthreads();
-    // tree over the pixel rows of each chunk
-    for (int h = tg.PPI / 2; h > 0; h /= 2) {
-        if (tg.pi < h) {
-#pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const float2 u = lds[(t + h * tg.CPP) * V + k];
-                float2 w = lds[t * V + k];
-                w.x += u.x;
-                w.y += u.y;
-                lds[t * V + k] = w;
-            }
-        }
-        __syncthreads();
-    }
+    tree_rows<V>(lds, tg);
     // row 0 holds the tile's channel sums, channel c at lds[c]
     float2* dst = part + (n * cfg.tiles + tile) * cfg.C;
     for (int c = t; c < (int)cfg.C; c += kT) dst[c] = lds[c];
@@ -392,23 +479,32 @@ __global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ s
 }
 
 // grid (otiles, N)
-template <typename T, int R>
+template <typename T, int R, bool WHOLE>
 __global__ __launch_bounds__(kT) void bwd_dx(const T* __restrict__ dy, const T* __restrict__ x,
                                              const float* __restrict__ mean, const float* __restrict__ rstd,
                                              const float* __restrict__ gamma, const float2* __restrict__ ab,
                                              T* __restrict__ dx, StreamCfg cfg) {
     const TileGeom tg = tile_geom<T, R>(cfg.C);
     constexpr int V = Vec<T>::V;
-    const int gq = (tg.q * V) / (int)cfg.D;
+    if (!tg.active) return;   // no barrier below
     const int64_t tile = blockIdx.x, n = blockIdx.y;
     const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
     u4v rx[R], rd[R];
     const int64_t p0 = tile * tg.TP + tg.pi;
     load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, rx);
     load_tile<T, R>(dy + off, cfg.HW, cfg.C, p0, tg.PPI, rd);
-    const float mu = mean[n * cfg.G + gq];
-    const float r = rstd[n * cfg.G + gq];
-    const float2 AB = ab[n * cfg.G + gq];
+    float mu[V], rs[V], Ak[V], Bk[V];
+    int64_t sl[V];
+    channel_slices<V, WHOLE>(tg.q, (int)cfg.D, n, cfg.G, sl);
+    per_channel<V, WHOLE>(mean, sl, mu);
+    per_channel<V, WHOLE>(rstd, sl, rs);
+    float2 abk[V];
+    per_channel<V, WHOLE>(ab, sl, abk);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        Ak[k] = abk[k].x;
+        Bk[k] = abk[k].y;
+    }
     float ga[V];
     load_params<V>(gamma, tg.q * V, 1.f, ga);
 #pragma unroll
@@ -421,9 +517,9 @@ __global__ __launch_bounds__(kT) void bwd_dx(const T* __restrict__ dy, const T* 
             Vec<T>::unpack(rd[j], dv);
 #pragma unroll
             for (int k = 0; k < V; ++k) {
-                const float xh = (xv[k] - mu) * r;
+                const float xh = (xv[k] - mu[k]) * rs[k];
                 const float gd = dv[k] * ga[k];
-                o[k] = r * ((gd - AB.x) - xh * AB.y);
+                o[k] = rs[k] * ((gd - Ak[k]) - xh * Bk[k]);
             }
             st16_nt(dx + off + p * cfg.C, Vec<T>::pack(o));
         }
@@ -476,7 +572,7 @@ BwdPlan bwd_plan(const Problem& p) {
     return b;
 }
 
-template <typename T>
+template <typename T, bool WHOLE>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     constexpr int R = GN_STREAM_R_STATS, RO = GN_STREAM_R_APPLY;
     const StreamCfg cfg = make_cfg(p, R, RO, a.eps);
@@ -484,12 +580,12 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     const dim3 grid((unsigned)cfg.tiles, (unsigned)p.N), ogrid((unsigned)cfg.otiles, (unsigned)p.N);
     hipError_t e = record(l.ev_begin, l.stream);
     if (e) return e;
-    hipLaunchKernelGGL((fwd_tile_stats<T, R>), grid, dim3(kT), 0, l.stream, (const T*)a.x, cfg, part);
+    hipLaunchKernelGGL((fwd_tile_stats<T, R, WHOLE>), grid, dim3(kT), 0, l.stream, (const T*)a.x, cfg, part);
     hipLaunchKernelGGL(fwd_finalize, dim3((unsigned)(p.N * p.G)), dim3(kFinT), 0, l.stream, part, cfg, a.mean, a.rstd);
     if ((e = hipGetLastError())) return e;
     int kernels = 2;
     if (a.y) {
-        hipLaunchKernelGGL((fwd_apply<T, RO>), ogrid, dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta, (T*)a.y,
+        hipLaunchKernelGGL((fwd_apply<T, RO, WHOLE>), ogrid, dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta, (T*)a.y,
                            a.mean, a.rstd, cfg);
         if ((e = hipGetLastError())) return e;
         ++kernels;
@@ -504,7 +600,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     return hipSuccess;
 }
 
-template <typename T>
+template <typename T, bool WHOLE>
 hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     constexpr int R = GN_STREAM_R_SUMS, RO = GN_STREAM_R_DX;
     const StreamCfg cfg = make_cfg(p, R, RO, 0.f);
@@ -522,7 +618,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     int kernels = 0;
     hipError_t e;
     if ((e = record(l.ev_begin, l.stream))) return e;
-    hipLaunchKernelGGL((bwd_tile_sums<T, R>), grid, dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean,
+    hipLaunchKernelGGL((bwd_tile_sums<T, R, WHOLE>), grid, dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean,
                        a.rstd, cfg, part);
     ++kernels;
     if (b.chunks > 1) {
@@ -549,7 +645,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     }
     if ((e = hipGetLastError())) return e;
     if (want_dx) {
-        hipLaunchKernelGGL((bwd_dx<T, RO>), ogrid, dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean,
+        hipLaunchKernelGGL((bwd_dx<T, RO, WHOLE>), ogrid, dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean,
                            a.rstd, a.gamma, (const float2*)ab, (T*)a.dx, cfg);
         ++kernels;
         if ((e = hipGetLastError())) return e;
@@ -566,14 +662,14 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
 
 }  // namespace
 
-// Same shape condition as the NHWC slab kernels: 16-byte chunks never straddle
-// a group and the chunks of one pixel divide the workgroup.
+// NHWC whose pixels are whole 16-byte chunks (C a multiple of 4 fp32 / 8
+// 16-bit channels) with at most kT chunks per pixel; any channels per group.
 bool stream_ok(const Problem& p) {
     if (p.layout != GN_NHWC || p.HW < 1) return false;
     const int V = vec_elems(p);
-    if (p.C % V != 0 || p.D % V != 0) return false;
+    if (p.C % V != 0) return false;
     const int64_t cpp = p.C / V;
-    if (cpp < 1 || cpp > kT || (kT % cpp) != 0) return false;
+    if (cpp < 1 || cpp > kT) return false;
     // grid limits: samples and column-sum chunks on grid y (at most 65535)
     if (p.N > 65535) return false;
     const int64_t chunks = (tiles_of(p, GN_STREAM_R_SUMS) + kRowsPerChunk - 1) / kRowsPerChunk;
@@ -586,19 +682,22 @@ size_t stream_fwd_ws(const Problem& p) {
 
 size_t stream_bwd_ws(const Problem& p, int32_t) { return bwd_plan(p).total; }
 
+// groups made of whole 16-byte chunks (the common case) or not
 hipError_t stream_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {
+    const bool whole = p.D % vec_elems(p) == 0;
     switch (p.dtype) {
-        case GN_F32: return fwd_t<float>(p, a, l);
-        case GN_F16: return fwd_t<_Float16>(p, a, l);
-        default: return fwd_t<__bf16>(p, a, l);
+        case GN_F32: return whole ? fwd_t<float, true>(p, a, l) : fwd_t<float, false>(p, a, l);
+        case GN_F16: return whole ? fwd_t<_Float16, true>(p, a, l) : fwd_t<_Float16, false>(p, a, l);
+        default: return whole ? fwd_t<__bf16, true>(p, a, l) : fwd_t<__bf16, false>(p, a, l);
     }
 }
 
 hipError_t stream_bwd(const Problem& p, const BwdArgs& a, const Launch& l) {
+    const bool whole = p.D % vec_elems(p) == 0;
     switch (p.dtype) {
-        case GN_F32: return bwd_t<float>(p, a, l);
-        case GN_F16: return bwd_t<_Float16>(p, a, l);
-        default: return bwd_t<__bf16>(p, a, l);
+        case GN_F32: return whole ? bwd_t<float, true>(p, a, l) : bwd_t<float, false>(p, a, l);
+        case GN_F16: return whole ? bwd_t<_Float16, true>(p, a, l) : bwd_t<_Float16, false>(p, a, l);
+        default: return whole ? bwd_t<__bf16, true>(p, a, l) : bwd_t<__bf16, false>(p, a, l);
     }
 }
 

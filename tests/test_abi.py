@@ -132,7 +132,13 @@ def test_path_selection(L):
         assert sel(bw, 112, 64, 512 * 512, 8, F32, NCHW) == _lib.GN_PATH_SLAB
     assert sel(0, 1, 128, 64 * 130, 16, F16, NHWC, _lib.GN_PATH_STREAM) == _lib.GN_PATH_STREAM
     assert sel(0, 2, 16, 64, 4, F32, NCHW, _lib.GN_PATH_STREAM) == -1      # stream is NHWC only
-    assert sel(0, 2, 96, 64, 4, F16, NHWC, _lib.GN_PATH_STREAM) == -1      # 12 chunks per pixel
+    assert sel(0, 2, 96, 64, 4, F16, NHWC, _lib.GN_PATH_STREAM) == _lib.GN_PATH_STREAM   # 12 chunks per pixel
+    assert sel(0, 2, 4100, 64, 4, F16, NHWC, _lib.GN_PATH_STREAM) == -1   # more chunks per pixel than threads
+    assert sel(0, 2, 36, 64, 4, F16, NHWC, _lib.GN_PATH_STREAM) == -1     # pixel not whole 16-byte chunks
+    # channel counts the slab kernels do not take (Stable Diffusion-like) stream
+    for bw in (0, 1):
+        assert sel(bw, 2, 320, 64 * 64, 32, F16, NHWC) == _lib.GN_PATH_STREAM
+        assert sel(bw, 2, 1280, 32 * 32, 32, F16, NHWC) == _lib.GN_PATH_STREAM
 
 
 def test_workspace_sizes_cover_every_mask(L):

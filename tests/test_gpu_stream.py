@@ -30,6 +30,16 @@ CASES = [
     # more than 64 backward tiles per sample: two column-sum levels
     W("stream_nhwc_f16_c64_twolevel", 2, 64, 130, 131, 8, "f16", "nhwc"),
     W("stream_nhwc_f32_c16_twolevel", 1, 16, 200, 181, 2, "f32", "nhwc"),
+    # channel counts the slab kernels do not take: chunks per pixel not
+    # dividing the workgroup (idle threads), groups not whole 16-byte chunks
+    # (a chunk spans two or more groups), one channel per group
+    W("stream_nhwc_f16_c320_g32", 2, 320, 37, 41, 32, "f16", "nhwc"),
+    W("stream_nhwc_f16_c640_g32", 1, 640, 30, 33, 32, "f16", "nhwc"),
+    W("stream_nhwc_bf16_c1280_g32", 2, 1280, 9, 13, 32, "bf16", "nhwc"),
+    W("stream_nhwc_f32_c96_g24", 2, 96, 20, 21, 24, "f32", "nhwc"),
+    W("stream_nhwc_f16_c24_g3", 3, 24, 40, 41, 3, "f16", "nhwc"),
+    W("stream_nhwc_f32_c12_g12", 2, 12, 30, 31, 12, "f32", "nhwc"),
+    W("stream_nhwc_f16_c2048_g1", 1, 2048, 6, 7, 1, "f16", "nhwc"),
 ]
 
 

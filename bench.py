@@ -44,6 +44,9 @@ WORKLOADS = {
     "rms_f16_4096x1024": ("rms_f16_4096x1024",),
     "rms_bf16_131072x4096": ("rms_bf16_131072x4096",),
     "rms_f16_131072x64": ("rms_f16_131072x64",),
+    # strided (non-contiguous) input: gn_forward_strided / gn_backward_strided
+    "nchw_f32_112x64x510x510_g8_crop1": ("nchw_f32_112x64x510x510_g8_crop1",),
+    "tiny_nchw_f32_2x32x14x14_g8_crop1": ("tiny_nchw_f32_2x32x14x14_g8_crop1",),
 }
 DEFAULT = "rows_f16_4096x1024+8192x768"
 
@@ -168,6 +171,14 @@ def main():
             lay = gn.GN_NCHW
             fws = gn.rms_forward_workspace_size(wl.N, wl.C, wl.G, code, args.force_path)
             bws = gn.rms_backward_workspace_size(wl.N, wl.C, wl.G, code, rms_mask, args.force_path)
+        elif wl.crop:
+            # views: outputs dense NCHW, inputs with their own strides
+            lay = None
+            y_, dx_ = torch.empty(x.shape, dtype=x.dtype, device=dev), torch.empty(x.shape, dtype=x.dtype, device=dev)
+            _, _, H_, W_, st = gn.strided_dims(x, y_, dy, dx_)
+            fws = gn.forward_strided_workspace_size(wl.N, wl.C, H_, W_, wl.G, code, st[0], st[1], args.force_path)
+            bws = gn.backward_strided_workspace_size(wl.N, wl.C, H_, W_, wl.G, code, st[2], st[0], st[3], mask,
+                                                     args.force_path)
         else:
             lay = gn.layout_of(x)
             fws = gn.forward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, args.force_path)
@@ -178,6 +189,8 @@ def main():
                   fws=torch.empty(max(fws, 1), dtype=torch.uint8, device=dev),
                   bws=torch.empty(max(bws, 1), dtype=torch.uint8, device=dev),
                   fplan=gn.PlanInfo(), bplan=gn.PlanInfo())
+        if wl.crop:
+            sh.update(y=y_, dx=dx_, hw=(H_, W_), strides=st)
         shapes.append(sh)
 
     # Pre-marshalled C-ABI calls (the binding's checks ran once above, through
@@ -188,7 +201,7 @@ def main():
     def calls_for(sh, stream_handle, evs):
         wl = sh["wl"]
         code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
-        lay = gn.layout_of(sh["x"]) if wl.op != "rms" else gn.GN_NCHW
+        lay = gn.GN_NCHW if (wl.op == "rms" or wl.crop) else gn.layout_of(sh["x"])
         P = lambda t: ctypes.c_void_p(t.data_ptr())
         out = []
         for kind in ("fwd", "bwd"):
@@ -208,6 +221,19 @@ def main():
                      wl.N, wl.C, wl.G, code, P(sh["bws"]), sh["bws"].numel(), ctypes.c_void_p(stream_handle),
                      ctypes.byref(o))
                 out.append((L.gn_rms_backward, a, o))
+            elif wl.crop and kind == "fwd":
+                st = sh["strides"]
+                a = (P(sh["x"]), st[0], P(sh["gamma"]), P(sh["beta"]), P(sh["y"]), st[1], P(sh["mean"]),
+                     P(sh["rstd"]), wl.N, wl.C, sh["hw"][0], sh["hw"][1], wl.G, ctypes.c_float(wl.eps), code,
+                     P(sh["fws"]), sh["fws"].numel(), ctypes.c_void_p(stream_handle), ctypes.byref(o))
+                out.append((L.gn_forward_strided, a, o))
+            elif wl.crop:
+                st = sh["strides"]
+                a = (P(sh["dy"]), st[2], P(sh["x"]), st[0], P(sh["mean"]), P(sh["rstd"]), P(sh["gamma"]),
+                     P(sh["dx"]), st[3], P(sh["dgamma"]), P(sh["dbeta"]), mask, wl.N, wl.C, sh["hw"][0],
+                     sh["hw"][1], wl.G, code, P(sh["bws"]), sh["bws"].numel(), ctypes.c_void_p(stream_handle),
+                     ctypes.byref(o))
+                out.append((L.gn_backward_strided, a, o))
             elif kind == "fwd":
                 a = (P(sh["x"]), P(sh["gamma"]), P(sh["beta"]), P(sh["y"]), P(sh["mean"]), P(sh["rstd"]),
                      wl.N, wl.C, wl.HW, wl.G, ctypes.c_float(wl.eps), code, lay, P(sh["fws"]),
@@ -296,8 +322,8 @@ def main():
         wl = sh["wl"]
         for c, (kind, plan) in enumerate((("fwd", sh["fplan"]), ("bwd", sh["bplan"]))):
             path = gn.PATH_NAMES[plan.path]
-            if path == "stream":
-                # the stream path's events bracket all kernels of the call: the
+            if path in ("stream", "generic"):
+                # these paths' events bracket all kernels of the call: the
                 # call's algorithmic bytes over the call's time
                 nbytes = wl.fwd_min_bytes() if kind == "fwd" else wl.bwd_min_bytes()
             elif kind == "fwd":
@@ -315,9 +341,11 @@ def main():
                      ("rows", "bwd"): ("rows_bwd_k", "rows_bwd_narrow_k"),
                      ("slab", "fwd"): (f"slab_{wl.layout}_fwd",), ("slab", "bwd"): (f"slab_{wl.layout}_bwd",),
                      ("stream", "fwd"): ("stream_fwd_call",), ("stream", "bwd"): ("stream_bwd_call",),
+                     ("generic", "fwd"): ("generic_fwd_call",), ("generic", "bwd"): ("generic_bwd_call",),
                      }.get((path, kind))
+            whole = path in ("stream", "generic")
             calls.append(dict(shape=wl.name, call=kind, path=path, kernels=plan.kernels,
-                              kernel=kname, grid=plan.grid if path != "stream" else "call",
+                              kernel=kname, grid=plan.grid if not whole else "call",
                               main_kernel_us=avg_ms * 1e3, main_kernel_bytes=nbytes,
                               main_kernel_gbs=nbytes / (avg_ms * 1e-3) / 1e9))
     tev.close()
@@ -332,12 +360,13 @@ def main():
                 "unit": "GB/s", "frac": round(dom["main_kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "traffic_over_algorithmic": (round(traffic / dom["main_kernel_bytes"], 3) if traffic else None),
-                "kernel": (f"{dom['call']} {dom['path']} " + ("call (all its kernels)" if dom["path"] == "stream"
+                "kernel": (f"{dom['call']} {dom['path']} " + ("call (all its kernels)"
+                                                                  if dom["path"] in ("stream", "generic")
                                                                   else "main kernel") + f" on {dom['shape']}"),
                 "avg_us": round(dom["main_kernel_us"], 3), "algorithmic_bytes": dom["main_kernel_bytes"],
                 "timing": ("HIP events (created without the system-scope fence) recorded by the library on "
                            "the call's stream around the main kernel "
-                           "(stream path: around all kernels of the call), "
+                           "(stream and generic paths: around all kernels of the call), "
                            + ("K eager steps queued behind a GPU spin after the graph-timed region"
                               if mode == "graph" else "over the timed region"))}
 
@@ -369,7 +398,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "launch": mode,
                    "shapes": [dict(N=s["wl"].N, C=s["wl"].C, H=s["wl"].H, W=s["wl"].W, G=s["wl"].G,
-                                   dtype=s["wl"].dtype, layout=s["wl"].layout) for s in shapes],
+                                   dtype=s["wl"].dtype, layout=s["wl"].layout,
+                                   **({"view": f"centre crop of ({s['wl'].H + 2 * s['wl'].crop}, "
+                                               f"{s['wl'].W + 2 * s['wl'].crop}) images"} if s["wl"].crop else {}))
+                              for s in shapes],
                    "op": shapes[0]["wl"].op,
                    "mask": "dx|dgamma" if shapes[0]["wl"].op == "rms" else "dx|dgamma|dbeta",
                    "bytes_per_step": bytes_per_step,

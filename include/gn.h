@@ -69,7 +69,8 @@ enum { GN_GRAD_DX = 1, GN_GRAD_DGAMMA = 2, GN_GRAD_DBETA = 4 };
 /* Kernel families; GN_PATH_AUTO lets the planner choose. */
 typedef enum gn_path {
     GN_PATH_AUTO = 0,
-    GN_PATH_GENERIC = 1,  /* any shape/alignment: partial sums, finalize, elementwise */
+    GN_PATH_GENERIC = 1,  /* any shape, alignment or strides: partial sums, finalize,
+                             elementwise */
     GN_PATH_ROWS = 2,     /* HW == 1: one wavefront per slice, slice kept in registers */
     GN_PATH_SLAB = 3,     /* cooperative capped grid over contiguous slabs with
                              grid-stride overflow tiles (one-pass backward) */
@@ -149,6 +150,63 @@ gn_status gn_backward(const void* dy, const void* x,
  * for arguments the call would reject. */
 int32_t gn_select_path(int32_t backward, int64_t N, int64_t C, int64_t HW, int64_t G,
                        gn_dtype dtype, gn_layout layout, const gn_options* opts);
+
+/*
+ * Strided tensors (ROCm/pytorch PR #3564's test run includes a correctness
+ * test on non-contiguous input; the POPCORNBENCH GroupNorm trace weighs
+ * reading arbitrary strides against copying the input first, and keeps a
+ * scalar path for shapes its vector loads do not fit).  The same operation
+ * on tensors of logical
+ * shape (N, C, H, W) whose element (n, c, h, w) sits at offset
+ *     n*s[0] + c*s[1] + h*s[2] + w*s[3]      (elements, not bytes)
+ * from the tensor's pointer, for a host array s[4] of strides per tensor:
+ * slices, crops, permuted and broadcast views are read and written where
+ * they are, without a copy.  Strides must be non-negative and the largest
+ * offset below 2^62; input tensors may overlap themselves (a stride of 0
+ * broadcasts), an output must map distinct elements to distinct addresses
+ * (GN_ERR_INVALID otherwise).  Outputs must not overlap inputs.  The stride
+ * arrays are read during the call only.
+ *
+ * When every tensor of the call is dense in one layout (NCHW or NHWC, the
+ * strides of extent-1 dimensions ignored), the call is exactly gn_forward /
+ * gn_backward with HW = H*W and that layout, fast paths and forced paths
+ * included.  Otherwise it runs the generic kernels (plan info: GN_PATH_GENERIC;
+ * a forced path other than GN_PATH_GENERIC is GN_ERR_UNSUPPORTED), which take
+ * any alignment.  Everything else -- dtypes, mean/rstd, gamma/beta, mask,
+ * workspace, stream, errors, determinism -- is as for gn_forward / gn_backward.
+ */
+
+/* Workspace bytes gn_forward_strided needs; y_strides NULL when y will be
+ * NULL.  0 for arguments the call would reject. */
+size_t gn_forward_strided_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t G,
+                                         gn_dtype dtype, const int64_t* x_strides,
+                                         const int64_t* y_strides, const gn_options* opts);
+
+/* x with strides x_strides (required); y with y_strides (ignored when y is
+ * NULL); mean, rstd: [N*G]; other arguments as for gn_forward. */
+gn_status gn_forward_strided(const void* x, const int64_t* x_strides,
+                             const float* gamma, const float* beta,
+                             void* y, const int64_t* y_strides, float* mean, float* rstd,
+                             int64_t N, int64_t C, int64_t H, int64_t W, int64_t G, float eps,
+                             gn_dtype dtype, void* workspace, size_t ws_bytes, void* stream,
+                             const gn_options* opts);
+
+/* Workspace bytes gn_backward_strided needs; dx_strides may be NULL when the
+ * mask has no GN_GRAD_DX. */
+size_t gn_backward_strided_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t G,
+                                          gn_dtype dtype, const int64_t* dy_strides,
+                                          const int64_t* x_strides, const int64_t* dx_strides,
+                                          int32_t mask, const gn_options* opts);
+
+/* dy, x with their strides (required); dx with dx_strides (required with
+ * GN_GRAD_DX); other arguments as for gn_backward. */
+gn_status gn_backward_strided(const void* dy, const int64_t* dy_strides,
+                              const void* x, const int64_t* x_strides,
+                              const float* mean, const float* rstd, const float* gamma,
+                              void* dx, const int64_t* dx_strides, float* dgamma, float* dbeta,
+                              int32_t mask, int64_t N, int64_t C, int64_t H, int64_t W, int64_t G,
+                              gn_dtype dtype, void* workspace, size_t ws_bytes, void* stream,
+                              const gn_options* opts);
 
 /*
  * RMSNorm over rows (ROCm/pytorch PR #3564 benchmarks an rms_norm operator

@@ -6,9 +6,13 @@ current HIP stream.  Every step of the computation runs in the library's HIP
 kernels; there is no CPU or PyTorch fallback -- if the library is missing or
 refuses a call, these functions raise.
 
-Tensors: x, dy are (N, C, *spatial) and dense, either contiguous (NCHW) or
-channels_last (NHWC); float32, float16 or bfloat16.  gamma/beta are float32
-(C,).  mean/rstd come back as float32 (N, G).
+Tensors: x, dy are (N, C, *spatial), float32, float16 or bfloat16.  Dense
+contiguous (NCHW) and channels_last (NHWC) tensors take the planner's tuned
+paths; any other strides (slices, crops, permuted or broadcast views) are
+passed as they are to the strided calls, which read and write them in place
+-- no copy -- as long as the spatial dimensions collapse into at most two
+strided ones.  gamma/beta are float32 (C,).  mean/rstd come back as float32
+(N, G).
 """
 from __future__ import annotations
 
@@ -21,7 +25,8 @@ from ._lib import (GN_BF16, GN_F16, GN_F32, GN_GRAD_DBETA, GN_GRAD_DGAMMA, GN_GR
                    PlanInfo)
 
 __all__ = ["forward", "backward", "forward_into", "backward_into", "forward_workspace_size",
-           "backward_workspace_size", "select_path", "layout_of", "GNError", "PlanInfo",
+           "backward_workspace_size", "forward_strided_workspace_size", "backward_strided_workspace_size",
+           "strided_dims", "common_layout", "select_path", "layout_of", "GNError", "PlanInfo",
            "rms_forward", "rms_backward", "rms_forward_into", "rms_backward_into",
            "rms_forward_workspace_size", "rms_backward_workspace_size",
            "GN_GRAD_DX", "GN_GRAD_DGAMMA", "GN_GRAD_DBETA", "GN_PATH_AUTO", "GN_PATH_GENERIC",
@@ -64,6 +69,63 @@ def _dims(t):
     return int(N), int(C), int(HW)
 
 
+def common_layout(*ts):
+    """The dense layout (GN_NCHW or GN_NHWC) every given tensor has, or None.
+    None entries are skipped."""
+    lay = None
+    for t in ts:
+        if t is None:
+            continue
+        try:
+            lt = layout_of(t)
+        except ValueError:
+            return None
+        if lay is None:
+            lay = lt
+        elif lt != lay:
+            return None
+    return lay
+
+
+def strided_dims(*ts):
+    """(N, C, H, W, [strides per tensor]) describing tensors of one shape
+    (N, C, *spatial) for the strided calls, without a copy.
+
+    Spatial dimensions of extent 1 are dropped; neighbours that are
+    contiguous in every tensor (outer stride = inner stride * inner extent)
+    are merged; at most two may remain (H, W) -- otherwise ValueError.  The
+    strides are element strides (n, c, h, w); a missing h or w dimension gets
+    extent 1 and stride 0."""
+    ts = [t for t in ts if t is not None]
+    shape = tuple(ts[0].shape)
+    if len(shape) < 2:
+        raise ValueError("expected tensors of shape (N, C, *spatial)")
+    for t in ts:
+        if tuple(t.shape) != shape:
+            raise ValueError("tensors must have the same shape")
+    groups = []
+    for i in range(2, len(shape)):
+        if shape[i] == 1:
+            continue
+        if groups and all(t.stride(groups[-1][-1]) == t.stride(i) * shape[i] for t in ts):
+            groups[-1].append(i)
+        else:
+            groups.append([i])
+    if len(groups) > 2:
+        raise ValueError("the spatial dimensions do not collapse into two strided dimensions; "
+                         "make the tensor contiguous first")
+    while len(groups) < 2:
+        groups.insert(0, [])
+    H = math.prod(shape[i] for i in groups[0]) if groups[0] else 1
+    W = math.prod(shape[i] for i in groups[1]) if groups[1] else 1
+    strides = []
+    for t in ts:
+        hs = t.stride(groups[0][-1]) if groups[0] else 0
+        ws = t.stride(groups[1][-1]) if groups[1] else 0
+        strides.append((ctypes.c_int64 * 4)(t.stride(0), t.stride(1), hs, ws))
+    return int(shape[0]), int(shape[1]), int(H), int(W), strides
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -97,6 +159,19 @@ def backward_workspace_size(N, C, HW, G, dtype_code, layout, mask, force_path=No
     return int(_lib.lib().gn_backward_workspace_size(N, C, HW, G, dtype_code, layout, mask, ctypes.byref(o)))
 
 
+def forward_strided_workspace_size(N, C, H, W, G, dtype_code, x_strides, y_strides, force_path=None) -> int:
+    o = _opts(force_path, 0, None, None)
+    return int(_lib.lib().gn_forward_strided_workspace_size(N, C, H, W, G, dtype_code, x_strides, y_strides,
+                                                             ctypes.byref(o)))
+
+
+def backward_strided_workspace_size(N, C, H, W, G, dtype_code, dy_strides, x_strides, dx_strides, mask,
+                                    force_path=None) -> int:
+    o = _opts(force_path, 0, None, None)
+    return int(_lib.lib().gn_backward_strided_workspace_size(N, C, H, W, G, dtype_code, dy_strides, x_strides,
+                                                              dx_strides, mask, ctypes.byref(o)))
+
+
 def select_path(backward: bool, N, C, HW, G, dtype_code, layout, force_path=None) -> int:
     o = _opts(force_path, 0, None, None)
     return int(_lib.lib().gn_select_path(1 if backward else 0, N, C, HW, G, dtype_code, layout, ctypes.byref(o)))
@@ -104,21 +179,34 @@ def select_path(backward: bool, N, C, HW, G, dtype_code, layout, force_path=None
 
 def forward_into(x, gamma, beta, num_groups, eps, y, mean, rstd, workspace, *, force_path=None,
                  max_resident=0, info=None, events=None, stream=None):
-    """gn_forward on preallocated outputs; returns nothing, raises GNError."""
+    """gn_forward (dense x and y in one layout) or gn_forward_strided (any
+    other strides) on preallocated outputs; returns nothing, raises GNError."""
     torch = _torch()
-    N, C, HW = _dims(x)
-    layout = layout_of(x)
+    if y is not None and (tuple(y.shape) != tuple(x.shape) or y.dtype != x.dtype):
+        raise ValueError("y must match x in shape and dtype")
+    layout = common_layout(x, y)
+    C = int(x.shape[1])
     _check_f32_vec(gamma, C, "gamma")
     _check_f32_vec(beta, C, "beta")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     o = _opts(force_path, max_resident, info, events)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.lib().gn_forward(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), N, C, HW,
-                               int(num_groups), float(eps), _dtype_code(x), layout, _ptr(workspace), ws_bytes,
-                               ctypes.c_void_p(stream), ctypes.byref(o))
+    if layout is not None:
+        N, C, HW = _dims(x)
+        st = _lib.lib().gn_forward(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), N, C, HW,
+                                   int(num_groups), float(eps), _dtype_code(x), layout, _ptr(workspace), ws_bytes,
+                                   ctypes.c_void_p(stream), ctypes.byref(o))
+        if st != 0:
+            raise GNError(st, "gn_forward")
+        return
+    N, C, H, W, strides = strided_dims(x, y)
+    st = _lib.lib().gn_forward_strided(_ptr(x), strides[0], _ptr(gamma), _ptr(beta), _ptr(y),
+                                       strides[1] if y is not None else None, _ptr(mean), _ptr(rstd), N, C, H, W,
+                                       int(num_groups), float(eps), _dtype_code(x), _ptr(workspace), ws_bytes,
+                                       ctypes.c_void_p(stream), ctypes.byref(o))
     if st != 0:
-        raise GNError(st, "gn_forward")
+        raise GNError(st, "gn_forward_strided")
 
 
 def forward(x, gamma, beta, num_groups: int, eps: float = 1e-5, *, compute_y: bool = True, force_path=None,
@@ -127,14 +215,21 @@ def forward(x, gamma, beta, num_groups: int, eps: float = 1e-5, *, compute_y: bo
     torch = _torch()
     if x.device.type != "cuda":
         raise ValueError("x must be on a HIP device")
-    N, C, HW = _dims(x)
-    layout = layout_of(x)
     G = int(num_groups)
     with torch.cuda.device(x.device):
+        # empty_like keeps x's strides when x is dense (in any dimension
+        # order), and is contiguous otherwise
         y = torch.empty_like(x) if compute_y else None
+        N, C = int(x.shape[0]), int(x.shape[1])
         mean = torch.empty(N * G, device=x.device, dtype=torch.float32)
         rstd = torch.empty(N * G, device=x.device, dtype=torch.float32)
-        wsb = forward_workspace_size(N, C, HW, G, _dtype_code(x), layout, force_path)
+        layout = common_layout(x, y)
+        if layout is not None:
+            wsb = forward_workspace_size(N, C, _dims(x)[2], G, _dtype_code(x), layout, force_path)
+        else:
+            _, _, H, W, strides = strided_dims(x, y)
+            wsb = forward_strided_workspace_size(N, C, H, W, G, _dtype_code(x), strides[0],
+                                                 strides[1] if y is not None else None, force_path)
         ws = torch.empty(max(wsb, 1), device=x.device, dtype=torch.uint8)
         forward_into(x, gamma, beta, G, eps, y, mean, rstd, ws, force_path=force_path,
                      max_resident=max_resident, info=info)
@@ -143,22 +238,37 @@ def forward(x, gamma, beta, num_groups: int, eps: float = 1e-5, *, compute_y: bo
 
 def backward_into(dy, x, mean, rstd, gamma, num_groups, mask, dx, dgamma, dbeta, workspace, *,
                   force_path=None, max_resident=0, info=None, events=None, stream=None):
-    """gn_backward on preallocated outputs; returns nothing, raises GNError."""
+    """gn_backward (dy, x, dx dense in one layout) or gn_backward_strided (any
+    other strides) on preallocated outputs; returns nothing, raises GNError."""
     torch = _torch()
-    N, C, HW = _dims(x)
-    layout = layout_of(x)
-    if tuple(dy.shape) != tuple(x.shape) or dy.dtype != x.dtype or layout_of(dy) != layout:
-        raise ValueError("dy must match x in shape, dtype and layout")
+    if tuple(dy.shape) != tuple(x.shape) or dy.dtype != x.dtype:
+        raise ValueError("dy must match x in shape and dtype")
+    if dx is not None and (tuple(dx.shape) != tuple(x.shape) or dx.dtype != x.dtype):
+        raise ValueError("dx must match x in shape and dtype")
+    want_dx = bool(int(mask) & GN_GRAD_DX) and dx is not None
+    layout = common_layout(dy, x, dx if want_dx else None)
+    C = int(x.shape[1])
     _check_f32_vec(gamma, C, "gamma")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     o = _opts(force_path, max_resident, info, events)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.lib().gn_backward(_ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd), _ptr(gamma), _ptr(dx), _ptr(dgamma),
-                                _ptr(dbeta), int(mask), N, C, HW, int(num_groups), _dtype_code(x), layout,
-                                _ptr(workspace), ws_bytes, ctypes.c_void_p(stream), ctypes.byref(o))
+    if layout is not None:
+        N, C, HW = _dims(x)
+        st = _lib.lib().gn_backward(_ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd), _ptr(gamma), _ptr(dx),
+                                    _ptr(dgamma), _ptr(dbeta), int(mask), N, C, HW, int(num_groups),
+                                    _dtype_code(x), layout, _ptr(workspace), ws_bytes, ctypes.c_void_p(stream),
+                                    ctypes.byref(o))
+        if st != 0:
+            raise GNError(st, "gn_backward")
+        return
+    N, C, H, W, strides = strided_dims(dy, x, dx if want_dx else None)
+    st = _lib.lib().gn_backward_strided(_ptr(dy), strides[0], _ptr(x), strides[1], _ptr(mean), _ptr(rstd),
+                                        _ptr(gamma), _ptr(dx), strides[2] if want_dx else None, _ptr(dgamma),
+                                        _ptr(dbeta), int(mask), N, C, H, W, int(num_groups), _dtype_code(x),
+                                        _ptr(workspace), ws_bytes, ctypes.c_void_p(stream), ctypes.byref(o))
     if st != 0:
-        raise GNError(st, "gn_backward")
+        raise GNError(st, "gn_backward_strided")
 
 
 def backward(dy, x, mean, rstd, gamma, num_groups: int, mask: int = GN_GRAD_DX | GN_GRAD_DGAMMA | GN_GRAD_DBETA,
@@ -167,14 +277,19 @@ def backward(dy, x, mean, rstd, gamma, num_groups: int, mask: int = GN_GRAD_DX |
     torch = _torch()
     if x.device.type != "cuda":
         raise ValueError("x must be on a HIP device")
-    N, C, HW = _dims(x)
-    layout = layout_of(x)
     G = int(num_groups)
     with torch.cuda.device(x.device):
         dx = torch.empty_like(x) if mask & GN_GRAD_DX else None
+        N, C = int(x.shape[0]), int(x.shape[1])
         dgamma = torch.empty(C, device=x.device, dtype=torch.float32) if mask & GN_GRAD_DGAMMA else None
         dbeta = torch.empty(C, device=x.device, dtype=torch.float32) if mask & GN_GRAD_DBETA else None
-        wsb = backward_workspace_size(N, C, HW, G, _dtype_code(x), layout, mask, force_path)
+        layout = common_layout(dy, x, dx)
+        if layout is not None:
+            wsb = backward_workspace_size(N, C, _dims(x)[2], G, _dtype_code(x), layout, mask, force_path)
+        else:
+            _, _, H, W, strides = strided_dims(dy, x, dx)
+            wsb = backward_strided_workspace_size(N, C, H, W, G, _dtype_code(x), strides[0], strides[1],
+                                                  strides[2] if dx is not None else None, mask, force_path)
         ws = torch.empty(max(wsb, 1), device=x.device, dtype=torch.uint8)
         backward_into(dy, x, mean.reshape(-1), rstd.reshape(-1), gamma, G, mask, dx, dgamma, dbeta, ws,
                       force_path=force_path, max_resident=max_resident, info=info)

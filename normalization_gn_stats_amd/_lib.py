@@ -25,6 +25,8 @@ PATH_NAMES = {GN_PATH_AUTO: "auto", GN_PATH_GENERIC: "generic", GN_PATH_ROWS: "r
 
 # every symbol include/gn.h declares
 EXPORTED = ("gn_forward_workspace_size", "gn_forward", "gn_backward_workspace_size", "gn_backward",
+            "gn_forward_strided_workspace_size", "gn_forward_strided", "gn_backward_strided_workspace_size",
+            "gn_backward_strided",
             "gn_select_path", "gn_status_string", "gn_version", "gn_rms_forward_workspace_size",
             "gn_rms_forward", "gn_rms_backward_workspace_size", "gn_rms_backward")
 
@@ -67,6 +69,17 @@ def lib() -> ctypes.CDLL:
     L.gn_forward.restype = i32
     L.gn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, i32, vp, sz, vp, op]
     L.gn_backward.restype = i32
+    pi = ctypes.POINTER(ctypes.c_int64)
+    L.gn_forward_strided_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, pi, pi, op]
+    L.gn_forward_strided_workspace_size.restype = sz
+    L.gn_forward_strided.argtypes = [vp, pi, vp, vp, vp, pi, vp, vp, i64, i64, i64, i64, i64, f, i32, vp, sz, vp,
+                                     op]
+    L.gn_forward_strided.restype = i32
+    L.gn_backward_strided_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, pi, pi, pi, i32, op]
+    L.gn_backward_strided_workspace_size.restype = sz
+    L.gn_backward_strided.argtypes = [vp, pi, vp, pi, vp, vp, vp, vp, pi, vp, vp, i32, i64, i64, i64, i64, i64, i32,
+                                      vp, sz, vp, op]
+    L.gn_backward_strided.restype = i32
     L.gn_select_path.argtypes = [i32, i64, i64, i64, i64, i32, i32, op]
     L.gn_select_path.restype = i32
     L.gn_rms_forward_workspace_size.argtypes = [i64, i64, i64, i32, op]

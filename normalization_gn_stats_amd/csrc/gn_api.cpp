@@ -4,6 +4,8 @@
 // the queried size, zero extent is a successful no-op), path selection and
 // dispatch to the kernel launchers.
 #include <math.h>
+
+#include <algorithm>
 #include <mutex>
 
 #include "gn_internal.hpp"
@@ -106,7 +108,7 @@ size_t fwd_ws(const Problem& p, int32_t path) {
         case GN_PATH_ROWS: return gn::rows_fwd_ws(p);
         case GN_PATH_SLAB: return gn::slab_fwd_ws(p);
         case GN_PATH_STREAM: return gn::stream_fwd_ws(p);
-        default: return gn::generic_fwd_ws(p);
+        default: return gn::generic_fwd_ws(p, gn::dense_strides(p));
     }
 }
 
@@ -115,7 +117,7 @@ size_t bwd_ws(const Problem& p, int32_t mask, int32_t path) {
         case GN_PATH_ROWS: return gn::rows_bwd_ws(p, mask);
         case GN_PATH_SLAB: return gn::slab_bwd_ws(p, mask);
         case GN_PATH_STREAM: return gn::stream_bwd_ws(p, mask);
-        default: return gn::generic_bwd_ws(p, mask);
+        default: return gn::generic_bwd_ws(p, gn::dense_strides(p), mask);
     }
 }
 
@@ -142,7 +144,7 @@ size_t gn_forward_workspace_size(int64_t N, int64_t C, int64_t HW, int64_t G, gn
     const int32_t path = plan(p, false, opts);
     if (path < 0) return 0;
     // the generic path is the fallback for unaligned pointers: cover it too
-    size_t a = fwd_ws(p, path), b = gn::generic_fwd_ws(p);
+    size_t a = fwd_ws(p, path), b = gn::generic_fwd_ws(p, gn::dense_strides(p));
     return a > b ? a : b;
 }
 
@@ -153,7 +155,7 @@ size_t gn_backward_workspace_size(int64_t N, int64_t C, int64_t HW, int64_t G, g
     if (mask <= 0 || mask > 7) return 0;
     const int32_t path = plan(p, true, opts);
     if (path < 0) return 0;
-    size_t a = bwd_ws(p, mask, path), b = gn::generic_bwd_ws(p, mask);
+    size_t a = bwd_ws(p, mask, path), b = gn::generic_bwd_ws(p, gn::dense_strides(p), mask);
     return a > b ? a : b;
 }
 
@@ -194,7 +196,7 @@ gn_status gn_forward(const void* x, const float* gamma, const float* beta, void*
     hipError_t e = path == GN_PATH_ROWS ? gn::rows_fwd(p, a, l)
                  : path == GN_PATH_SLAB ? gn::slab_fwd(p, a, l)
                  : path == GN_PATH_STREAM ? gn::stream_fwd(p, a, l)
-                                        : gn::generic_fwd(p, a, l);
+                                        : gn::generic_fwd(p, gn::dense_strides(p), a, l);
     return e == hipSuccess ? GN_OK : GN_ERR_HIP;
 }
 
@@ -236,8 +238,194 @@ gn_status gn_backward(const void* dy, const void* x, const float* mean, const fl
     hipError_t e = path == GN_PATH_ROWS ? gn::rows_bwd(p, a, l)
                  : path == GN_PATH_SLAB ? gn::slab_bwd(p, a, l)
                  : path == GN_PATH_STREAM ? gn::stream_bwd(p, a, l)
-                                        : gn::generic_bwd(p, a, l);
+                                        : gn::generic_bwd(p, gn::dense_strides(p), a, l);
     return e == hipSuccess ? GN_OK : GN_ERR_HIP;
+}
+
+// ---- strided tensors ---------------------------------------------------------
+namespace {
+// Checks one tensor's element strides (n, c, h, w) against its extents; an
+// output must map distinct elements to distinct addresses.  Sets `dense` to
+// the mask of dense layouts the strides describe (bit 0 NCHW, bit 1 NHWC).
+gn_status check_strides(const int64_t* st, const Problem& p, int64_t H, int64_t W, bool output, int* dense) {
+    if (st == nullptr) return GN_ERR_INVALID;
+    const int64_t ext[4] = {p.N, p.C, H, W};
+    __int128 span = 0;
+    for (int k = 0; k < 4; ++k) {
+        if (st[k] < 0) return GN_ERR_INVALID;
+        span += (__int128)(ext[k] - 1) * st[k];
+    }
+    if (span >= ((__int128)1 << 62)) return GN_ERR_INVALID;
+    if (output) {
+        // injective iff, taking dimensions of extent > 1 by increasing stride,
+        // each stride exceeds the span of all smaller ones
+        int idx[4], m = 0;
+        for (int k = 0; k < 4; ++k)
+            if (ext[k] > 1) idx[m++] = k;
+        for (int i = 1; i < m; ++i)
+            for (int j = i; j > 0 && st[idx[j]] < st[idx[j - 1]]; --j) std::swap(idx[j], idx[j - 1]);
+        __int128 below = 0;
+        for (int i = 0; i < m; ++i) {
+            if ((__int128)st[idx[i]] <= below) return GN_ERR_INVALID;
+            below += (__int128)(ext[idx[i]] - 1) * st[idx[i]];
+        }
+    }
+    const int64_t nchw[4] = {p.C * p.HW, p.HW, W, 1};
+    const int64_t nhwc[4] = {p.HW * p.C, 1, W * p.C, p.C};
+    bool a = true, b = true;
+    for (int k = 0; k < 4; ++k) {
+        if (ext[k] <= 1) continue;   // the stride of an extent-1 dimension is never used
+        a = a && st[k] == nchw[k];
+        b = b && st[k] == nhwc[k];
+    }
+    *dense &= (a ? 1 : 0) | (b ? 2 : 0);
+    return GN_OK;
+}
+
+gn_status strided_problem(int64_t N, int64_t C, int64_t H, int64_t W, int64_t G, gn_dtype dtype, Problem* p) {
+    if (H < 0 || W < 0) return GN_ERR_INVALID;
+    if (H > 0 && W > INT64_MAX / H) return GN_ERR_INVALID;
+    return make_problem(N, C, H * W, G, dtype, GN_NCHW, p);
+}
+
+void copy4(int64_t* d, const int64_t* s) {
+    for (int k = 0; k < 4; ++k) d[k] = s ? s[k] : 0;
+}
+
+// Resolves a forward call: GN_OK with *layout >= 0 (every tensor dense in that
+// layout: use the dense entry point) or -1 with *sd filled (generic kernels).
+gn_status fwd_strides(const Problem& p, int64_t H, int64_t W, const int64_t* xs, const int64_t* ys, bool has_y,
+                      int* layout, gn::Strides* sd) {
+    int dense = 3;
+    gn_status st = check_strides(xs, p, H, W, false, &dense);
+    if (st == GN_OK && has_y) st = check_strides(ys, p, H, W, true, &dense);
+    if (st != GN_OK) return st;
+    *layout = (dense & 1) ? GN_NCHW : (dense & 2) ? GN_NHWC : -1;
+    sd->H = H;
+    sd->W = W;
+    copy4(sd->x, xs);
+    copy4(sd->y, has_y ? ys : xs);
+    copy4(sd->dy, xs);
+    copy4(sd->dx, xs);
+    return GN_OK;
+}
+
+gn_status bwd_strides(const Problem& p, int64_t H, int64_t W, const int64_t* dys, const int64_t* xs,
+                      const int64_t* dxs, bool has_dx, int* layout, gn::Strides* sd) {
+    int dense = 3;
+    gn_status st = check_strides(dys, p, H, W, false, &dense);
+    if (st == GN_OK) st = check_strides(xs, p, H, W, false, &dense);
+    if (st == GN_OK && has_dx) st = check_strides(dxs, p, H, W, true, &dense);
+    if (st != GN_OK) return st;
+    *layout = (dense & 1) ? GN_NCHW : (dense & 2) ? GN_NHWC : -1;
+    sd->H = H;
+    sd->W = W;
+    copy4(sd->x, xs);
+    copy4(sd->y, xs);
+    copy4(sd->dy, dys);
+    copy4(sd->dx, has_dx ? dxs : xs);
+    return GN_OK;
+}
+
+bool generic_allowed(const gn_options* opts) {
+    const int32_t f = forced(opts);
+    return f == GN_PATH_AUTO || f == GN_PATH_GENERIC;
+}
+}  // namespace
+
+size_t gn_forward_strided_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t G, gn_dtype dtype,
+                                         const int64_t* x_strides, const int64_t* y_strides,
+                                         const gn_options* opts) {
+    Problem p;
+    if (strided_problem(N, C, H, W, G, dtype, &p) != GN_OK || zero_extent(p)) return 0;
+    int layout;
+    gn::Strides sd;
+    if (fwd_strides(p, H, W, x_strides, y_strides, y_strides != nullptr, &layout, &sd) != GN_OK) return 0;
+    if (layout >= 0) return gn_forward_workspace_size(N, C, H * W, G, dtype, (gn_layout)layout, opts);
+    if (!generic_allowed(opts)) return 0;
+    return gn::generic_fwd_ws(p, sd);
+}
+
+gn_status gn_forward_strided(const void* x, const int64_t* x_strides, const float* gamma, const float* beta,
+                             void* y, const int64_t* y_strides, float* mean, float* rstd, int64_t N, int64_t C,
+                             int64_t H, int64_t W, int64_t G, float eps, gn_dtype dtype, void* workspace,
+                             size_t ws_bytes, void* stream, const gn_options* opts) {
+    Problem p;
+    gn_status st = strided_problem(N, C, H, W, G, dtype, &p);
+    if (st != GN_OK) return st;
+    if (!(eps >= 0.f) || isinf(eps)) return GN_ERR_INVALID;
+    if ((gamma == nullptr) != (beta == nullptr)) return GN_ERR_INVALID;
+    if (zero_extent(p)) {
+        if (opts && opts->info) *opts->info = gn_plan_info{GN_PATH_AUTO, 0, 0, 0, 0, 0};
+        return GN_OK;
+    }
+    if (x == nullptr || mean == nullptr || rstd == nullptr) return GN_ERR_INVALID;
+    int layout;
+    gn::Strides sd;
+    if ((st = fwd_strides(p, H, W, x_strides, y_strides, y != nullptr, &layout, &sd)) != GN_OK) return st;
+    if (layout >= 0)
+        return gn_forward(x, gamma, beta, y, mean, rstd, N, C, H * W, G, eps, dtype, (gn_layout)layout, workspace,
+                          ws_bytes, stream, opts);
+    if (!generic_allowed(opts)) return GN_ERR_UNSUPPORTED;
+    const size_t need = gn::generic_fwd_ws(p, sd);
+    if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
+    gn::FwdArgs a{x, gamma, beta, y, mean, rstd, eps};
+    gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
+    if (l.info) *l.info = gn_plan_info{GN_PATH_GENERIC, 0, 0, 0, 0, 0};
+    return gn::generic_fwd(p, sd, a, l) == hipSuccess ? GN_OK : GN_ERR_HIP;
+}
+
+size_t gn_backward_strided_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t G, gn_dtype dtype,
+                                          const int64_t* dy_strides, const int64_t* x_strides,
+                                          const int64_t* dx_strides, int32_t mask, const gn_options* opts) {
+    Problem p;
+    if (strided_problem(N, C, H, W, G, dtype, &p) != GN_OK || zero_extent(p)) return 0;
+    if (mask <= 0 || mask > 7) return 0;
+    int layout;
+    gn::Strides sd;
+    if (bwd_strides(p, H, W, dy_strides, x_strides, dx_strides, (mask & GN_GRAD_DX) != 0, &layout, &sd) != GN_OK)
+        return 0;
+    if (layout >= 0) return gn_backward_workspace_size(N, C, H * W, G, dtype, (gn_layout)layout, mask, opts);
+    if (!generic_allowed(opts)) return 0;
+    return gn::generic_bwd_ws(p, sd, mask);
+}
+
+gn_status gn_backward_strided(const void* dy, const int64_t* dy_strides, const void* x, const int64_t* x_strides,
+                              const float* mean, const float* rstd, const float* gamma, void* dx,
+                              const int64_t* dx_strides, float* dgamma, float* dbeta, int32_t mask, int64_t N,
+                              int64_t C, int64_t H, int64_t W, int64_t G, gn_dtype dtype, void* workspace,
+                              size_t ws_bytes, void* stream, const gn_options* opts) {
+    Problem p;
+    gn_status st = strided_problem(N, C, H, W, G, dtype, &p);
+    if (st != GN_OK) return st;
+    if (mask <= 0 || mask > 7) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DX) && dx == nullptr) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DGAMMA) && dgamma == nullptr) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DBETA) && dbeta == nullptr) return GN_ERR_INVALID;
+    if ((mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) && gamma == nullptr) return GN_ERR_INVALID;
+    if (zero_extent(p)) {
+        if (opts && opts->info) *opts->info = gn_plan_info{GN_PATH_AUTO, 0, 0, 0, 0, 0};
+        return GN_OK;
+    }
+    if (dy == nullptr || x == nullptr || mean == nullptr || rstd == nullptr) return GN_ERR_INVALID;
+    int layout;
+    gn::Strides sd;
+    if ((st = bwd_strides(p, H, W, dy_strides, x_strides, dx_strides, (mask & GN_GRAD_DX) != 0, &layout, &sd)) !=
+        GN_OK)
+        return st;
+    if (layout >= 0)
+        return gn_backward(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, mask, N, C, H * W, G, dtype,
+                           (gn_layout)layout, workspace, ws_bytes, stream, opts);
+    if (!generic_allowed(opts)) return GN_ERR_UNSUPPORTED;
+    const size_t need = gn::generic_bwd_ws(p, sd, mask);
+    if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
+    gn::BwdArgs a{dy, x, mean, rstd, gamma,
+                  (mask & GN_GRAD_DX) ? dx : nullptr,
+                  (mask & GN_GRAD_DGAMMA) ? dgamma : nullptr,
+                  (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask};
+    gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
+    if (l.info) *l.info = gn_plan_info{GN_PATH_GENERIC, 0, 0, 0, 0, 0};
+    return gn::generic_bwd(p, sd, a, l) == hipSuccess ? GN_OK : GN_ERR_HIP;
 }
 
 // ---- RMSNorm over rows: the rows kernels with the mean taken as 0 ----------
@@ -326,6 +514,6 @@ const char* gn_status_string(gn_status s) {
     }
 }
 
-int32_t gn_version(void) { return 200; }
+int32_t gn_version(void) { return 300; }
 
 }  // extern "C"

@@ -68,11 +68,22 @@ const DeviceInfo& device_info();
 // Records ev (if any) on the stream; returns hipSuccess or the error.
 hipError_t record(hipEvent_t ev, hipStream_t s);
 
-// ---- generic path: any shape, any alignment --------------------------------
-size_t generic_fwd_ws(const Problem& p);
-size_t generic_bwd_ws(const Problem& p, int32_t mask);
-hipError_t generic_fwd(const Problem& p, const FwdArgs& a, const Launch& l);
-hipError_t generic_bwd(const Problem& p, const BwdArgs& a, const Launch& l);
+// Element strides of each activation tensor, indexed 0 n, 1 c, 2 h, 3 w, over
+// a spatial extent H x W (H*W == Problem::HW).  Validated by the C ABI: non-
+// negative, offsets within int64, outputs free of self-overlap.
+struct Strides {
+    int64_t H, W;
+    int64_t x[4], y[4], dy[4], dx[4];
+};
+
+// The strides of the dense layout p.layout (H = 1, W = HW) for every tensor.
+Strides dense_strides(const Problem& p);
+
+// ---- generic path: any shape, strides and alignment --------------------------
+size_t generic_fwd_ws(const Problem& p, const Strides& s);
+size_t generic_bwd_ws(const Problem& p, const Strides& s, int32_t mask);
+hipError_t generic_fwd(const Problem& p, const Strides& s, const FwdArgs& a, const Launch& l);
+hipError_t generic_bwd(const Problem& p, const Strides& s, const BwdArgs& a, const Launch& l);
 
 // ---- rows path: HW == 1, one wavefront per slice ----------------------------
 bool rows_ok(const Problem& p);   // shape condition (alignment checked separately)

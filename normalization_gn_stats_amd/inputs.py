@@ -11,7 +11,12 @@ Recipe (per workload, seed 0 unless stated):
   * gamma = 1 + 0.1*randn(C) and beta = 0.1*randn(C) (float32), except where the
     workload says gamma, beta ~ N(0, 1) (the NHWC image workload, as in the
     apex PR #2018 reproducer, which draws weight and bias with randn);
-  * NHWC workloads are made dense in channels_last order, as that reproducer does.
+  * NHWC workloads are made dense in channels_last order, as that reproducer does;
+  * a workload with crop = k > 0 draws x and dy over spatial extent
+    (H + 2k, W + 2k) and uses their centre (H, W) crops: views whose rows are
+    strided, read and written in place (a non-contiguous input);
+  * ``draw`` / ``draw_affine``: the same distributions for tensors of any
+    shape (the strided-view tests cut their views out of these).
 """
 from __future__ import annotations
 
@@ -36,6 +41,7 @@ class Workload:
     affine: str = "n1"  # "n1": gamma ~ N(1, 0.1), beta ~ N(0, 0.1); "n01": both ~ N(0, 1)
     eps: float = 1e-5
     op: str = "gn"          # "gn": GroupNorm; "rms": RMSNorm over rows (HW == 1, no beta)
+    crop: int = 0           # > 0: x, dy are centre (H, W) crops of (H + 2*crop, W + 2*crop) buffers
 
     @property
     def HW(self) -> int:
@@ -94,8 +100,14 @@ RMS_A = Workload("rms_f16_4096x1024", 4096, 1024, 1, 1, 1, "f16", "nchw", eps=1e
 RMS_BIG = Workload("rms_bf16_131072x4096", 131072, 4096, 1, 1, 1, "bf16", "nchw", eps=1e-6, op="rms")
 RMS_NARROW = Workload("rms_f16_131072x64", 131072, 64, 1, 1, 1, "f16", "nchw", eps=1e-6, op="rms")
 
+# Non-contiguous input: the 112x64 images of the NCHW configuration with a
+# one-pixel border cropped away (rows of 510 elements 512 apart), read and
+# written in place; and a small case of the same kind for the oracle.
+CROP_BIG = Workload("nchw_f32_112x64x510x510_g8_crop1", 112, 64, 510, 510, 8, "f32", "nchw", crop=1)
+CROP_TINY = Workload("tiny_nchw_f32_2x32x14x14_g8_crop1", 2, 32, 14, 14, 8, "f32", "nchw", crop=1)
+
 WORKLOADS = {w.name: w for w in (TINY, ROWS_A, ROWS_B, NHWC_IMG, NCHW_BIG, ROWS_BIG, ROWS_NARROW,
-                                 RMS_A, RMS_BIG, RMS_NARROW)}
+                                 RMS_A, RMS_BIG, RMS_NARROW, CROP_BIG, CROP_TINY)}
 
 
 def make_inputs(wl: Workload, seed: int = 0, device: str = "cpu"):
@@ -105,14 +117,15 @@ def make_inputs(wl: Workload, seed: int = 0, device: str = "cpu"):
     the workload's layout; gamma, beta are float32 of shape (C,)."""
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
-    shape = (wl.N, wl.C, wl.H, wl.W)
+    k = wl.crop
+    shape = (wl.N, wl.C, wl.H + 2 * k, wl.W + 2 * k)
     out = {}
     for name in ("x", "dy"):
         t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
         t = t.to(wl.torch_dtype)
         if wl.layout == "nhwc":
             t = t.contiguous(memory_format=torch.channels_last)
-        out[name] = t
+        out[name] = t[:, :, k:k + wl.H, k:k + wl.W] if k else t
     if wl.affine == "n01":
         out["gamma"] = torch.randn(wl.C, generator=gen, device=device, dtype=torch.float32)
         out["beta"] = torch.randn(wl.C, generator=gen, device=device, dtype=torch.float32)
@@ -120,6 +133,28 @@ def make_inputs(wl: Workload, seed: int = 0, device: str = "cpu"):
         out["gamma"] = 1.0 + 0.1 * torch.randn(wl.C, generator=gen, device=device, dtype=torch.float32)
         out["beta"] = 0.1 * torch.randn(wl.C, generator=gen, device=device, dtype=torch.float32)
     return out
+
+
+def draw(shape, dtype: str, seed: int, device: str = "cpu", channels_last: bool = False) -> torch.Tensor:
+    """Standard normal float32 values of ``shape`` from a generator seeded with
+    ``seed``, cast to ``dtype`` (round to nearest even); channels_last: dense
+    with the channel dimension (1) innermost."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    t = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32).to(DTYPES[dtype])
+    if channels_last:
+        nd = len(shape)
+        t = t.permute(0, *range(2, nd), 1).contiguous().permute(0, nd - 1, *range(1, nd - 1))
+    return t
+
+
+def draw_affine(C: int, seed: int, device: str = "cpu"):
+    """gamma ~ N(1, 0.1), beta ~ N(0, 0.1), float32 (C,), seeded."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    g = 1.0 + 0.1 * torch.randn(C, generator=gen, device=device, dtype=torch.float32)
+    b = 0.1 * torch.randn(C, generator=gen, device=device, dtype=torch.float32)
+    return g, b
 
 
 def memory_image(t: torch.Tensor, layout: str) -> torch.Tensor:

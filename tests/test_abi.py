@@ -202,3 +202,116 @@ def test_rms_zero_extent_and_sizes(L):
     assert L.gn_rms_backward_workspace_size(4096, 1024, 1, F16, _lib.GN_GRAD_DX, None) == 0
     assert L.gn_rms_backward_workspace_size(4096, 1024, 1, F16, _lib.GN_GRAD_DGAMMA, None) > 0
     assert L.gn_rms_backward_workspace_size(4096, 1024, 1, F16, _lib.GN_GRAD_DBETA, None) == 0
+
+
+# ---- strided tensors --------------------------------------------------------
+I64x4 = ctypes.c_int64 * 4
+
+
+def _st(*v):
+    return I64x4(*v)
+
+
+def dense_nchw(N, C, H, W):
+    return _st(C * H * W, H * W, W, 1)
+
+
+def dense_nhwc(N, C, H, W):
+    return _st(H * W * C, 1, W * C, C)
+
+
+def sfwd(L, x=FAKE, xs="crop", g=None, b=None, y=FAKE, ys="dense", m=FAKE, r=FAKE, N=2, C=8, H=4, W=6, G=2,
+         eps=1e-5, dt=F32, ws=None, wsb=0, opts=None):
+    if isinstance(xs, str):
+        xs = _st(C * H * (W + 2), H * (W + 2), W + 2, 1)    # a crop of a wider NCHW buffer
+    if isinstance(ys, str):
+        ys = dense_nchw(N, C, H, W)
+    return L.gn_forward_strided(x, xs, g, b, y, ys, m, r, N, C, H, W, G, eps, dt, ws, wsb, None, opts)
+
+
+def sbwd(L, dy=FAKE, dys="crop", x=FAKE, xs="crop", m=FAKE, r=FAKE, g=FAKE, dx=FAKE, dxs="dense", dg=FAKE,
+         db=FAKE, mask=7, N=2, C=8, H=4, W=6, G=2, dt=F32, ws=None, wsb=0, opts=None):
+    crop = _st(C * H * (W + 2), H * (W + 2), W + 2, 1)
+    dys = crop if isinstance(dys, str) else dys
+    xs = crop if isinstance(xs, str) else xs
+    dxs = dense_nchw(N, C, H, W) if isinstance(dxs, str) else dxs
+    return L.gn_backward_strided(dy, dys, x, xs, m, r, g, dx, dxs, dg, db, mask, N, C, H, W, G, dt, ws, wsb, None,
+                                 opts)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), _lib.GN_ERR_INVALID),
+    (dict(H=-1), _lib.GN_ERR_INVALID),
+    (dict(W=-2), _lib.GN_ERR_INVALID),
+    (dict(G=3), _lib.GN_ERR_INVALID),
+    (dict(dt=9), _lib.GN_ERR_UNSUPPORTED),
+    (dict(xs=None), _lib.GN_ERR_INVALID),                              # strides required
+    (dict(ys=None), _lib.GN_ERR_INVALID),                              # ... for y too when y is given
+    (dict(xs=_st(-1, 24, 6, 1)), _lib.GN_ERR_INVALID),                 # negative stride
+    (dict(ys=_st(0, 24, 6, 1)), _lib.GN_ERR_INVALID),                  # output broadcast over n: overlap
+    (dict(ys=_st(48, 1, 6, 1)), _lib.GN_ERR_INVALID),                  # c and w collide in the output
+    (dict(xs=_st(1 << 62, 24, 6, 1)), _lib.GN_ERR_INVALID),            # offsets beyond 2^62
+    (dict(g=FAKE), _lib.GN_ERR_INVALID),                               # affine all-or-none
+    (dict(x=None), _lib.GN_ERR_INVALID),
+    (dict(m=None), _lib.GN_ERR_INVALID),
+    (dict(eps=-1.0), _lib.GN_ERR_INVALID),
+    (dict(opts=_forced(_lib.GN_PATH_ROWS)), _lib.GN_ERR_UNSUPPORTED),  # only generic serves strides
+    (dict(opts=_forced(_lib.GN_PATH_SLAB)), _lib.GN_ERR_UNSUPPORTED),
+    (dict(ws=FAKE, wsb=16), _lib.GN_ERR_WORKSPACE),
+])
+def test_forward_strided_rejects(L, kw, status):
+    assert sfwd(L, **kw) == status
+
+
+def test_forward_strided_input_may_overlap(L):
+    # a broadcast input (stride 0 over n) passes validation: only the workspace is missing
+    assert sfwd(L, xs=_st(0, 24, 6, 1), ws=FAKE, wsb=16) == _lib.GN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=0), _lib.GN_ERR_INVALID),
+    (dict(dys=None), _lib.GN_ERR_INVALID),
+    (dict(xs=None), _lib.GN_ERR_INVALID),
+    (dict(dxs=None), _lib.GN_ERR_INVALID),                             # dx requested without strides
+    (dict(dxs=_st(0, 24, 6, 1)), _lib.GN_ERR_INVALID),                 # overlapping dx
+    (dict(dx=None), _lib.GN_ERR_INVALID),
+    (dict(g=None), _lib.GN_ERR_INVALID),
+    (dict(dy=None), _lib.GN_ERR_INVALID),
+    (dict(opts=_forced(_lib.GN_PATH_STREAM)), _lib.GN_ERR_UNSUPPORTED),
+    (dict(ws=FAKE, wsb=16), _lib.GN_ERR_WORKSPACE),
+    (dict(mask=6, dxs=None, dx=None, ws=FAKE, wsb=16), _lib.GN_ERR_WORKSPACE),   # no dx: its strides unused
+])
+def test_backward_strided_rejects(L, kw, status):
+    assert sbwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(C=0), dict(H=0), dict(W=0)])
+def test_strided_zero_extent_is_a_noop(L, kw):
+    assert sfwd(L, xs=None, ys=None, **kw) == _lib.GN_OK
+    assert sbwd(L, dys=None, xs=None, dxs=None, **kw) == _lib.GN_OK
+
+
+@pytest.mark.parametrize("N,C,H,W,G,dt", [(2, 8, 4, 6, 2, F32), (4, 1024, 1, 1, 1, F16), (1, 128, 1024, 2048, 16, F16),
+                                          (112, 64, 512, 512, 8, F32), (2, 36, 3, 5, 4, BF16)])
+def test_dense_strides_are_the_dense_call(L, N, C, H, W, G, dt):
+    # dense strides describe exactly the dense call: same workspace, both layouts
+    for lay, mk in ((NCHW, dense_nchw), (NHWC, dense_nhwc)):
+        s = mk(N, C, H, W)
+        assert (L.gn_forward_strided_workspace_size(N, C, H, W, G, dt, s, s, None) ==
+                L.gn_forward_workspace_size(N, C, H * W, G, dt, lay, None))
+        for mask in (1, 6, 7):
+            assert (L.gn_backward_strided_workspace_size(N, C, H, W, G, dt, s, s, s, mask, None) ==
+                    L.gn_backward_workspace_size(N, C, H * W, G, dt, lay, mask, None))
+
+
+def test_strided_workspace_sizes(L):
+    crop = _st(64 * 512 * 512, 512 * 512, 512, 1)
+    dense = dense_nchw(112, 64, 510, 510)
+    n = L.gn_forward_strided_workspace_size(112, 64, 510, 510, 8, F32, crop, dense, None)
+    assert n > 0
+    assert L.gn_forward_strided_workspace_size(112, 64, 510, 510, 8, F32, crop, dense, _forced(_lib.GN_PATH_SLAB)) == 0
+    assert L.gn_forward_strided_workspace_size(112, 64, 510, 510, 8, F32, crop, dense,
+                                               _forced(_lib.GN_PATH_GENERIC)) == n
+    for mask in range(1, 8):
+        assert L.gn_backward_strided_workspace_size(112, 64, 510, 510, 8, F32, crop, crop, dense, mask, None) > 0
+    assert L.gn_backward_strided_workspace_size(112, 64, 510, 510, 8, F32, crop, crop, dense, 0, None) == 0

@@ -337,7 +337,7 @@ def main():
             # kernels that can be the call's main kernel (the rows path picks one of
             # several by the slice width and count; the grid tells them apart in
             # the recorded counters)
-            kname = {("rows", "fwd"): ("rows_fwd_k", "rows_fwd_lds_k", "rows_fwd_narrow_k"),
+            kname = {("rows", "fwd"): ("rows_fwd_k", "rows_fwd_lds_k", "rows_fwd_narrow_k", "rows_fwd_cs_k"),
                      ("rows", "bwd"): ("rows_bwd_k", "rows_bwd_narrow_k"),
                      ("slab", "fwd"): (f"slab_{wl.layout}_fwd",), ("slab", "bwd"): (f"slab_{wl.layout}_bwd",),
                      ("stream", "fwd"): ("stream_fwd_call",), ("stream", "bwd"): ("stream_bwd_call",),

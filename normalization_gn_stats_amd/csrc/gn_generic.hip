@@ -17,6 +17,16 @@
 //   B3  elementwise dx = rstd*(gamma_c*dy - A/M - xhat*B/M)
 //   B4  per channel, per tile of the (n, h, w) range: sum dy, sum dy*xhat
 //   B5  per channel: sum the tile partials in tile order -> dbeta, dgamma
+// With large spatial planes (H*W >= kPlaneMinHW) stored in unit-stride runs
+// of at least a wave in dy and x (NCHW-like: a plane is read coalesced), B1
+// and B4 become one pass:
+// A, B, dbeta and dgamma are all sums of the per-(n, c) plane sums
+// S1 = sum dy and S2 = sum dy*xhat (A = sum over the group's channels of
+// gamma_c*S1, dbeta_c = sum over n of S1, and likewise with S2), so
+//   P1  per (n, c) plane, per tile: S1, S2
+//   P2  per slice: A, B from the plane partials of its channels
+//   P3  per channel: dbeta, dgamma from the plane partials of all samples
+// read dy and x once instead of twice.
 // Every sum has a fixed order, so results are bitwise reproducible.
 //
 // Addressing.  Each pass walks a box of "digits" -- the logical dimensions
@@ -32,6 +42,7 @@
 // tile spans a range of rows and a range of columns; when rows are shorter
 // than a workgroup, one workgroup covers several rows at a time.
 #include <algorithm>
+#include <type_traits>
 
 #include "gn_device.hpp"
 #include "gn_internal.hpp"
@@ -45,9 +56,19 @@ constexpr int kMaxD = 5;                 // digits: w, h, channel-in-group, grou
 constexpr int kMaxTensors = 3;           // dy, x, dx
 constexpr int64_t kRedTile = 16384;      // elements per workgroup in the reductions
 constexpr int kMaxParts = 4096;          // partial results per slice / per channel
-constexpr int64_t kElemTile = 8192;      // elements per tile in the elementwise passes
-constexpr int kRedU = 8;                 // loads in flight per lane and tensor: reductions
-constexpr int kElemU = 4;                //   elementwise passes
+#ifndef GN_GEN_ELEM_TILE
+#define GN_GEN_ELEM_TILE 8192
+#endif
+#ifndef GN_GEN_RED_U
+#define GN_GEN_RED_U 8
+#endif
+#ifndef GN_GEN_ELEM_U
+#define GN_GEN_ELEM_U 8
+#endif
+constexpr int64_t kElemTile = GN_GEN_ELEM_TILE;   // elements per tile in the elementwise passes
+constexpr int kRedU = GN_GEN_RED_U;               // loads in flight per lane and tensor: reductions
+constexpr int kElemU = GN_GEN_ELEM_U;             //   elementwise passes
+constexpr int64_t kPlaneMinHW = 512;     // backward by plane sums from this plane size on
 
 struct Box {
     int64_t ext[kMaxD];                  // extents, digit 0 innermost (unused digits: 1)
@@ -193,8 +214,32 @@ __device__ inline TileSpan tile_span(const Tiling& tl, int64_t t) {
     return sp;
 }
 
+// Element loads and stores.  Every pass streams its tensors once, so by default
+// they bypass the caches' retention (non-temporal), as the vector paths do.
+#ifndef GN_GEN_NT
+#define GN_GEN_NT 1
+#endif
 template <typename T>
-__device__ inline float ldf(const T* p, int64_t o) { return Vec<T>::to_f(p[o]); }
+using Bits = typename std::conditional<sizeof(T) == 4, uint32_t, uint16_t>::type;
+
+template <typename T>
+__device__ inline float ldf(const T* p, int64_t o) {
+#if GN_GEN_NT
+    const Bits<T> u = __builtin_nontemporal_load(reinterpret_cast<const Bits<T>*>(p + o));
+    return Vec<T>::to_f(__builtin_bit_cast(T, u));
+#else
+    return Vec<T>::to_f(p[o]);
+#endif
+}
+
+template <typename T>
+__device__ inline void stf(T* p, float v) {
+#if GN_GEN_NT
+    __builtin_nontemporal_store(__builtin_bit_cast(Bits<T>, Vec<T>::from_f(v)), reinterpret_cast<Bits<T>*>(p));
+#else
+    *p = Vec<T>::from_f(v);
+#endif
+}
 
 // ---- F1 --------------------------------------------------------------------
 // box digits: w, h, channel in group (x only, no weights)
@@ -293,7 +338,7 @@ __global__ __launch_bounds__(kT) void gen_apply(const T* __restrict__ x, T* __re
 #pragma unroll
                     for (int u = 0; u < U; ++u)
                         if (col + (int64_t)u * tl.cpr < sp.c1)
-                            py[u * tl.cpr * sy] = Vec<T>::from_f(fmaf(v[u] - mu, a, bb));
+                            stf(py + u * tl.cpr * sy, fmaf(v[u] - mu, a, bb));
                     px += U * tl.cpr * sx;
                     py += U * tl.cpr * sy;
                 }
@@ -302,7 +347,7 @@ __global__ __launch_bounds__(kT) void gen_apply(const T* __restrict__ x, T* __re
                     const int64_t ce = c + col * b.cw[0], se = s + col * b.sw[0];
                     const float a = rstd[se] * (gamma ? gamma[ce] : 1.f);
                     const float bb = beta ? beta[ce] : 0.f;
-                    *py = Vec<T>::from_f(fmaf(ldf(px, 0) - mean[se], a, bb));
+                    stf(py, fmaf(ldf(px, 0) - mean[se], a, bb));
                     px += tl.cpr * sx;
                     py += tl.cpr * sy;
                 }
@@ -433,7 +478,7 @@ __global__ __launch_bounds__(kT) void gen_dx(const T* __restrict__ dy, const T* 
                         if (col + (int64_t)u * tl.cpr < sp.c1) {
                             const float xh = (vx[u] - mu) * rs;
                             const float gd = vd[u] * gm;
-                            po[u * tl.cpr * so] = Vec<T>::from_f(rs * (gd - am - xh * bm));
+                            stf(po + u * tl.cpr * so, rs * (gd - am - xh * bm));
                         }
                     }
                     pd += U * tl.cpr * sd;
@@ -447,7 +492,7 @@ __global__ __launch_bounds__(kT) void gen_dx(const T* __restrict__ dy, const T* 
                     const float xh = (ldf(px, 0) - mean[se]) * rs;
                     const float gd = ldf(pd, 0) * (gamma ? gamma[ce] : 1.f);
                     const float2 q = ab[se];
-                    *po = Vec<T>::from_f(rs * (gd - q.x * invM - xh * (q.y * invM)));
+                    stf(po, rs * (gd - q.x * invM - xh * (q.y * invM)));
                     pd += tl.cpr * sd;
                     px += tl.cpr * sx;
                     po += tl.cpr * so;
@@ -513,6 +558,98 @@ __global__ __launch_bounds__(kT) void gen_param_partial(const T* __restrict__ dy
     if (threadIdx.x == 0) part[c * Q + blockIdx.y] = make_float2(acc[0], acc[1]);
 }
 
+// ---- P1 --------------------------------------------------------------------
+// box digits: w, h (tensors dy, x); one (n, c) plane per blockIdx.x
+template <typename T, int U = kRedU>
+__global__ __launch_bounds__(kT) void gen_plane_partial(const T* __restrict__ dy, const T* __restrict__ x,
+                                                        const float* __restrict__ mean,
+                                                        const float* __restrict__ rstd, Box b, Tiling tl,
+                                                        int64_t C, int64_t D, int64_t G, int64_t dsn, int64_t dsc,
+                                                        int64_t xsn, int64_t xsc, float2* __restrict__ part,
+                                                        int P) {
+    const int64_t pl = blockIdx.x;
+    const int64_t n = pl / C, c = pl - n * C;
+    const int64_t s = n * G + c / D;
+    const float mu = mean[s], rs = rstd[s];
+    const int rsub = threadIdx.x / tl.cpr, lc = threadIdx.x - rsub * tl.cpr;
+    const TileSpan sp = tile_span(tl, blockIdx.y);
+    const int64_t sd = b.st[0][0], sx = b.st[1][0];
+    float acc[2] = {0.f, 0.f};
+    if (rsub < tl.rstep) {
+        for (int64_t r = sp.r0 + rsub; r < sp.r1; r += tl.rstep) {
+            int64_t off[2] = {n * dsn + c * dsc, n * xsn + c * xsc};
+            int64_t cc = 0, ss = 0;
+            add_row<2>(b, r, off, cc, ss);
+            int64_t col = sp.c0 + lc;
+            const T* pd = dy + off[0] + col * sd;
+            const T* px = x + off[1] + col * sx;
+            for (; col < sp.c1; col += U * tl.cpr) {
+                float vd[U], vx[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const bool in = col + (int64_t)u * tl.cpr < sp.c1;
+                    vd[u] = in ? ldf(pd, u * tl.cpr * sd) : 0.f;
+                    vx[u] = in ? ldf(px, u * tl.cpr * sx) : mu;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    acc[0] += vd[u];
+                    acc[1] += vd[u] * ((vx[u] - mu) * rs);
+                }
+                pd += U * tl.cpr * sd;
+                px += U * tl.cpr * sx;
+            }
+        }
+    }
+    __shared__ float lds[kNW * 2];
+    block_sum<2, kNW>(acc, lds);
+    if (threadIdx.x == 0) part[pl * P + blockIdx.y] = make_float2(acc[0], acc[1]);
+}
+
+// ---- P2 --------------------------------------------------------------------
+// one wave per slice (n, g): A = sum over its channels and tiles of gamma_c*S1
+__global__ __launch_bounds__(kWave) void gen_plane_ab(const float2* __restrict__ part, int P,
+                                                      const float* __restrict__ gamma, int64_t C, int64_t D,
+                                                      int64_t G, float2* __restrict__ ab) {
+    const int64_t s = blockIdx.x;
+    const int64_t n = s / G, g = s - n * G;
+    const int lane = threadIdx.x;
+    const float2* base = part + (n * C + g * D) * P;   // the group's planes are consecutive
+    float a = 0.f, bb = 0.f;
+    for (int64_t k = lane; k < D * P; k += kWave) {
+        const int64_t cl = k / P;
+        const float gm = gamma ? gamma[g * D + cl] : 1.f;
+        const float2 q = base[k];
+        a += gm * q.x;
+        bb += gm * q.y;
+    }
+    a = wave_sum(a);
+    bb = wave_sum(bb);
+    if (lane == 0) ab[s] = make_float2(a, bb);
+}
+
+// ---- P3 --------------------------------------------------------------------
+// one wave per channel: dbeta = sum over samples and tiles of S1, dgamma of S2
+__global__ __launch_bounds__(kWave) void gen_plane_params(const float2* __restrict__ part, int P, int64_t N,
+                                                          int64_t C, float* __restrict__ dbeta,
+                                                          float* __restrict__ dgamma) {
+    const int64_t c = blockIdx.x;
+    const int lane = threadIdx.x;
+    float a = 0.f, bb = 0.f;
+    for (int64_t k = lane; k < N * P; k += kWave) {
+        const int64_t n = k / P, t = k - n * P;
+        const float2 q = part[(n * C + c) * P + t];
+        a += q.x;
+        bb += q.y;
+    }
+    a = wave_sum(a);
+    bb = wave_sum(bb);
+    if (lane == 0) {
+        if (dbeta) dbeta[c] = a;
+        if (dgamma) dgamma[c] = bb;
+    }
+}
+
 // ---- boxes of each pass -------------------------------------------------------
 // Digit specs list the dimensions innermost-first in the logical (n, c, h, w)
 // order, which breaks stride ties.  Strides index: 0 n, 1 c, 2 h, 3 w.
@@ -565,6 +702,17 @@ Box param_box(const Problem& p, const Strides& sd, const int64_t* const* st, int
     return make_box(d, 3, nt);
 }
 
+Box plane_box(const Strides& sd, const int64_t* const* st, int nt) {
+    DigitSpec d[2] = {};
+    d[0].ext = sd.W;
+    d[1].ext = sd.H;
+    for (int t = 0; t < nt; ++t) {
+        d[0].st[t] = st[t][3];
+        d[1].st[t] = st[t][2];
+    }
+    return make_box(d, 2, nt);
+}
+
 bool rowconst(const Box& b) { return b.cw[0] == 0 && b.sw[0] == 0; }
 
 int elem_grid(const Tiling& t) {
@@ -591,8 +739,9 @@ FwdPlan fwd_plan(const Problem& p, const Strides& sd) {
 }
 
 struct BwdPlan {
-    Box abox, ebox, pbox;
-    Tiling atl, etl, ptl;
+    bool planes;                 // reductions by per-(n, c) plane sums
+    Box abox, ebox, pbox, lbox;
+    Tiling atl, etl, ptl, ltl;
 };
 
 BwdPlan bwd_plan(const Problem& p, const Strides& sd) {
@@ -605,6 +754,9 @@ BwdPlan bwd_plan(const Problem& p, const Strides& sd) {
     b.etl = make_tiling(b.ebox, kElemTile, 0, kElemU);
     b.pbox = param_box(p, sd, dyx, 2);
     b.ptl = make_tiling(b.pbox, kRedTile, kMaxParts, kRedU);
+    b.lbox = plane_box(sd, dyx, 2);
+    b.ltl = make_tiling(b.lbox, kRedTile, kMaxParts, kRedU);
+    b.planes = p.HW >= kPlaneMinHW && b.lbox.st[0][0] == 1 && b.lbox.st[1][0] == 1 && b.lbox.ext[0] >= kWave;
     return b;
 }
 
@@ -651,7 +803,34 @@ hipError_t bwd_t(const Problem& p, const Strides& sd, const BwdArgs& a, const La
     hipError_t e;
     int kernels = 0;
     if ((e = record(l.ev_begin, l.stream))) return e;
-    if (a.mask & GN_GRAD_DX) {
+    if (bp.planes) {
+        const int P = (int)bp.ltl.tiles;
+        float2* part = (float2*)ws;
+        float2* ab = (float2*)(ws + align256((size_t)p.N * p.C * P * sizeof(float2)));
+        hipLaunchKernelGGL(gen_plane_partial<T>, dim3((unsigned)(p.N * p.C), P), dim3(kT), 0, l.stream, dy, x,
+                           a.mean, a.rstd, bp.lbox, bp.ltl, p.C, p.D, p.G, sd.dy[0], sd.dy[1], sd.x[0], sd.x[1],
+                           part, P);
+        kernels = 1;
+        if (a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) {
+            hipLaunchKernelGGL(gen_plane_params, dim3((unsigned)p.C), dim3(kWave), 0, l.stream, part, P, p.N, p.C,
+                               (a.mask & GN_GRAD_DBETA) ? a.dbeta : nullptr,
+                               (a.mask & GN_GRAD_DGAMMA) ? a.dgamma : nullptr);
+            ++kernels;
+        }
+        if (a.mask & GN_GRAD_DX) {
+            hipLaunchKernelGGL(gen_plane_ab, dim3((unsigned)p.S), dim3(kWave), 0, l.stream, part, P, a.gamma, p.C,
+                               p.D, p.G, ab);
+            const int grid = elem_grid(bp.etl);
+            if (rowconst(bp.ebox))
+                hipLaunchKernelGGL((gen_dx<T, true>), dim3(grid), dim3(kT), 0, l.stream, dy, x, a.mean, a.rstd,
+                                   a.gamma, ab, (T*)a.dx, bp.ebox, bp.etl, p.M);
+            else
+                hipLaunchKernelGGL((gen_dx<T, false>), dim3(grid), dim3(kT), 0, l.stream, dy, x, a.mean, a.rstd,
+                                   a.gamma, ab, (T*)a.dx, bp.ebox, bp.etl, p.M);
+            kernels += 2;
+        }
+    }
+    if (!bp.planes && (a.mask & GN_GRAD_DX)) {
         const int P = (int)bp.atl.tiles;
         float2* part = (float2*)ws;
         float2* ab = (float2*)(ws + align256((size_t)p.S * P * sizeof(float2)));
@@ -674,7 +853,7 @@ hipError_t bwd_t(const Problem& p, const Strides& sd, const BwdArgs& a, const La
                                a.gamma, ab, (T*)a.dx, bp.ebox, bp.etl, p.M);
         kernels += 3;
     }
-    if (a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) {
+    if (!bp.planes && (a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA))) {
         const int Q = (int)bp.ptl.tiles;
         float2* part = (float2*)ws;   // the dx stage above is ordered before on the stream
         if (rowconst(bp.pbox))
@@ -721,6 +900,8 @@ size_t generic_fwd_ws(const Problem& p, const Strides& sd) {
 
 size_t generic_bwd_ws(const Problem& p, const Strides& sd, int32_t mask) {
     const BwdPlan b = bwd_plan(p, sd);
+    if (b.planes)
+        return align256((size_t)p.N * p.C * b.ltl.tiles * sizeof(float2)) + align256((size_t)p.S * sizeof(float2));
     size_t need = 0;
     if (mask & GN_GRAD_DX)
         need = align256((size_t)p.S * b.atl.tiles * sizeof(float2)) + align256((size_t)p.S * sizeof(float2));

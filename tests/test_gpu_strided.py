@@ -128,6 +128,12 @@ def _multi_tile_nhwc(dt):
             inputs.draw((1, 32, 200, 200), dt, 32, DEV, channels_last=True)[:, :, 3:190, 5:199])
 
 
+def _planes_wide(dt):
+    # planes of 20x74 in unit-stride rows: the backward's plane-sum reductions
+    return (inputs.draw((3, 20, 24, 80), dt, 35, DEV)[..., 2:22, 3:77],
+            inputs.draw((3, 20, 24, 80), dt, 36, DEV)[..., 2:22, 3:77])
+
+
 def _unaligned(dt):
     # views starting one element past a 16-byte boundary
     def mk(seed):
@@ -150,6 +156,9 @@ CASES = {
     "multi_tile_nchw_f16": ("f16", 8, _multi_tile_nchw),
     "multi_tile_nhwc_bf16": ("bf16", 4, _multi_tile_nhwc),
     "unaligned_f16": ("f16", 3, _unaligned),
+    "planes_f32_g1": ("f32", 1, _planes_wide),
+    "planes_bf16_g5": ("bf16", 5, _planes_wide),
+    "planes_f16_g20": ("f16", 20, _planes_wide),
 }
 
 
@@ -178,6 +187,15 @@ def test_strided_masks(mask):
     if not mask & gn.GN_GRAD_DX:
         assert out["dx"] is None
     _check(f"mask{mask}", "bf16", out, _oracle(x, dy, gamma, beta, 6, 1e-5, mask), mask)
+
+
+@pytest.mark.parametrize("mask", [gn.GN_GRAD_DX, gn.GN_GRAD_DGAMMA, gn.GN_GRAD_DBETA, ALL])
+def test_plane_sum_masks(mask):
+    _need_gpu()
+    x, dy = _planes_wide("f16")
+    gamma, beta = inputs.draw_affine(20, 48, DEV)
+    out = _run(x, dy, gamma, beta, 4, mask=mask)
+    _check(f"planes mask{mask}", "f16", out, _oracle(x, dy, gamma, beta, 4, 1e-5, mask), mask)
 
 
 def test_strided_no_affine():

@@ -4,11 +4,12 @@ bench.py times (automatic path choice, default options).
 * NHWC fp16 1x128x1024x2048, G=16 and rows bf16 131072x4096: every output
   against the fp64 oracle on the whole tensor.
 * RMSNorm bf16 131072x4096: every output against the fp64 oracle.
-* NCHW fp32 112x64x512x512, G=8 (7.5 GB per tensor): y, dx, mean and rstd of
-  sampled slices, each the oracle's result on that slice alone (a slice is
-  its own GroupNorm problem with one group); dgamma/dbeta of two whole groups,
-  the oracle's result on the group's sub-tensor (all samples, the group's
-  channels, one group).
+* NCHW fp32 112x64x512x512, G=8 (7.5 GB per tensor), and its 510x510 centre
+  crops (the strided workload): y, dx, mean and rstd of sampled slices, each
+  the oracle's result on that slice alone (a slice is its own GroupNorm
+  problem with one group); dgamma/dbeta of two whole groups, the oracle's
+  result on the group's sub-tensor (all samples, the group's channels, one
+  group).
 """
 import gc
 
@@ -75,11 +76,22 @@ def test_full_rows_bf16_131072x4096():
 @pytest.mark.timeout(900)
 def test_full_nchw_sampled():
     _need_gpu()
-    wl = inputs.NCHW_BIG
+    _nchw_sampled(inputs.NCHW_BIG, gn.GN_PATH_SLAB)
+
+
+@pytest.mark.timeout(900)
+def test_full_nchw_crop_sampled():
+    """The strided workload bench.py times: 510x510 centre crops of the
+    112x64 images, read and written in place by the generic kernels."""
+    _need_gpu()
+    _nchw_sampled(inputs.CROP_BIG, gn.GN_PATH_GENERIC)
+
+
+def _nchw_sampled(wl, expect_path):
     say(f"[full] {wl.name}: generating on the device")
     data = inputs.make_inputs(wl, seed=0, device="cuda")
     out = run_gpu(wl, data)
-    assert out["fwd_plan"].path == gn.GN_PATH_SLAB and out["bwd_plan"].path == gn.GN_PATH_SLAB
+    assert out["fwd_plan"].path == expect_path and out["bwd_plan"].path == expect_path
     rtol, atol = TOL[wl.dtype]
     eps = float(np.float32(wl.eps))
     D = wl.C // wl.G
@@ -138,4 +150,6 @@ def test_full_sizes_are_the_benchmark_workloads():
     assert (inputs.NHWC_IMG.N, inputs.NHWC_IMG.C, inputs.NHWC_IMG.HW) == (1, 128, 1024 * 2048)
     assert (inputs.ROWS_BIG.N, inputs.ROWS_BIG.C) == (131072, 4096)
     assert (inputs.NCHW_BIG.N, inputs.NCHW_BIG.C, inputs.NCHW_BIG.HW) == (112, 64, 512 * 512)
+    assert (inputs.CROP_BIG.N, inputs.CROP_BIG.C, inputs.CROP_BIG.H, inputs.CROP_BIG.W, inputs.CROP_BIG.crop) == \
+        (112, 64, 510, 510, 1)
     assert ALL == 7

@@ -256,13 +256,17 @@ __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, co
     }
     __syncthreads();
     const float invD = 1.0f / (float)D;
-    for (; n < N; n += stride) {
+    // One slice: issue the loads of the slice after it into `nx`, then reduce
+    // and write slice n from `c`.  The walk alternates the two register sets
+    // (no copy between them: a copy would wait for loads still in flight and
+    // delay the next slice's loads until they land).
+    auto step = [&](int64_t n, const u4v (&c)[NV], u4v (&nx)[NV]) {
         const int64_t nn = n + stride;
-        if (nn < N) load(nn, nxt);
+        if (nn < N) load(nn, nx);
         float v[NV][V];
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            Vec<T>::unpack(cur[j], v[j]);
+            Vec<T>::unpack(c[j], v[j]);
             if (j * kWave + lane >= nvec) {
 #pragma unroll
                 for (int k = 0; k < V; ++k) v[j][k] = 0.f;   // not part of the slice
@@ -306,8 +310,11 @@ __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, co
                 }
             }
         }
-#pragma unroll
-        for (int j = 0; j < NV; ++j) cur[j] = nxt[j];
+    };
+    for (; n < N; n += 2 * stride) {
+        step(n, cur, nxt);
+        if (n + stride >= N) break;
+        step(n + stride, nxt, cur);
     }
 }
 
@@ -892,7 +899,7 @@ hipError_t fwd_nv(const Problem& p, const FwdArgs& a, const Launch& l) {
     const int64_t resident = (int64_t)occ * device_info().cu_count;
     int64_t cap = resident / p.G;
     if (cap < 1) cap = 1;
-    const bool walk = (p.N + kNW * cap - 1) / (kNW * cap) >= GN_ROWS_FWD_MIN_SPW;
+    const bool walk = p.N / (kNW * cap) >= GN_ROWS_FWD_MIN_SPW;   // whole slices per wave
     hipError_t e;
     if ((e = record(l.ev_begin, l.stream))) return e;
     if (walk) {

@@ -607,23 +607,26 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
 
 // Phase 1 of the backward for slab sb: per-tile sums of dy and dy*xhat (the
 // member's first tile already in bx, bd when `preloaded`); the last tile of x
-// and dy stays in bx, bd.
+// and dy stays in bx, bd, and ga gets gamma of its channel.  mu, r: the slab's
+// saved statistics, loaded by the caller ahead of the bulk traffic (a wave's
+// loads complete in issue order, so a late small load waits for all of it).
 template <typename T, int R>
 __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __restrict__ x,
-                                          const float* __restrict__ mean, const float* __restrict__ rstd,
-                                          const SlabCfg& cfg, int64_t sb, int m, u4v (&bx)[R], u4v (&bd)[R],
-                                          float2* part, float* lds, bool preloaded) {
+                                          const float* __restrict__ gamma, const SlabCfg& cfg, int64_t sb, int m,
+                                          float mu, float r, u4v (&bx)[R], u4v (&bd)[R], float& ga, float2* part,
+                                          float* lds, bool preloaded) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
     const int t = threadIdx.x;
-    const float mu = mean[sb], r = rstd[sb];
+    const int64_t g = sb - (sb / cfg.G) * cfg.G;
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
-        const int64_t k0 = (tile - (tile / cfg.tpc) * cfg.tpc) * TE;
+        const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
         if (!(preloaded && tile == m)) {
             nchw_load_tile<T, R, true>(x, cfg, sb, tile, bx);
             nchw_load_tile<T, R, true>(dy, cfg, sb, tile, bd);
         }
+        ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
         float acc[2] = {0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < R; ++j) {
@@ -654,13 +657,13 @@ template <typename T, int R>
 __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __restrict__ x,
                                        const float* __restrict__ mean, const float* __restrict__ rstd,
                                        const float* __restrict__ gamma, T* __restrict__ dx, const SlabCfg& cfg,
-                                       int64_t sb, int m, int64_t last, u4v (&bx)[R], u4v (&bd)[R],
-                                       const float2* part, float2* stot, float2* stage, float2* chan) {
+                                       int64_t sb, int m, int64_t last, float mu, float r, u4v (&bx)[R],
+                                       u4v (&bd)[R], float ga_last, const float2* part, float2* stot, float2* stage,
+                                       float2* chan) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
     const int t = threadIdx.x;
     const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
-    const float mu = mean[sb], r = rstd[sb];
     // channel sums: tiles cl*tpc .. cl*tpc+tpc-1 belong to channel cl
     float2 run = make_float2(0.f, 0.f);   // thread cl's running sum (cl < D <= kT)
     for (int64_t s0 = 0; s0 < cfg.tiles; s0 += kStage) {
@@ -697,7 +700,7 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
     for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
         const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
         const int64_t pb = base + cl * cfg.HW;
-        const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
+        const float ga = tile == last ? ga_last : (gamma ? gamma[g * cfg.D + cl] : 1.f);
         if (tile != last) {
             nchw_load_tile<T, R, true>(x, cfg, sb, tile, bx);
             nchw_load_tile<T, R, true>(dy, cfg, sb, tile, bd);
@@ -743,24 +746,35 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
     u4v cx[R], cd[R], nx[R], nd[R];
     int64_t sb = team;
     if (sb >= cfg.n_slabs) return;   // uniform over the team
-    int64_t last = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, sb, m, cx, cd, part, lds, false);
+    float mu = mean[sb], r = rstd[sb], ga = 1.f;
+    int64_t last = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, sb, m, mu, r, cx, cd, ga, part, lds, false);
     team_arrive(&ctr[sb * 4 + 0]);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
         const bool more = nsb < cfg.n_slabs;   // uniform over the team
-        if (more && m < cfg.tiles) {
-            nchw_load_tile<T, R, true>(x, cfg, nsb, m, nx);
-            nchw_load_tile<T, R, true>(dy, cfg, nsb, m, nd);
+        float nmu = 0.f, nr = 0.f, nga = 1.f;
+        if (more) {
+            nmu = mean[nsb];   // ahead of the prefetch and the dx stores
+            nr = rstd[nsb];
+            if (m < cfg.tiles) {
+                nchw_load_tile<T, R, true>(x, cfg, nsb, m, nx);
+                nchw_load_tile<T, R, true>(dy, cfg, nsb, m, nd);
+            }
         }
         team_wait(&ctr[sb * 4 + 0], (uint32_t)cfg.team, err);
-        nchw_bwd_phase2<T, R>(dy, x, mean, rstd, gamma, dx, cfg, sb, m, last, cx, cd, part, stot, stage, chan);
+        nchw_bwd_phase2<T, R>(dy, x, mean, rstd, gamma, dx, cfg, sb, m, last, mu, r, cx, cd, ga, part, stot, stage,
+                              chan);
         if (!more) break;
-        const int64_t nlast = nchw_bwd_phase1<T, R>(dy, x, mean, rstd, cfg, nsb, m, nx, nd, part, lds, true);
+        const int64_t nlast =
+            nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, nsb, m, nmu, nr, nx, nd, nga, part, lds, true);
         team_arrive(&ctr[nsb * 4 + 0]);
 #pragma unroll
         for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }
         last = nlast;
         sb = nsb;
+        mu = nmu;
+        r = nr;
+        ga = nga;
     }
 }
 
@@ -804,9 +818,13 @@ __global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ s
 // -- the power of two at or above the plane's chunks per thread, at most
 // GN_SLAB_NCHW_RF / RB -- so that a small plane does not leave most of a
 // fixed-size tile empty.
+// Largest forward tile of a 16-bit dtype: 32 chunks per thread (two register
+// tiles of them) leave no room for the unpacked halves and spill.
+constexpr int kNchwRF16 = GN_SLAB_NCHW_RF < 16 ? GN_SLAB_NCHW_RF : 16;
+
 int nchw_r(const Problem& p, bool backward) {
     const int64_t per_thread = (p.HW / (p.elem_bytes == 4 ? 4 : 8) + kT - 1) / kT;
-    const int rmax = backward ? GN_SLAB_NCHW_RB : GN_SLAB_NCHW_RF;
+    const int rmax = backward ? GN_SLAB_NCHW_RB : (p.elem_bytes == 4 ? GN_SLAB_NCHW_RF : kNchwRF16);
     int r = 1;
     while (r < per_thread && r < rmax) r *= 2;
     return r;
@@ -903,14 +921,14 @@ hipError_t launch_coop(K kernel, int64_t grid, void** args, hipStream_t s, bool 
 }
 
 template <typename T>
-auto nchw_fwd_kernel(int R) -> decltype(&slab_nchw_fwd<T, GN_SLAB_NCHW_RF>) {
-    switch (R) {
+auto nchw_fwd_kernel(int R) -> decltype(&slab_nchw_fwd<T, 1>) {
+    switch (R) {   // R as nchw_r gives it for this dtype
         case 1: return slab_nchw_fwd<T, 1>;
         case 2: return slab_nchw_fwd<T, 2>;
         case 4: return slab_nchw_fwd<T, 4>;
         case 8: return slab_nchw_fwd<T, 8>;
         case 16: return slab_nchw_fwd<T, 16>;
-        default: return slab_nchw_fwd<T, GN_SLAB_NCHW_RF>;
+        default: return slab_nchw_fwd<T, sizeof(T) == 4 ? GN_SLAB_NCHW_RF : kNchwRF16>;
     }
 }
 

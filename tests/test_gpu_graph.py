@@ -19,21 +19,34 @@ W = inputs.Workload
     (W("graph_slab_nhwc_f16", 2, 64, 37, 29, 8, "f16", "nhwc"), "slab"),
     (W("graph_stream_nhwc_f16", 2, 64, 130, 131, 8, "f16", "nhwc"), "stream"),
     (W("graph_rows_narrow_f16", 3000, 64, 1, 1, 1, "f16", "nchw"), None),
+    (W("graph_crop_f32", 2, 16, 20, 21, 4, "f32", "nchw", crop=1), None),   # strided views, in place
+    (W("graph_crop_planes_bf16", 2, 8, 24, 70, 2, "bf16", "nchw", crop=2), None),   # plane-sum backward
 ], ids=lambda v: getattr(v, "name", str(v)))
 def test_graph_replays_match_eager(wl, force):
     if not torch.cuda.is_available():
         pytest.skip("no HIP device")
     say(f"[graph] {wl.name}")
     dev = torch.device("cuda", 0)
-    d = {k: v.to(dev) for k, v in inputs.make_inputs(wl, seed=4).items()}
     N, C, HW, G = wl.N, wl.C, wl.HW, wl.G
     code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
-    lay = gn.layout_of(d["x"])
-    fws = torch.empty(max(gn.forward_workspace_size(N, C, HW, G, code, lay, force), 1), dtype=torch.uint8, device=dev)
-    bws = torch.empty(max(gn.backward_workspace_size(N, C, HW, G, code, lay, ALL, force), 1), dtype=torch.uint8,
-                      device=dev)
-    out = dict(y=torch.empty_like(d["x"]), mean=torch.empty(N * G, device=dev), rstd=torch.empty(N * G, device=dev),
-               dx=torch.empty_like(d["x"]), dgamma=torch.empty(C, device=dev), dbeta=torch.empty(C, device=dev))
+    if wl.crop:
+        # views drawn on the device (a copy to the device would make them dense)
+        d = inputs.make_inputs(wl, seed=4, device="cuda")
+        y = torch.empty(d["x"].shape, dtype=d["x"].dtype, device=dev)
+        dx = torch.empty_like(y)
+        _, _, H_, W_, st = gn.strided_dims(d["x"], y, d["dy"], dx)
+        fwb = gn.forward_strided_workspace_size(N, C, H_, W_, G, code, st[0], st[1], force)
+        bwb = gn.backward_strided_workspace_size(N, C, H_, W_, G, code, st[2], st[0], st[3], ALL, force)
+    else:
+        d = {k: v.to(dev) for k, v in inputs.make_inputs(wl, seed=4).items()}
+        lay = gn.layout_of(d["x"])
+        y, dx = torch.empty_like(d["x"]), torch.empty_like(d["x"])
+        fwb = gn.forward_workspace_size(N, C, HW, G, code, lay, force)
+        bwb = gn.backward_workspace_size(N, C, HW, G, code, lay, ALL, force)
+    fws = torch.empty(max(fwb, 1), dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(bwb, 1), dtype=torch.uint8, device=dev)
+    out = dict(y=y, mean=torch.empty(N * G, device=dev), rstd=torch.empty(N * G, device=dev),
+               dx=dx, dgamma=torch.empty(C, device=dev), dbeta=torch.empty(C, device=dev))
 
     def step(stream_handle):
         gn.forward_into(d["x"], d["gamma"], d["beta"], G, wl.eps, out["y"], out["mean"], out["rstd"], fws,

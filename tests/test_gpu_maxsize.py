@@ -116,6 +116,15 @@ def test_max_nchw_slab_f32():
 
 
 @pytest.mark.timeout(900)
+def test_max_strided_crop_bf16():
+    """Centre crops of 2x32x8195x4098 buffers: a strided view past 2^31
+    elements (offsets up to ~2^31 as well) on the generic kernels."""
+    _need_gpu()
+    wl = W("max_crop_bf16", 2, 32, 8193, 4096, 4, "bf16", "nchw", crop=1)
+    _run_case(wl, None, gn.GN_PATH_GENERIC, [(0, 0), (1, 3)])
+
+
+@pytest.mark.timeout(900)
 def test_max_generic_nhwc_bf16():
     _need_gpu()
     wl = W("max_generic_bf16", 2, 32, 8193, 4096, 4, "bf16", "nhwc")

@@ -296,3 +296,65 @@ def test_strided_is_deterministic():
     b = _run(x, dy, gamma, beta, 4)
     for k in ("y", "mean", "rstd", "dx", "dgamma", "dbeta"):
         assert torch.equal(a[k], b[k]), k
+
+
+def _random_view(rng, shape, dt, seed, allow_broadcast):
+    """A seeded view of logical `shape` cut out of a larger dense tensor:
+    dimensions permuted in memory, each given a margin (crop) and possibly a
+    step, or (inputs only) broadcast along one dimension."""
+    nd = len(shape)
+    steps = [int(rng.choice([1, 1, 1, 2, 3])) for _ in range(nd)]
+    margins = [int(rng.integers(0, 3)) for _ in range(nd)]
+    base_shape = [shape[i] * steps[i] + margins[i] for i in range(nd)]
+    perm = [int(v) for v in rng.permutation(nd)]
+    # a dense buffer whose memory order is `perm`, viewed in logical order
+    base = inputs.draw([base_shape[p] for p in perm], dt, seed, DEV)
+    inv = [perm.index(i) for i in range(nd)]
+    base = base.permute(*inv)
+    idx = tuple(slice(margins[i], margins[i] + shape[i] * steps[i], steps[i]) for i in range(nd))
+    v = base[idx]
+    if allow_broadcast and rng.random() < 0.25:
+        d = int(rng.integers(0, nd))
+        one = [slice(None)] * nd
+        one[d] = slice(0, 1)
+        v = v[tuple(one)].expand(*shape)
+    assert tuple(v.shape) == tuple(shape)
+    return v
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_strided_views(case):
+    """Seeded random views for x, dy (inputs) and y, dx (outputs): permuted
+    memory orders, margins, steps and broadcasts, ragged extents, every dtype,
+    3-, 4- and 5-D; forward and backward against the oracle."""
+    _need_gpu()
+    rng = np.random.default_rng(1000 + case)
+    dt = ["f32", "f16", "bf16"][case % 3]
+    nd = [4, 4, 3, 5][case % 4]
+    G = int(rng.choice([1, 2, 4]))
+    C = G * int(rng.integers(1, 6))
+    N = int(rng.integers(1, 4))
+    spatial = [int(rng.integers(1, 20)) for _ in range(nd - 2)]
+    if nd == 5:
+        spatial = [int(rng.integers(1, 6)) for _ in range(3)]
+    shape = [N, C, *spatial]
+    x = _random_view(rng, shape, dt, 2 * case, True)
+    dy = _random_view(rng, shape, dt, 2 * case + 1, True)
+    y = _random_view(rng, shape, dt, 500 + case, False)
+    dx = _random_view(rng, shape, dt, 700 + case, False)
+    gamma, beta = inputs.draw_affine(C, 900 + case, DEV)
+    say(f"[strided-random] case {case}: {dt} shape {shape} G={G} x.stride={x.stride()} y.stride={y.stride()}")
+    try:
+        gn.strided_dims(x, y, dy, dx)
+    except ValueError:
+        pytest.skip("these views need three spatial dimensions")   # the binding's documented limit
+    mean = torch.empty(N * G, device=DEV)
+    rstd = torch.empty(N * G, device=DEV)
+    dg = torch.empty(C, device=DEV)
+    db = torch.empty(C, device=DEV)
+    ws = torch.empty(1 << 24, device=DEV, dtype=torch.uint8)
+    gn.forward_into(x, gamma, beta, G, 1e-5, y, mean, rstd, ws)
+    gn.backward_into(dy, x, mean, rstd, gamma, G, ALL, dx, dg, db, ws)
+    torch.cuda.synchronize()
+    _check(f"random {case}", dt, dict(y=y, mean=mean, rstd=rstd, dx=dx, dgamma=dg, dbeta=db),
+           _oracle(x, dy, gamma, beta, G, 1e-5, ALL), ALL)

@@ -519,19 +519,19 @@ __global__ __launch_bounds__(kT) void rows_bwd_narrow_k(const T* __restrict__ dy
 // slices of a wave in a block are loaded before any is used.  The per-slice
 // sums A and B are wave sums (CS = 1) or wave sums added in part order
 // through LDS (CS > 1).
-template <typename T, int NV, int RB, int CS>
-__global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const T* __restrict__ x,
+template <typename T, int NV, int RB, int CS, int NW = kNW>
+__global__ __launch_bounds__(NW * kWave) void rows_bwd_k(const T* __restrict__ dy, const T* __restrict__ x,
                                                  const float* __restrict__ mean, const float* __restrict__ rstd,
                                                  const float* __restrict__ gamma, T* __restrict__ dx,
                                                  float2* __restrict__ part, int64_t N, int64_t G, int64_t C,
                                                  int D, int NB, int want_dx, int want_params,
                                                  int rms) {
     constexpr int V = Vec<T>::V;
-    constexpr int SLOTS = kNW / CS;
+    constexpr int SLOTS = NW / CS;
     constexpr int RPB = SLOTS * RB;
     constexpr bool kHoistGamma = NV * V <= 16;   // gamma of the lane's columns kept in registers
-    extern __shared__ float2 lds_cols[];         // [D] when want_params
-    __shared__ float2 red[RB][kNW];              // per-wave (a, b) of each slice of the block
+    extern __shared__ float2 lds_cols[];         // [SLOTS][D] when want_params
+    __shared__ float2 red[RB][NW];               // per-wave (a, b) of each slice of the block
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int slot = wave / CS;
@@ -688,27 +688,28 @@ __global__ __launch_bounds__(kT) void rows_bwd_k(const T* __restrict__ dy, const
         }
     }
     if (!want_params) return;
-    // column sums of the row slots added into LDS in slot order (the parts of
-    // one slot cover disjoint columns)
-    for (int sl = 0; sl < SLOTS; ++sl) {
-        if (slot == sl) {
+    // column sums of the row slots: each slot's into its own LDS row (the parts
+    // of one slot cover disjoint columns), then every column added over the
+    // slots in slot order
 #pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                const int vi = vbase + j * kWave + lane;
-                if (vi >= nvec) continue;
+    for (int j = 0; j < NV; ++j) {
+        const int vi = vbase + j * kWave + lane;
+        if (vi >= nvec) continue;
 #pragma unroll
-                for (int k = 0; k < V; ++k) {
-                    float2 c = sl == 0 ? make_float2(0.f, 0.f) : lds_cols[vi * V + k];
-                    c.x += cs1[j][k];
-                    c.y += cs2[j][k];
-                    lds_cols[vi * V + k] = c;
-                }
-            }
-        }
-        __syncthreads();
+        for (int k = 0; k < V; ++k) lds_cols[slot * D + vi * V + k] = make_float2(cs1[j][k], cs2[j][k]);
     }
+    __syncthreads();
     float2* dst = part + ((int64_t)g * NB + b) * D;
-    for (int c = threadIdx.x; c < D; c += kT) dst[c] = lds_cols[c];
+    for (int c = threadIdx.x; c < D; c += NW * kWave) {
+        float2 t = lds_cols[c];
+#pragma unroll
+        for (int sl = 1; sl < SLOTS; ++sl) {
+            const float2 u = lds_cols[sl * D + c];
+            t.x += u.x;
+            t.y += u.y;
+        }
+        dst[c] = t;
+    }
 }
 
 // dbeta[g*D + c] = sum_b part[g][b][c].x, dgamma likewise with .y, b in
@@ -920,16 +921,16 @@ hipError_t fwd_nv(const Problem& p, const FwdArgs& a, const Launch& l) {
     return hipSuccess;
 }
 
-template <typename T, int NV, int RB, int CS>
+template <typename T, int NV, int RB, int CS, int NW = kNW>
 hipError_t bwd_launch(const Problem& p, const BwdArgs& a, const Launch& l) {
     const int NB = rows_nb(p);
     const bool params = (a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) != 0;
     const unsigned grid = (unsigned)NB;
-    const size_t lds = params ? (size_t)p.D * sizeof(float2) : 0;
+    const size_t lds = params ? (size_t)(NW / CS) * p.D * sizeof(float2) : 0;   // [slots][D]
     float2* part = (float2*)l.ws;
     hipError_t e;
     if ((e = record(l.ev_begin, l.stream))) return e;
-    hipLaunchKernelGGL((rows_bwd_k<T, NV, RB, CS>), dim3(grid, (unsigned)p.G), dim3(kT), lds, l.stream,
+    hipLaunchKernelGGL((rows_bwd_k<T, NV, RB, CS, NW>), dim3(grid, (unsigned)p.G), dim3(NW * kWave), lds, l.stream,
                        (const T*)a.dy, (const T*)a.x, a.mean, a.rstd, a.gamma, (T*)a.dx, part, p.N, p.G, p.C,
                        (int)p.D, NB, (a.mask & GN_GRAD_DX) ? 1 : 0, params ? 1 : 0, a.rms);
     if ((e = hipGetLastError())) return e;

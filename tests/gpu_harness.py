@@ -78,8 +78,8 @@ def check_against_oracle(wl, data, out, mask=ALL):
     rtol, atol = TOL[wl.dtype]
     x64 = img64(data["x"], wl.layout)
     dy64 = img64(data["dy"], wl.layout)
-    g64 = data["gamma"].double().numpy()
-    b64 = data["beta"].double().numpy()
+    g64 = data["gamma"].double().cpu().numpy()
+    b64 = data["beta"].double().cpu().numpy()
     eps = float(np.float32(wl.eps))
     ry, rmean, rrstd = oracle.forward(x64, g64, b64, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
     close(img64(out["y"], wl.layout), ry, rtol, atol, f"{wl.name} y")

@@ -348,6 +348,26 @@ def main():
                               kernel=kname, grid=plan.grid if not whole else "call",
                               main_kernel_us=avg_ms * 1e3, main_kernel_bytes=nbytes,
                               main_kernel_gbs=nbytes / (avg_ms * 1e-3) / 1e9))
+    # ---- small (cache-resident) workloads: the calls again with the caches
+    # flushed before each one -- a 512 MiB scratch fill outside the library's
+    # events -- so that each call reads its inputs from HBM ----------------------
+    flushed = None
+    if mode == "graph":
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        reps = min(K, 20)
+        fev = [[[tev.new() for _ in range(2)] for _ in range(2 * len(shapes))] for _ in range(reps)]
+        for i in range(reps):
+            for k, sh in enumerate(shapes):
+                for c, call in enumerate(calls_for(sh, sp, (fev[i][2 * k], fev[i][2 * k + 1]))):
+                    scratch.fill_(i & 0xFF)
+                    run([call])
+        torch.cuda.synchronize()
+        flushed = {}
+        for k, sh in enumerate(shapes):
+            for c, kind in enumerate(("fwd", "bwd")):
+                d = [tev.elapsed_ms(fev[i][2 * k + c][0], fev[i][2 * k + c][1]) for i in range(reps)]
+                flushed[f"{kind}:{sh['wl'].name}"] = round(1e3 * sum(d) / len(d), 3)
+        del scratch
     tev.close()
     dom = max(calls, key=lambda c: c["main_kernel_us"])
     traffic = None
@@ -369,6 +389,23 @@ def main():
                            "(stream and generic paths: around all kernels of the call), "
                            + ("K eager steps queued behind a GPU spin after the graph-timed region"
                               if mode == "graph" else "over the timed region"))}
+
+    # measured device-to-device copy of 1 GiB (read + write), the practical
+    # ceiling of a streaming kernel on this part: a second denominator
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for i in range(3):
+        ce[2 * i].record(stream)
+        cdst.copy_(csrc)
+        ce[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    copy_ms = sorted(ce[2 * i].elapsed_time(ce[2 * i + 1]) for i in range(3))[1]
+    copy_gbs = 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9
+    del csrc, cdst
+    roofline["copy_gbs"] = round(copy_gbs, 1)
+    roofline["frac_of_copy"] = round(dom["main_kernel_gbs"] / copy_gbs, 4)
 
     if args.copy_calibration_mib > 0:
         src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
@@ -407,6 +444,7 @@ def main():
                    "bytes_per_step": bytes_per_step,
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "us_per_call": {f"{c['call']}:{c['shape']}": round(c["main_kernel_us"], 3) for c in calls},
+        "us_per_call_flushed": flushed,
         "calls": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in c.items()} for c in calls],
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -445,7 +483,27 @@ def cpu_baseline(shapes, seconds, bytes_per_step):
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 10000:
             break
+    one = None
+    if bytes_per_step < (256 << 20):   # small workloads: the same on one thread
+        nt = oracle.num_threads()
+        oracle.set_num_threads(1)
+        r1, t1 = 0, time.perf_counter()
+        while True:
+            for wl, x, dy, g, b, eps in prepared:
+                if wl.op == "rms":
+                    oracle.rms_forward(x, g, wl.N, wl.C, wl.G, eps)
+                    oracle.rms_backward(dy, x, g, wl.N, wl.C, wl.G, eps)
+                    continue
+                oracle.forward(x, g, b, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
+                oracle.backward(dy, x, g, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
+            r1 += 1
+            e1 = time.perf_counter() - t1
+            if e1 >= min(seconds, 3.0) or r1 >= 1000:
+                break
+        oracle.set_num_threads(nt)
+        one = round(bytes_per_step * r1 / e1 / 1e9, 3)
     return {"value": round(bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "value_one_thread": one,
             "kind": "oracle",
             "sample": f"{reps} full steps of the workload (fwd+bwd of every shape) in {el:.1f} s, fp64 C oracle, "
                       f"OpenMP threads={oracle.num_threads()}, host cpus={os.cpu_count()}"}

@@ -422,9 +422,75 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
 // straddle a plane: tile = (plane cl, k) covers elements [k*TE, (k+1)*TE) of
 // plane cl, TE = kT*R*V; chunk j of thread t is element k*TE + (j*kT + t)*V.
 //
-// Between arriving at a slab's barrier and waiting on it, a member issues the
-// loads of its first tile of the team's next slab, so that HBM keeps streaming
-// while the team synchronises (prefetch into a second register tile).
+// Tile partials of the NCHW kernels: one 64-bit word per tile, all ones until
+// the tile's member publishes it (the launch's clear kernel fills the block).
+// The value is its own ready flag: the writer issues one agent-scope atomic
+// store and goes on (no counter, no fence, no wait for the store), and the
+// readers poll the words they need.  Neither half of a published word holds
+// the all-ones pattern (that NaN is stored as the canonical quiet NaN), and a
+// reader takes a word only when neither half does, so it never takes a word
+// that is unpublished or, were the 8-byte store ever seen in halves, half
+// published.  A wave's memory operations complete in issue
+// order, so a member that waits for its own store before signalling -- as a
+// counter barrier must -- also waits for all the bulk traffic it issued
+// before it; polling the data itself takes that drain off every round.
+
+__device__ inline bool unpublished(uint64_t w) {
+    return (uint32_t)w == 0xFFFFFFFFu || (uint32_t)(w >> 32) == 0xFFFFFFFFu;
+}
+
+__device__ inline void put_partial(uint64_t* p, float lo, float hi) {
+    uint32_t l = __float_as_uint(lo), h = __float_as_uint(hi);
+    if (l == 0xFFFFFFFFu) l = 0x7FC00000u;
+    if (h == 0xFFFFFFFFu) h = 0x7FC00000u;
+    const uint64_t w = (uint64_t)l | ((uint64_t)h << 32);
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint64_t peek_partial(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits (bounded: on expiry raises *err and returns NaNs) until *p is
+// published, w being a first read of it; returns (lo, hi).
+__device__ inline float2 settle_partial(const uint64_t* p, uint64_t w, uint32_t* err) {
+    uint32_t spins = 0;
+    while (unpublished(w)) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+            __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
+}
+
+__device__ inline float2 poll_partial(const uint64_t* p, uint32_t* err) {
+    return settle_partial(p, peek_partial(p), err);
+}
+
+// Elements of NCHW tile `tile` (the last tile of each channel plane may be
+// short).  32-bit index arithmetic: the host keeps a slab's tiles below 2^31.
+__device__ inline float nchw_tile_count(const SlabCfg& cfg, int64_t tile, int64_t TE) {
+    const int64_t k0 = (int64_t)((uint32_t)tile % (uint32_t)cfg.tpc) * TE;
+    const int64_t rem = cfg.HW - k0;
+    return (float)(rem < TE ? rem : TE);
+}
+
+// The thread index, opaque to the optimiser: the per-chunk element offsets of a
+// tile derived from it are then recomputed in each phase instead of being
+// hoisted out of the slab loop, where 32 of them, held in 64-bit registers
+// next to two register tiles, spill.
+__device__ inline int tile_tid() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// A member prefetches its first tile of the team's next slab before it waits
+// for the current slab's partials, so that HBM keeps streaming while the team
+// synchronises (a second register tile).
 // NT: non-temporal loads (the backward's measured choice; the forward runs
 // faster with plain loads and stores).
 template <typename T, int R, bool NT>
@@ -435,27 +501,27 @@ __device__ inline void nchw_load_tile(const T* __restrict__ src, const SlabCfg& 
     const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
     const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
     const T* p = src + (n * cfg.C + g * cfg.D + cl) * cfg.HW;
+    const int t = tile_tid();
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const int64_t e = min(k0 + (int64_t)(j * kT + (int)threadIdx.x) * V, cfg.HW - V);   // in bounds
+        const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);   // in bounds
         dst[j] = NT ? ld16_nt(p + e) : ld16(p + e);
     }
 }
 
 // Phase 1 of the forward for slab sb: statistics of member m's tiles (the
-// first one already in buf when `preloaded`), one
-// (count, mean, M2) partial per tile -- an exact two-pass over the tile in
-// registers: workgroup sum -> tile mean -> workgroup sum of squared
-// deviations.  The last tile stays in buf; its channel's gamma/beta are
-// fetched here so that phase 2 does not wait for them.  Returns the last tile
-// index (-1 if the member has none).
+// first one already in buf when `preloaded`), one published (mean, M2)
+// partial per tile -- an exact two-pass over the tile in registers: workgroup
+// sum -> tile mean -> workgroup sum of squared deviations.  The last tile
+// stays in buf; its channel's gamma/beta are fetched here so that phase 2 does
+// not wait for them.  Returns the last tile index (-1 if the member has none).
 template <typename T, int R>
 __device__ inline int64_t nchw_fwd_phase1(const T* __restrict__ x, const float* __restrict__ gamma,
                                           const float* __restrict__ beta, const SlabCfg& cfg, int64_t sb, int m,
-                                          u4v (&buf)[R], float2& gb, float4* part, float* lds, bool preloaded) {
+                                          u4v (&buf)[R], float2& gb, uint64_t* part, float* lds, bool preloaded) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
-    const int t = threadIdx.x;
+    const int t = tile_tid();
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
         const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
@@ -490,43 +556,70 @@ __device__ inline int64_t nchw_fwd_phase1(const T* __restrict__ x, const float* 
             }
         }
         block_sum<1, kNW>(q, lds);
-        if (t == 0) xstore_stat(&part[sb * cfg.pstride + tile], Stat{cnt, mt, q[0]});
+        if (t == 0) put_partial(&part[sb * cfg.pstride + tile], mt, q[0]);
         last = tile;
     }
     return last;
 }
 
-// Phase 2 of the forward for slab sb: every member combines all tile
-// partials in the same order -- slab mean = sum(n_i*mean_i)/sum(n_i), then
-// M2 = sum(M2_i + n_i*(mean_i - mean)^2) (the parallel form of Chan et al.'s
-// update), each a fixed-order workgroup sum -- then writes y for its tiles
-// (the last one from buf, the earlier ones reloaded in reverse order).
+// Phase 2 of the forward for slab sb: every member waits for and combines all
+// tile partials in the same order -- slab mean = sum(n_i*mean_i)/sum(n_i),
+// then M2 = sum(M2_i + n_i*(mean_i - mean)^2) (the parallel form of Chan et
+// al.'s update), each a fixed-order workgroup sum -- then writes y for its
+// tiles (the last one from buf, the earlier ones reloaded in reverse order).
 template <typename T, int R>
 __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __restrict__ gamma,
                                        const float* __restrict__ beta, T* __restrict__ y, float* mean,
                                        float* rstd, const SlabCfg& cfg, int64_t sb, int m, int64_t last,
-                                       u4v (&buf)[R], float2 gb, const float4* part, float* lds) {
+                                       u4v (&buf)[R], float2 gb, const uint64_t* part, uint32_t* err, float* lds) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
-    const int t = threadIdx.x;
+    constexpr int kKeep = 1;   // partials a thread keeps in registers (slabs of up to kKeep * kT tiles)
+    const int t = tile_tid();
     const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
-    // Plain (L2-cacheable) loads: this slab's partial block was written once,
-    // through to the coherence point, before the barrier, and it shares no
-    // 128-byte line with other slabs, so no XCD can hold a stale copy; the
-    // first member of an XCD to read a line brings it into that XCD's L2.
+    const uint64_t* ps = part + sb * cfg.pstride;
+    uint64_t w[kKeep];
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) {   // all first reads in flight together
+        const int64_t i = t + (int64_t)k * kT;
+        w[k] = i < cfg.tiles ? peek_partial(ps + i) : 0;
+    }
+    float2 keep[kKeep];
     float sums[2] = {0.f, 0.f};   // sum n_i*mean_i, sum n_i
-    for (int64_t i = t; i < cfg.tiles; i += kT) {
-        const float4 v = part[sb * cfg.pstride + i];
-        sums[0] = fmaf(v.x, v.y, sums[0]);
-        sums[1] += v.x;
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) {
+        const int64_t i = t + (int64_t)k * kT;
+        keep[k] = make_float2(0.f, 0.f);
+        if (i < cfg.tiles) {
+            keep[k] = settle_partial(ps + i, w[k], err);
+            const float c = nchw_tile_count(cfg, i, TE);
+            sums[0] = fmaf(c, keep[k].x, sums[0]);
+            sums[1] += c;
+        }
+    }
+    for (int64_t i = t + (int64_t)kKeep * kT; i < cfg.tiles; i += kT) {
+        const float2 v = poll_partial(ps + i, err);
+        const float c = nchw_tile_count(cfg, i, TE);
+        sums[0] = fmaf(c, v.x, sums[0]);
+        sums[1] += c;
     }
     block_sum<2, kNW>(sums, lds);
     const float mu = sums[0] / sums[1];
     float m2[1] = {0.f};
-    for (int64_t i = t; i < cfg.tiles; i += kT) {
-        const float4 v = part[sb * cfg.pstride + i];
-        const float d = v.y - mu;
-        m2[0] += fmaf(v.x * d, d, v.z);
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) {
+        const int64_t i = t + (int64_t)k * kT;
+        if (i < cfg.tiles) {
+            const float c = nchw_tile_count(cfg, i, TE);
+            const float d = keep[k].x - mu;
+            m2[0] += fmaf(c * d, d, keep[k].y);
+        }
+    }
+    for (int64_t i = t + (int64_t)kKeep * kT; i < cfg.tiles; i += kT) {
+        const float2 v = poll_partial(ps + i, err);   // published: returns at once
+        const float c = nchw_tile_count(cfg, i, TE);
+        const float d = v.x - mu;
+        m2[0] += fmaf(c * d, d, v.y);
     }
     block_sum<1, kNW>(m2, lds);
     float var = m2[0] / (float)(cfg.D * cfg.HW);
@@ -563,20 +656,17 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
     }
 }
 
-// Two slabs in flight per team: after arriving at slab s's barrier a member
-// runs phase 1 of the team's next slab (into the second register tile) and
-// arrives there too, and only then waits on s -- slab s's barrier has had a
-// whole phase of slack, and the y stores of s are issued right before the
-// loads of the slab after, so that the two streams overlap in the memory
-// system.  (A wave's memory operations complete in issue order -- one
-// counter for loads and stores -- so every dependent load also waits for the
-// bulk traffic issued before it; of the orders measured, this one is the
-// fastest for the forward.)
+// Two slabs in flight per team: a member publishes the partials of slab s,
+// then runs phase 1 of the team's next slab (loads, statistics, publish)
+// before it needs the partials of s, so that they have had a whole phase to
+// arrive.  (Measured slower: prefetching the next slab's first tile, then
+// phase 2 of s while it streams, then phase 1 from registers; and
+// non-temporal loads.)
 template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
                                                     const float* __restrict__ beta, T* __restrict__ y,
-                                                    float* mean, float* rstd, SlabCfg cfg, uint32_t* ctr,
-                                                    uint32_t* err, float4* part, uint32_t* /*res: NHWC only*/) {
+                                                    float* mean, float* rstd, SlabCfg cfg, uint32_t* /*ctr*/,
+                                                    uint32_t* err, uint64_t* part, uint32_t* /*res: NHWC only*/) {
     const int team = blockIdx.x / cfg.team;
     const int m = blockIdx.x - team * cfg.team;
     __shared__ float lds[kNW * 2];
@@ -585,17 +675,13 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
     int64_t sb = team;
     if (sb >= cfg.n_slabs) return;   // uniform over the team
     int64_t last = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, sb, m, cur, gcur, part, lds, false);
-    team_arrive(&ctr[sb * 4 + 0]);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
         const bool more = nsb < cfg.n_slabs;   // uniform over the team
         int64_t nlast = -1;
-        if (more) {
-            nlast = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, nsb, m, nxt, gnxt, part, lds, false);
-            team_arrive(&ctr[nsb * 4 + 0]);
-        }
-        team_wait(&ctr[sb * 4 + 0], (uint32_t)cfg.team, err);
-        nchw_fwd_phase2<T, R>(x, gamma, beta, y, mean, rstd, cfg, sb, m, last, cur, gcur, part, lds);
+        if (more) nlast = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, nsb, m, nxt, gnxt, part, lds, false);
+        __builtin_amdgcn_sched_barrier(0);   // keep the two slabs' phases apart
+        nchw_fwd_phase2<T, R>(x, gamma, beta, y, mean, rstd, cfg, sb, m, last, cur, gcur, part, err, lds);
         if (!more) break;
 #pragma unroll
         for (int j = 0; j < R; ++j) cur[j] = nxt[j];
@@ -606,19 +692,18 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
 }
 
 // Phase 1 of the backward for slab sb: per-tile sums of dy and dy*xhat (the
-// member's first tile already in bx, bd when `preloaded`); the last tile of x
-// and dy stays in bx, bd, and ga gets gamma of its channel.  mu, r: the slab's
-// saved statistics, loaded by the caller ahead of the bulk traffic (a wave's
-// loads complete in issue order, so a late small load waits for all of it).
+// member's first tile already in bx, bd when `preloaded`), published per tile;
+// the last tile of x and dy stays in bx, bd.  mu, r: the slab's saved
+// statistics, loaded by the caller ahead of the bulk traffic (a wave's loads
+// complete in issue order, so a late small load waits for all of it).
 template <typename T, int R>
 __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __restrict__ x,
                                           const float* __restrict__ gamma, const SlabCfg& cfg, int64_t sb, int m,
-                                          float mu, float r, u4v (&bx)[R], u4v (&bd)[R], float& ga, float2* part,
+                                          float mu, float r, u4v (&bx)[R], u4v (&bd)[R], uint64_t* part,
                                           float* lds, bool preloaded) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
-    const int t = threadIdx.x;
-    const int64_t g = sb - (sb / cfg.G) * cfg.G;
+    const int t = tile_tid();
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
         const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
@@ -626,7 +711,6 @@ __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __r
             nchw_load_tile<T, R, true>(x, cfg, sb, tile, bx);
             nchw_load_tile<T, R, true>(dy, cfg, sb, tile, bd);
         }
-        ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
         float acc[2] = {0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < R; ++j) {
@@ -642,7 +726,7 @@ __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __r
             }
         }
         block_sum<2, kNW>(acc, lds);
-        if (t == 0) xstore2(&part[sb * cfg.pstride + tile], make_float2(acc[0], acc[1]));
+        if (t == 0) put_partial(&part[sb * cfg.pstride + tile], acc[0], acc[1]);
         last = tile;
     }
     return last;
@@ -651,25 +735,37 @@ __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __r
 constexpr int kStage = 1024;   // tile partials staged in LDS per step of the channel sums
 
 // Phase 2 of the backward for slab sb: per-channel sums of the slab (each in
-// tile order, partials staged through LDS), A and B (channel order), then dx
-// for the member's tiles (last from registers, the others reloaded).
+// tile order, partials waited for and staged through LDS), A and B (channel
+// order), then dx for the member's tiles (last from registers, the others
+// reloaded).  gam: gamma of channel t of the slab's group (t < D), loaded by
+// the caller ahead of the bulk traffic; shared through LDS (gch).
 template <typename T, int R>
 __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __restrict__ x,
-                                       const float* __restrict__ mean, const float* __restrict__ rstd,
                                        const float* __restrict__ gamma, T* __restrict__ dx, const SlabCfg& cfg,
                                        int64_t sb, int m, int64_t last, float mu, float r, u4v (&bx)[R],
-                                       u4v (&bd)[R], float ga_last, const float2* part, float2* stot, float2* stage,
-                                       float2* chan) {
+                                       u4v (&bd)[R], float gam, const uint64_t* part, uint32_t* err,
+                                       float2* stot, float2* stage, float2* chan, float* gch) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
-    const int t = threadIdx.x;
+    constexpr int kPer = kStage / kT;
+    const int t = tile_tid();
     const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
     // channel sums: tiles cl*tpc .. cl*tpc+tpc-1 belong to channel cl
     float2 run = make_float2(0.f, 0.f);   // thread cl's running sum (cl < D <= kT)
     for (int64_t s0 = 0; s0 < cfg.tiles; s0 += kStage) {
         const int64_t cnt = cfg.tiles - s0 < kStage ? cfg.tiles - s0 : kStage;
-        // plain loads of this slab's partial block: see nchw_fwd_phase2
-        for (int64_t i = t; i < cnt; i += kT) stage[i] = part[sb * cfg.pstride + s0 + i];
+        const uint64_t* ps = part + sb * cfg.pstride + s0;
+        uint64_t w[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {   // all first reads in flight together
+            const int64_t i = t + (int64_t)k * kT;
+            w[k] = i < cnt ? peek_partial(ps + i) : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int64_t i = t + (int64_t)k * kT;
+            if (i < cnt) stage[i] = settle_partial(ps + i, w[k], err);
+        }
         __syncthreads();
         if (t < cfg.D) {
             const int64_t lo = (int64_t)t * cfg.tpc, hi = lo + cfg.tpc;
@@ -682,14 +778,14 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
     }
     if (t < cfg.D) {
         chan[t] = run;
+        gch[t] = gam;
         if (m == 0) stot[n * cfg.C + g * cfg.D + t] = run;
     }
     __syncthreads();
     float A = 0.f, B = 0.f;
     for (int cl = 0; cl < cfg.D; ++cl) {
-        const float ga = gamma ? gamma[g * cfg.D + cl] : 1.f;
-        A = fmaf(ga, chan[cl].x, A);
-        B = fmaf(ga, chan[cl].y, B);
+        A = fmaf(gch[cl], chan[cl].x, A);
+        B = fmaf(gch[cl], chan[cl].y, B);
     }
     __syncthreads();
     if (!cfg.want_dx) return;
@@ -700,7 +796,7 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
     for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
         const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
         const int64_t pb = base + cl * cfg.HW;
-        const float ga = tile == last ? ga_last : (gamma ? gamma[g * cfg.D + cl] : 1.f);
+        const float ga = gch[cl];
         if (tile != last) {
             nchw_load_tile<T, R, true>(x, cfg, sb, tile, bx);
             nchw_load_tile<T, R, true>(dy, cfg, sb, tile, bd);
@@ -725,63 +821,84 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
     }
 }
 
-// part: [slab][tile] float2 (sum dy, sum dy*xhat of the tile); stot: [N][C] float2.
-// Two slabs in flight as in the forward, in the order measured fastest for
-// the backward: the loads of the next slab's first tile are issued before
-// the wait on slab s's barrier, so that they stream during the wait and
-// during the dx stores of s; the next slab's sums then start from registers.
-// Requires D <= kT (checked on the host).
+// Loop order of the backward, the faster of two measured for each type: fp32
+// (four register tiles of 16 chunks, one workgroup per CU) prefetches its
+// first tile of the next slab, then runs phase 2 of the current slab while it
+// streams and phase 1 of the next from registers; 16-bit types (tiles of 8
+// chunks, two workgroups per CU) run phase 1 of the next slab first, as the
+// forward does.
+template <typename T>
+constexpr bool kBwdPhase1First = sizeof(T) != 4;
+
+// part: [slab][tile] published (sum dy, sum dy*xhat) words; stot: [N][C] float2.
+// Two slabs in flight, as in the forward.  Requires D <= kT (checked on the
+// host).
 template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, const T* __restrict__ x,
                                                     const float* __restrict__ mean,
                                                     const float* __restrict__ rstd,
                                                     const float* __restrict__ gamma, T* __restrict__ dx,
-                                                    SlabCfg cfg, uint32_t* ctr, uint32_t* err, float2* part,
+                                                    SlabCfg cfg, uint32_t* /*ctr*/, uint32_t* err, uint64_t* part,
                                                     float2* stot, uint32_t* /*res: NHWC only*/) {
     const int team = blockIdx.x / cfg.team;
     const int m = blockIdx.x - team * cfg.team;
     __shared__ float lds[kNW * 2];
     __shared__ float2 chan[kT];
+    __shared__ float gch[kT];
     __shared__ float2 stage[kStage];
     u4v cx[R], cd[R], nx[R], nd[R];
+    const int t = threadIdx.x;
     int64_t sb = team;
     if (sb >= cfg.n_slabs) return;   // uniform over the team
-    float mu = mean[sb], r = rstd[sb], ga = 1.f;
-    int64_t last = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, sb, m, mu, r, cx, cd, ga, part, lds, false);
-    team_arrive(&ctr[sb * 4 + 0]);
+    float mu = mean[sb], r = rstd[sb];
+    float gam = (gamma && t < cfg.D) ? gamma[(sb % cfg.G) * cfg.D + t] : 1.f;
+    int64_t last = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, sb, m, mu, r, cx, cd, part, lds, false);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
         const bool more = nsb < cfg.n_slabs;   // uniform over the team
-        float nmu = 0.f, nr = 0.f, nga = 1.f;
-        if (more) {
-            nmu = mean[nsb];   // ahead of the prefetch and the dx stores
-            nr = rstd[nsb];
-            if (m < cfg.tiles) {
-                nchw_load_tile<T, R, true>(x, cfg, nsb, m, nx);
-                nchw_load_tile<T, R, true>(dy, cfg, nsb, m, nd);
+        float nmu = 0.f, nr = 0.f, ngam = 1.f;
+        int64_t nlast = -1;
+        if constexpr (kBwdPhase1First<T>) {
+            if (more) {
+                nmu = mean[nsb];
+                nr = rstd[nsb];
+                if (gamma && t < cfg.D) ngam = gamma[(nsb % cfg.G) * cfg.D + t];
+                nlast = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, nsb, m, nmu, nr, nx, nd, part, lds, false);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            nchw_bwd_phase2<T, R>(dy, x, gamma, dx, cfg, sb, m, last, mu, r, cx, cd, gam, part, err, stot, stage,
+                                  chan, gch);
+            if (!more) break;
+        } else {
+            if (more) {
+                nmu = mean[nsb];   // ahead of the prefetch and the dx stores
+                nr = rstd[nsb];
+                if (gamma && t < cfg.D) ngam = gamma[(nsb % cfg.G) * cfg.D + t];
+                if (m < cfg.tiles) {
+                    nchw_load_tile<T, R, true>(x, cfg, nsb, m, nx);
+                    nchw_load_tile<T, R, true>(dy, cfg, nsb, m, nd);
+                }
+            }
+            nchw_bwd_phase2<T, R>(dy, x, gamma, dx, cfg, sb, m, last, mu, r, cx, cd, gam, part, err, stot, stage,
+                                  chan, gch);
+            if (!more) break;
+            nlast = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, nsb, m, nmu, nr, nx, nd, part, lds, true);
         }
-        team_wait(&ctr[sb * 4 + 0], (uint32_t)cfg.team, err);
-        nchw_bwd_phase2<T, R>(dy, x, mean, rstd, gamma, dx, cfg, sb, m, last, mu, r, cx, cd, ga, part, stot, stage,
-                              chan);
-        if (!more) break;
-        const int64_t nlast =
-            nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, nsb, m, nmu, nr, nx, nd, nga, part, lds, true);
-        team_arrive(&ctr[nsb * 4 + 0]);
 #pragma unroll
         for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }
         last = nlast;
         sb = nsb;
         mu = nmu;
         r = nr;
-        ga = nga;
+        gam = ngam;
     }
 }
 
 // ---- helpers ---------------------------------------------------------------
-__global__ void clear_words(uint32_t* p, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
+// Words [0, zeros) := 0, [zeros, total) := all ones.
+__global__ void clear_words(uint32_t* p, int64_t zeros, int64_t total) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = i < zeros ? 0u : ~0u;
 }
 
 // dbeta_c = sum_n stot[n][c].x, dgamma_c = sum_n stot[n][c].y (n in order)
@@ -808,23 +925,33 @@ __global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ s
 #ifndef GN_SLAB_NHWC_RB
 #define GN_SLAB_NHWC_RB 8
 #endif
+// NCHW, largest tile per dtype and direction (measured on 112 x 64 x 512 x 512,
+// G = 8): fp32 forward 16 -- its two register tiles leave room for two
+// workgroups per CU, which 32 does not; fp32 backward 16 (four register tiles:
+// x and dy of two slabs; 8 is slower); 16-bit forward and backward 8 -- 16
+// chunks of a 16-bit type, with their unpacked halves, hold one workgroup per
+// CU, and run slower.  Smaller planes take the power of two at or above the
+// plane's chunks per thread, so that a small plane does not leave most of a
+// fixed-size tile empty.
 #ifndef GN_SLAB_NCHW_RF
-#define GN_SLAB_NCHW_RF 32
+#define GN_SLAB_NCHW_RF 16
 #endif
 #ifndef GN_SLAB_NCHW_RB
 #define GN_SLAB_NCHW_RB 16
 #endif
-// NCHW: the tile (R 16-byte chunks per thread) is sized to the channel plane
-// -- the power of two at or above the plane's chunks per thread, at most
-// GN_SLAB_NCHW_RF / RB -- so that a small plane does not leave most of a
-// fixed-size tile empty.
-// Largest forward tile of a 16-bit dtype: 32 chunks per thread (two register
-// tiles of them) leave no room for the unpacked halves and spill.
-constexpr int kNchwRF16 = GN_SLAB_NCHW_RF < 16 ? GN_SLAB_NCHW_RF : 16;
+#ifndef GN_SLAB_NCHW_RF16
+#define GN_SLAB_NCHW_RF16 8
+#endif
+#ifndef GN_SLAB_NCHW_RB16
+#define GN_SLAB_NCHW_RB16 8
+#endif
+constexpr int kNchwRF16 = GN_SLAB_NCHW_RF16 < 16 ? GN_SLAB_NCHW_RF16 : 16;
+constexpr int kNchwRB16 = GN_SLAB_NCHW_RB16 < 16 ? GN_SLAB_NCHW_RB16 : 16;
 
 int nchw_r(const Problem& p, bool backward) {
     const int64_t per_thread = (p.HW / (p.elem_bytes == 4 ? 4 : 8) + kT - 1) / kT;
-    const int rmax = backward ? GN_SLAB_NCHW_RB : (p.elem_bytes == 4 ? GN_SLAB_NCHW_RF : kNchwRF16);
+    const int rmax = backward ? (p.elem_bytes == 4 ? GN_SLAB_NCHW_RB : kNchwRB16)
+                              : (p.elem_bytes == 4 ? GN_SLAB_NCHW_RF : kNchwRF16);
     int r = 1;
     while (r < per_thread && r < rmax) r *= 2;
     return r;
@@ -844,6 +971,7 @@ struct Plan {
     int64_t grid;
     int64_t resident;
     size_t off_ctr, off_err, off_res, off_part, off_stot, total;
+    size_t ones_end;   // [off_part, ones_end): filled with ones each call (NCHW partial words)
 };
 
 int64_t tiles_per_slab(const Problem& p, int R, int64_t* tpc) {
@@ -880,7 +1008,7 @@ Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
     if (team < 1) team = 1;
     pl.cfg.tiles = tiles;
     pl.cfg.tpc = tpc;
-    pl.cfg.pstride = (tiles + 15) / 16 * 16;   // 16 slots: whole 128-byte lines for float4 and float2
+    pl.cfg.pstride = (tiles + 15) / 16 * 16;   // 16 slots: whole 128-byte lines of 8- and 16-byte slots
     pl.cfg.n_slabs = n_slabs;
     size_t off = 256;            // [0, 256): error word
     pl.off_err = 0;
@@ -894,9 +1022,9 @@ Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
         part = backward ? (size_t)n_slabs * p.C * pl.cfg.pstride * sizeof(float2)
                         : (size_t)n_slabs * p.G * pl.cfg.pstride * sizeof(float4);
     else
-        part = backward ? (size_t)n_slabs * pl.cfg.pstride * sizeof(float2)
-                        : (size_t)n_slabs * pl.cfg.pstride * sizeof(float4);
+        part = (size_t)n_slabs * pl.cfg.pstride * sizeof(uint64_t);
     off += al(part);
+    pl.ones_end = p.layout == GN_NHWC ? pl.off_part : off;
     pl.off_stot = off;
     if (backward) off += al((size_t)p.N * p.C * sizeof(float2));
     pl.total = off;
@@ -904,13 +1032,15 @@ Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
     return pl;
 }
 
-// Zeroes the error word, the sync words and the resident flags (one fill
-// kernel: no memset node, so the call stays safe to capture in a graph).
+// Zeroes the error word, the sync words and the resident flags, and sets the
+// NCHW partial words to the unpublished pattern (one fill kernel: no memset
+// node, so the call stays safe to capture in a graph).
 hipError_t clear_sync_words(char* ws, const Plan& pl, hipStream_t s) {
-    const int64_t words = (int64_t)(pl.off_part / sizeof(uint32_t));
+    const int64_t zeros = (int64_t)(pl.off_part / sizeof(uint32_t));
+    const int64_t words = (int64_t)(pl.ones_end / sizeof(uint32_t));
     int64_t blocks = (words + 255) / 256;
     if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(clear_words, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)ws, words);
+    hipLaunchKernelGGL(clear_words, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)ws, zeros, words);
     return hipGetLastError();
 }
 
@@ -939,7 +1069,7 @@ auto nchw_bwd_kernel(int R) -> decltype(&slab_nchw_bwd<T, GN_SLAB_NCHW_RB>) {
         case 2: return slab_nchw_bwd<T, 2>;
         case 4: return slab_nchw_bwd<T, 4>;
         case 8: return slab_nchw_bwd<T, 8>;
-        default: return slab_nchw_bwd<T, GN_SLAB_NCHW_RB>;
+        default: return slab_nchw_bwd<T, sizeof(T) == 4 ? GN_SLAB_NCHW_RB : kNchwRB16>;
     }
 }
 
@@ -963,7 +1093,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     char* ws = (char*)l.ws;
     uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
     uint32_t* err = (uint32_t*)(ws + pl.off_err);
-    float4* part = (float4*)(ws + pl.off_part);
+    void* part = ws + pl.off_part;   // NHWC: float4 per (group, tile); NCHW: one word per tile
     uint32_t* res = (uint32_t*)(ws + pl.off_res);
     hipError_t e;
     if ((e = clear_sync_words(ws, pl, l.stream))) return e;
@@ -1013,7 +1143,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     char* ws = (char*)l.ws;
     uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
     uint32_t* err = (uint32_t*)(ws + pl.off_err);
-    float2* part = (float2*)(ws + pl.off_part);
+    void* part = ws + pl.off_part;   // NHWC: float2 per (channel, tile); NCHW: one word per tile
     float2* stot = (float2*)(ws + pl.off_stot);
     uint32_t* res = (uint32_t*)(ws + pl.off_res);
     hipError_t e;
@@ -1059,6 +1189,10 @@ bool slab_ok(const Problem& p) {
         return p.HW >= 1;
     }
     if (p.HW % V != 0) return false;   // every channel plane starts 16-byte aligned
+    int64_t tpc;
+    if (tiles_per_slab(p, tile_chunks(p, true), &tpc) >= ((int64_t)1 << 31) ||
+        tiles_per_slab(p, tile_chunks(p, false), &tpc) >= ((int64_t)1 << 31))
+        return false;                   // tile indices of a slab in 32 bits
     return p.HW >= V && p.D <= kT;      // channel sums of a slab: one thread per channel
 }
 

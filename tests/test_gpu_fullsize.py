@@ -4,12 +4,12 @@ bench.py times (automatic path choice, default options).
 * NHWC fp16 1x128x1024x2048, G=16 and rows bf16 131072x4096: every output
   against the fp64 oracle on the whole tensor.
 * RMSNorm bf16 131072x4096: every output against the fp64 oracle.
-* NCHW fp32 112x64x512x512, G=8 (7.5 GB per tensor), and its 510x510 centre
-  crops (the strided workload): y, dx, mean and rstd of sampled slices, each
-  the oracle's result on that slice alone (a slice is its own GroupNorm
-  problem with one group); dgamma/dbeta of two whole groups, the oracle's
-  result on the group's sub-tensor (all samples, the group's channels, one
-  group).
+* NCHW fp32 112x64x512x512, G=8 (7.5 GB per tensor), the same shape in bf16,
+  and its 510x510 centre crops (the strided workload): y, dx, mean and rstd of
+  sampled slices, each the oracle's result on that slice alone (a slice is its
+  own GroupNorm problem with one group); dgamma/dbeta of two whole groups, the
+  oracle's result on the group's sub-tensor (all samples, the group's
+  channels, one group).
 """
 import gc
 
@@ -77,6 +77,17 @@ def test_full_rows_bf16_131072x4096():
 def test_full_nchw_sampled():
     _need_gpu()
     _nchw_sampled(inputs.NCHW_BIG, gn.GN_PATH_SLAB)
+
+
+# The NCHW benchmark shape in bf16: the slab kernels' 16-bit tiles (8 chunks
+# per thread) and their own loop order in the backward.
+NCHW_BIG_BF16 = inputs.Workload("nchw_bf16_112x64x512x512_g8", 112, 64, 512, 512, 8, "bf16", "nchw")
+
+
+@pytest.mark.timeout(900)
+def test_full_nchw_bf16_sampled():
+    _need_gpu()
+    _nchw_sampled(NCHW_BIG_BF16, gn.GN_PATH_SLAB)
 
 
 @pytest.mark.timeout(900)

@@ -50,6 +50,31 @@ def test_slab_parity(wl, cap):
     check_against_oracle(wl, data, out)
 
 
+# NCHW slabs of more than 1024 tiles (forced: the planner keeps the slab path
+# for slabs of at most 1024): the forward's merge beyond the partials a thread
+# keeps in registers, and the backward's per-channel sums over more than one
+# LDS-staged chunk of tile partials; ragged last tile of every plane.
+MANY_TILES = [
+    W("slab_nchw_f32_d8_many_tiles", 1, 8, 150, 16384 + 40, 1, "f32", "nchw"),
+    W("slab_nchw_bf16_d4_many_tiles", 1, 8, 300, 16384 + 24, 2, "bf16", "nchw"),
+]
+
+
+@pytest.mark.parametrize("cap", [0, 8], ids=lambda c: f"cap{c}")
+@pytest.mark.parametrize("wl", MANY_TILES, ids=lambda w: w.name)
+def test_slab_many_tiles(wl, cap):
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    say(f"[slab] {wl.name} cap={cap}")
+    data = inputs.make_inputs(wl, seed=4)
+    out = run_gpu(wl, data, force_path="slab", max_resident=cap)
+    fp, bp = out["fwd_plan"], out["bwd_plan"]
+    assert fp.path == gn.GN_PATH_SLAB and bp.path == gn.GN_PATH_SLAB
+    slabs = wl.N * wl.G
+    assert fp.tiles // slabs > 1024 and bp.tiles // slabs > 1024
+    check_against_oracle(wl, data, out)
+
+
 def test_overflow_tiles_exist_under_a_cap():
     """With the cap below the tile count, members own several tiles."""
     if not torch.cuda.is_available():

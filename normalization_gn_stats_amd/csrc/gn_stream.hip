@@ -212,6 +212,17 @@ __device__ inline void load_params(const float* __restrict__ p, int64_t c0, floa
     }
 }
 
+// Chunks j = 0 .. R-1 of a thread's tile that hold a pixel (p0 + j*PPI < HW),
+// as one 32-bit count: the per-chunk tests of several passes then share one
+// register instead of R 64-bit pixel indices kept live between the passes.
+template <int R>
+__device__ inline int valid_chunks(bool active, int64_t p0, int64_t HW, int PPI) {
+    const int64_t rem = HW - p0;
+    if (!active || rem <= 0) return 0;
+    const int r = (int)(rem < (int64_t)R * PPI ? rem : (int64_t)R * PPI);
+    return (r + PPI - 1) / PPI;
+}
+
 // ---- forward ----------------------------------------------------------------
 // grid (tiles, N); part: [N*G][tiles] float4 (count, mean, M2, -) of each
 // group over the tile -- an exact two-pass over the tile: per-channel sums ->
@@ -231,12 +242,13 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats(const T* __restrict__ x, St
     u4v reg[R];
     const int64_t p0 = tile * tg.TP + tg.pi;
     load_tile<T, R>(x + n * cfg.HW * cfg.C + tg.q * V, cfg.HW, cfg.C, p0, tg.PPI, reg);
+    const int nv = valid_chunks<R>(tg.active, p0, cfg.HW, tg.PPI);
     float acc[V];
 #pragma unroll
     for (int k = 0; k < V; ++k) acc[k] = 0.f;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        if (tg.active && p0 + (int64_t)j * tg.PPI < cfg.HW) {
+        if (j < nv) {
             float v[V];
             Vec<T>::unpack(reg[j], v);
 #pragma unroll
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(kT) void fwd_tile_stats(const T* __restrict__ x, St
     for (int k = 0; k < V; ++k) acc[k] = 0.f;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        if (tg.active && p0 + (int64_t)j * tg.PPI < cfg.HW) {
+        if (j < nv) {
             float v[V];
             Vec<T>::unpack(reg[j], v);
 #pragma unroll
@@ -372,6 +384,7 @@ __global__ __launch_bounds__(kT) void bwd_tile_sums(const T* __restrict__ dy, co
     const int64_t p0 = tile * tg.TP + tg.pi;
     load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, rx);
     load_tile<T, R>(dy + off, cfg.HW, cfg.C, p0, tg.PPI, rd);
+    const int nv = valid_chunks<R>(tg.active, p0, cfg.HW, tg.PPI);
     float mu[V], rs[V];
     int64_t sl[V];
     channel_slices<V, WHOLE>(tg.q, (int)cfg.D, n, cfg.G, sl);
@@ -382,7 +395,7 @@ __global__ __launch_bounds__(kT) void bwd_tile_sums(const T* __restrict__ dy, co
     for (int k = 0; k < V; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        if (tg.active && p0 + (int64_t)j * tg.PPI < cfg.HW) {
+        if (j < nv) {
             float xv[V], dv[V];
             Vec<T>::unpack(rx[j], xv);
             Vec<T>::unpack(rd[j], dv);
@@ -491,8 +504,6 @@ __global__ __launch_bounds__(kT) void bwd_dx(const T* __restrict__ dy, const T* 
     const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
     u4v rx[R], rd[R];
     const int64_t p0 = tile * tg.TP + tg.pi;
-    load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, rx);
-    load_tile<T, R>(dy + off, cfg.HW, cfg.C, p0, tg.PPI, rd);
     float mu[V], rs[V], Ak[V], Bk[V];
     int64_t sl[V];
     channel_slices<V, WHOLE>(tg.q, (int)cfg.D, n, cfg.G, sl);
@@ -507,6 +518,11 @@ __global__ __launch_bounds__(kT) void bwd_dx(const T* __restrict__ dy, const T* 
     }
     float ga[V];
     load_params<V>(gamma, tg.q * V, 1.f, ga);
+    // the tile after the per-channel values (measured: 434 -> 428 us for the
+    // 1x128x1024x2048 fp16 backward; the forward's apply is faster the other
+    // way round)
+    load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, rx);
+    load_tile<T, R>(dy + off, cfg.HW, cfg.C, p0, tg.PPI, rd);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int64_t p = p0 + (int64_t)j * tg.PPI;

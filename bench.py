@@ -15,6 +15,7 @@ HIP events that the library records on the call's stream around that kernel.
 ``cpu_baseline`` times the fp64 oracle on the host cores over a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --rows-sweep [--steps K]   (context table, one line per shape)
 """
 from __future__ import annotations
 
@@ -134,6 +135,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times (a known-size "
                          "kernel that scales the rocprofv3 byte counters)")
+    ap.add_argument("--rows-sweep", action="store_true",
+                    help="instead of the bench line: forward/backward times of the rows shapes the pages time on "
+                         "MI350X, one JSON line per shape")
     ap.add_argument("--mode", default="auto", choices=["auto", "graph", "eager"],
                     help="graph: the timed steps run as one captured HIP graph (no host in the loop)")
     args = ap.parse_args()
@@ -153,6 +157,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.rows_sweep:
+        rows_sweep(args.steps)
+        return
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     mask = gn.GN_GRAD_DX | gn.GN_GRAD_DGAMMA | gn.GN_GRAD_DBETA
@@ -450,6 +457,88 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+# Rows shapes of the LayerNorm / RMSNorm backward table in ROCm/pytorch PR
+# #3564 (MI350X, "Tiled+Two-pass" and "Tiled only" columns, in microseconds),
+# for context on other hardware.
+ROWS_SWEEP = [  # (op, N, C, dtype, pages' tiled+two-pass us, pages' tiled-only us)
+    ("gn", 32, 512, "f16", 8.16, 7.94), ("gn", 96, 768, "f16", 20.78, 20.71),
+    ("gn", 192, 1024, "bf16", 8.51, 8.20), ("gn", 4096, 1024, "f16", 13.12, 31.07),
+    ("gn", 1024, 768, "f16", 11.05, 11.15), ("gn", 4096, 1024, "bf16", 13.10, 31.28),
+    ("gn", 4096, 1024, "f32", 15.90, 30.87), ("gn", 131072, 64, "f16", 27.70, 26.48),
+    ("gn", 131072, 4096, "bf16", 513.38, 509.65), ("gn", 8192, 768, "f16", 16.56, 58.22),
+    ("rms", 4096, 1024, "f16", 11.18, 22.34), ("rms", 131072, 4096, "bf16", 476.03, 476.18),
+    ("rms", 131072, 64, "f16", 17.29, 16.73),
+]
+
+
+def rows_sweep(K):
+    """Forward, full backward and gamma/beta-only backward of every ROWS_SWEEP
+    shape, each as a HIP graph of K back-to-back calls timed with events around
+    the replay; one JSON line per shape (microseconds per call)."""
+    import torch
+
+    import normalization_gn_stats_amd as gn
+    from normalization_gn_stats_amd import inputs
+
+    dev = torch.device("cuda", 0)
+
+    def per_call_us(fn):
+        fn(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            h = torch.cuda.current_stream().cuda_stream
+            for _ in range(K):
+                fn(h)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / K, 2)
+
+    for op, N, C, dt, pages_2p, pages_tiled in ROWS_SWEEP:
+        name = f"{op}_{dt}_{N}x{C}"
+        log(f"rows sweep: {name}")
+        wl = inputs.Workload(name, N, C, 1, 1, 1, dt, "nchw", eps=1e-6 if op == "rms" else 1e-5, op=op)
+        d = inputs.make_inputs(wl, seed=0, device="cuda")
+        code = {"f32": 0, "f16": 1, "bf16": 2}[dt]
+        x, dy = d["x"].reshape(N, C), d["dy"].reshape(N, C)
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        mean, rstd = torch.empty(N, device=dev), torch.empty(N, device=dev)
+        dg, db = torch.empty(C, device=dev), torch.empty(C, device=dev)
+
+        def ws(nbytes):
+            return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+        res = {"shape": name, "unit": "us/call"}
+        if op == "gn":
+            x4, dy4, y4, dx4 = (t.reshape(N, C, 1, 1) for t in (x, dy, y, dx))
+            fws = ws(gn.forward_workspace_size(N, C, 1, 1, code, gn._lib.GN_NCHW))
+            res["fwd"] = per_call_us(lambda h: gn.forward_into(x4, d["gamma"], d["beta"], 1, wl.eps, y4, mean, rstd,
+                                                               fws, stream=h))
+            masks = (("bwd", 7), ("bwd_dgamma_dbeta", 6))
+            for key, mask in masks:
+                bws = ws(gn.backward_workspace_size(N, C, 1, 1, code, gn._lib.GN_NCHW, mask))
+                res[key] = per_call_us(lambda h: gn.backward_into(dy4, x4, mean, rstd, d["gamma"], 1, mask, dx4, dg,
+                                                                  db, bws, stream=h))
+        else:
+            fws = ws(gn.rms_forward_workspace_size(N, C, 1, code))
+            res["fwd"] = per_call_us(lambda h: gn.rms_forward_into(x, d["gamma"], 1, wl.eps, y, rstd, fws,
+                                                                   stream=h))
+            for key, mask in (("bwd", 3), ("bwd_dgamma", 2)):
+                bws = ws(gn.rms_backward_workspace_size(N, C, 1, code, mask))
+                res[key] = per_call_us(lambda h: gn.rms_backward_into(dy, x, rstd, d["gamma"], 1, mask, dx, dg, bws,
+                                                                      stream=h))
+        res["pages_mi350x_tiled_two_pass"] = pages_2p
+        res["pages_mi350x_tiled_only"] = pages_tiled
+        print(json.dumps(res), flush=True)
+        del d, x, dy, y, dx
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(shapes, seconds, bytes_per_step):

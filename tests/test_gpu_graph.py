@@ -17,6 +17,7 @@ W = inputs.Workload
     (W("graph_gen_bf16", 2, 16, 20, 21, 4, "bf16", "nhwc"), "generic"),
     (inputs.TINY, None),
     (W("graph_slab_nhwc_f16", 2, 64, 37, 29, 8, "f16", "nhwc"), "slab"),
+    (W("graph_slab_nchw_bf16", 2, 8, 64, 600, 2, "bf16", "nchw"), "slab"),   # 12 polled tile words per slab
     (W("graph_stream_nhwc_f16", 2, 64, 130, 131, 8, "f16", "nhwc"), "stream"),
     (W("graph_rows_narrow_f16", 3000, 64, 1, 1, 1, "f16", "nchw"), None),
     (W("graph_crop_f32", 2, 16, 20, 21, 4, "f32", "nchw", crop=1), None),   # strided views, in place

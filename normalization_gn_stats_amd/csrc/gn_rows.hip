@@ -526,6 +526,16 @@ __global__ __launch_bounds__(kT) void rows_bwd_narrow_k(const T* __restrict__ dy
 // with up to 2 or 4 in flight 580 and 597 us.  The bursts of dx stores from
 // every wave otherwise slow the other waves' loads.  Narrower slices (the
 // small, latency-bound shapes) keep their bursts.
+//
+// The wide slices are also read with non-temporal loads: 131072 x 4096 bf16,
+// graph of 20 calls, full backward 577 -> 566 us and the dgamma/dbeta-only
+// backward 358 -> 320 us.  Narrower slices keep plain loads (the small shapes
+// ran 10-20% slower with non-temporal ones).
+#ifndef GN_ROWS_BWD_NT_WIDE
+#define GN_ROWS_BWD_NT_WIDE 1
+#endif
+constexpr bool kBwdNtWide = GN_ROWS_BWD_NT_WIDE != 0;
+
 template <typename T, int NV, int RB, int CS, int NW = kNW>
 __global__ __launch_bounds__(NW * kWave) void rows_bwd_k(const T* __restrict__ dy, const T* __restrict__ x,
                                                  const float* __restrict__ mean, const float* __restrict__ rstd,
@@ -598,8 +608,13 @@ __global__ __launch_bounds__(NW * kWave) void rows_bwd_k(const T* __restrict__ d
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int vi = min(vbase + j * kWave + lane, nvec - 1);
-                rx[r][j] = ld16(x + base + (int64_t)vi * V);
-                rd[r][j] = ld16(dy + base + (int64_t)vi * V);
+                if constexpr (CS == 4 && kBwdNtWide) {
+                    rx[r][j] = ld16_nt(x + base + (int64_t)vi * V);
+                    rd[r][j] = ld16_nt(dy + base + (int64_t)vi * V);
+                } else {
+                    rx[r][j] = ld16(x + base + (int64_t)vi * V);
+                    rd[r][j] = ld16(dy + base + (int64_t)vi * V);
+                }
             }
             mu[r] = rms ? 0.f : mean[n * G + g];
             rs[r] = rstd[n * G + g];

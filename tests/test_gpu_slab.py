@@ -30,6 +30,13 @@ CASES = [
     W("slab_nchw_bf16_c12_g3", 3, 12, 40, 52, 3, "bf16", "nchw"),
     # tiles sized to small channel planes (ten channels per group, 64x64)
     W("slab_nchw_f16_c320_g32", 2, 320, 64, 64, 32, "f16", "nchw"),
+    # 2, 4 (ragged last tile), 16 (the 512x512 fp32 planes) and 64 tiles per
+    # channel plane, 256 and 512 tiles per slab
+    W("slab_nchw_bf16_tpc2", 2, 8, 128, 256, 2, "bf16", "nchw"),
+    W("slab_nchw_f32_tpc4_ragged", 2, 8, 224, 256, 2, "f32", "nchw"),
+    W("slab_nchw_f32_tpc16_d8", 1, 16, 512, 512, 2, "f32", "nchw"),
+    W("slab_nchw_f16_tpc64_d4", 1, 4, 1024, 1024, 1, "f16", "nchw"),
+    W("slab_nchw_f16_tpc64_d8", 1, 8, 1024, 1024, 1, "f16", "nchw"),
     inputs.TINY,
 ]
 

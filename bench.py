@@ -52,13 +52,29 @@ WORKLOADS = {
 DEFAULT = "rows_f16_4096x1024+8192x768"
 
 
-def source_fingerprint() -> str:
-    """sha256 over the kernel sources (csrc/), to tell whether byte counters
-    recorded in profiles/traffic.json still describe the kernels built now."""
+# The source file that defines each kernel (by name prefix) or each whole call;
+# every kernel also depends on the shared headers and the C-ABI file.
+KERNEL_SOURCES = (
+    (("rows_",), "gn_rows.hip"),
+    (("slab_", "clear_words", "params_over_n"), "gn_slab.hip"),
+    (("fwd_tile_stats", "fwd_finalize", "fwd_apply", "bwd_tile_sums", "col_sums", "bwd_group_ab", "bwd_dx",
+      "stream_"), "gn_stream.hip"),
+    (("gen_", "generic_"), "gn_generic.hip"),
+)
+COMMON_SOURCES = ("gn_device.hpp", "gn_internal.hpp", "gn_api.cpp")
+
+
+def source_fingerprint(kernel_name: str) -> str:
+    """sha256 over the sources a kernel is built from (its own .hip file, the
+    shared headers and the C-ABI file), to tell whether byte counters recorded
+    in profiles/traffic.json still describe the kernel built now."""
     import hashlib
+    own = [f for prefixes, f in KERNEL_SOURCES if kernel_name.startswith(prefixes)]
+    if not own:
+        raise KeyError(f"no source file known for kernel {kernel_name}")
     h = hashlib.sha256()
     d = os.path.join(HERE, "normalization_gn_stats_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in sorted(COMMON_SOURCES + (own[0],)):
         h.update(f.encode())
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
@@ -67,15 +83,15 @@ def source_fingerprint() -> str:
 def recorded_traffic(workload, kernel_name, grid):
     """HBM bytes per launch of this kernel from profiles/traffic.json (rocprofv3
     FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when
-    missing or taken on different kernel sources."""
+    missing or taken on different sources of that kernel."""
     try:
         t = json.load(open(os.path.join(HERE, "profiles", "traffic.json")))
     except (OSError, ValueError):
         return None
-    if t.get("source_fingerprint") != source_fingerprint():
-        return None
     e = t.get("kernels", {}).get(f"{workload}|{kernel_name}|{grid}")
     if not e or e.get("read_bytes") is None or e.get("write_bytes") is None:
+        return None
+    if e.get("source_fingerprint") != source_fingerprint(kernel_name):
         return None
     return int(e["read_bytes"] + e["write_bytes"])
 

@@ -521,16 +521,22 @@ __global__ __launch_bounds__(kT) void rows_bwd_narrow_k(const T* __restrict__ dy
 // through LDS (CS > 1).
 //
 // With four waves per slice (wide slices: the large, bandwidth-bound shapes)
-// each dx store waits until the wave's earlier stores have completed: one
-// store in flight per wave.  Measured on 131072 x 4096 bf16: 610 -> 574 us;
-// with up to 2 or 4 in flight 580 and 597 us.  The bursts of dx stores from
-// every wave otherwise slow the other waves' loads.  Narrower slices (the
-// small, latency-bound shapes) keep their bursts.
-//
-// The wide slices are also read with non-temporal loads: 131072 x 4096 bf16,
-// graph of 20 calls, full backward 577 -> 566 us and the dgamma/dbeta-only
-// backward 358 -> 320 us.  Narrower slices keep plain loads (the small shapes
-// ran 10-20% slower with non-temporal ones).
+// x and dy are read with non-temporal loads, and each dx store first waits
+// until at most one earlier memory operation of the wave is outstanding: two
+// stores in flight per wave.  The bursts of dx stores from every wave
+// otherwise slow the other waves' loads.  Measured on 131072 x 4096 bf16:
+//   plain loads, stores in flight unlimited / 4 / 2 / 1: 610 / 597 / 580 / 574
+//   us (graph of 20 calls);
+//   non-temporal loads, 1 in flight: 577 -> 566 us (graph), dgamma/dbeta-only
+//   backward 358 -> 320 us;
+//   non-temporal loads, unlimited / 4 / 2 / 1 in flight: 597 / 564 / 563 /
+//   595 us in alternating eager calls (medians of four rounds; 585 / 558 /
+//   562 / 570 us in a graph).
+// Narrower slices (the small, latency-bound shapes) keep plain loads and
+// their store bursts: they ran 10-20% slower with non-temporal loads.
+#ifndef GN_ROWS_BWD_DX_INFLIGHT
+#define GN_ROWS_BWD_DX_INFLIGHT 2
+#endif
 #ifndef GN_ROWS_BWD_NT_WIDE
 #define GN_ROWS_BWD_NT_WIDE 1
 #endif
@@ -707,7 +713,8 @@ __global__ __launch_bounds__(NW * kWave) void rows_bwd_k(const T* __restrict__ d
                     const float gd = dv[k] * gv[k];
                     o[k] = rs[r] * ((gd - A[r]) - xh * B[r]);
                 }
-                if constexpr (CS == 4) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): one dx store in flight
+                if constexpr (CS == 4 && GN_ROWS_BWD_DX_INFLIGHT > 0)
+                    __builtin_amdgcn_s_waitcnt(0x0F70 | (GN_ROWS_BWD_DX_INFLIGHT - 1));   // vmcnt(K - 1)
                 st16_nt(dx + base + (int64_t)vi * V, Vec<T>::pack(o));
             }
         }

@@ -1,0 +1,56 @@
+"""Host-side checks of bench.py's bookkeeping (no GPU): every kernel the
+recorded byte counters name maps to the source file it is built from, and a
+counter entry is used only while that file and the shared sources are
+unchanged."""
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+TRAFFIC = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+
+
+def test_every_recorded_kernel_has_a_source_file():
+    for key in TRAFFIC["kernels"]:
+        kernel = key.split("|")[1]
+        fp = bench.source_fingerprint(kernel)
+        assert len(fp) == 16
+
+
+def test_kernel_source_table_names_existing_files():
+    d = os.path.join(ROOT, "normalization_gn_stats_amd", "csrc")
+    for _, f in bench.KERNEL_SOURCES:
+        assert os.path.exists(os.path.join(d, f)), f
+    for f in bench.COMMON_SOURCES:
+        assert os.path.exists(os.path.join(d, f)), f
+
+
+def test_unknown_kernel_name_is_an_error():
+    with pytest.raises(KeyError):
+        bench.source_fingerprint("no_such_kernel")
+
+
+def test_fingerprints_differ_per_source_file():
+    assert bench.source_fingerprint("rows_bwd_k") != bench.source_fingerprint("slab_nchw_bwd")
+    assert bench.source_fingerprint("rows_bwd_k") == bench.source_fingerprint("rows_colsum_k")
+
+
+def test_stale_entry_gives_no_traffic(tmp_path, monkeypatch):
+    key = next(iter(TRAFFIC["kernels"]))
+    workload, kernel, grid = key.split("|")
+    entry = dict(TRAFFIC["kernels"][key], source_fingerprint="0" * 16)
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "traffic.json").write_text(json.dumps({"kernels": {key: entry}}))
+    csrc = tmp_path / "normalization_gn_stats_amd"
+    os.symlink(os.path.join(ROOT, "normalization_gn_stats_amd"), csrc)
+    monkeypatch.setattr(bench, "HERE", str(tmp_path))
+    assert bench.recorded_traffic(workload, kernel, grid) is None
+    entry["source_fingerprint"] = bench.source_fingerprint(kernel)
+    (prof / "traffic.json").write_text(json.dumps({"kernels": {key: entry}}))
+    assert bench.recorded_traffic(workload, kernel, grid) == int(entry["read_bytes"] + entry["write_bytes"])

@@ -800,6 +800,14 @@ __global__ __launch_bounds__(kT) void rows_colsum_k(const float2* __restrict__ p
 #ifndef GN_ROWS_BWD_RB
 #define GN_ROWS_BWD_RB 4
 #endif
+// Slices per wave per block when four waves share a slice (the wide,
+// bandwidth-bound shapes): 2.  131072 x 4096 bf16 backward with 2 instead of
+// 4: 557 -> 538 us in a graph of 20 calls, 569 -> 549 us in alternating eager
+// calls.  The narrower slices keep 4 (with 2, their column sums take twice
+// the partial rows, and the calls measured no faster).
+#ifndef GN_ROWS_BWD_RB_WIDE
+#define GN_ROWS_BWD_RB_WIDE 2
+#endif
 
 // 16-byte vectors per lane of the forward (one wave per slice): 1, 2, 4, 8, or
 // 0 when the slice does not fit one wave.
@@ -827,7 +835,7 @@ BwdShape bwd_shape(const Problem& p) {
     const int64_t nvec = p.D / V;
     for (int cs : {1, 2, 4}) {
         const int64_t nv = (nvec + cs * kWave - 1) / (cs * kWave);
-        if (nv <= 2) return BwdShape{cs, nv <= 1 ? 1 : 2, GN_ROWS_BWD_RB};
+        if (nv <= 2) return BwdShape{cs, nv <= 1 ? 1 : 2, cs == 4 ? GN_ROWS_BWD_RB_WIDE : GN_ROWS_BWD_RB};
     }
     const int64_t nv = (nvec + 4 * kWave - 1) / (4 * kWave);
     if (nv <= 4) return BwdShape{4, 4, 2};
@@ -1046,15 +1054,15 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
         case 32: return bwd_narrow<T, 32>(p, a, l);
         default: break;
     }
-    constexpr int RBS = GN_ROWS_BWD_RB;
+    constexpr int RBS = GN_ROWS_BWD_RB, RBW = GN_ROWS_BWD_RB_WIDE;
     const BwdShape sh = bwd_shape(p);
     switch (sh.cs * 100 + sh.nv) {
         case 101: return bwd_launch<T, 1, RBS, 1>(p, a, l);
         case 102: return bwd_launch<T, 2, RBS, 1>(p, a, l);
         case 201: return bwd_launch<T, 1, RBS, 2>(p, a, l);
         case 202: return bwd_launch<T, 2, RBS, 2>(p, a, l);
-        case 401: return bwd_launch<T, 1, RBS, 4>(p, a, l);
-        case 402: return bwd_launch<T, 2, RBS, 4>(p, a, l);
+        case 401: return bwd_launch<T, 1, RBW, 4>(p, a, l);
+        case 402: return bwd_launch<T, 2, RBW, 4>(p, a, l);
         case 404: return bwd_launch<T, 4, 2, 4>(p, a, l);
         default: return bwd_launch<T, 8, 1, 4>(p, a, l);
     }

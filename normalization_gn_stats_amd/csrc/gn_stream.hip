@@ -38,12 +38,16 @@ constexpr int kNW = kT / kWave;
 
 // 16-byte chunks per thread per tile (of x, and of dy in the backward), per
 // kernel, as measured on the 1x128x1024x2048 fp16 image: 16 for the two
-// reductions and the forward's output pass, 4 for dx.
+// reductions, 4 for the two output passes (forward output, rocprofv3 averages
+// over 42 dispatches: 16 -> 178.0 us, 8 -> 166.5 us, 4 -> 161.2 us, 2 -> 162.8
+// us; dx: 2 -> 268.0 us, 4 -> 253.5 us, 8 -> 271.9 us).  The output passes
+// store what they load; fewer stores per thread in one burst keep the write
+// stream from stalling the loads.
 #ifndef GN_STREAM_R_STATS
 #define GN_STREAM_R_STATS 16
 #endif
 #ifndef GN_STREAM_R_APPLY
-#define GN_STREAM_R_APPLY 16
+#define GN_STREAM_R_APPLY 4
 #endif
 #ifndef GN_STREAM_R_SUMS
 #define GN_STREAM_R_SUMS 16

@@ -511,23 +511,22 @@ __device__ inline void nchw_load_tile(const T* __restrict__ src, const SlabCfg& 
     }
 }
 
-// Phase 1 of the forward for slab sb: statistics of member m's tiles (the
-// first one already in buf when `preloaded`), one published (mean, M2)
-// partial per tile -- an exact two-pass over the tile in registers: workgroup
+// Phase 1 of the forward for slab sb: statistics of member m's tiles, one
+// published (mean, M2) partial per tile -- an exact two-pass over the tile in registers: workgroup
 // sum -> tile mean -> workgroup sum of squared deviations.  The last tile
 // stays in buf; its channel's gamma/beta are fetched here so that phase 2 does
 // not wait for them.  Returns the last tile index (-1 if the member has none).
 template <typename T, int R>
 __device__ inline int64_t nchw_fwd_phase1(const T* __restrict__ x, const float* __restrict__ gamma,
                                           const float* __restrict__ beta, const SlabCfg& cfg, int64_t sb, int m,
-                                          u4v (&buf)[R], float2& gb, uint64_t* part, float* lds, bool preloaded) {
+                                          u4v (&buf)[R], float2& gb, uint64_t* part, float* lds) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
     const int t = tile_tid();
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
         const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
-        if (!(preloaded && tile == m)) nchw_load_tile<T, R>(x, cfg, sb, tile, buf);
+        nchw_load_tile<T, R>(x, cfg, sb, tile, buf);
         const int64_t c = (sb - (sb / cfg.G) * cfg.G) * cfg.D + cl;
         gb = make_float2(gamma ? gamma[c] : 1.f, beta ? beta[c] : 0.f);
         const int64_t rem = cfg.HW - k0;
@@ -675,12 +674,12 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
     float2 gcur = make_float2(1.f, 0.f), gnxt = gcur;
     int64_t sb = team;
     if (sb >= cfg.n_slabs) return;   // uniform over the team
-    int64_t last = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, sb, m, cur, gcur, part, lds, false);
+    int64_t last = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, sb, m, cur, gcur, part, lds);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
         const bool more = nsb < cfg.n_slabs;   // uniform over the team
         int64_t nlast = -1;
-        if (more) nlast = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, nsb, m, nxt, gnxt, part, lds, false);
+        if (more) nlast = nchw_fwd_phase1<T, R>(x, gamma, beta, cfg, nsb, m, nxt, gnxt, part, lds);
         __builtin_amdgcn_sched_barrier(0);   // keep the two slabs' phases apart
         nchw_fwd_phase2<T, R>(x, gamma, beta, y, mean, rstd, cfg, sb, m, last, cur, gcur, part, err, lds);
         if (!more) break;
@@ -692,8 +691,8 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
     }
 }
 
-// Phase 1 of the backward for slab sb: per-tile sums of dy and dy*xhat (the
-// member's first tile already in bx, bd when `preloaded`), published per tile;
+// Phase 1 of the backward for slab sb: per-tile sums of dy and dy*xhat of
+// member m's tiles, published per tile;
 // the last tile of x and dy stays in bx, bd.  mu, r: the slab's saved
 // statistics, loaded by the caller ahead of the bulk traffic (a wave's loads
 // complete in issue order, so a late small load waits for all of it).
@@ -701,17 +700,15 @@ template <typename T, int R>
 __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __restrict__ x,
                                           const float* __restrict__ gamma, const SlabCfg& cfg, int64_t sb, int m,
                                           float mu, float r, u4v (&bx)[R], u4v (&bd)[R], uint64_t* part,
-                                          float* lds, bool preloaded) {
+                                          float* lds) {
     constexpr int V = Vec<T>::V;
     constexpr int64_t TE = (int64_t)kT * R * V;
     const int t = tile_tid();
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
         const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
-        if (!(preloaded && tile == m)) {
-            nchw_load_tile<T, R>(x, cfg, sb, tile, bx);
-            nchw_load_tile<T, R>(dy, cfg, sb, tile, bd);
-        }
+        nchw_load_tile<T, R>(x, cfg, sb, tile, bx);
+        nchw_load_tile<T, R>(dy, cfg, sb, tile, bd);
         float acc[2] = {0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < R; ++j) {
@@ -822,18 +819,14 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
     }
 }
 
-// Loop order of the backward, the faster of two measured for each type: fp32
-// (four register tiles of 16 chunks, one workgroup per CU) prefetches its
-// first tile of the next slab, then runs phase 2 of the current slab while it
-// streams and phase 1 of the next from registers; 16-bit types (tiles of 8
-// chunks, two workgroups per CU) run phase 1 of the next slab first, as the
-// forward does.
-template <typename T>
-constexpr bool kBwdPhase1First = sizeof(T) != 4;
-
 // part: [slab][tile] published (sum dy, sum dy*xhat) words; stot: [N][C] float2.
-// Two slabs in flight, as in the forward.  Requires D <= kT (checked on the
-// host).
+// Two slabs in flight, as in the forward: a member runs phase 1 of the team's
+// next slab (loads, sums, publish) before phase 2 of the current one needs
+// its partials.  Requires D <= kT (checked on the host).  (fp32 112 x 64 x
+// 512 x 512, tiles of 8 chunks, two workgroups per CU: 3.93 ms, against 4.38
+// ms for tiles of 16 chunks, one workgroup per CU and the other order --
+// the first tile of the next slab prefetched, phase 2 of the current slab
+// while it streams, phase 1 of the next from registers.)
 template <typename T, int R>
 __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, const T* __restrict__ x,
                                                     const float* __restrict__ mean,
@@ -853,38 +846,22 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
     if (sb >= cfg.n_slabs) return;   // uniform over the team
     float mu = mean[sb], r = rstd[sb];
     float gam = (gamma && t < cfg.D) ? gamma[(sb % cfg.G) * cfg.D + t] : 1.f;
-    int64_t last = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, sb, m, mu, r, cx, cd, part, lds, false);
+    int64_t last = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, sb, m, mu, r, cx, cd, part, lds);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
         const bool more = nsb < cfg.n_slabs;   // uniform over the team
         float nmu = 0.f, nr = 0.f, ngam = 1.f;
         int64_t nlast = -1;
-        if constexpr (kBwdPhase1First<T>) {
-            if (more) {
-                nmu = mean[nsb];
-                nr = rstd[nsb];
-                if (gamma && t < cfg.D) ngam = gamma[(nsb % cfg.G) * cfg.D + t];
-                nlast = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, nsb, m, nmu, nr, nx, nd, part, lds, false);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            nchw_bwd_phase2<T, R>(dy, x, gamma, dx, cfg, sb, m, last, mu, r, cx, cd, gam, part, err, stot, stage,
-                                  chan, gch);
-            if (!more) break;
-        } else {
-            if (more) {
-                nmu = mean[nsb];   // ahead of the prefetch and the dx stores
-                nr = rstd[nsb];
-                if (gamma && t < cfg.D) ngam = gamma[(nsb % cfg.G) * cfg.D + t];
-                if (m < cfg.tiles) {
-                    nchw_load_tile<T, R>(x, cfg, nsb, m, nx);
-                    nchw_load_tile<T, R>(dy, cfg, nsb, m, nd);
-                }
-            }
-            nchw_bwd_phase2<T, R>(dy, x, gamma, dx, cfg, sb, m, last, mu, r, cx, cd, gam, part, err, stot, stage,
-                                  chan, gch);
-            if (!more) break;
-            nlast = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, nsb, m, nmu, nr, nx, nd, part, lds, true);
+        if (more) {
+            nmu = mean[nsb];
+            nr = rstd[nsb];
+            if (gamma && t < cfg.D) ngam = gamma[(nsb % cfg.G) * cfg.D + t];
+            nlast = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, nsb, m, nmu, nr, nx, nd, part, lds);
         }
+        __builtin_amdgcn_sched_barrier(0);   // keep the two slabs' phases apart
+        nchw_bwd_phase2<T, R>(dy, x, gamma, dx, cfg, sb, m, last, mu, r, cx, cd, gam, part, err, stot, stage,
+                              chan, gch);
+        if (!more) break;
 #pragma unroll
         for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }
         last = nlast;
@@ -928,8 +905,9 @@ __global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ s
 #endif
 // NCHW, largest tile per dtype and direction (measured on 112 x 64 x 512 x 512,
 // G = 8): fp32 forward 16 -- its two register tiles leave room for two
-// workgroups per CU, which 32 does not; fp32 backward 16 (four register tiles:
-// x and dy of two slabs; 8 is slower); 16-bit forward and backward 8 -- 16
+// workgroups per CU, which 32 does not; fp32 backward 8 (four register tiles:
+// x and dy of two slabs, two workgroups per CU; 16 leaves one workgroup per
+// CU and is slower); 16-bit forward and backward 8 -- 16
 // chunks of a 16-bit type, with their unpacked halves, hold one workgroup per
 // CU, and run slower.  Smaller planes take the power of two at or above the
 // plane's chunks per thread, so that a small plane does not leave most of a
@@ -938,7 +916,7 @@ __global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ s
 #define GN_SLAB_NCHW_RF 16
 #endif
 #ifndef GN_SLAB_NCHW_RB
-#define GN_SLAB_NCHW_RB 16
+#define GN_SLAB_NCHW_RB 8
 #endif
 #ifndef GN_SLAB_NCHW_RF16
 #define GN_SLAB_NCHW_RF16 8

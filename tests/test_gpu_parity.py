@@ -50,6 +50,11 @@ SMALL = [
     (W("rows_wide_f16_129x16384", 129, 16384, 1, 1, 1, "f16", "nchw"), None, gn.GN_PATH_ROWS),
     (W("rows_wide_f32_201x3072", 201, 3072, 1, 1, 1, "f32", "nchw"), None, gn.GN_PATH_ROWS),
     (W("rows_wide_f32_g2_50x16384", 50, 16384, 1, 1, 2, "f32", "nhwc"), None, gn.GN_PATH_ROWS),
+    # four waves per slice with at most two vectors per lane (two slices per
+    # wave per block in the backward), several groups, odd slice counts
+    (W("rows_cs4_bf16_g2_77x8192", 77, 8192, 1, 1, 2, "bf16", "nhwc"), None, gn.GN_PATH_ROWS),
+    (W("rows_cs4_f32_g2_65x4096", 65, 4096, 1, 1, 2, "f32", "nchw"), None, gn.GN_PATH_ROWS),
+    (W("rows_cs4_f16_g2_31x6144", 31, 6144, 1, 1, 2, "f16", "nchw"), None, gn.GN_PATH_ROWS),
     # narrow slices (at most 32 vectors): several slices per wavefront, from
     # 64 slices per wave (one vector each) to 2 (32 vectors each), with idle
     # lanes (6 vectors on 8 lanes) and ragged last row sets

@@ -915,9 +915,11 @@ __global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ s
 // G = 8): fp32 forward 16 -- its two register tiles leave room for two
 // workgroups per CU, which 32 does not; fp32 backward 8 (four register tiles:
 // x and dy of two slabs, two workgroups per CU; 16 leaves one workgroup per
-// CU and is slower); 16-bit forward and backward 8 -- 16
-// chunks of a 16-bit type, with their unpacked halves, hold one workgroup per
-// CU, and run slower.  Smaller planes take the power of two at or above the
+// CU and is slower); 16-bit forward 8 -- 16 chunks of a 16-bit type, with
+// their unpacked halves, hold two workgroups per CU instead of four and run
+// slower; 16-bit backward 4 (121 VGPRs, four workgroups per CU: bf16 2.30 ->
+// 2.27 ms against 8 chunks, 198 VGPRs and two workgroups per CU).  Smaller
+// planes take the power of two at or above the
 // plane's chunks per thread, so that a small plane does not leave most of a
 // fixed-size tile empty.
 #ifndef GN_SLAB_NCHW_RF
@@ -930,7 +932,7 @@ __global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ s
 #define GN_SLAB_NCHW_RF16 8
 #endif
 #ifndef GN_SLAB_NCHW_RB16
-#define GN_SLAB_NCHW_RB16 8
+#define GN_SLAB_NCHW_RB16 4
 #endif
 constexpr int kNchwRF16 = GN_SLAB_NCHW_RF16 < 16 ? GN_SLAB_NCHW_RF16 : 16;
 constexpr int kNchwRB16 = GN_SLAB_NCHW_RB16 < 16 ? GN_SLAB_NCHW_RB16 : 16;

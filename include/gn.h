@@ -55,7 +55,10 @@ typedef enum gn_status {
     GN_ERR_UNSUPPORTED = 2,  /* dtype or layout outside the enums, or a forced
                                 path that cannot serve these arguments */
     GN_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the size query returned */
-    GN_ERR_HIP = 4           /* the HIP runtime refused a launch */
+    GN_ERR_HIP = 4,          /* the HIP runtime refused a launch */
+    GN_ERR_WAIT = 5          /* reported by gn_read_status only: a bounded wait
+                                between cooperating workgroups gave up (see
+                                gn_options.status_word) */
 } gn_status;
 
 typedef enum gn_dtype { GN_F32 = 0, GN_F16 = 1, GN_BF16 = 2 } gn_dtype;
@@ -91,17 +94,48 @@ typedef struct gn_plan_info {
     int64_t team;            /* workgroups cooperating on one slab (slab path) */
 } gn_plan_info;
 
-/* Optional knobs (pass NULL for defaults). */
+/* Bit that the kernels OR into gn_options.status_word when a bounded wait
+ * gives up. */
+#define GN_STATUS_WAIT_EXPIRED 1u
+
+/* gn_options.debug_flags: GN_DEBUG_UNMET_WAITS raises the target of every
+ * wait between cooperating workgroups out of reach, so that each of them
+ * expires after spin_limit polls -- for tests of the failure report only. */
+#define GN_DEBUG_UNMET_WAITS 1u
+
+/* Optional knobs (pass NULL for defaults).
+ *
+ * Failure report of the cooperative (slab) kernels.  Their workgroups
+ * exchange partial results inside one launch (apex PR #2018, Solution: a
+ * cooperative grid capped at the residency limit, so that every workgroup is
+ * resident and the global reduction can complete).  Every such wait is
+ * bounded: if the co-residency the launch guarantees were ever broken, a
+ * waiting workgroup gives up after spin_limit polls instead of hanging,
+ * ORs GN_STATUS_WAIT_EXPIRED into *status_word, and writes NaN to every
+ * output it would have derived from the incomplete exchange (y or dx
+ * elements, mean/rstd, dgamma/dbeta): no finite wrong value is written.
+ * The call itself has already returned GN_OK (it returns before the
+ * kernels run), so the report is read afterwards with gn_read_status. */
 typedef struct gn_options {
     int32_t force_path;             /* gn_path; GN_PATH_AUTO = planner's choice */
     int32_t max_resident_override;  /* > 0: cap the cooperative grid at this many
                                        workgroups (forces overflow tiles) */
     gn_plan_info* info;             /* host pointer, may be NULL */
-    void* event_begin;              /* hipEvent_t recorded on `stream` right before
-                                       the call's main kernel (GN_PATH_STREAM:
-                                       before its first kernel), or NULL */
-    void* event_end;                /* hipEvent_t recorded right after it
-                                       (GN_PATH_STREAM: after its last), or NULL */
+    void* event_begin;              /* hipEvent_t recorded on `stream` before the
+                                       call's first kernel, or NULL */
+    void* event_end;                /* hipEvent_t recorded after its last kernel, or NULL */
+    void* kernel_begin;             /* hipEvent_t recorded right before the call's
+                                       main kernel (GN_PATH_STREAM and
+                                       GN_PATH_GENERIC: before the first kernel), or NULL */
+    void* kernel_end;               /* recorded right after it (GN_PATH_STREAM and
+                                       GN_PATH_GENERIC: after the last kernel), or NULL */
+    uint32_t* status_word;          /* DEVICE pointer to one 32-bit word, or NULL:
+                                       the kernels OR GN_STATUS_WAIT_EXPIRED into it
+                                       when a wait gives up; never cleared by the
+                                       library (the caller zeroes it) */
+    uint32_t spin_limit;            /* polls before a wait gives up; 0 = default (2^25,
+                                       about a second) */
+    uint32_t debug_flags;           /* 0, or GN_DEBUG_UNMET_WAITS (tests only) */
 } gn_options;
 
 /* Workspace bytes gn_forward needs for these arguments (0 is possible).
@@ -247,6 +281,15 @@ gn_status gn_rms_backward(const void* dy, const void* x, const float* rstd, cons
                           int64_t N, int64_t C, int64_t G, gn_dtype dtype,
                           void* workspace, size_t ws_bytes, void* stream,
                           const gn_options* opts);
+
+/* Reads a status word that calls of this library OR their failure reports
+ * into (gn_options.status_word): waits for all work queued on `stream`
+ * (hipStreamSynchronize), copies the word to the host, and returns GN_OK
+ * when it is 0, GN_ERR_WAIT when it holds GN_STATUS_WAIT_EXPIRED, or
+ * GN_ERR_HIP when the synchronisation or the copy fails.  reset != 0 zeroes
+ * the word afterwards (a blocking copy).  *word_out (host pointer, may be
+ * NULL) receives the word as read.  Not for use under stream capture. */
+gn_status gn_read_status(uint32_t* status_word, void* stream, int32_t reset, uint32_t* word_out);
 
 /* Static description of a status code (never NULL). */
 const char* gn_status_string(gn_status status);

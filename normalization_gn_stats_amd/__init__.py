@@ -20,15 +20,16 @@ import ctypes
 import math
 
 from . import _lib
-from ._lib import (GN_BF16, GN_F16, GN_F32, GN_GRAD_DBETA, GN_GRAD_DGAMMA, GN_GRAD_DX, GN_NCHW, GN_NHWC,
-                   GN_PATH_AUTO, GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB, GN_PATH_STREAM, PATH_NAMES, GNError,
-                   PlanInfo)
+from ._lib import (GN_BF16, GN_DEBUG_UNMET_WAITS, GN_ERR_WAIT, GN_F16, GN_F32, GN_GRAD_DBETA, GN_GRAD_DGAMMA,
+                   GN_GRAD_DX, GN_NCHW, GN_NHWC, GN_OK, GN_PATH_AUTO, GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB,
+                   GN_PATH_STREAM, PATH_NAMES, GNError, PlanInfo)
 
 __all__ = ["forward", "backward", "forward_into", "backward_into", "forward_workspace_size",
            "backward_workspace_size", "forward_strided_workspace_size", "backward_strided_workspace_size",
            "strided_dims", "common_layout", "select_path", "layout_of", "GNError", "PlanInfo",
            "rms_forward", "rms_backward", "rms_forward_into", "rms_backward_into",
-           "rms_forward_workspace_size", "rms_backward_workspace_size",
+           "rms_forward_workspace_size", "rms_backward_workspace_size", "status_word", "read_status",
+           "Debug", "GN_OK", "GN_ERR_WAIT", "GN_DEBUG_UNMET_WAITS",
            "GN_GRAD_DX", "GN_GRAD_DGAMMA", "GN_GRAD_DBETA", "GN_PATH_AUTO", "GN_PATH_GENERIC",
            "GN_PATH_ROWS", "GN_PATH_SLAB", "GN_PATH_STREAM", "PATH_NAMES"]
 
@@ -130,7 +131,17 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _opts(force_path, max_resident, info, events):
+class Debug:
+    """Failure-report knobs of gn_options (tests): spin_limit polls before a
+    wait between workgroups gives up (0: the library's default); flags
+    GN_DEBUG_UNMET_WAITS makes every such wait give up."""
+
+    def __init__(self, spin_limit: int = 0, flags: int = 0):
+        self.spin_limit = int(spin_limit)
+        self.flags = int(flags)
+
+
+def _opts(force_path, max_resident, info, events, kernel_events=None, status=None, debug=None):
     o = _lib.Options()
     o.force_path = _PATHS[force_path] if not isinstance(force_path, int) else force_path
     o.max_resident_override = int(max_resident or 0)
@@ -138,7 +149,44 @@ def _opts(force_path, max_resident, info, events):
     if events is not None:
         o.event_begin = ctypes.c_void_p(events[0])
         o.event_end = ctypes.c_void_p(events[1])
+    if kernel_events is not None:
+        o.kernel_begin = ctypes.c_void_p(kernel_events[0])
+        o.kernel_end = ctypes.c_void_p(kernel_events[1])
+    if status is not None:
+        o.status_word = ctypes.c_void_p(_status_ptr(status))
+    if debug is not None:
+        o.spin_limit = debug.spin_limit
+        o.debug_flags = debug.flags
     return o
+
+
+def _status_ptr(t) -> int:
+    torch = _torch()
+    if t.device.type != "cuda" or t.dtype not in (torch.int32, torch.uint32) or t.numel() < 1:
+        raise ValueError("status must be a 32-bit integer tensor of at least one element on the device")
+    return t.data_ptr()
+
+
+def status_word(device=None):
+    """A zeroed device word for gn_options.status_word (int32 tensor of one
+    element): the kernels OR their failure reports into it."""
+    torch = _torch()
+    return torch.zeros(1, dtype=torch.int32, device=device if device is not None else "cuda")
+
+
+def read_status(status, reset: bool = True, stream=None) -> int:
+    """gn_read_status: waits for the stream, reads the word, returns GN_OK or
+    GN_ERR_WAIT (a bounded wait gave up: that call's outputs are NaN where
+    affected); zeroes the word when reset."""
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(status.device).cuda_stream
+    w = ctypes.c_uint32()
+    st = _lib.lib().gn_read_status(ctypes.c_void_p(_status_ptr(status)), ctypes.c_void_p(stream),
+                                   1 if reset else 0, ctypes.byref(w))
+    if st not in (GN_OK, GN_ERR_WAIT):
+        raise GNError(st, "gn_read_status")
+    return st
 
 
 def _check_f32_vec(t, C, name):
@@ -178,7 +226,7 @@ def select_path(backward: bool, N, C, HW, G, dtype_code, layout, force_path=None
 
 
 def forward_into(x, gamma, beta, num_groups, eps, y, mean, rstd, workspace, *, force_path=None,
-                 max_resident=0, info=None, events=None, stream=None):
+                 max_resident=0, info=None, events=None, kernel_events=None, status=None, debug=None, stream=None):
     """gn_forward (dense x and y in one layout) or gn_forward_strided (any
     other strides) on preallocated outputs; returns nothing, raises GNError."""
     torch = _torch()
@@ -190,7 +238,7 @@ def forward_into(x, gamma, beta, num_groups, eps, y, mean, rstd, workspace, *, f
     _check_f32_vec(beta, C, "beta")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    o = _opts(force_path, max_resident, info, events)
+    o = _opts(force_path, max_resident, info, events, kernel_events, status, debug)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if layout is not None:
         N, C, HW = _dims(x)
@@ -210,8 +258,10 @@ def forward_into(x, gamma, beta, num_groups, eps, y, mean, rstd, workspace, *, f
 
 
 def forward(x, gamma, beta, num_groups: int, eps: float = 1e-5, *, compute_y: bool = True, force_path=None,
-            max_resident: int = 0, info: PlanInfo | None = None):
-    """Returns (y, mean, rstd); y is None when compute_y is False."""
+            max_resident: int = 0, info: PlanInfo | None = None, status=None, debug: Debug | None = None):
+    """Returns (y, mean, rstd); y is None when compute_y is False.  status: a
+    device word (``status_word()``) that receives the failure report of the
+    cooperative kernels; read it with ``read_status``."""
     torch = _torch()
     if x.device.type != "cuda":
         raise ValueError("x must be on a HIP device")
@@ -232,12 +282,13 @@ def forward(x, gamma, beta, num_groups: int, eps: float = 1e-5, *, compute_y: bo
                                                  strides[1] if y is not None else None, force_path)
         ws = torch.empty(max(wsb, 1), device=x.device, dtype=torch.uint8)
         forward_into(x, gamma, beta, G, eps, y, mean, rstd, ws, force_path=force_path,
-                     max_resident=max_resident, info=info)
+                     max_resident=max_resident, info=info, status=status, debug=debug)
     return y, mean.view(N, G), rstd.view(N, G)
 
 
 def backward_into(dy, x, mean, rstd, gamma, num_groups, mask, dx, dgamma, dbeta, workspace, *,
-                  force_path=None, max_resident=0, info=None, events=None, stream=None):
+                  force_path=None, max_resident=0, info=None, events=None, kernel_events=None, status=None,
+                  debug=None, stream=None):
     """gn_backward (dy, x, dx dense in one layout) or gn_backward_strided (any
     other strides) on preallocated outputs; returns nothing, raises GNError."""
     torch = _torch()
@@ -251,7 +302,7 @@ def backward_into(dy, x, mean, rstd, gamma, num_groups, mask, dx, dgamma, dbeta,
     _check_f32_vec(gamma, C, "gamma")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    o = _opts(force_path, max_resident, info, events)
+    o = _opts(force_path, max_resident, info, events, kernel_events, status, debug)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if layout is not None:
         N, C, HW = _dims(x)
@@ -272,8 +323,10 @@ def backward_into(dy, x, mean, rstd, gamma, num_groups, mask, dx, dgamma, dbeta,
 
 
 def backward(dy, x, mean, rstd, gamma, num_groups: int, mask: int = GN_GRAD_DX | GN_GRAD_DGAMMA | GN_GRAD_DBETA,
-             *, force_path=None, max_resident: int = 0, info: PlanInfo | None = None):
-    """Returns (dx, dgamma, dbeta), each None when not selected by mask."""
+             *, force_path=None, max_resident: int = 0, info: PlanInfo | None = None, status=None,
+             debug: Debug | None = None):
+    """Returns (dx, dgamma, dbeta), each None when not selected by mask.
+    status, debug: as for ``forward``."""
     torch = _torch()
     if x.device.type != "cuda":
         raise ValueError("x must be on a HIP device")
@@ -292,7 +345,7 @@ def backward(dy, x, mean, rstd, gamma, num_groups: int, mask: int = GN_GRAD_DX |
                                                   strides[2] if dx is not None else None, mask, force_path)
         ws = torch.empty(max(wsb, 1), device=x.device, dtype=torch.uint8)
         backward_into(dy, x, mean.reshape(-1), rstd.reshape(-1), gamma, G, mask, dx, dgamma, dbeta, ws,
-                      force_path=force_path, max_resident=max_resident, info=info)
+                      force_path=force_path, max_resident=max_resident, info=info, status=status, debug=debug)
     return dx, dgamma, dbeta
 
 
@@ -314,14 +367,14 @@ def rms_backward_workspace_size(N, C, G, dtype_code, mask, force_path=None) -> i
 
 
 def rms_forward_into(x, gamma, num_groups, eps, y, rstd, workspace, *, force_path=None, info=None, events=None,
-                     stream=None):
+                     kernel_events=None, stream=None):
     """gn_rms_forward on preallocated outputs; returns nothing, raises GNError."""
     torch = _torch()
     N, C = _rows_dims(x)
     _check_f32_vec(gamma, C, "gamma")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    o = _opts(force_path, 0, info, events)
+    o = _opts(force_path, 0, info, events, kernel_events)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.lib().gn_rms_forward(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), N, C, int(num_groups), float(eps),
                                    _dtype_code(x), _ptr(workspace), ws_bytes, ctypes.c_void_p(stream),
@@ -349,7 +402,7 @@ def rms_forward(x, gamma, eps: float = 1e-6, num_groups: int = 1, *, compute_y: 
 
 
 def rms_backward_into(dy, x, rstd, gamma, num_groups, mask, dx, dgamma, workspace, *, force_path=None, info=None,
-                      events=None, stream=None):
+                      events=None, kernel_events=None, stream=None):
     """gn_rms_backward on preallocated outputs; returns nothing, raises GNError."""
     torch = _torch()
     N, C = _rows_dims(x)
@@ -358,7 +411,7 @@ def rms_backward_into(dy, x, rstd, gamma, num_groups, mask, dx, dgamma, workspac
     _check_f32_vec(gamma, C, "gamma")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    o = _opts(force_path, 0, info, events)
+    o = _opts(force_path, 0, info, events, kernel_events)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.lib().gn_rms_backward(_ptr(dy), _ptr(x), _ptr(rstd), _ptr(gamma), _ptr(dx), _ptr(dgamma), int(mask),
                                     N, C, int(num_groups), _dtype_code(x), _ptr(workspace), ws_bytes,

@@ -15,7 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # with different tile constants); by default the in-tree build is used.
 LIB_PATH = os.environ.get("GN_LIB_PATH") or os.path.join(HERE, "lib", "libgn_mi355x.so")
 
-GN_OK, GN_ERR_INVALID, GN_ERR_UNSUPPORTED, GN_ERR_WORKSPACE, GN_ERR_HIP = range(5)
+GN_OK, GN_ERR_INVALID, GN_ERR_UNSUPPORTED, GN_ERR_WORKSPACE, GN_ERR_HIP, GN_ERR_WAIT = range(6)
+GN_STATUS_WAIT_EXPIRED = 1
+GN_DEBUG_UNMET_WAITS = 1
 GN_F32, GN_F16, GN_BF16 = range(3)
 GN_NCHW, GN_NHWC = range(2)
 GN_GRAD_DX, GN_GRAD_DGAMMA, GN_GRAD_DBETA = 1, 2, 4
@@ -28,7 +30,7 @@ EXPORTED = ("gn_forward_workspace_size", "gn_forward", "gn_backward_workspace_si
             "gn_forward_strided_workspace_size", "gn_forward_strided", "gn_backward_strided_workspace_size",
             "gn_backward_strided",
             "gn_select_path", "gn_status_string", "gn_version", "gn_rms_forward_workspace_size",
-            "gn_rms_forward", "gn_rms_backward_workspace_size", "gn_rms_backward")
+            "gn_rms_forward", "gn_rms_backward_workspace_size", "gn_rms_backward", "gn_read_status")
 
 
 class PlanInfo(ctypes.Structure):
@@ -39,7 +41,9 @@ class PlanInfo(ctypes.Structure):
 class Options(ctypes.Structure):
     _fields_ = [("force_path", ctypes.c_int32), ("max_resident_override", ctypes.c_int32),
                 ("info", ctypes.POINTER(PlanInfo)), ("event_begin", ctypes.c_void_p),
-                ("event_end", ctypes.c_void_p)]
+                ("event_end", ctypes.c_void_p), ("kernel_begin", ctypes.c_void_p),
+                ("kernel_end", ctypes.c_void_p), ("status_word", ctypes.c_void_p),
+                ("spin_limit", ctypes.c_uint32), ("debug_flags", ctypes.c_uint32)]
 
 
 class GNError(RuntimeError):
@@ -90,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.gn_rms_backward_workspace_size.restype = sz
     L.gn_rms_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp, sz, vp, op]
     L.gn_rms_backward.restype = i32
+    L.gn_read_status.argtypes = [vp, vp, i32, ctypes.POINTER(ctypes.c_uint32)]
+    L.gn_read_status.restype = i32
     L.gn_status_string.argtypes = [i32]
     L.gn_status_string.restype = ctypes.c_char_p
     L.gn_version.restype = i32

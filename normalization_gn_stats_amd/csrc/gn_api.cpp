@@ -126,11 +126,24 @@ gn::Launch make_launch(void* ws, size_t ws_bytes, void* stream, const gn_options
     l.stream = (hipStream_t)stream;
     l.ws = ws;
     l.ws_bytes = ws_bytes;
-    l.ev_begin = opts ? (hipEvent_t)opts->event_begin : nullptr;
-    l.ev_end = opts ? (hipEvent_t)opts->event_end : nullptr;
+    l.ev_begin = opts ? (hipEvent_t)opts->kernel_begin : nullptr;
+    l.ev_end = opts ? (hipEvent_t)opts->kernel_end : nullptr;
     l.max_resident_override = opts ? opts->max_resident_override : 0;
     l.info = opts ? opts->info : nullptr;
+    l.status_word = opts ? opts->status_word : nullptr;
+    l.spin_limit = (opts && opts->spin_limit) ? opts->spin_limit : gn::kDefaultSpinLimit;
+    l.unmet_waits = (opts && (opts->debug_flags & GN_DEBUG_UNMET_WAITS)) ? 1u : 0u;
     return l;
+}
+
+// Runs one launcher between the caller's whole-call events (if any).
+template <typename F>
+gn_status with_call_events(const gn_options* opts, void* stream, F&& launch) {
+    hipStream_t s = (hipStream_t)stream;
+    if (opts && opts->event_begin && gn::record((hipEvent_t)opts->event_begin, s) != hipSuccess) return GN_ERR_HIP;
+    if (launch() != hipSuccess) return GN_ERR_HIP;
+    if (opts && opts->event_end && gn::record((hipEvent_t)opts->event_end, s) != hipSuccess) return GN_ERR_HIP;
+    return GN_OK;
 }
 
 }  // namespace
@@ -193,11 +206,12 @@ gn_status gn_forward(const void* x, const float* gamma, const float* beta, void*
     gn::FwdArgs a{x, gamma, beta, y, mean, rstd, eps};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
-    hipError_t e = path == GN_PATH_ROWS ? gn::rows_fwd(p, a, l)
-                 : path == GN_PATH_SLAB ? gn::slab_fwd(p, a, l)
-                 : path == GN_PATH_STREAM ? gn::stream_fwd(p, a, l)
-                                        : gn::generic_fwd(p, gn::dense_strides(p), a, l);
-    return e == hipSuccess ? GN_OK : GN_ERR_HIP;
+    return with_call_events(opts, stream, [&] {
+        return path == GN_PATH_ROWS ? gn::rows_fwd(p, a, l)
+             : path == GN_PATH_SLAB ? gn::slab_fwd(p, a, l)
+             : path == GN_PATH_STREAM ? gn::stream_fwd(p, a, l)
+                                    : gn::generic_fwd(p, gn::dense_strides(p), a, l);
+    });
 }
 
 gn_status gn_backward(const void* dy, const void* x, const float* mean, const float* rstd, const float* gamma,
@@ -235,11 +249,12 @@ gn_status gn_backward(const void* dy, const void* x, const float* mean, const fl
                   (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
-    hipError_t e = path == GN_PATH_ROWS ? gn::rows_bwd(p, a, l)
-                 : path == GN_PATH_SLAB ? gn::slab_bwd(p, a, l)
-                 : path == GN_PATH_STREAM ? gn::stream_bwd(p, a, l)
-                                        : gn::generic_bwd(p, gn::dense_strides(p), a, l);
-    return e == hipSuccess ? GN_OK : GN_ERR_HIP;
+    return with_call_events(opts, stream, [&] {
+        return path == GN_PATH_ROWS ? gn::rows_bwd(p, a, l)
+             : path == GN_PATH_SLAB ? gn::slab_bwd(p, a, l)
+             : path == GN_PATH_STREAM ? gn::stream_bwd(p, a, l)
+                                    : gn::generic_bwd(p, gn::dense_strides(p), a, l);
+    });
 }
 
 // ---- strided tensors ---------------------------------------------------------
@@ -372,7 +387,7 @@ gn_status gn_forward_strided(const void* x, const int64_t* x_strides, const floa
     gn::FwdArgs a{x, gamma, beta, y, mean, rstd, eps};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{GN_PATH_GENERIC, 0, 0, 0, 0, 0};
-    return gn::generic_fwd(p, sd, a, l) == hipSuccess ? GN_OK : GN_ERR_HIP;
+    return with_call_events(opts, stream, [&] { return gn::generic_fwd(p, sd, a, l); });
 }
 
 size_t gn_backward_strided_workspace_size(int64_t N, int64_t C, int64_t H, int64_t W, int64_t G, gn_dtype dtype,
@@ -425,7 +440,7 @@ gn_status gn_backward_strided(const void* dy, const int64_t* dy_strides, const v
                   (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{GN_PATH_GENERIC, 0, 0, 0, 0, 0};
-    return gn::generic_bwd(p, sd, a, l) == hipSuccess ? GN_OK : GN_ERR_HIP;
+    return with_call_events(opts, stream, [&] { return gn::generic_bwd(p, sd, a, l); });
 }
 
 // ---- RMSNorm over rows: the rows kernels with the mean taken as 0 ----------
@@ -465,7 +480,7 @@ gn_status gn_rms_forward(const void* x, const float* gamma, void* y, float* rstd
     gn::FwdArgs a{x, gamma, nullptr, y, nullptr, rstd, eps, 1};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{GN_PATH_ROWS, 0, 0, 0, 0, 0};
-    return gn::rows_fwd(p, a, l) == hipSuccess ? GN_OK : GN_ERR_HIP;
+    return with_call_events(opts, stream, [&] { return gn::rows_fwd(p, a, l); });
 }
 
 size_t gn_rms_backward_workspace_size(int64_t N, int64_t C, int64_t G, gn_dtype dtype, int32_t mask,
@@ -500,7 +515,29 @@ gn_status gn_rms_backward(const void* dy, const void* x, const float* rstd, cons
                   nullptr, mask, 1};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{GN_PATH_ROWS, 0, 0, 0, 0, 0};
-    return gn::rows_bwd(p, a, l) == hipSuccess ? GN_OK : GN_ERR_HIP;
+    return with_call_events(opts, stream, [&] { return gn::rows_bwd(p, a, l); });
+}
+
+gn_status gn_read_status(uint32_t* status_word, void* stream, int32_t reset, uint32_t* word_out) {
+    if (status_word == nullptr) return GN_ERR_INVALID;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return GN_ERR_HIP;
+    }
+    uint32_t w = 0;
+    if (hipMemcpy(&w, status_word, sizeof(w), hipMemcpyDeviceToHost) != hipSuccess) {
+        (void)hipGetLastError();
+        return GN_ERR_HIP;
+    }
+    if (word_out) *word_out = w;
+    if (reset) {
+        const uint32_t zero = 0;
+        if (hipMemcpy(status_word, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipGetLastError();
+            return GN_ERR_HIP;
+        }
+    }
+    return (w & GN_STATUS_WAIT_EXPIRED) ? GN_ERR_WAIT : GN_OK;
 }
 
 const char* gn_status_string(gn_status s) {
@@ -510,10 +547,11 @@ const char* gn_status_string(gn_status s) {
         case GN_ERR_UNSUPPORTED: return "unsupported dtype, layout or forced path";
         case GN_ERR_WORKSPACE: return "workspace too small";
         case GN_ERR_HIP: return "HIP launch failed";
+        case GN_ERR_WAIT: return "a bounded wait between cooperating workgroups gave up; the call's outputs are NaN where affected";
         default: return "unknown status";
     }
 }
 
-int32_t gn_version(void) { return 300; }
+int32_t gn_version(void) { return 400; }
 
 }  // extern "C"

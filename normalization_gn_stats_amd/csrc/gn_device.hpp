@@ -224,10 +224,11 @@ __device__ inline Stat stat_of(const float (&v)[K], int valid) {
     return Stat{n, m, q};
 }
 
-// Spin limit of the barriers: far above any legitimate wait (the longest are a
-// few milliseconds); on expiry the wave stops waiting and raises *err, so that
-// a broken co-residency assumption shows as an error flag instead of a hang.
-constexpr uint32_t kSpinLimit = 1u << 25;
+// Failure report of a bounded wait (the bit the host API calls
+// GN_STATUS_WAIT_EXPIRED): a wait that gives up ORs it into the call's status
+// word instead of hanging, and its workgroup writes NaN wherever it would
+// have used the missing data.
+constexpr uint32_t kWaitExpired = 1u;
 
 // ---------------------------------------------------------------------------
 // exchange between the workgroups of one launch without cache maintenance
@@ -278,23 +279,34 @@ __device__ inline void team_arrive(uint32_t* ctr) {
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline void team_wait(uint32_t* ctr, uint32_t target, uint32_t* err) {
+// Returns true when every member arrived; false when the wait gave up after
+// `limit` polls (then kWaitExpired is ORed into *err).  `unmet` = 1 raises the
+// target out of reach (tests of the failure report).  The result is the same
+// for every thread of the workgroup.
+__device__ inline bool team_wait(uint32_t* ctr, uint32_t target, uint32_t* err, uint32_t limit, uint32_t unmet) {
+    __shared__ uint32_t s_gave_up;
     if (threadIdx.x == 0) {
-        uint32_t spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        uint32_t spins = 0, gave_up = 0;
+        const uint32_t goal = target + unmet;
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < goal) {
             __builtin_amdgcn_s_sleep(2);
-            if (++spins > kSpinLimit) {   // bounded: report instead of hanging
-                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (++spins > limit) {   // bounded: report instead of hanging
+                __hip_atomic_fetch_or(err, kWaitExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                gave_up = 1;
                 break;
             }
         }
+        s_gave_up = gave_up;
     }
     __syncthreads();
+    const bool ok = s_gave_up == 0;
+    __syncthreads();   // every thread has read the flag before thread 0 can write it again
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return ok;
 }
-__device__ inline void team_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+__device__ inline bool team_barrier(uint32_t* ctr, uint32_t target, uint32_t* err, uint32_t limit, uint32_t unmet) {
     team_arrive(ctr);
-    team_wait(ctr, target, err);
+    return team_wait(ctr, target, err, limit, unmet);
 }
 
 }  // namespace gn

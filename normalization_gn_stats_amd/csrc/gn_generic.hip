@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kWave) void gen_stats_final(const float4* __restric
     st = wave_merge_strided(st, 1);
     if (lane == 0) {
         float var = st.m2 / (float)M;
-        var = var > 0.f ? var : 0.f;
+        var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
         mean[s] = st.mean;
         rstd[s] = 1.0f / sqrtf(var + eps);
     }

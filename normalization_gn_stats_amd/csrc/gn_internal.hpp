@@ -51,11 +51,19 @@ struct Launch {
     hipStream_t stream;
     void* ws;              // device workspace (may be NULL when its size is 0)
     size_t ws_bytes;
-    hipEvent_t ev_begin;   // recorded around the main kernel when not NULL
-    hipEvent_t ev_end;
+    hipEvent_t ev_begin;   // recorded around the main kernel when not NULL (the
+    hipEvent_t ev_end;     // C ABI records the whole-call events itself)
     int32_t max_resident_override;
     gn_plan_info* info;    // may be NULL
+    uint32_t* status_word; // device word for failure reports, or NULL
+    uint32_t spin_limit;   // polls before a bounded wait gives up (never 0)
+    uint32_t unmet_waits;  // 1: every wait's target out of reach (failure-report tests)
 };
+
+// Polls before a bounded wait between workgroups gives up (2^25 polls with a
+// short sleep each: about a second, far above the longest legitimate wait of
+// a few milliseconds).
+constexpr uint32_t kDefaultSpinLimit = 1u << 25;
 
 // Device facts used by the planner (queried once per device).
 struct DeviceInfo {

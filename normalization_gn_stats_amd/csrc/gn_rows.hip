@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_k(const T* __restrict__ x, const 
         }
     }
     float var = wave_sum(q) * invD;
-    var = var > 0.f ? var : 0.f;
+    var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
     const float r = 1.0f / sqrtf(var + eps);
     if (lane == 0) {
         if (mean) mean[s] = mu;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_cs_k(const T* __restrict__ x, con
 #pragma unroll
     for (int k = 1; k < CS; ++k) t += red[1][slot * CS + k];
     float var = t * invD;
-    var = var > 0.f ? var : 0.f;
+    var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
     const float r = 1.0f / sqrtf(var + eps);
     if (!live) return;
     if (cpart == 0 && lane == 0) {
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, co
             }
         }
         float var = wave_sum(q) * invD;
-        var = var > 0.f ? var : 0.f;
+        var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
         const float r = 1.0f / sqrtf(var + eps);
         const int64_t sl = n * G + g;
         if (lane == 0) {
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kT) void rows_fwd_narrow_k(const T* __restrict__ x,
             }
         }
         float var = seg_sum<LPR>(q) * invD;
-        var = var > 0.f ? var : 0.f;
+        var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
         const float rs = 1.0f / sqrtf(var + eps);
         if (n < N) {
             if (vi == 0) {

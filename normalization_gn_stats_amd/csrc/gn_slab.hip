@@ -46,7 +46,11 @@ struct SlabCfg {
     int32_t want_dx;   // backward: write dx
     float* dgamma;     // backward, one-slab case: written by the finalizers
     float* dbeta;
+    uint32_t spin_limit;   // polls before a wait between workgroups gives up
+    uint32_t unmet;        // 1: every wait's target out of reach (failure-report tests)
 };
+
+__device__ inline float qnan() { return __uint_as_float(0x7FC00000u); }
 
 // ============================================================================
 // NHWC
@@ -180,7 +184,9 @@ __global__ __launch_bounds__(kT) void slab_nhwc_fwd(const T* __restrict__ x, con
             tile = ntile;
         }
         if (last >= 0 && t == 0) __hip_atomic_store(&res[sb * cfg.tiles + last], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        team_barrier(&sw[0], (uint32_t)cfg.team, err);
+        // a member whose wait gave up merges incomplete partials: it writes
+        // NaN statistics instead (and, after the second wait, NaN outputs)
+        const bool all_tiles = team_barrier(&sw[0], (uint32_t)cfg.team, err, cfg.spin_limit, cfg.unmet);
 
         // ---- distributed finalize: member m owns groups m, m + team, ... ----
         // tile partials merged in tile order: mean = sum(n_i*mean_i)/sum(n_i),
@@ -207,19 +213,19 @@ __global__ __launch_bounds__(kT) void slab_nhwc_fwd(const T* __restrict__ x, con
             block_sum<1, kNW>(m2, lds);
             if (t == 0) {
                 float var = m2[0] / (float)(cfg.D * cfg.HW);
-                var = var > 0.f ? var : 0.f;
-                xstore(&mean[n * G + g], mu);
-                xstore(&rstd[n * G + g], 1.0f / sqrtf(var + cfg.eps));
+                var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
+                xstore(&mean[n * G + g], all_tiles ? mu : qnan());
+                xstore(&rstd[n * G + g], all_tiles ? 1.0f / sqrtf(var + cfg.eps) : qnan());
             }
         }
-        team_barrier(&sw[1], (uint32_t)cfg.team, err);
+        const bool all_stats = team_barrier(&sw[1], (uint32_t)cfg.team, err, cfg.spin_limit, cfg.unmet);
         if (y == nullptr) continue;
 
         // ---- phase 2: normalize + affine; the resident tile, then tiles
         // drawn in reverse order (next tile's loads issued before the current
         // one is written); streaming stores for y ----
-        const float mu = xload(&mean[n * G + gq]);
-        const float r = xload(&rstd[n * G + gq]);
+        const float mu = all_stats ? xload(&mean[n * G + gq]) : qnan();
+        const float r = all_stats ? xload(&rstd[n * G + gq]) : qnan();
         float a[V], b[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
@@ -339,7 +345,8 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
             tile = ntile;
         }
         if (last >= 0 && t == 0) __hip_atomic_store(&res[sb * cfg.tiles + last], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        team_barrier(&sw[0], (uint32_t)cfg.team, err);
+        // a member whose wait gave up writes NaN channel sums (and dx below)
+        const bool all_tiles = team_barrier(&sw[0], (uint32_t)cfg.team, err, cfg.spin_limit, cfg.unmet);
 
         // ---- distributed finalize: member m owns channels m, m + team, ...
         // (plain loads of the tile partials: see slab_nhwc_fwd) ----
@@ -353,13 +360,14 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
             }
             block_sum<2, kNW>(acc, lds);
             if (t == 0) {
+                if (!all_tiles) acc[0] = acc[1] = qnan();
                 xstore2(&stot[n * C + c], make_float2(acc[0], acc[1]));
                 if (cfg.dbeta) cfg.dbeta[c] = acc[0];     // one-slab case: final already
                 if (cfg.dgamma) cfg.dgamma[c] = acc[1];
             }
         }
         if (!cfg.want_dx) continue;   // uniform over the grid: no member waits below
-        team_barrier(&sw[1], (uint32_t)cfg.team, err);
+        const bool all_sums = team_barrier(&sw[1], (uint32_t)cfg.team, err, cfg.spin_limit, cfg.unmet);
 
         // ---- phase 2: dx = rstd*(gamma_c*dy - A/M - xhat*B/M) ----
         float A = 0.f, B = 0.f;
@@ -370,8 +378,8 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
             B = fmaf(ga, v.y, B);
         }
         const float invM = 1.0f / (float)(cfg.D * cfg.HW);
-        A *= invM;
-        B *= invM;
+        A = all_sums ? A * invM : qnan();
+        B = all_sums ? B * invM : qnan();
         float ga[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) ga[k] = gamma ? gamma[q * V + k] : 1.f;
@@ -451,14 +459,18 @@ __device__ inline uint64_t peek_partial(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Waits (bounded: on expiry raises *err and returns NaNs) until *p is
-// published, w being a first read of it; returns (lo, hi).
-__device__ inline float2 settle_partial(const uint64_t* p, uint64_t w, uint32_t* err) {
+// Waits until *p is published, w being a first read of it; returns (lo, hi).
+// Bounded: after cfg.spin_limit polls it ORs kWaitExpired into *err and
+// returns NaNs, which every sum, statistic and output derived from the
+// partial then carries.  cfg.unmet (tests of the failure report) makes every
+// word read as unpublished.
+__device__ inline float2 settle_partial(const uint64_t* p, uint64_t w, const SlabCfg& cfg, uint32_t* err) {
     uint32_t spins = 0;
-    while (unpublished(w)) {
+    while (unpublished(w) || cfg.unmet) {
         __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
-            __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (++spins > cfg.spin_limit) {
+            __hip_atomic_fetch_or(err, kWaitExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            w = ~0ull;   // both halves NaN
             break;
         }
         w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -466,8 +478,8 @@ __device__ inline float2 settle_partial(const uint64_t* p, uint64_t w, uint32_t*
     return make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
 }
 
-__device__ inline float2 poll_partial(const uint64_t* p, uint32_t* err) {
-    return settle_partial(p, peek_partial(p), err);
+__device__ inline float2 poll_partial(const uint64_t* p, const SlabCfg& cfg, uint32_t* err) {
+    return settle_partial(p, peek_partial(p), cfg, err);
 }
 
 // Elements of NCHW tile `tile` (the last tile of each channel plane may be
@@ -600,14 +612,14 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
         const int64_t i = t + (int64_t)k * kT;
         keep[k] = make_float2(0.f, 0.f);
         if (i < cfg.tiles) {
-            keep[k] = settle_partial(ps + i, w[k], err);
+            keep[k] = settle_partial(ps + i, w[k], cfg, err);
             const float c = nchw_tile_count(cfg, i, TE);
             sums[0] = fmaf(c, keep[k].x, sums[0]);
             sums[1] += c;
         }
     }
     for (int64_t i = t + (int64_t)kKeep * kT; i < cfg.tiles; i += kT) {
-        const float2 v = poll_partial(ps + i, err);
+        const float2 v = poll_partial(ps + i, cfg, err);
         const float c = nchw_tile_count(cfg, i, TE);
         sums[0] = fmaf(c, v.x, sums[0]);
         sums[1] += c;
@@ -625,14 +637,14 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
         }
     }
     for (int64_t i = t + (int64_t)kKeep * kT; i < cfg.tiles; i += kT) {
-        const float2 v = poll_partial(ps + i, err);   // published: returns at once
+        const float2 v = poll_partial(ps + i, cfg, err);   // published: returns at once
         const float c = nchw_tile_count(cfg, i, TE);
         const float d = v.x - mu;
         m2[0] += fmaf(c * d, d, v.y);
     }
     block_sum<1, kNW>(m2, lds);
     float var = m2[0] / (float)(cfg.D * cfg.HW);
-    var = var > 0.f ? var : 0.f;
+    var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
     const float r = 1.0f / sqrtf(var + cfg.eps);
     if (m == 0 && t == 0) {
         mean[sb] = mu;
@@ -770,7 +782,7 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t i = t + (int64_t)k * kT;
-            if (i < cnt) stage[i] = settle_partial(ps + i, w[k], err);
+            if (i < cnt) stage[i] = settle_partial(ps + i, w[k], cfg, err);
         }
         __syncthreads();
         if (t < cfg.D) {
@@ -1074,6 +1086,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     SlabCfg cfg = pl.cfg;
     cfg.N = p.N; cfg.C = p.C; cfg.HW = p.HW; cfg.G = p.G; cfg.D = p.D; cfg.eps = a.eps;
     cfg.want_dx = 0; cfg.dgamma = nullptr; cfg.dbeta = nullptr;
+    cfg.spin_limit = l.spin_limit; cfg.unmet = l.unmet_waits;
     int64_t nteams = cap / cfg.team;
     if (nteams > cfg.n_slabs) nteams = cfg.n_slabs;
     if (nteams < 1) nteams = 1;
@@ -1081,7 +1094,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     const int64_t grid = nteams * cfg.team;
     char* ws = (char*)l.ws;
     uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
-    uint32_t* err = (uint32_t*)(ws + pl.off_err);
+    uint32_t* err = l.status_word ? l.status_word : (uint32_t*)(ws + pl.off_err);
     void* part = ws + pl.off_part;   // NHWC: float4 per (group, tile); NCHW: one word per tile
     uint32_t* res = (uint32_t*)(ws + pl.off_res);
     hipError_t e;
@@ -1124,6 +1137,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     const bool one_slab_params = nhwc && p.N == 1;
     cfg.dgamma = one_slab_params ? a.dgamma : nullptr;
     cfg.dbeta = one_slab_params ? a.dbeta : nullptr;
+    cfg.spin_limit = l.spin_limit; cfg.unmet = l.unmet_waits;
     int64_t nteams = cap / cfg.team;
     if (nteams > cfg.n_slabs) nteams = cfg.n_slabs;
     if (nteams < 1) nteams = 1;
@@ -1131,7 +1145,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     const int64_t grid = nteams * cfg.team;
     char* ws = (char*)l.ws;
     uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
-    uint32_t* err = (uint32_t*)(ws + pl.off_err);
+    uint32_t* err = l.status_word ? l.status_word : (uint32_t*)(ws + pl.off_err);
     void* part = ws + pl.off_part;   // NHWC: float2 per (channel, tile); NCHW: one word per tile
     float2* stot = (float2*)(ws + pl.off_stot);
     uint32_t* res = (uint32_t*)(ws + pl.off_res);

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kFinT) void fwd_finalize(const float4* __restrict__
     block_sum<1, kFinNW>(m2, lds);
     if (t == 0) {
         float var = m2[0] / (float)(cfg.D * cfg.HW);
-        var = var > 0.f ? var : 0.f;
+        var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
         mean[sg] = mu;
         rstd[sg] = 1.0f / sqrtf(var + cfg.eps);
     }

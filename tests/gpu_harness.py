@@ -59,17 +59,22 @@ def img64(t: torch.Tensor, layout: str) -> np.ndarray:
 
 
 def run_gpu(wl, data, force_path=None, mask=ALL, max_resident=0):
-    """Returns dict of GPU outputs (torch tensors on the device) and the plans."""
+    """Returns dict of GPU outputs (torch tensors on the device) and the plans.
+    Both calls report into a status word, which must read GN_OK afterwards
+    (no bounded wait between workgroups gave up)."""
     dev = torch.device("cuda", 0)
     x = data["x"].to(dev)
     dy = data["dy"].to(dev)
     gamma = data["gamma"].to(dev)
     beta = data["beta"].to(dev)
     fi, bi = gn.PlanInfo(), gn.PlanInfo()
+    status = gn.status_word(dev)
     y, mean, rstd = gn.forward(x, gamma, beta, wl.G, wl.eps, force_path=force_path, max_resident=max_resident,
-                               info=fi)
+                               info=fi, status=status)
+    assert gn.read_status(status) == gn.GN_OK, f"{wl.name}: a forward wait gave up"
     dx, dg, db = gn.backward(dy, x, mean, rstd, gamma, wl.G, mask, force_path=force_path,
-                             max_resident=max_resident, info=bi)
+                             max_resident=max_resident, info=bi, status=status)
+    assert gn.read_status(status) == gn.GN_OK, f"{wl.name}: a backward wait gave up"
     torch.cuda.synchronize()
     return dict(y=y, mean=mean, rstd=rstd, dx=dx, dgamma=dg, dbeta=db, fwd_plan=fi, bwd_plan=bi)
 

@@ -50,9 +50,33 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(5):
+    for s in range(6):
         assert L.gn_status_string(s)
+    assert L.gn_status_string(_lib.GN_ERR_WAIT) != L.gn_status_string(99)
     assert L.gn_version() >= 100
+
+
+def test_read_status_rejects_null_word(L):
+    # checked before any HIP call
+    assert L.gn_read_status(None, None, 0, None) == _lib.GN_ERR_INVALID
+
+
+def test_options_layout_matches_header():
+    """The binding's gn_options mirrors the header's struct (size and field
+    offsets), checked against a C program compiled from include/gn.h."""
+    import tempfile
+    names = [f[0] for f in _lib.Options._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"gn.h\"\nint main(void){printf(\"%zu\\n\", sizeof(gn_options));"
+    for n in names:
+        src += f'printf("%zu\\n", offsetof(gn_options, {n}));'
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "o.c"), os.path.join(d, "o")
+        open(c, "w").write(src)
+        subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), c, "-o", exe])
+        got = [int(v) for v in subprocess.check_output([exe], text=True).split()]
+    assert got[0] == ctypes.sizeof(_lib.Options)
+    assert got[1:] == [getattr(_lib.Options, n).offset for n in names]
 
 
 def fwd(L, x=FAKE, g=None, b=None, y=FAKE, m=FAKE, r=FAKE, N=2, C=8, HW=4, G=2, eps=1e-5, dt=F32, lay=NCHW,

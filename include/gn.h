@@ -179,6 +179,33 @@ gn_status gn_backward(const void* dy, const void* x,
                       void* workspace, size_t ws_bytes, void* stream,
                       const gn_options* opts);
 
+/* Size of the static device array behind gn_backward_scratch (bytes). */
+#define GN_SCRATCH_BYTES (32u << 20)
+
+/*
+ * gn_backward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The library's own workspace is a static device array
+ * of GN_SCRATCH_BYTES (32 MiB), one per device the library runs on, held until
+ * the process ends; the call allocates nothing and calls no allocating
+ * routine.  Returns GN_ERR_WORKSPACE, before anything is enqueued, when the
+ * call would need more than that (gn_backward_workspace_size for the same
+ * arguments above GN_SCRATCH_BYTES; e.g. the generic path's partials for
+ * large unaligned or oddly shaped tensors), and GN_ERR_HIP when the array's
+ * device address cannot be obtained (the first call on each device looks it
+ * up, with that device current).  Every call on one device shares that
+ * device's array, and each call re-initialises what it needs of it: calls
+ * whose work overlaps on one device (other streams, other host threads)
+ * race and give undefined results -- serialise them.  Inputs, outputs,
+ * options, errors and results are those of gn_backward.
+ */
+gn_status gn_backward_scratch(const void* dy, const void* x,
+                              const float* mean, const float* rstd, const float* gamma,
+                              void* dx, float* dgamma, float* dbeta, int32_t mask,
+                              int64_t N, int64_t C, int64_t HW, int64_t G,
+                              gn_dtype dtype, gn_layout layout, void* stream,
+                              const gn_options* opts);
+
 /* The path gn_forward (backward = 0) or gn_backward (backward = 1) would take
  * for these arguments, without enqueuing anything.  Returns a gn_path, or -1
  * for arguments the call would reject. */

@@ -24,7 +24,7 @@ from ._lib import (GN_BF16, GN_DEBUG_UNMET_WAITS, GN_ERR_WAIT, GN_F16, GN_F32, G
                    GN_GRAD_DX, GN_NCHW, GN_NHWC, GN_OK, GN_PATH_AUTO, GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB,
                    GN_PATH_STREAM, PATH_NAMES, GNError, PlanInfo)
 
-__all__ = ["forward", "backward", "forward_into", "backward_into", "forward_workspace_size",
+__all__ = ["forward", "backward", "forward_into", "backward_into", "backward_scratch_into", "forward_workspace_size",
            "backward_workspace_size", "forward_strided_workspace_size", "backward_strided_workspace_size",
            "strided_dims", "common_layout", "select_path", "layout_of", "GNError", "PlanInfo",
            "rms_forward", "rms_backward", "rms_forward_into", "rms_backward_into",
@@ -320,6 +320,34 @@ def backward_into(dy, x, mean, rstd, gamma, num_groups, mask, dx, dgamma, dbeta,
                                         _ptr(workspace), ws_bytes, ctypes.c_void_p(stream), ctypes.byref(o))
     if st != 0:
         raise GNError(st, "gn_backward_strided")
+
+
+def backward_scratch_into(dy, x, mean, rstd, gamma, num_groups, mask, dx, dgamma, dbeta, *, force_path=None,
+                          max_resident=0, info=None, events=None, kernel_events=None, status=None, debug=None,
+                          stream=None):
+    """gn_backward_scratch: gn_backward on preallocated outputs with the
+    library's static device scratch instead of a workspace (dense dy, x, dx
+    in one layout); returns nothing, raises GNError."""
+    torch = _torch()
+    if tuple(dy.shape) != tuple(x.shape) or dy.dtype != x.dtype:
+        raise ValueError("dy must match x in shape and dtype")
+    if dx is not None and (tuple(dx.shape) != tuple(x.shape) or dx.dtype != x.dtype):
+        raise ValueError("dx must match x in shape and dtype")
+    want_dx = bool(int(mask) & GN_GRAD_DX) and dx is not None
+    layout = common_layout(dy, x, dx if want_dx else None)
+    if layout is None:
+        raise ValueError("gn_backward_scratch takes dense tensors in one layout")
+    C = int(x.shape[1])
+    _check_f32_vec(gamma, C, "gamma")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    o = _opts(force_path, max_resident, info, events, kernel_events, status, debug)
+    N, C, HW = _dims(x)
+    st = _lib.lib().gn_backward_scratch(_ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd), _ptr(gamma), _ptr(dx),
+                                        _ptr(dgamma), _ptr(dbeta), int(mask), N, C, HW, int(num_groups),
+                                        _dtype_code(x), layout, ctypes.c_void_p(stream), ctypes.byref(o))
+    if st != 0:
+        raise GNError(st, "gn_backward_scratch")
 
 
 def backward(dy, x, mean, rstd, gamma, num_groups: int, mask: int = GN_GRAD_DX | GN_GRAD_DGAMMA | GN_GRAD_DBETA,

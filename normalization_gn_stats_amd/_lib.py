@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("GN_LIB_PATH") or os.path.join(HERE, "lib", "libgn_mi3
 GN_OK, GN_ERR_INVALID, GN_ERR_UNSUPPORTED, GN_ERR_WORKSPACE, GN_ERR_HIP, GN_ERR_WAIT = range(6)
 GN_STATUS_WAIT_EXPIRED = 1
 GN_DEBUG_UNMET_WAITS = 1
+GN_SCRATCH_BYTES = 32 << 20
 GN_F32, GN_F16, GN_BF16 = range(3)
 GN_NCHW, GN_NHWC = range(2)
 GN_GRAD_DX, GN_GRAD_DGAMMA, GN_GRAD_DBETA = 1, 2, 4
@@ -30,7 +31,8 @@ EXPORTED = ("gn_forward_workspace_size", "gn_forward", "gn_backward_workspace_si
             "gn_forward_strided_workspace_size", "gn_forward_strided", "gn_backward_strided_workspace_size",
             "gn_backward_strided",
             "gn_select_path", "gn_status_string", "gn_version", "gn_rms_forward_workspace_size",
-            "gn_rms_forward", "gn_rms_backward_workspace_size", "gn_rms_backward", "gn_read_status")
+            "gn_rms_forward", "gn_rms_backward_workspace_size", "gn_rms_backward", "gn_read_status",
+            "gn_backward_scratch")
 
 
 class PlanInfo(ctypes.Structure):
@@ -94,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.gn_rms_backward_workspace_size.restype = sz
     L.gn_rms_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp, sz, vp, op]
     L.gn_rms_backward.restype = i32
+    L.gn_backward_scratch.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, i32, vp, op]
+    L.gn_backward_scratch.restype = i32
     L.gn_read_status.argtypes = [vp, vp, i32, ctypes.POINTER(ctypes.c_uint32)]
     L.gn_read_status.restype = i32
     L.gn_status_string.argtypes = [i32]

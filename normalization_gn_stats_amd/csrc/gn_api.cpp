@@ -53,6 +53,14 @@ hipError_t record(hipEvent_t ev, hipStream_t s) {
 
 using gn::Problem;
 
+// A static device array for callers that cannot allocate: the workspace of
+// gn_backward_scratch (each device holds its own copy).  In host code its name
+// is only a handle; the device address of each device's copy comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed
+// to kernels.
+static constexpr size_t kScratchBytes = (size_t)GN_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -146,6 +154,80 @@ gn_status with_call_events(const gn_options* opts, void* stream, F&& launch) {
     return GN_OK;
 }
 
+// ---- the backward, with the caller's workspace or the library's scratch ----
+void* g_scratch[64];
+bool g_scratch_ok[64];
+std::mutex g_scratch_mu;
+
+// This device's address of `scratch` (the current device), or NULL on failure.
+void* scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ok[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch[dev] = ptr;
+        g_scratch_ok[dev] = true;
+    }
+    return g_scratch[dev];
+}
+
+gn_status backward_call(const void* dy, const void* x, const float* mean, const float* rstd, const float* gamma,
+                        void* dx, float* dgamma, float* dbeta, int32_t mask, int64_t N, int64_t C, int64_t HW,
+                        int64_t G, gn_dtype dtype, gn_layout layout, void* workspace, size_t ws_bytes,
+                        bool use_scratch, void* stream, const gn_options* opts) {
+    Problem p;
+    gn_status st = make_problem(N, C, HW, G, dtype, layout, &p);
+    if (st != GN_OK) return st;
+    if (mask <= 0 || mask > 7) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DX) && dx == nullptr) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DGAMMA) && dgamma == nullptr) return GN_ERR_INVALID;
+    if ((mask & GN_GRAD_DBETA) && dbeta == nullptr) return GN_ERR_INVALID;
+    if ((mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) && gamma == nullptr) return GN_ERR_INVALID;
+    if (zero_extent(p)) {
+        if (opts && opts->info) *opts->info = gn_plan_info{GN_PATH_AUTO, 0, 0, 0, 0, 0};
+        return GN_OK;
+    }
+    if (dy == nullptr || x == nullptr || mean == nullptr || rstd == nullptr) return GN_ERR_INVALID;
+    int32_t path = plan(p, true, opts);
+    if (path < 0) return GN_ERR_UNSUPPORTED;
+    if (path != GN_PATH_GENERIC) {
+        const bool al = aligned16(dy) && aligned16(x) && aligned16(gamma) &&
+                        (!(mask & GN_GRAD_DX) || aligned16(dx));
+        if (!al) {
+            if (forced(opts) != GN_PATH_AUTO) return GN_ERR_UNSUPPORTED;
+            path = GN_PATH_GENERIC;
+        }
+    }
+    const size_t need = bwd_ws(p, mask, path);
+    if (use_scratch) {
+        if (need > kScratchBytes) return GN_ERR_WORKSPACE;
+        workspace = need > 0 ? scratch_address() : nullptr;
+        if (need > 0 && workspace == nullptr) return GN_ERR_HIP;
+        ws_bytes = kScratchBytes;
+    }
+    if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
+    gn::BwdArgs a{dy, x, mean, rstd, gamma,
+                  (mask & GN_GRAD_DX) ? dx : nullptr,
+                  (mask & GN_GRAD_DGAMMA) ? dgamma : nullptr,
+                  (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask};
+    gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
+    if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
+    return with_call_events(opts, stream, [&] {
+        return path == GN_PATH_ROWS ? gn::rows_bwd(p, a, l)
+             : path == GN_PATH_SLAB ? gn::slab_bwd(p, a, l)
+             : path == GN_PATH_STREAM ? gn::stream_bwd(p, a, l)
+                                    : gn::generic_bwd(p, gn::dense_strides(p), a, l);
+    });
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,43 +300,16 @@ gn_status gn_backward(const void* dy, const void* x, const float* mean, const fl
                       void* dx, float* dgamma, float* dbeta, int32_t mask, int64_t N, int64_t C, int64_t HW,
                       int64_t G, gn_dtype dtype, gn_layout layout, void* workspace, size_t ws_bytes,
                       void* stream, const gn_options* opts) {
-    Problem p;
-    gn_status st = make_problem(N, C, HW, G, dtype, layout, &p);
-    if (st != GN_OK) return st;
-    if (mask <= 0 || mask > 7) return GN_ERR_INVALID;
-    if ((mask & GN_GRAD_DX) && dx == nullptr) return GN_ERR_INVALID;
-    if ((mask & GN_GRAD_DGAMMA) && dgamma == nullptr) return GN_ERR_INVALID;
-    if ((mask & GN_GRAD_DBETA) && dbeta == nullptr) return GN_ERR_INVALID;
-    if ((mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) && gamma == nullptr) return GN_ERR_INVALID;
-    if (zero_extent(p)) {
-        if (opts && opts->info) *opts->info = gn_plan_info{GN_PATH_AUTO, 0, 0, 0, 0, 0};
-        return GN_OK;
-    }
-    if (dy == nullptr || x == nullptr || mean == nullptr || rstd == nullptr) return GN_ERR_INVALID;
-    int32_t path = plan(p, true, opts);
-    if (path < 0) return GN_ERR_UNSUPPORTED;
-    if (path != GN_PATH_GENERIC) {
-        const bool al = aligned16(dy) && aligned16(x) && aligned16(gamma) &&
-                        (!(mask & GN_GRAD_DX) || aligned16(dx));
-        if (!al) {
-            if (forced(opts) != GN_PATH_AUTO) return GN_ERR_UNSUPPORTED;
-            path = GN_PATH_GENERIC;
-        }
-    }
-    const size_t need = bwd_ws(p, mask, path);
-    if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
-    gn::BwdArgs a{dy, x, mean, rstd, gamma,
-                  (mask & GN_GRAD_DX) ? dx : nullptr,
-                  (mask & GN_GRAD_DGAMMA) ? dgamma : nullptr,
-                  (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask};
-    gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
-    if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
-    return with_call_events(opts, stream, [&] {
-        return path == GN_PATH_ROWS ? gn::rows_bwd(p, a, l)
-             : path == GN_PATH_SLAB ? gn::slab_bwd(p, a, l)
-             : path == GN_PATH_STREAM ? gn::stream_bwd(p, a, l)
-                                    : gn::generic_bwd(p, gn::dense_strides(p), a, l);
-    });
+    return backward_call(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, mask, N, C, HW, G, dtype, layout, workspace,
+                         ws_bytes, false, stream, opts);
+}
+
+gn_status gn_backward_scratch(const void* dy, const void* x, const float* mean, const float* rstd,
+                              const float* gamma, void* dx, float* dgamma, float* dbeta, int32_t mask, int64_t N,
+                              int64_t C, int64_t HW, int64_t G, gn_dtype dtype, gn_layout layout, void* stream,
+                              const gn_options* opts) {
+    return backward_call(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, mask, N, C, HW, G, dtype, layout, nullptr,
+                         0, true, stream, opts);
 }
 
 // ---- strided tensors ---------------------------------------------------------

@@ -339,3 +339,22 @@ def test_strided_workspace_sizes(L):
     for mask in range(1, 8):
         assert L.gn_backward_strided_workspace_size(112, 64, 510, 510, 8, F32, crop, crop, dense, mask, None) > 0
     assert L.gn_backward_strided_workspace_size(112, 64, 510, 510, 8, F32, crop, crop, dense, 0, None) == 0
+
+
+def test_scratch_backward_rejects_sizes_beyond_the_array(L):
+    """gn_backward_scratch refuses, on the host, a call whose workspace would
+    exceed the static array (rows bf16, 262144 channels in 16 segments: 64 MiB
+    of column partials)."""
+    N, C, G = 65536, 262144, 16
+    assert L.gn_backward_workspace_size(N, C, 1, G, BF16, NCHW, 7, None) > _lib.GN_SCRATCH_BYTES
+    assert L.gn_backward_scratch(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 7, N, C, 1, G, BF16, NCHW,
+                                 None, None) == _lib.GN_ERR_WORKSPACE
+    # argument checks come first, as in gn_backward
+    assert L.gn_backward_scratch(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 7, 2, 8, 4, 2, F32, NCHW,
+                                 None, None) == _lib.GN_ERR_INVALID
+
+
+def test_scratch_size_matches_header():
+    txt = open(HEADER).read()
+    m = re.search(r"#define GN_SCRATCH_BYTES \((\d+)u << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.GN_SCRATCH_BYTES

@@ -2,19 +2,26 @@
 """GroupNorm forward+backward throughput on one MI355X.
 
 A step is one forward (statistics + normalize/affine) and one backward
-(per-slice reductions, dx, dgamma/dbeta) over every shape of the workload,
-on synthetic seeded inputs already resident in HBM.  The default workload is
-the LayerNorm-shaped GroupNorm (G = 1, one spatial position) at 4096 x 1024
-and 8192 x 768, float16 activations, float32 affine parameters.
+(per-slice reductions, dx, dgamma/dbeta) over every shape of the workload, on
+synthetic seeded inputs already resident in HBM.  The headline workload is
+the NCHW float32 GroupNorm of 112 x 64 x 512 x 512 with 8 groups (the
+POPCORNBENCH GroupNorm problem's shape, 7.5 GB per tensor), the largest of
+the five benchmark configurations.
 
-Prints ONE JSON line on stdout.  ``value`` is the step's algorithmic bytes
-(read x, write y, gamma/beta, mean/rstd; read dy, x, gamma, mean/rstd, write
-dx, dgamma/dbeta) divided by the measured step time, in GB/s.  The
-``roofline`` object covers the kernel that takes most of the step, timed with
-HIP events that the library records on the call's stream around that kernel.
-``cpu_baseline`` times the fp64 oracle on the host cores over a bounded sample.
+Prints ONE JSON line on stdout:
+* ``value``: the headline step's algorithmic bytes (read x, write y,
+  gamma/beta, mean/rstd; read dy, x, gamma, mean/rstd, write dx,
+  dgamma/dbeta) over the measured step time, in GB/s;
+* ``roofline``: the kernel that takes most of the step, timed with HIP
+  events that the library records on the call's stream around that kernel;
+  its rocprofv3 byte counters (``profiles/traffic.json``) as ``traffic``;
+* ``configs``: the same per-call figures for each of the five benchmark
+  configurations (whole-call and main-kernel microseconds, TB/s and % of the
+  8 TB/s peak, forward and backward separately);
+* ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample
+  of the headline workload (whole samples of the tensor).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--configs all|none]
        python bench.py --rows-sweep [--steps K]   (context table, one line per shape)
 """
 from __future__ import annotations
@@ -49,7 +56,17 @@ WORKLOADS = {
     "nchw_f32_112x64x510x510_g8_crop1": ("nchw_f32_112x64x510x510_g8_crop1",),
     "tiny_nchw_f32_2x32x14x14_g8_crop1": ("tiny_nchw_f32_2x32x14x14_g8_crop1",),
 }
-DEFAULT = "rows_f16_4096x1024+8192x768"
+DEFAULT = "nchw_f32_112x64x512x512_g8"
+
+# The five benchmark configurations, in their order: the per-config figures
+# of the JSON line.
+CONFIGS = (
+    ("1", "tiny_nchw_f32_2x32x16x16_g8"),
+    ("2", "rows_f16_4096x1024+8192x768"),
+    ("3", "nhwc_f16_1x128x1024x2048_g16"),
+    ("4", "nchw_f32_112x64x512x512_g8"),
+    ("5", "rows_bf16_131072x4096"),
+)
 
 
 # The source file that defines each kernel (by name prefix) or each whole call;
@@ -61,7 +78,7 @@ KERNEL_SOURCES = (
       "stream_"), "gn_stream.hip"),
     (("gen_", "generic_"), "gn_generic.hip"),
 )
-COMMON_SOURCES = ("gn_device.hpp", "gn_internal.hpp", "gn_api.cpp")
+COMMON_SOURCES = ("gn_device.hpp", "gn_internal.hpp", "gn_api.cpp", "gn_slab_plan.hpp")
 
 
 def source_fingerprint(kernel_name: str) -> str:
@@ -75,8 +92,11 @@ def source_fingerprint(kernel_name: str) -> str:
     h = hashlib.sha256()
     d = os.path.join(HERE, "normalization_gn_stats_amd", "csrc")
     for f in sorted(COMMON_SOURCES + (own[0],)):
+        p = os.path.join(d, f)
+        if not os.path.exists(p):
+            continue
         h.update(f.encode())
-        h.update(open(os.path.join(d, f), "rb").read())
+        h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -138,13 +158,26 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS),
                     help="rms_* workloads run RMSNorm over rows (gn_rms_forward / gn_rms_backward)")
+    ap.add_argument("--configs", default="all", choices=["all", "none"],
+                    help="all: also time the five benchmark configurations (per-config figures)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the oracle CPU-baseline sample (0 disables it)")
     ap.add_argument("--force-path", default=None, choices=[None, "generic", "rows", "slab", "stream"])
@@ -159,14 +192,12 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the GroupNorm path here runs on a single MI355X)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this GroupNorm engine "
+              "runs on a single MI355X (how it would shard across GPUs is described in DESIGN.md)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
-
-    import normalization_gn_stats_amd as gn
-    from normalization_gn_stats_amd import inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
@@ -176,6 +207,149 @@ def main():
     if args.rows_sweep:
         rows_sweep(args.steps)
         return
+
+    K, W = args.steps, args.warmup
+    log(f"headline workload {args.workload}")
+    head = measure(args.workload, K, W, args.mode, args.force_path, keep_inputs=args.cpu_seconds > 0)
+    value = head["bytes_per_step"] / (head["ms_per_step"] * 1e-3) / 1e9
+
+    # ---- roofline of the dominant kernel of the headline step ----------------
+    dom = max(head["calls"], key=lambda c: c["main_kernel_us"])
+    traffic = None
+    for kn in dom["kernel"] or ():
+        traffic = recorded_traffic(args.workload, kn, dom["grid"])
+        if traffic is not None:
+            dom["kernel"] = kn
+            break
+    roofline = {"bound": "hbm", "achieved": round(dom["main_kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dom["main_kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "traffic_over_algorithmic": (round(traffic / dom["main_kernel_bytes"], 3) if traffic else None),
+                "kernel": (f"{dom['call']} {dom['path']} " + ("call (all its kernels)"
+                                                                  if dom["path"] in ("stream", "generic")
+                                                                  else "main kernel") + f" on {dom['shape']}"),
+                "kernel_name": (dom["kernel"] if isinstance(dom["kernel"], str) else None),
+                "avg_us": round(dom["main_kernel_us"], 3), "algorithmic_bytes": dom["main_kernel_bytes"],
+                "timing": ("HIP events (created without the system-scope fence) recorded by the library on "
+                           "the call's stream around the main kernel "
+                           "(stream and generic paths: around all kernels of the call), "
+                           + ("K eager steps queued behind a GPU spin after the graph-timed region"
+                              if head["mode"] == "graph" else "over the timed region"))}
+
+    # measured device-to-device copy of 1 GiB (read + write), the practical
+    # ceiling of a streaming kernel on this part: a second denominator
+    copy_gbs = copy_bandwidth()
+    roofline["copy_gbs"] = round(copy_gbs, 1)
+    roofline["frac_of_copy"] = round(dom["main_kernel_gbs"] / copy_gbs, 4)
+
+    if args.copy_calibration_mib > 0:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- oracle CPU baseline on a bounded sample --------------------------------
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(head["shapes"], args.cpu_seconds, head["bytes_per_step"])
+    head["shapes"] = None
+    torch.cuda.empty_cache()
+
+    # ---- the five benchmark configurations --------------------------------------
+    configs = None
+    if args.configs == "all":
+        configs = {}
+        for label, wname in CONFIGS:
+            if wname == args.workload and args.force_path is None:
+                r = head
+            else:
+                log(f"config {label}: {wname}")
+                r = measure(wname, K, W, "auto", None)
+                r["shapes"] = None
+                torch.cuda.empty_cache()
+            configs[label] = config_summary(wname, r)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "launch": head["mode"], "shapes": head["shape_desc"],
+                   "op": head["op"], "mask": head["mask"], "bytes_per_step": head["bytes_per_step"],
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "us_per_call": {f"{c['call']}:{c['shape']}": round(c["call_us"], 3) for c in head["calls"]},
+        "main_kernel_us": {f"{c['call']}:{c['shape']}": round(c["main_kernel_us"], 3) for c in head["calls"]},
+        "us_per_call_flushed": head["flushed"],
+        "calls": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in c.items()} for c in head["calls"]],
+        "roofline": roofline,
+        "configs": configs,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def copy_bandwidth() -> float:
+    import torch
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for i in range(3):
+        ce[2 * i].record(stream)
+        cdst.copy_(csrc)
+        ce[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    copy_ms = sorted(ce[2 * i].elapsed_time(ce[2 * i + 1]) for i in range(3))[1]
+    del csrc, cdst
+    return 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9
+
+
+def config_summary(wname, r):
+    """Per-config figures: per shape, forward and backward whole-call and
+    main-kernel microseconds and the call's algorithmic TB/s and % of peak."""
+    shapes = {}
+    for c in r["calls"]:
+        d = shapes.setdefault(c["shape"], {"path": {}})
+        k = c["call"]
+        d["path"][k] = c["path"]
+        d[f"{k}_us"] = round(c["call_us"], 3)
+        d[f"{k}_main_kernel_us"] = round(c["main_kernel_us"], 3)
+        d[f"{k}_bytes"] = c["call_bytes"]
+        gbs = c["call_bytes"] / (c["call_us"] * 1e-6) / 1e9
+        d[f"{k}_tbs"] = round(gbs / 1e3, 3)
+        d[f"{k}_pct_of_peak"] = round(100 * gbs / HBM_PEAK_GBS, 2)
+    out = {"workload": wname, "launch": r["mode"], "shapes": shapes}
+    if r["flushed"]:
+        out["us_per_call_flushed"] = r["flushed"]
+    return out
+
+
+def measure(workload, K, W, mode, force_path, keep_inputs=False):
+    """Times K steps of one workload (all its shapes, forward then backward).
+
+    Returns the step time, per-call whole-call and main-kernel times (from
+    the library's events), the bytes per step and, for graph-timed small
+    workloads, cold-cache call times."""
+    import ctypes
+
+    import torch
+
+    import normalization_gn_stats_amd as gn
+    from normalization_gn_stats_amd import inputs
+
+    dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     mask = gn.GN_GRAD_DX | gn.GN_GRAD_DGAMMA | gn.GN_GRAD_DBETA
@@ -183,7 +357,7 @@ def main():
 
     # ---- inputs resident in HBM, outputs and workspaces preallocated ----------
     shapes = []
-    for name in WORKLOADS[args.workload]:
+    for name in WORKLOADS[workload]:
         wl = inputs.WORKLOADS[name]
         log(f"generating {wl.name}")
         d = inputs.make_inputs(wl, seed=0, device="cuda")
@@ -191,21 +365,19 @@ def main():
         code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
         if wl.op == "rms":   # [N, C] rows
             x, dy = x.reshape(wl.N, wl.C), dy.reshape(wl.N, wl.C)
-            lay = gn.GN_NCHW
-            fws = gn.rms_forward_workspace_size(wl.N, wl.C, wl.G, code, args.force_path)
-            bws = gn.rms_backward_workspace_size(wl.N, wl.C, wl.G, code, rms_mask, args.force_path)
+            fws = gn.rms_forward_workspace_size(wl.N, wl.C, wl.G, code, force_path)
+            bws = gn.rms_backward_workspace_size(wl.N, wl.C, wl.G, code, rms_mask, force_path)
         elif wl.crop:
             # views: outputs dense NCHW, inputs with their own strides
-            lay = None
             y_, dx_ = torch.empty(x.shape, dtype=x.dtype, device=dev), torch.empty(x.shape, dtype=x.dtype, device=dev)
             _, _, H_, W_, st = gn.strided_dims(x, y_, dy, dx_)
-            fws = gn.forward_strided_workspace_size(wl.N, wl.C, H_, W_, wl.G, code, st[0], st[1], args.force_path)
+            fws = gn.forward_strided_workspace_size(wl.N, wl.C, H_, W_, wl.G, code, st[0], st[1], force_path)
             bws = gn.backward_strided_workspace_size(wl.N, wl.C, H_, W_, wl.G, code, st[2], st[0], st[3], mask,
-                                                     args.force_path)
+                                                     force_path)
         else:
             lay = gn.layout_of(x)
-            fws = gn.forward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, args.force_path)
-            bws = gn.backward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, mask, args.force_path)
+            fws = gn.forward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, force_path)
+            bws = gn.backward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, mask, force_path)
         sh = dict(wl=wl, x=x, dy=dy, gamma=gamma, beta=beta, y=torch.empty_like(x), dx=torch.empty_like(x),
                   mean=torch.empty(wl.N * wl.G, device=dev), rstd=torch.empty(wl.N * wl.G, device=dev),
                   dgamma=torch.empty(wl.C, device=dev), dbeta=torch.empty(wl.C, device=dev),
@@ -219,9 +391,9 @@ def main():
     # Pre-marshalled C-ABI calls (the binding's checks ran once above, through
     # the size queries); a call costs one ctypes dispatch.
     L = gn._lib.lib()
-    import ctypes
 
     def calls_for(sh, stream_handle, evs):
+        """evs: None, or per call kind ((call_begin, call_end), (kernel_begin, kernel_end))."""
         wl = sh["wl"]
         code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
         lay = gn.GN_NCHW if (wl.op == "rms" or wl.crop) else gn.layout_of(sh["x"])
@@ -229,12 +401,12 @@ def main():
         out = []
         for kind in ("fwd", "bwd"):
             o = gn._lib.Options()
-            o.force_path = {None: 0, "generic": 1, "rows": 2, "slab": 3, "stream": 4}[args.force_path]
+            o.force_path = {None: 0, "generic": 1, "rows": 2, "slab": 3, "stream": 4}[force_path]
             o.info = ctypes.pointer(sh["fplan" if kind == "fwd" else "bplan"])
             if evs is not None:
-                b, e = evs[0 if kind == "fwd" else 1]
-                o.event_begin = ctypes.c_void_p(b)
-                o.event_end = ctypes.c_void_p(e)
+                (cb, ce), (kb, ke) = evs[0 if kind == "fwd" else 1]
+                o.event_begin, o.event_end = ctypes.c_void_p(cb), ctypes.c_void_p(ce)
+                o.kernel_begin, o.kernel_end = ctypes.c_void_p(kb), ctypes.c_void_p(ke)
             if wl.op == "rms" and kind == "fwd":
                 a = (P(sh["x"]), P(sh["gamma"]), P(sh["y"]), P(sh["rstd"]), wl.N, wl.C, wl.G, ctypes.c_float(wl.eps),
                      code, P(sh["fws"]), sh["fws"].numel(), ctypes.c_void_p(stream_handle), ctypes.byref(o))
@@ -277,15 +449,13 @@ def main():
 
     plain = [c for sh in shapes for c in calls_for(sh, sp, None)]
 
-    log(f"warmup {args.warmup} steps")
+    log(f"warmup {W} steps")
     t_w0 = time.perf_counter()
-    for _ in range(args.warmup):
+    for _ in range(W):
         run(plain)
     torch.cuda.synchronize()
-    warm_ms = (time.perf_counter() - t_w0) * 1e3 / max(args.warmup, 1)
+    warm_ms = (time.perf_counter() - t_w0) * 1e3 / max(W, 1)
 
-    K = args.steps
-    mode = args.mode
     if mode == "auto":
         mode = "graph" if warm_ms < 2.0 else "eager"
 
@@ -303,9 +473,13 @@ def main():
         graph.replay()             # first replay uploads the graph
         torch.cuda.synchronize()
 
-    # per-step, per-shape (fwd, bwd) x (begin, end) events around each main kernel
+    # per step, per shape, per call (fwd, bwd): (call events, kernel events)
     tev = TimingEvents()
-    events = [[[[tev.new() for _ in range(2)] for _ in range(2)] for _ in shapes] for _ in range(K)]
+
+    def ev_pair():
+        return (tev.new(), tev.new())
+
+    events = [[[(ev_pair(), ev_pair()) for _ in range(2)] for _ in shapes] for _ in range(K)]
     evcalls = [[c for k, sh in enumerate(shapes) for c in calls_for(sh, sp, events[i][k])] for i in range(K)]
 
     log(f"timing {K} steps ({mode})")
@@ -321,9 +495,9 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / K
 
     if graph is not None:
-        # Kernel durations: the same K steps issued eagerly with the library's
-        # events around each main kernel, queued behind a GPU spin so that the
-        # kernels run back to back and each event pair brackets its kernel only.
+        # Call and kernel durations: the same K steps issued eagerly with the
+        # library's events, queued behind a GPU spin so that the kernels run
+        # back to back and each event pair brackets its own work only.
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record(stream)
         torch.cuda._sleep(1_000_000)
@@ -337,26 +511,25 @@ def main():
         torch.cuda.synchronize()
 
     bytes_per_step = sum(sh["wl"].fwd_min_bytes() + sh["wl"].bwd_min_bytes() for sh in shapes)
-    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # ---- per-call kernel durations from the library-recorded events ----------
+    # ---- per-call durations from the library-recorded events ------------------
     calls = []
     for k, sh in enumerate(shapes):
         wl = sh["wl"]
         for c, (kind, plan) in enumerate((("fwd", sh["fplan"]), ("bwd", sh["bplan"]))):
             path = gn.PATH_NAMES[plan.path]
-            if path in ("stream", "generic"):
-                # these paths' events bracket all kernels of the call: the
-                # call's algorithmic bytes over the call's time
-                nbytes = wl.fwd_min_bytes() if kind == "fwd" else wl.bwd_min_bytes()
-            elif kind == "fwd":
-                nbytes = wl.fwd_min_bytes()
+            call_bytes = wl.fwd_min_bytes() if kind == "fwd" else wl.bwd_min_bytes()
+            if path in ("stream", "generic") or kind == "fwd":
+                # stream/generic: the kernel events bracket all kernels of the call
+                nbytes = call_bytes
             else:
                 # the main backward kernel writes dx; dgamma/dbeta (2*C*4 bytes) are
                 # written by the small column-sum kernel when one follows
-                nbytes = wl.bwd_min_bytes() - (2 * wl.C * 4 if plan.kernels > 1 else 0)
-            durs = [tev.elapsed_ms(events[i][k][c][0], events[i][k][c][1]) for i in range(K)]
-            avg_ms = sum(durs) / len(durs)
+                nbytes = call_bytes - (2 * wl.C * 4 if plan.kernels > 1 else 0)
+            call_ms = [tev.elapsed_ms(*events[i][k][c][0]) for i in range(K)]
+            kern_ms = [tev.elapsed_ms(*events[i][k][c][1]) for i in range(K)]
+            call_avg = sum(call_ms) / K
+            kern_avg = sum(kern_ms) / K
             # kernels that can be the call's main kernel (the rows path picks one of
             # several by the slice width and count; the grid tells them apart in
             # the recorded counters)
@@ -369,8 +542,9 @@ def main():
             whole = path in ("stream", "generic")
             calls.append(dict(shape=wl.name, call=kind, path=path, kernels=plan.kernels,
                               kernel=kname, grid=plan.grid if not whole else "call",
-                              main_kernel_us=avg_ms * 1e3, main_kernel_bytes=nbytes,
-                              main_kernel_gbs=nbytes / (avg_ms * 1e-3) / 1e9))
+                              call_us=call_avg * 1e3, call_bytes=call_bytes,
+                              main_kernel_us=kern_avg * 1e3, main_kernel_bytes=nbytes,
+                              main_kernel_gbs=nbytes / (kern_avg * 1e-3) / 1e9))
     # ---- small (cache-resident) workloads: the calls again with the caches
     # flushed before each one -- a 512 MiB scratch fill outside the library's
     # events -- so that each call reads its inputs from HBM ----------------------
@@ -378,101 +552,31 @@ def main():
     if mode == "graph":
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         reps = min(K, 20)
-        fev = [[[tev.new() for _ in range(2)] for _ in range(2 * len(shapes))] for _ in range(reps)]
+        fev = [[[(ev_pair(), ev_pair()) for _ in range(2)] for _ in shapes] for _ in range(reps)]
         for i in range(reps):
             for k, sh in enumerate(shapes):
-                for c, call in enumerate(calls_for(sh, sp, (fev[i][2 * k], fev[i][2 * k + 1]))):
+                for call in calls_for(sh, sp, fev[i][k]):
                     scratch.fill_(i & 0xFF)
                     run([call])
         torch.cuda.synchronize()
         flushed = {}
         for k, sh in enumerate(shapes):
             for c, kind in enumerate(("fwd", "bwd")):
-                d = [tev.elapsed_ms(fev[i][2 * k + c][0], fev[i][2 * k + c][1]) for i in range(reps)]
+                d = [tev.elapsed_ms(*fev[i][k][c][0]) for i in range(reps)]
                 flushed[f"{kind}:{sh['wl'].name}"] = round(1e3 * sum(d) / len(d), 3)
         del scratch
     tev.close()
-    dom = max(calls, key=lambda c: c["main_kernel_us"])
-    traffic = None
-    for kn in dom["kernel"] or ():
-        traffic = recorded_traffic(args.workload, kn, dom["grid"])
-        if traffic is not None:
-            dom["kernel"] = kn
-            break
-    roofline = {"bound": "hbm", "achieved": round(dom["main_kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dom["main_kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                "traffic_over_algorithmic": (round(traffic / dom["main_kernel_bytes"], 3) if traffic else None),
-                "kernel": (f"{dom['call']} {dom['path']} " + ("call (all its kernels)"
-                                                                  if dom["path"] in ("stream", "generic")
-                                                                  else "main kernel") + f" on {dom['shape']}"),
-                "avg_us": round(dom["main_kernel_us"], 3), "algorithmic_bytes": dom["main_kernel_bytes"],
-                "timing": ("HIP events (created without the system-scope fence) recorded by the library on "
-                           "the call's stream around the main kernel "
-                           "(stream and generic paths: around all kernels of the call), "
-                           + ("K eager steps queued behind a GPU spin after the graph-timed region"
-                              if mode == "graph" else "over the timed region"))}
-
-    # measured device-to-device copy of 1 GiB (read + write), the practical
-    # ceiling of a streaming kernel on this part: a second denominator
-    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cdst = torch.empty_like(csrc)
-    cdst.copy_(csrc)
-    ce = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    for i in range(3):
-        ce[2 * i].record(stream)
-        cdst.copy_(csrc)
-        ce[2 * i + 1].record(stream)
-    torch.cuda.synchronize()
-    copy_ms = sorted(ce[2 * i].elapsed_time(ce[2 * i + 1]) for i in range(3))[1]
-    copy_gbs = 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9
-    del csrc, cdst
-    roofline["copy_gbs"] = round(copy_gbs, 1)
-    roofline["frac_of_copy"] = round(dom["main_kernel_gbs"] / copy_gbs, 4)
-
-    if args.copy_calibration_mib > 0:
-        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    # ---- oracle CPU baseline on a bounded sample -------------------------------
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(shapes, args.cpu_seconds, bytes_per_step)
-
-    out = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": shapes[0]["wl"].dtype,
-        "data": "synthetic",
-        "config": {"workload": args.workload, "launch": mode,
-                   "shapes": [dict(N=s["wl"].N, C=s["wl"].C, H=s["wl"].H, W=s["wl"].W, G=s["wl"].G,
-                                   dtype=s["wl"].dtype, layout=s["wl"].layout,
-                                   **({"view": f"centre crop of ({s['wl'].H + 2 * s['wl'].crop}, "
-                                               f"{s['wl'].W + 2 * s['wl'].crop}) images"} if s["wl"].crop else {}))
-                              for s in shapes],
-                   "op": shapes[0]["wl"].op,
-                   "mask": "dx|dgamma" if shapes[0]["wl"].op == "rms" else "dx|dgamma|dbeta",
-                   "bytes_per_step": bytes_per_step,
-                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
-        "us_per_call": {f"{c['call']}:{c['shape']}": round(c["main_kernel_us"], 3) for c in calls},
-        "us_per_call_flushed": flushed,
-        "calls": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in c.items()} for c in calls],
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
+    if graph is not None:
+        del graph
+    wl0 = shapes[0]["wl"]
+    desc = [dict(N=s["wl"].N, C=s["wl"].C, H=s["wl"].H, W=s["wl"].W, G=s["wl"].G, dtype=s["wl"].dtype,
+                 layout=s["wl"].layout,
+                 **({"view": f"centre crop of ({s['wl'].H + 2 * s['wl'].crop}, "
+                             f"{s['wl'].W + 2 * s['wl'].crop}) images"} if s["wl"].crop else {}))
+            for s in shapes]
+    return dict(mode=mode, ms_per_step=ms_per_step, bytes_per_step=bytes_per_step, calls=calls, flushed=flushed,
+                shapes=shapes if keep_inputs else None, shape_desc=desc, dtype=wl0.dtype, op=wl0.op,
+                mask="dx|dgamma" if wl0.op == "rms" else "dx|dgamma|dbeta")
 
 
 # Rows shapes of the LayerNorm / RMSNorm backward table in ROCm/pytorch PR
@@ -558,60 +662,68 @@ def rows_sweep(K):
 
 
 def cpu_baseline(shapes, seconds, bytes_per_step):
-    """The fp64 oracle (as it stands) on the same workload, repeated until about
-    `seconds` of CPU time; reported in the metric's unit (algorithmic GB/s)."""
+    """The fp64 oracle (as it stands) on a bounded sample of the workload:
+    whole samples n = 0, 1, ... of each shape (a sample is its own GroupNorm
+    problem, N = 1 ... k), copied to the host and widened to float64 outside
+    the timer, forward and backward, until about `seconds` of oracle time.
+    Reported in the metric's unit: algorithmic GB/s of the samples done."""
     import numpy as np
+    import torch
 
     import oracle
-    from normalization_gn_stats_amd import inputs
 
     log("cpu baseline: oracle on the host cores")
-    prepared = []
+    threads = oracle.num_threads()
+    done_bytes, elapsed, samples, calls = 0, 0.0, 0, 0
+    per_shape = []
     for sh in shapes:
         wl = sh["wl"]
-        x = inputs.memory_image(sh["x"], wl.layout).to("cpu", dtype=__import__("torch").float64).numpy()
-        dy = inputs.memory_image(sh["dy"], wl.layout).to("cpu", dtype=__import__("torch").float64).numpy()
+        # samples per oracle call: enough slices to occupy every thread
+        chunk = max(1, min(wl.N, -(-2 * threads // wl.G)))
+        frac = chunk / wl.N
+        nbytes = (wl.fwd_min_bytes() + wl.bwd_min_bytes()) * frac   # this chunk's share of the step
         g = sh["gamma"].double().cpu().numpy()
         b = sh["beta"].double().cpu().numpy()
-        prepared.append((wl, x, dy, g, b, float(np.float32(wl.eps))))
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        for wl, x, dy, g, b, eps in prepared:
+        eps = float(np.float32(wl.eps))
+        per_shape.append((wl, chunk, nbytes, g, b, eps))
+    budget = seconds / len(per_shape)
+    for (wl, chunk, nbytes, g, b, eps), sh in zip(per_shape, shapes):
+        t_shape = 0.0
+        n0 = 0
+        while t_shape < budget and n0 < wl.N:
+            n1 = min(wl.N, n0 + chunk)
+            xs = sh["x"][n0:n1]
+            dys = sh["dy"][n0:n1]
+            from normalization_gn_stats_amd import inputs
+            x64 = inputs.memory_image(xs, wl.layout).to("cpu", torch.float64).numpy()
+            dy64 = inputs.memory_image(dys, wl.layout).to("cpu", torch.float64).numpy()
+            nn = n1 - n0
+            t0 = time.perf_counter()
             if wl.op == "rms":
-                oracle.rms_forward(x, g, wl.N, wl.C, wl.G, eps)
-                oracle.rms_backward(dy, x, g, wl.N, wl.C, wl.G, eps)
-                continue
-            oracle.forward(x, g, b, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
-            oracle.backward(dy, x, g, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 10000:
-            break
-    one = None
-    if bytes_per_step < (256 << 20):   # small workloads: the same on one thread
-        nt = oracle.num_threads()
-        oracle.set_num_threads(1)
-        r1, t1 = 0, time.perf_counter()
-        while True:
-            for wl, x, dy, g, b, eps in prepared:
-                if wl.op == "rms":
-                    oracle.rms_forward(x, g, wl.N, wl.C, wl.G, eps)
-                    oracle.rms_backward(dy, x, g, wl.N, wl.C, wl.G, eps)
-                    continue
-                oracle.forward(x, g, b, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
-                oracle.backward(dy, x, g, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
-            r1 += 1
-            e1 = time.perf_counter() - t1
-            if e1 >= min(seconds, 3.0) or r1 >= 1000:
-                break
-        oracle.set_num_threads(nt)
-        one = round(bytes_per_step * r1 / e1 / 1e9, 3)
-    return {"value": round(bytes_per_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "value_one_thread": one,
+                oracle.rms_forward(x64, g, nn, wl.C, wl.G, eps)
+                oracle.rms_backward(dy64, x64, g, nn, wl.C, wl.G, eps)
+            else:
+                oracle.forward(x64, g, b, nn, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
+                oracle.backward(dy64, x64, g, nn, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
+            dt = time.perf_counter() - t0
+            t_shape += dt
+            elapsed += dt
+            done_bytes += nbytes * nn / chunk
+            samples += nn
+            calls += 1
+            n0 = n1
+            if n0 >= wl.N:
+                n0 = 0   # small workloads: repeat the whole tensor
+                if t_shape >= budget:
+                    break
+    wl0 = shapes[0]["wl"]
+    return {"value": round(done_bytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{reps} full steps of the workload (fwd+bwd of every shape) in {el:.1f} s, fp64 C oracle, "
-                      f"OpenMP threads={oracle.num_threads()}, host cpus={os.cpu_count()}"}
+            "sample": (f"{samples} samples (n = 0, 1, ...) of {', '.join(s['wl'].name for s in shapes)} "
+                       f"in {calls} oracle calls of up to {per_shape[0][1]} samples ({per_shape[0][1] * wl0.G} "
+                       f"slices), forward + backward, {elapsed:.1f} s of fp64 C oracle time "
+                       f"(host copies and widening excluded); {threads} OpenMP threads on {os.cpu_count()} host "
+                       f"cpus, {cpu_model()}")}
 
 
 if __name__ == "__main__":

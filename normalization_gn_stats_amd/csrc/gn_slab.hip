@@ -27,11 +27,12 @@
 //            regrouped by channel), dgamma_c = sum_n S2[n,c], dbeta_c = sum_n S1[n,c].
 #include "gn_device.hpp"
 #include "gn_internal.hpp"
+#include "gn_slab_plan.hpp"
 
 namespace gn {
 namespace {
 
-constexpr int kT = 256;
+constexpr int kT = slab::kThreads;
 constexpr int kNW = kT / kWave;
 
 struct SlabCfg {
@@ -85,9 +86,8 @@ __device__ inline int64_t grab_tile(uint32_t* counter, int* s_slot) {
 // before the first barrier and not read by anyone before it.
 __device__ inline int64_t grab_phase2_tile(uint32_t* counter, const uint32_t* res, int64_t tiles, int* s_slot) {
     while (true) {
-        const int64_t k = grab_tile(counter, s_slot);
-        if (k >= tiles) return -1;
-        const int64_t tile = tiles - 1 - k;
+        const int64_t tile = slab::nhwc_phase2_tile(grab_tile(counter, s_slot), tiles);
+        if (tile < 0) return -1;
         if (!res[tile]) return tile;
     }
 }
@@ -96,7 +96,8 @@ template <typename T, int R>
 __device__ inline void nhwc_load(const T* __restrict__ src, int64_t HW, int64_t C, int64_t p0, int PPI, u4v (&dst)[R]) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const int64_t p = min(p0 + (int64_t)j * PPI, HW - 1);   // in bounds; dropped by the caller if past HW
+        // in bounds; dropped by the caller if past HW
+        const int64_t p = slab::nhwc_pixel_load(p0 + (int64_t)j * PPI, HW);
         dst[j] = ld16_nt(src + p * C);
     }
 }
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(kT) void slab_nhwc_fwd(const T* __restrict__ x, con
     const int q = t % CPP;
     const int pi = t / CPP;
     const int PPI = kT / CPP;
-    const int64_t TP = (int64_t)PPI * R;
+    const int64_t TP = slab::nhwc_tile_pixels(cfg.C, V, R);
     const int gq = (q * V) / (int)cfg.D;
     const int qpg = (int)cfg.D / V;   // chunks per group
     const int team = blockIdx.x / cfg.team;
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(kT) void slab_nhwc_bwd(const T* __restrict__ dy, co
     const int q = t % CPP;
     const int pi = t / CPP;
     const int PPI = kT / CPP;
-    const int64_t TP = (int64_t)PPI * R;
+    const int64_t TP = slab::nhwc_tile_pixels(cfg.C, V, R);
     const int gq = (q * V) / (int)cfg.D;
     const int team = blockIdx.x / cfg.team;
     const int m = blockIdx.x - team * cfg.team;
@@ -483,11 +484,9 @@ __device__ inline float2 poll_partial(const uint64_t* p, const SlabCfg& cfg, uin
 }
 
 // Elements of NCHW tile `tile` (the last tile of each channel plane may be
-// short).  32-bit index arithmetic: the host keeps a slab's tiles below 2^31.
+// short), as a float.
 __device__ inline float nchw_tile_count(const SlabCfg& cfg, int64_t tile, int64_t TE) {
-    const int64_t k0 = (int64_t)((uint32_t)tile % (uint32_t)cfg.tpc) * TE;
-    const int64_t rem = cfg.HW - k0;
-    return (float)(rem < TE ? rem : TE);
+    return (float)slab::nchw_tile_count(tile, cfg.tpc, TE, cfg.HW);
 }
 
 // The thread index, opaque to the optimiser: the per-chunk element offsets of a
@@ -511,14 +510,15 @@ template <typename T, int R>
 __device__ inline void nchw_load_tile(const T* __restrict__ src, const SlabCfg& cfg, int64_t sb, int64_t tile,
                                       u4v (&dst)[R]) {
     constexpr int V = Vec<T>::V;
-    constexpr int64_t TE = (int64_t)kT * R * V;
+    constexpr int64_t TE = slab::nchw_tile_elems(V, R);
     const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
-    const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+    int64_t cl, k0;
+    slab::nchw_tile_pos(tile, cfg.tpc, TE, &cl, &k0);
     const T* p = src + (n * cfg.C + g * cfg.D + cl) * cfg.HW;
     const int t = tile_tid();
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const int64_t e = min(k0 + (int64_t)(j * kT + t) * V, cfg.HW - V);   // in bounds
+        const int64_t e = slab::nchw_chunk_load(slab::nchw_chunk_elem(k0, j, t, V), cfg.HW, V);   // in bounds
         dst[j] = ld16_nt(p + e);
     }
 }
@@ -533,11 +533,12 @@ __device__ inline int64_t nchw_fwd_phase1(const T* __restrict__ x, const float* 
                                           const float* __restrict__ beta, const SlabCfg& cfg, int64_t sb, int m,
                                           u4v (&buf)[R], float2& gb, uint64_t* part, float* lds) {
     constexpr int V = Vec<T>::V;
-    constexpr int64_t TE = (int64_t)kT * R * V;
+    constexpr int64_t TE = slab::nchw_tile_elems(V, R);
     const int t = tile_tid();
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
-        const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+        int64_t cl, k0;
+        slab::nchw_tile_pos(tile, cfg.tpc, TE, &cl, &k0);
         nchw_load_tile<T, R>(x, cfg, sb, tile, buf);
         const int64_t c = (sb - (sb / cfg.G) * cfg.G) * cfg.D + cl;
         gb = make_float2(gamma ? gamma[c] : 1.f, beta ? beta[c] : 0.f);
@@ -546,7 +547,7 @@ __device__ inline int64_t nchw_fwd_phase1(const T* __restrict__ x, const float* 
         float acc[1] = {0.f};
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
+            if (slab::nchw_chunk_elem(k0, j, t, V) < cfg.HW) {
                 float v[V];
                 Vec<T>::unpack(buf[j], v);
 #pragma unroll
@@ -566,7 +567,7 @@ __device__ inline int64_t nchw_fwd_phase1(const T* __restrict__ x, const float* 
         float q[1] = {0.f};
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
+            if (slab::nchw_chunk_elem(k0, j, t, V) < cfg.HW) {
                 float v[V];
                 Vec<T>::unpack(buf[j], v);
 #pragma unroll
@@ -594,7 +595,7 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
                                        float* rstd, const SlabCfg& cfg, int64_t sb, int m, int64_t last,
                                        u4v (&buf)[R], float2 gb, const uint64_t* part, uint32_t* err, float* lds) {
     constexpr int V = Vec<T>::V;
-    constexpr int64_t TE = (int64_t)kT * R * V;
+    constexpr int64_t TE = slab::nchw_tile_elems(V, R);
     constexpr int kKeep = 1;   // partials a thread keeps in registers (slabs of up to kKeep * kT tiles)
     const int t = tile_tid();
     const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
@@ -653,7 +654,8 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
     if (y == nullptr) return;
     const int64_t base = (n * cfg.C + g * cfg.D) * cfg.HW;
     for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
-        const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+        int64_t cl, k0;
+        slab::nchw_tile_pos(tile, cfg.tpc, TE, &cl, &k0);
         float2 p = gb;
         if (tile != last) {
             nchw_load_tile<T, R>(x, cfg, sb, tile, buf);
@@ -665,7 +667,7 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
         T* dst = y + base + cl * cfg.HW;
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            const int64_t e = k0 + (int64_t)(j * kT + t) * V;
+            const int64_t e = slab::nchw_chunk_elem(k0, j, t, V);
             if (e < cfg.HW) {
                 float v[V], o[V];
                 Vec<T>::unpack(buf[j], v);
@@ -722,17 +724,18 @@ __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __r
                                           float mu, float r, u4v (&bx)[R], u4v (&bd)[R], uint64_t* part,
                                           float* lds) {
     constexpr int V = Vec<T>::V;
-    constexpr int64_t TE = (int64_t)kT * R * V;
+    constexpr int64_t TE = slab::nchw_tile_elems(V, R);
     const int t = tile_tid();
     int64_t last = -1;
     for (int64_t tile = m; tile < cfg.tiles; tile += cfg.team) {
-        const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+        int64_t cl, k0;
+        slab::nchw_tile_pos(tile, cfg.tpc, TE, &cl, &k0);
         nchw_load_tile<T, R>(x, cfg, sb, tile, bx);
         nchw_load_tile<T, R>(dy, cfg, sb, tile, bd);
         float acc[2] = {0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            if (k0 + (int64_t)(j * kT + t) * V < cfg.HW) {
+            if (slab::nchw_chunk_elem(k0, j, t, V) < cfg.HW) {
                 float xv[V], dv[V];
                 Vec<T>::unpack(bx[j], xv);
                 Vec<T>::unpack(bd[j], dv);
@@ -764,7 +767,7 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
                                        u4v (&bd)[R], float gam, const uint64_t* part, uint32_t* err,
                                        float2* stot, float2* stage, float2* chan, float* gch) {
     constexpr int V = Vec<T>::V;
-    constexpr int64_t TE = (int64_t)kT * R * V;
+    constexpr int64_t TE = slab::nchw_tile_elems(V, R);
     constexpr int kPer = kStage / kT;
     const int t = tile_tid();
     const int64_t n = sb / cfg.G, g = sb - n * cfg.G;
@@ -812,7 +815,8 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
     B *= invM;
     const int64_t base = (n * cfg.C + g * cfg.D) * cfg.HW;
     for (int64_t tile = last; tile >= 0; tile -= cfg.team) {
-        const int64_t cl = tile / cfg.tpc, k0 = (tile - cl * cfg.tpc) * TE;
+        int64_t cl, k0;
+        slab::nchw_tile_pos(tile, cfg.tpc, TE, &cl, &k0);
         const int64_t pb = base + cl * cfg.HW;
         const float ga = gch[cl];
         if (tile != last) {
@@ -821,7 +825,7 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
         }
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            const int64_t e = k0 + (int64_t)(j * kT + t) * V;
+            const int64_t e = slab::nchw_chunk_elem(k0, j, t, V);
             if (e < cfg.HW) {
 #pragma clang fp contract(off)
                 float xv[V], dv[V], o[V];
@@ -975,17 +979,15 @@ struct Plan {
     size_t ones_end;   // [off_part, ones_end): filled with ones each call (NCHW partial words)
 };
 
+// The schedule of this problem for a resident-workgroup cap (gn_slab_plan.hpp).
+slab::Geometry geometry(const Problem& p, int R, int64_t cap) {
+    return slab::plan(p.layout == GN_NHWC, p.N, p.C, p.HW, p.G, vec_elems(p), R, cap);
+}
+
 int64_t tiles_per_slab(const Problem& p, int R, int64_t* tpc) {
-    const int V = vec_elems(p);
-    if (p.layout == GN_NHWC) {
-        const int CPP = (int)(p.C / V);
-        const int64_t TP = (int64_t)(kT / CPP) * R;
-        *tpc = 0;
-        return (p.HW + TP - 1) / TP;
-    }
-    const int64_t TE = (int64_t)kT * R * V;
-    *tpc = (p.HW + TE - 1) / TE;
-    return p.D * *tpc;
+    const slab::Geometry g = geometry(p, R, 1);
+    *tpc = g.tpc;
+    return g.tiles;
 }
 
 template <typename K>
@@ -998,19 +1000,21 @@ int64_t resident_cap(K kernel, int cu_count) {
     return (int64_t)(blocks > 0 ? blocks : 1) * cu_count;
 }
 
-// Workspace layout, sized for the largest team (the slab's tile count), so
-// that the size does not depend on the device.
-Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
+// The grid plan for resident-workgroup cap `cap` and the workspace layout.
+// The layout does not depend on the cap (the size queries pass the slab's tile
+// count), so the size does not depend on the device.
+Plan layout_ws(const Problem& p, bool backward, int64_t cap) {
     Plan pl{};
-    int64_t tpc = 0;
-    const int64_t tiles = tiles_per_slab(p, tile_chunks(p, backward), &tpc);
-    const int64_t n_slabs = p.layout == GN_NHWC ? p.N : p.S;
-    int64_t team = tiles < team_max ? tiles : team_max;
-    if (team < 1) team = 1;
+    const slab::Geometry g = geometry(p, tile_chunks(p, backward), cap);
+    const int64_t tiles = g.tiles;
+    const int64_t n_slabs = g.n_slabs;
     pl.cfg.tiles = tiles;
-    pl.cfg.tpc = tpc;
-    pl.cfg.pstride = (tiles + 15) / 16 * 16;   // 16 slots: whole 128-byte lines of 8- and 16-byte slots
+    pl.cfg.tpc = g.tpc;
+    pl.cfg.pstride = g.pstride;
     pl.cfg.n_slabs = n_slabs;
+    pl.cfg.team = (int32_t)g.team;
+    pl.cfg.nteams = (int32_t)g.nteams;
+    pl.grid = g.grid;
     size_t off = 256;            // [0, 256): error word
     pl.off_err = 0;
     pl.off_ctr = off;            // 4 sync words per slab
@@ -1029,7 +1033,6 @@ Plan layout_ws(const Problem& p, bool backward, int64_t team_max) {
     pl.off_stot = off;
     if (backward) off += al((size_t)p.N * p.C * sizeof(float2));
     pl.total = off;
-    pl.cfg.team = (int32_t)team;
     return pl;
 }
 
@@ -1087,11 +1090,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     cfg.N = p.N; cfg.C = p.C; cfg.HW = p.HW; cfg.G = p.G; cfg.D = p.D; cfg.eps = a.eps;
     cfg.want_dx = 0; cfg.dgamma = nullptr; cfg.dbeta = nullptr;
     cfg.spin_limit = l.spin_limit; cfg.unmet = l.unmet_waits;
-    int64_t nteams = cap / cfg.team;
-    if (nteams > cfg.n_slabs) nteams = cfg.n_slabs;
-    if (nteams < 1) nteams = 1;
-    cfg.nteams = (int32_t)nteams;
-    const int64_t grid = nteams * cfg.team;
+    const int64_t grid = pl.grid;   // <= cap: every workgroup co-resident
     char* ws = (char*)l.ws;
     uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
     uint32_t* err = l.status_word ? l.status_word : (uint32_t*)(ws + pl.off_err);
@@ -1138,11 +1137,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     cfg.dgamma = one_slab_params ? a.dgamma : nullptr;
     cfg.dbeta = one_slab_params ? a.dbeta : nullptr;
     cfg.spin_limit = l.spin_limit; cfg.unmet = l.unmet_waits;
-    int64_t nteams = cap / cfg.team;
-    if (nteams > cfg.n_slabs) nteams = cfg.n_slabs;
-    if (nteams < 1) nteams = 1;
-    cfg.nteams = (int32_t)nteams;
-    const int64_t grid = nteams * cfg.team;
+    const int64_t grid = pl.grid;   // <= cap: every workgroup co-resident
     char* ws = (char*)l.ws;
     uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
     uint32_t* err = l.status_word ? l.status_word : (uint32_t*)(ws + pl.off_err);

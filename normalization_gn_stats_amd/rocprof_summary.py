@@ -57,7 +57,8 @@ def _get(row: dict, *names):
 def short_name(kernel: str) -> str:
     """Kernel name without namespaces, template arguments and parameter list
     (gn::(anonymous namespace)::slab_nchw_bwd<float, 8>(...) -> slab_nchw_bwd)."""
-    k = kernel.split("(")[0] if not kernel.startswith("void ") else kernel[5:].split("(")[0]
+    k = kernel[5:] if kernel.startswith("void ") else kernel
+    k = k.replace("(anonymous namespace)", "anonymous").split("(")[0]
     depth, base = 0, ""
     for ch in k:
         if ch == "<":

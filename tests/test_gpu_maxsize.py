@@ -3,10 +3,9 @@
 Each case has more than 2^31 elements per tensor, so that any 32-bit index in
 a kernel would wrap.  The oracle checks sampled slices -- those at the start,
 those whose offsets cross 2^31, and the last -- each on its own (a slice is
-its own GroupNorm problem with one group).  Where the oracle cannot run on the
-whole tensor, dbeta is checked by its closed form (the column sum of dy, here
-summed in float64 by torch on the device) and dgamma by the same sum of
-dy * xhat taken from the saved statistics.
+its own GroupNorm problem with one group), and dgamma/dbeta of every channel:
+the oracle runs over chunks of whole samples on the host and its per-chunk
+dgamma/dbeta are summed in float64.
 """
 import gc
 
@@ -51,27 +50,34 @@ def _check_slice(wl, data, out, n, g, eps, rtol, atol, tag):
           f"{tag} dx ({n},{g})")
 
 
-def _check_params_by_definition(wl, data, out, tag):
-    """dbeta_c = sum of dy over (n, p); dgamma_c = sum of dy * xhat with the
-    saved statistics; float64 on the device, in chunks of samples."""
-    dev = data["x"].device
-    D = wl.C // wl.G
-    db = torch.zeros(wl.C, dtype=torch.float64, device=dev)
-    dg = torch.zeros(wl.C, dtype=torch.float64, device=dev)
-    mean = out["mean"].reshape(wl.N, wl.G).double()
-    rstd = out["rstd"].reshape(wl.N, wl.G).double()
+def _check_params_with_oracle(wl, data, out, tag):
+    """dgamma/dbeta of all channels against the oracle, walked over chunks of
+    whole samples (a sample's slices hold every element its statistics
+    depend on): the oracle's dgamma/dbeta of each chunk, summed over the
+    chunks in float64 (the definition sums over n and p)."""
+    eps = float(np.float32(wl.eps))
+    gam = data["gamma"].double().cpu().numpy()
+    dg = np.zeros(wl.C, np.float64)
+    db = np.zeros(wl.C, np.float64)
     step = max(1, (1 << 27) // (wl.C * wl.HW))
     for n0 in range(0, wl.N, step):
         n1 = min(wl.N, n0 + step)
-        x = data["x"][n0:n1].double().reshape(n1 - n0, wl.C, wl.HW)
-        dy = data["dy"][n0:n1].double().reshape(n1 - n0, wl.C, wl.HW)
-        mu = mean[n0:n1].repeat_interleave(D, dim=1).unsqueeze(-1)
-        rs = rstd[n0:n1].repeat_interleave(D, dim=1).unsqueeze(-1)
-        db += dy.sum(dim=(0, 2))
-        dg += (dy * (x - mu) * rs).sum(dim=(0, 2))
-        del x, dy, mu, rs
-    rel_l2(out["dbeta"].cpu().numpy(), db.cpu().numpy(), f"{tag} dbeta", PARAM_REL_L2)
-    rel_l2(out["dgamma"].cpu().numpy(), dg.cpu().numpy(), f"{tag} dgamma", PARAM_REL_L2)
+        say(f"[max] {tag}: oracle dgamma/dbeta, samples {n0}..{n1 - 1}")
+        x = inputs.memory_image(data["x"][n0:n1].contiguous(
+            memory_format=torch.channels_last if wl.layout == "nhwc" else torch.contiguous_format), wl.layout)
+        dy = inputs.memory_image(data["dy"][n0:n1].contiguous(
+            memory_format=torch.channels_last if wl.layout == "nhwc" else torch.contiguous_format), wl.layout)
+        x64 = x.to("cpu", torch.float64).numpy()
+        dy64 = dy.to("cpu", torch.float64).numpy()
+        del x, dy
+        _, rdg, rdb, _, _ = oracle.backward(dy64, x64, gam, n1 - n0, wl.C, wl.HW, wl.G, eps, layout=wl.layout,
+                                            want_dx=False)
+        dg += rdg
+        db += rdb
+        del x64, dy64
+        gc.collect()
+    rel_l2(out["dbeta"].cpu().numpy(), db, f"{tag} dbeta", PARAM_REL_L2)
+    rel_l2(out["dgamma"].cpu().numpy(), dg, f"{tag} dgamma", PARAM_REL_L2)
 
 
 def _run_case(wl, force, expect, slices):
@@ -86,7 +92,7 @@ def _run_case(wl, force, expect, slices):
         say(f"[max] {wl.name}: slice ({n}, {g})")
         _check_slice(wl, data, out, n, g, eps, rtol, atol, wl.name)
     say(f"[max] {wl.name}: dgamma / dbeta")
-    _check_params_by_definition(wl, data, out, wl.name)
+    _check_params_with_oracle(wl, data, out, wl.name)
     say(f"[max] {wl.name}: within tolerance")
     del data, out
     _free()

@@ -232,9 +232,9 @@ def main():
                 "avg_us": round(dom["main_kernel_us"], 3), "algorithmic_bytes": dom["main_kernel_bytes"],
                 "timing": ("HIP events (created without the system-scope fence) recorded by the library on "
                            "the call's stream around the main kernel "
-                           "(stream and generic paths: around all kernels of the call), "
-                           + ("K eager steps queued behind a GPU spin after the graph-timed region"
-                              if head["mode"] == "graph" else "over the timed region"))}
+                           "(stream and generic paths: around all kernels of the call), in a pass of K eager "
+                           "steps of their own " + ("queued behind a GPU spin after the graph-timed region"
+                                                    if head["mode"] == "graph" else "after the timed region"))}
 
     # measured device-to-device copy of 1 GiB (read + write), the practical
     # ceiling of a streaming kernel on this part: a second denominator
@@ -393,7 +393,8 @@ def measure(workload, K, W, mode, force_path, keep_inputs=False):
     L = gn._lib.lib()
 
     def calls_for(sh, stream_handle, evs):
-        """evs: None, or per call kind ((call_begin, call_end), (kernel_begin, kernel_end))."""
+        """evs: None, or per call kind ((call_begin, call_end), (kernel_begin, kernel_end)),
+        either pair None."""
         wl = sh["wl"]
         code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
         lay = gn.GN_NCHW if (wl.op == "rms" or wl.crop) else gn.layout_of(sh["x"])
@@ -404,9 +405,11 @@ def measure(workload, K, W, mode, force_path, keep_inputs=False):
             o.force_path = {None: 0, "generic": 1, "rows": 2, "slab": 3, "stream": 4}[force_path]
             o.info = ctypes.pointer(sh["fplan" if kind == "fwd" else "bplan"])
             if evs is not None:
-                (cb, ce), (kb, ke) = evs[0 if kind == "fwd" else 1]
-                o.event_begin, o.event_end = ctypes.c_void_p(cb), ctypes.c_void_p(ce)
-                o.kernel_begin, o.kernel_end = ctypes.c_void_p(kb), ctypes.c_void_p(ke)
+                cpair, kpair = evs[0 if kind == "fwd" else 1]
+                if cpair is not None:
+                    o.event_begin, o.event_end = ctypes.c_void_p(cpair[0]), ctypes.c_void_p(cpair[1])
+                if kpair is not None:
+                    o.kernel_begin, o.kernel_end = ctypes.c_void_p(kpair[0]), ctypes.c_void_p(kpair[1])
             if wl.op == "rms" and kind == "fwd":
                 a = (P(sh["x"]), P(sh["gamma"]), P(sh["y"]), P(sh["rstd"]), wl.N, wl.C, wl.G, ctypes.c_float(wl.eps),
                      code, P(sh["fws"]), sh["fws"].numel(), ctypes.c_void_p(stream_handle), ctypes.byref(o))
@@ -473,14 +476,20 @@ def measure(workload, K, W, mode, force_path, keep_inputs=False):
         graph.replay()             # first replay uploads the graph
         torch.cuda.synchronize()
 
-    # per step, per shape, per call (fwd, bwd): (call events, kernel events)
+    # per step, per shape, per call (fwd, bwd): call events and kernel events,
+    # recorded in separate passes so that neither pair brackets the other's
+    # records (an event record between two kernels costs about a microsecond)
     tev = TimingEvents()
 
     def ev_pair():
         return (tev.new(), tev.new())
 
-    events = [[[(ev_pair(), ev_pair()) for _ in range(2)] for _ in shapes] for _ in range(K)]
-    evcalls = [[c for k, sh in enumerate(shapes) for c in calls_for(sh, sp, events[i][k])] for i in range(K)]
+    cev = [[[ev_pair() for _ in range(2)] for _ in shapes] for _ in range(K)]
+    kev = [[[ev_pair() for _ in range(2)] for _ in shapes] for _ in range(K)]
+    call_pass = [[c for k, sh in enumerate(shapes)
+                  for c in calls_for(sh, sp, [(cev[i][k][0], None), (cev[i][k][1], None)])] for i in range(K)]
+    kern_pass = [[c for k, sh in enumerate(shapes)
+                  for c in calls_for(sh, sp, [(None, kev[i][k][0]), (None, kev[i][k][1])])] for i in range(K)]
 
     log(f"timing {K} steps ({mode})")
     torch.cuda.synchronize()
@@ -488,16 +497,15 @@ def measure(workload, K, W, mode, force_path, keep_inputs=False):
     if graph is not None:
         graph.replay()
     else:
-        for cl in evcalls:
+        for cl in call_pass:   # eager: the call events ride in the timed steps
             run(cl)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
 
-    if graph is not None:
-        # Call and kernel durations: the same K steps issued eagerly with the
-        # library's events, queued behind a GPU spin so that the kernels run
-        # back to back and each event pair brackets its own work only.
+    def behind_spin(passes):
+        """The passes' K steps issued eagerly behind a GPU spin, so that the
+        kernels run back to back (the host is not in the loop)."""
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record(stream)
         torch.cuda._sleep(1_000_000)
@@ -506,7 +514,15 @@ def measure(workload, K, W, mode, force_path, keep_inputs=False):
         cycles_per_ms = 1_000_000 / max(c0.elapsed_time(c1), 1e-3)
         host_ms = warm_ms * K * 3 + 20.0
         torch.cuda._sleep(int(cycles_per_ms * host_ms))
-        for cl in evcalls:
+        for cl in passes:
+            run(cl)
+        torch.cuda.synchronize()
+
+    if graph is not None:
+        behind_spin(call_pass)
+        behind_spin(kern_pass)
+    else:
+        for cl in kern_pass:
             run(cl)
         torch.cuda.synchronize()
 
@@ -526,8 +542,8 @@ def measure(workload, K, W, mode, force_path, keep_inputs=False):
                 # the main backward kernel writes dx; dgamma/dbeta (2*C*4 bytes) are
                 # written by the small column-sum kernel when one follows
                 nbytes = call_bytes - (2 * wl.C * 4 if plan.kernels > 1 else 0)
-            call_ms = [tev.elapsed_ms(*events[i][k][c][0]) for i in range(K)]
-            kern_ms = [tev.elapsed_ms(*events[i][k][c][1]) for i in range(K)]
+            call_ms = [tev.elapsed_ms(*cev[i][k][c]) for i in range(K)]
+            kern_ms = [tev.elapsed_ms(*kev[i][k][c]) for i in range(K)]
             call_avg = sum(call_ms) / K
             kern_avg = sum(kern_ms) / K
             # kernels that can be the call's main kernel (the rows path picks one of
@@ -552,17 +568,17 @@ def measure(workload, K, W, mode, force_path, keep_inputs=False):
     if mode == "graph":
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         reps = min(K, 20)
-        fev = [[[(ev_pair(), ev_pair()) for _ in range(2)] for _ in shapes] for _ in range(reps)]
+        fev = [[[ev_pair() for _ in range(2)] for _ in shapes] for _ in range(reps)]
         for i in range(reps):
             for k, sh in enumerate(shapes):
-                for call in calls_for(sh, sp, fev[i][k]):
+                for call in calls_for(sh, sp, [(fev[i][k][0], None), (fev[i][k][1], None)]):
                     scratch.fill_(i & 0xFF)
                     run([call])
         torch.cuda.synchronize()
         flushed = {}
         for k, sh in enumerate(shapes):
             for c, kind in enumerate(("fwd", "bwd")):
-                d = [tev.elapsed_ms(*fev[i][k][c][0]) for i in range(reps)]
+                d = [tev.elapsed_ms(*fev[i][k][c]) for i in range(reps)]
                 flushed[f"{kind}:{sh['wl'].name}"] = round(1e3 * sum(d) / len(d), 3)
         del scratch
     tev.close()

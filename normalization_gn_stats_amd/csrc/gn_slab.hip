@@ -979,9 +979,24 @@ struct Plan {
     size_t ones_end;   // [off_part, ones_end): filled with ones each call (NCHW partial words)
 };
 
+// Slabs of at most this many bytes (per tensor) are processed by one
+// workgroup each, launched normally: there is no exchange between workgroups,
+// and the cooperative launch, whose cost is fixed, would dominate such calls
+// (graphs of 50 back-to-back calls: 2 x 32 x 16 x 16 fp32 forward 25 -> 9.2 us,
+// backward 27.7 -> 11 us; 16 x 128 x 64 x 64 fp16 G=32 32.5 -> 16 us).  Up to
+// 128 KiB slabs still gain on their own (8 x 64 x 64 x 64 fp32: 26.6 -> 18.4
+// us), but graphs captured with such launches slowed later graphs of
+// cooperative launches in the same process threefold, which eager launches
+// did not; 512 KiB slabs run faster cooperatively.
+#ifndef GN_SLAB_SOLO_BYTES
+#define GN_SLAB_SOLO_BYTES 65536
+#endif
+
 // The schedule of this problem for a resident-workgroup cap (gn_slab_plan.hpp).
 slab::Geometry geometry(const Problem& p, int R, int64_t cap) {
-    return slab::plan(p.layout == GN_NHWC, p.N, p.C, p.HW, p.G, vec_elems(p), R, cap);
+    const int64_t slab_bytes = (p.layout == GN_NHWC ? p.C : p.D) * p.HW * p.elem_bytes;
+    const int64_t max_team = slab_bytes <= (int64_t)GN_SLAB_SOLO_BYTES ? 1 : INT64_MAX;
+    return slab::plan(p.layout == GN_NHWC, p.N, p.C, p.HW, p.G, vec_elems(p), R, cap, max_team);
 }
 
 int64_t tiles_per_slab(const Problem& p, int R, int64_t* tpc) {

@@ -44,10 +44,11 @@ GN_HD constexpr int64_t nhwc_tile_pixels(int64_t C, int V, int R) { return (int6
 GN_HD constexpr int64_t nchw_tile_elems(int V, int R) { return (int64_t)kThreads * R * V; }
 
 // The plan for a resident-workgroup cap `cap` (>= 1): the team is the slab's
-// tile count or the cap, whichever is smaller; as many teams as the cap holds,
-// at most one per slab.  Hence grid <= cap, and every slab is walked by
-// exactly one team.
-inline Geometry plan(bool nhwc, int64_t N, int64_t C, int64_t HW, int64_t G, int V, int R, int64_t cap) {
+// tile count, the cap or `max_team`, whichever is smallest; as many teams as
+// the cap holds, at most one per slab.  Hence grid <= cap, and every slab is
+// walked by exactly one team.
+inline Geometry plan(bool nhwc, int64_t N, int64_t C, int64_t HW, int64_t G, int V, int R, int64_t cap,
+                     int64_t max_team = INT64_MAX) {
     Geometry g{};
     const int64_t D = C / G;
     if (nhwc) {
@@ -64,6 +65,7 @@ inline Geometry plan(bool nhwc, int64_t N, int64_t C, int64_t HW, int64_t G, int
     g.pstride = (g.tiles + 15) / 16 * 16;
     if (cap < 1) cap = 1;
     g.team = g.tiles < cap ? g.tiles : cap;
+    if (g.team > max_team) g.team = max_team;
     if (g.team < 1) g.team = 1;
     g.nteams = cap / g.team;
     if (g.nteams > g.n_slabs) g.nteams = g.n_slabs;

@@ -54,9 +54,29 @@ def _get(row: dict, *names):
     raise KeyError(f"none of {names} in {sorted(low)}")
 
 
+def _mangled_last_name(kernel: str):
+    """Last identifier of an Itanium-mangled nested name
+    (_ZN2gn12_GLOBAL__N_110rows_bwd_kI... -> rows_bwd_k), or None."""
+    if not kernel.startswith("_ZN"):
+        return None
+    i, last = 3, None
+    while i < len(kernel) and kernel[i].isdigit():
+        j = i
+        while j < len(kernel) and kernel[j].isdigit():
+            j += 1
+        n = int(kernel[i:j])
+        last = kernel[j:j + n]
+        i = j + n
+    return last
+
+
 def short_name(kernel: str) -> str:
     """Kernel name without namespaces, template arguments and parameter list
-    (gn::(anonymous namespace)::slab_nchw_bwd<float, 8>(...) -> slab_nchw_bwd)."""
+    (gn::(anonymous namespace)::slab_nchw_bwd<float, 8>(...) -> slab_nchw_bwd;
+    mangled names as rocprofv3 reports some template kernels likewise)."""
+    m = _mangled_last_name(kernel)
+    if m:
+        return m
     k = kernel[5:] if kernel.startswith("void ") else kernel
     k = k.replace("(anonymous namespace)", "anonymous").split("(")[0]
     depth, base = 0, ""
@@ -118,7 +138,9 @@ def counters(pmc_dir: str, counter: str) -> list[tuple[str, int, float]]:
 def calibration(values: list[tuple[str, int, float]], copy_mib: int) -> float:
     """Bytes per counter unit: copy_mib MiB over the counter of the copy
     dispatches (the three largest dispatches of a copy kernel, median)."""
-    copies = sorted((v for n, _, v in values if "copy" in n.lower()), reverse=True)[:3]
+    # the runtime's device-to-device blit kernel (torch's copy_ of a same-dtype
+    # buffer), not other kernels whose names mention a copy (dtype conversions)
+    copies = sorted((v for n, _, v in values if n.startswith("__amd_rocclr_copyBuffer")), reverse=True)[:3]
     if not copies:
         raise ValueError("no copy kernel dispatches to calibrate the counter with")
     return copy_mib * (1 << 20) / statistics.median(copies)
@@ -172,6 +194,7 @@ def summarize(workload: str, trace: str, fetch: str, write: str, copy_mib: int, 
                          write=(statistics.mean(wr) * w_scale if wr else None)))
     rows.sort(key=lambda r: -r["avg_us"] * r["dispatches"])
     mains = [r["kernel"] for r in rows[:2]]
+    calls = call_totals(rows)
     fname = "_".join(dict.fromkeys(mains)) + f"__{workload}.md"
     lines = [f"# rocprofv3 summary: GroupNorm kernels on workload `{workload}`", "",
              "Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
@@ -192,7 +215,7 @@ def summarize(workload: str, trace: str, fetch: str, write: str, copy_mib: int, 
               "file): " + ", ".join(f"{f} `{h}`" for f, h in fps), "",
               "| kernel | workgroups | dispatches | avg duration (µs) | HBM read (MiB, scaled) | HBM write (MiB, scaled) |",
               "|---|---|---|---|---|---|"]
-    for r in rows:
+    for r in rows + calls:
         rd = f"{r['read'] / 2**20:.1f}" if r["read"] is not None else "—"
         wr = f"{r['write'] / 2**20:.1f}" if r["write"] is not None else "—"
         lines.append(f"| {r['kernel']} | {r['workgroups']} | {r['dispatches']} | {r['avg_us']:.2f} | {rd} | {wr} |")
@@ -218,7 +241,7 @@ def summarize(workload: str, trace: str, fetch: str, write: str, copy_mib: int, 
     ks = traffic.setdefault("kernels", {})
     for k in [k for k in ks if k.startswith(f"{workload}|")]:
         del ks[k]
-    for r in rows:
+    for r in rows + calls:
         ks[f"{workload}|{r['kernel']}|{r['workgroups']}"] = dict(
             avg_us=round(r["avg_us"], 3), read_bytes=r["read"], write_bytes=r["write"],
             source_fingerprint=fingerprint(r["kernel"]))
@@ -226,6 +249,36 @@ def summarize(workload: str, trace: str, fetch: str, write: str, copy_mib: int, 
         json.dump(traffic, fh, indent=1, sort_keys=True)
         fh.write("\n")
     return os.path.join(profiles, fname)
+
+
+# Kernels of one call of the multi-kernel paths (stream, generic): the first
+# is the anchor whose dispatch count is the number of calls.
+CALLS = {
+    "stream_fwd_call": ("fwd_tile_stats", "fwd_finalize", "fwd_apply"),
+    "stream_bwd_call": ("bwd_tile_sums", "col_sums", "bwd_group_ab", "params_over_n", "bwd_dx"),
+    "generic_fwd_call": ("gen_stats_partial", "gen_stats_final", "gen_apply"),
+    "generic_bwd_call": ("gen_dx", "gen_ab_partial", "gen_param_partial", "gen_plane_ab", "gen_plane_params",
+                         "gen_plane_partial", "gen_sum_rows"),
+}
+
+
+def call_totals(rows: list) -> list:
+    """Per call of a multi-kernel path: the sums over its kernels of the
+    time and bytes per call (every dispatch of a member kernel, divided by
+    the anchor's dispatch count)."""
+    out = []
+    for call, members in CALLS.items():
+        anchor = [r for r in rows if r["kernel"] == members[0]]
+        if not anchor:
+            continue
+        n = sum(r["dispatches"] for r in anchor)
+        mem = [r for r in rows if r["kernel"] in members]
+        tot = lambda k: (sum(r[k] * r["dispatches"] for r in mem) / n
+                         if all(r[k] is not None for r in mem) else None)
+        out.append(dict(kernel=call, full=call, workgroups="call", dispatches=n,
+                        avg_us=sum(r["avg_us"] * r["dispatches"] for r in mem) / n,
+                        read=tot("read"), write=tot("write")))
+    return out
 
 
 def KERNEL_SOURCES_FILE(kernel: str) -> str:

@@ -70,7 +70,7 @@ CONFIGS = (
 
 
 # The source file that defines each kernel (by name prefix) or each whole call;
-# every kernel also depends on the shared headers and the C-ABI file.
+# a kernel also depends on the local headers that file includes.
 KERNEL_SOURCES = (
     (("rows_",), "gn_rows.hip"),
     (("slab_", "clear_words", "params_over_n"), "gn_slab.hip"),
@@ -78,24 +78,35 @@ KERNEL_SOURCES = (
       "stream_"), "gn_stream.hip"),
     (("gen_", "generic_"), "gn_generic.hip"),
 )
-COMMON_SOURCES = ("gn_device.hpp", "gn_internal.hpp", "gn_api.cpp", "gn_slab_plan.hpp")
+CSRC = os.path.join(HERE, "normalization_gn_stats_amd", "csrc")
 
 
-def source_fingerprint(kernel_name: str) -> str:
-    """sha256 over the sources a kernel is built from (its own .hip file, the
-    shared headers and the C-ABI file), to tell whether byte counters recorded
-    in profiles/traffic.json still describe the kernel built now."""
-    import hashlib
+def source_files(kernel_name: str) -> list:
+    """Paths of the sources a kernel is compiled from: its .hip file and every
+    local header it includes ("..." includes, followed transitively)."""
+    import re
     own = [f for prefixes, f in KERNEL_SOURCES if kernel_name.startswith(prefixes)]
     if not own:
         raise KeyError(f"no source file known for kernel {kernel_name}")
-    h = hashlib.sha256()
-    d = os.path.join(HERE, "normalization_gn_stats_amd", "csrc")
-    for f in sorted(COMMON_SOURCES + (own[0],)):
-        p = os.path.join(d, f)
-        if not os.path.exists(p):
+    seen, todo = [], [os.path.normpath(os.path.join(CSRC, own[0]))]
+    while todo:
+        p = todo.pop()
+        if p in seen:
             continue
-        h.update(f.encode())
+        seen.append(p)
+        for inc in re.findall(r'^\s*#\s*include\s+"([^"]+)"', open(p).read(), re.M):
+            todo.append(os.path.normpath(os.path.join(os.path.dirname(p), inc)))
+    return sorted(seen)
+
+
+def source_fingerprint(kernel_name: str) -> str:
+    """sha256 over the sources a kernel is compiled from, to tell whether byte
+    counters recorded in profiles/traffic.json still describe the kernel built
+    now."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in source_files(kernel_name):
+        h.update(os.path.relpath(p, CSRC).encode())
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 

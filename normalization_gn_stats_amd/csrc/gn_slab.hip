@@ -705,7 +705,7 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
         __builtin_amdgcn_sched_barrier(0);   // keep the two slabs' phases apart
         nchw_fwd_phase2<T, R>(x, gamma, beta, y, mean, rstd, cfg, sb, m, last, cur, gcur, part, err, lds);
         if (!more) break;
-#pragma unroll
+        // register moves (folded into one copy before unrolling: no pragma)
         for (int j = 0; j < R; ++j) cur[j] = nxt[j];
         gcur = gnxt;
         last = nlast;
@@ -886,8 +886,7 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
         nchw_bwd_phase2<T, R>(dy, x, gamma, dx, cfg, sb, m, last, mu, r, cx, cd, gam, part, err, stot, stage,
                               chan, gch);
         if (!more) break;
-#pragma unroll
-        for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }
+        for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }   // register moves
         last = nlast;
         sb = nsb;
         mu = nmu;

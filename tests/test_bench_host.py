@@ -26,8 +26,16 @@ def test_kernel_source_table_names_existing_files():
     d = os.path.join(ROOT, "normalization_gn_stats_amd", "csrc")
     for _, f in bench.KERNEL_SOURCES:
         assert os.path.exists(os.path.join(d, f)), f
-    for f in bench.COMMON_SOURCES:
-        assert os.path.exists(os.path.join(d, f)), f
+
+
+def test_fingerprint_covers_the_included_headers_only():
+    names = lambda k: {os.path.basename(p) for p in bench.source_files(k)}
+    assert names("slab_nchw_bwd") == {"gn_slab.hip", "gn_device.hpp", "gn_internal.hpp", "gn_slab_plan.hpp", "gn.h"}
+    assert names("rows_bwd_k") == {"gn_rows.hip", "gn_device.hpp", "gn_internal.hpp", "gn.h"}
+    assert names("bwd_dx") == {"gn_stream.hip", "gn_device.hpp", "gn_internal.hpp", "gn.h"}
+    assert names("gen_dx") == {"gn_generic.hip", "gn_device.hpp", "gn_internal.hpp", "gn.h"}
+    for k in ("slab_nchw_bwd", "rows_bwd_k", "bwd_dx", "gen_dx"):
+        assert all(os.path.exists(p) for p in bench.source_files(k))
 
 
 def test_unknown_kernel_name_is_an_error():

@@ -133,8 +133,9 @@ typedef struct gn_options {
                                        the kernels OR GN_STATUS_WAIT_EXPIRED into it
                                        when a wait gives up; never cleared by the
                                        library (the caller zeroes it) */
-    uint32_t spin_limit;            /* polls before a wait gives up; 0 = default (2^25,
-                                       about a second) */
+    uint32_t spin_limit;            /* polls before a wait gives up; 0 = default (2^20;
+                                       a poll follows a sleep of 0.1 to 3.4 us,
+                                       so the default gives up within seconds) */
     uint32_t debug_flags;           /* 0, or GN_DEBUG_UNMET_WAITS (tests only) */
 } gn_options;
 

@@ -60,10 +60,11 @@ struct Launch {
     uint32_t unmet_waits;  // 1: every wait's target out of reach (failure-report tests)
 };
 
-// Polls before a bounded wait between workgroups gives up (2^25 polls with a
-// short sleep each: about a second, far above the longest legitimate wait of
-// a few milliseconds).
-constexpr uint32_t kDefaultSpinLimit = 1u << 25;
+// Polls before a bounded wait between workgroups gives up: 2^20 polls, each
+// after a sleep of 128 to 8128 clocks depending on the wait (about 0.1 to 3.4
+// us), i.e. at most a few seconds -- far above the longest legitimate wait of
+// a few milliseconds.
+constexpr uint32_t kDefaultSpinLimit = 1u << 20;
 
 // Device facts used by the planner (queried once per device).
 struct DeviceInfo {

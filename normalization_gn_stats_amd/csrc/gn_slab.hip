@@ -460,15 +460,36 @@ __device__ inline uint64_t peek_partial(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Sleep between two reads of a word not yet published, in units of 64
+// clocks (s_sleep), per kernel.  Every member of a team polls all of its
+// slab's words at once, so each round of re-reads puts one agent-scope load
+// per word and member in front of the bulk traffic at the coherence point;
+// polling slowly leaves HBM to the data.  112 x 64 x 512 x 512 fp32, three
+// alternating rounds: backward 4028-4042 us with a sleep of 1, 3988-4016 with
+// 8, 3886-3906 with 32, 3837-3871 with 64, 3877-3897 with 127; forward
+// 2632-2637 us with 1, 2597-2612 with 64, 2569-2575 with 127.
+#ifndef GN_SLAB_POLL_SLEEP_F
+#define GN_SLAB_POLL_SLEEP_F 127
+#endif
+#ifndef GN_SLAB_POLL_SLEEP_B
+#define GN_SLAB_POLL_SLEEP_B 64
+#endif
+static_assert(GN_SLAB_POLL_SLEEP_F >= 1 && GN_SLAB_POLL_SLEEP_F <= 127, "s_sleep takes 1..127");
+static_assert(GN_SLAB_POLL_SLEEP_B >= 1 && GN_SLAB_POLL_SLEEP_B <= 127, "s_sleep takes 1..127");
+
 // Waits until *p is published, w being a first read of it; returns (lo, hi).
 // Bounded: after cfg.spin_limit polls it ORs kWaitExpired into *err and
 // returns NaNs, which every sum, statistic and output derived from the
 // partial then carries.  cfg.unmet (tests of the failure report) makes every
 // word read as unpublished.
+template <int kSleep>
 __device__ inline float2 settle_partial(const uint64_t* p, uint64_t w, const SlabCfg& cfg, uint32_t* err) {
     uint32_t spins = 0;
     while (unpublished(w) || cfg.unmet) {
-        __builtin_amdgcn_s_sleep(1);
+        if (cfg.team == 1)
+            __builtin_amdgcn_s_sleep(1);   // the workgroup's own word, about to land
+        else
+            __builtin_amdgcn_s_sleep(kSleep);
         if (++spins > cfg.spin_limit) {
             __hip_atomic_fetch_or(err, kWaitExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             w = ~0ull;   // both halves NaN
@@ -479,8 +500,9 @@ __device__ inline float2 settle_partial(const uint64_t* p, uint64_t w, const Sla
     return make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
 }
 
+template <int kSleep>
 __device__ inline float2 poll_partial(const uint64_t* p, const SlabCfg& cfg, uint32_t* err) {
-    return settle_partial(p, peek_partial(p), cfg, err);
+    return settle_partial<kSleep>(p, peek_partial(p), cfg, err);
 }
 
 // Elements of NCHW tile `tile` (the last tile of each channel plane may be
@@ -613,14 +635,14 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
         const int64_t i = t + (int64_t)k * kT;
         keep[k] = make_float2(0.f, 0.f);
         if (i < cfg.tiles) {
-            keep[k] = settle_partial(ps + i, w[k], cfg, err);
+            keep[k] = settle_partial<GN_SLAB_POLL_SLEEP_F>(ps + i, w[k], cfg, err);
             const float c = nchw_tile_count(cfg, i, TE);
             sums[0] = fmaf(c, keep[k].x, sums[0]);
             sums[1] += c;
         }
     }
     for (int64_t i = t + (int64_t)kKeep * kT; i < cfg.tiles; i += kT) {
-        const float2 v = poll_partial(ps + i, cfg, err);
+        const float2 v = poll_partial<GN_SLAB_POLL_SLEEP_F>(ps + i, cfg, err);
         const float c = nchw_tile_count(cfg, i, TE);
         sums[0] = fmaf(c, v.x, sums[0]);
         sums[1] += c;
@@ -638,7 +660,7 @@ __device__ inline void nchw_fwd_phase2(const T* __restrict__ x, const float* __r
         }
     }
     for (int64_t i = t + (int64_t)kKeep * kT; i < cfg.tiles; i += kT) {
-        const float2 v = poll_partial(ps + i, cfg, err);   // published: returns at once
+        const float2 v = poll_partial<GN_SLAB_POLL_SLEEP_F>(ps + i, cfg, err);   // published: returns at once
         const float c = nchw_tile_count(cfg, i, TE);
         const float d = v.x - mu;
         m2[0] += fmaf(c * d, d, v.y);
@@ -785,7 +807,7 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t i = t + (int64_t)k * kT;
-            if (i < cnt) stage[i] = settle_partial(ps + i, w[k], cfg, err);
+            if (i < cnt) stage[i] = settle_partial<GN_SLAB_POLL_SLEEP_B>(ps + i, w[k], cfg, err);
         }
         __syncthreads();
         if (t < cfg.D) {

@@ -204,7 +204,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this GroupNorm engine "
-              "runs on a single MI355X (how it would shard across GPUs is described in DESIGN.md)",
+              "runs on a single MI355X: slices are independent per sample, so data parallelism over N needs only "
+              "an all-reduce of dgamma/dbeta, which this library leaves to the caller",
               file=sys.stderr)
         sys.exit(2)
 

@@ -46,6 +46,7 @@ WORKLOADS = {
     "rows_f16_8192x768": ("rows_f16_8192x768",),
     "nhwc_f16_1x128x1024x2048_g16": ("nhwc_f16_1x128x1024x2048_g16",),
     "nchw_f32_112x64x512x512_g8": ("nchw_f32_112x64x512x512_g8",),
+    "nchw_bf16_112x64x512x512_g8": ("nchw_bf16_112x64x512x512_g8",),
     "rows_bf16_131072x4096": ("rows_bf16_131072x4096",),
     "rows_f16_131072x64": ("rows_f16_131072x64",),
     # RMSNorm over rows (gn_rms_forward / gn_rms_backward)

@@ -464,18 +464,24 @@ __device__ inline uint64_t peek_partial(const uint64_t* p) {
 // clocks (s_sleep), per kernel.  Every member of a team polls all of its
 // slab's words at once, so each round of re-reads puts one agent-scope load
 // per word and member in front of the bulk traffic at the coherence point;
-// polling slowly leaves HBM to the data.  112 x 64 x 512 x 512 fp32, three
-// alternating rounds: backward 4028-4042 us with a sleep of 1, 3988-4016 with
-// 8, 3886-3906 with 32, 3837-3871 with 64, 3877-3897 with 127; forward
-// 2632-2637 us with 1, 2597-2612 with 64, 2569-2575 with 127.
+// polling slowly leaves HBM to the data.  112 x 64 x 512 x 512, three
+// alternating rounds: fp32 backward 4028-4042 us with a sleep of 1, 3988-4016
+// with 8, 3886-3906 with 32, 3837-3871 with 64, 3877-3897 with 127; fp32
+// forward 2632-2637 us with 1, 2597-2612 with 64, 2569-2575 with 127; bf16
+// backward (twice the tiles per slab) 2206-2211 us with 32, 2173-2177 with 64,
+// 2153-2157 with 127.
 #ifndef GN_SLAB_POLL_SLEEP_F
 #define GN_SLAB_POLL_SLEEP_F 127
 #endif
 #ifndef GN_SLAB_POLL_SLEEP_B
-#define GN_SLAB_POLL_SLEEP_B 64
+#define GN_SLAB_POLL_SLEEP_B 64     // fp32
+#endif
+#ifndef GN_SLAB_POLL_SLEEP_B16
+#define GN_SLAB_POLL_SLEEP_B16 127  // fp16, bf16
 #endif
 static_assert(GN_SLAB_POLL_SLEEP_F >= 1 && GN_SLAB_POLL_SLEEP_F <= 127, "s_sleep takes 1..127");
 static_assert(GN_SLAB_POLL_SLEEP_B >= 1 && GN_SLAB_POLL_SLEEP_B <= 127, "s_sleep takes 1..127");
+static_assert(GN_SLAB_POLL_SLEEP_B16 >= 1 && GN_SLAB_POLL_SLEEP_B16 <= 127, "s_sleep takes 1..127");
 
 // Waits until *p is published, w being a first read of it; returns (lo, hi).
 // Bounded: after cfg.spin_limit polls it ORs kWaitExpired into *err and
@@ -807,7 +813,9 @@ __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __rest
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t i = t + (int64_t)k * kT;
-            if (i < cnt) stage[i] = settle_partial<GN_SLAB_POLL_SLEEP_B>(ps + i, w[k], cfg, err);
+            if (i < cnt)
+                stage[i] = settle_partial<sizeof(T) == 4 ? GN_SLAB_POLL_SLEEP_B : GN_SLAB_POLL_SLEEP_B16>(
+                    ps + i, w[k], cfg, err);
         }
         __syncthreads();
         if (t < cfg.D) {

@@ -91,6 +91,8 @@ ROWS_B = Workload("rows_f16_8192x768", 8192, 768, 1, 1, 1, "f16", "nchw")
 NHWC_IMG = Workload("nhwc_f16_1x128x1024x2048_g16", 1, 128, 1024, 2048, 16, "f16", "nhwc", affine="n01")
 NCHW_BIG = Workload("nchw_f32_112x64x512x512_g8", 112, 64, 512, 512, 8, "f32", "nchw")
 ROWS_BIG = Workload("rows_bf16_131072x4096", 131072, 4096, 1, 1, 1, "bf16", "nchw")
+# The NCHW configuration's shape in bf16 (the same slab kernels at 2-byte elements).
+NCHW_BIG_BF16 = Workload("nchw_bf16_112x64x512x512_g8", 112, 64, 512, 512, 8, "bf16", "nchw")
 # Narrow rows with many of them (the "huge M" LayerNorm shape of the same table).
 ROWS_NARROW = Workload("rows_f16_131072x64", 131072, 64, 1, 1, 1, "f16", "nchw")
 
@@ -106,7 +108,7 @@ RMS_NARROW = Workload("rms_f16_131072x64", 131072, 64, 1, 1, 1, "f16", "nchw", e
 CROP_BIG = Workload("nchw_f32_112x64x510x510_g8_crop1", 112, 64, 510, 510, 8, "f32", "nchw", crop=1)
 CROP_TINY = Workload("tiny_nchw_f32_2x32x14x14_g8_crop1", 2, 32, 14, 14, 8, "f32", "nchw", crop=1)
 
-WORKLOADS = {w.name: w for w in (TINY, ROWS_A, ROWS_B, NHWC_IMG, NCHW_BIG, ROWS_BIG, ROWS_NARROW,
+WORKLOADS = {w.name: w for w in (TINY, ROWS_A, ROWS_B, NHWC_IMG, NCHW_BIG, NCHW_BIG_BF16, ROWS_BIG, ROWS_NARROW,
                                  RMS_A, RMS_BIG, RMS_NARROW, CROP_BIG, CROP_TINY)}
 
 

@@ -103,10 +103,16 @@ int32_t plan(const Problem& p, bool backward, const gn_options* opts) {
     if (f == GN_PATH_STREAM) return gn::stream_ok(p) ? GN_PATH_STREAM : -1;
     if (f != GN_PATH_AUTO) return -1;
     if (gn::rows_ok(p)) return GN_PATH_ROWS;
-    // NHWC: the cooperative slab kernels when a sample fits the co-resident
-    // grid; the stream kernels for larger samples and for channel counts the
-    // slab kernels do not take
-    if (gn::stream_ok(p) && (!gn::slab_ok(p) || !gn::slab_resident(p, backward))) return GN_PATH_STREAM;
+    // NHWC: the stream kernels whenever they take the shape.  Against the
+    // cooperative slab kernels they measured 2-6x faster at every NHWC size
+    // tried (fp16/fp32, 2x32x16x16 to 16x256x64x64 and 1x128x512x512,
+    // forward and backward, graph or eager): at these sizes the cooperative
+    // launch and the two team barriers per slab cost more than the second
+    // read of each tile saves, and on the 1x128x1024x2048 image the slab
+    // kernels re-read almost every tile anyway.  The slab kernels take the
+    // NHWC shapes beyond the stream grid (more than 65535 samples), and NCHW.
+    (void)backward;
+    if (gn::stream_ok(p)) return GN_PATH_STREAM;
     if (gn::slab_ok(p)) return GN_PATH_SLAB;
     return GN_PATH_GENERIC;
 }

@@ -107,7 +107,6 @@ size_t slab_fwd_ws(const Problem& p);
 size_t slab_bwd_ws(const Problem& p, int32_t mask);
 hipError_t slab_fwd(const Problem& p, const FwdArgs& a, const Launch& l);
 hipError_t slab_bwd(const Problem& p, const BwdArgs& a, const Launch& l);
-bool slab_resident(const Problem& p, bool backward);   // a slab fits the co-resident grid
 
 // ---- stream path: NHWC as a few launches of one tile per workgroup ----------
 bool stream_ok(const Problem& p);

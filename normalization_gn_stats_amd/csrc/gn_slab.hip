@@ -1238,15 +1238,6 @@ bool slab_ok(const Problem& p) {
     return p.HW >= V && p.D <= kT;      // channel sums of a slab: one thread per channel
 }
 
-// True when one slab's tiles do not outnumber the workgroups an MI355X keeps
-// resident (256 CUs x 4), i.e. the cooperative grid can hold the whole slab in
-// registers; a fixed figure, so that the choice does not depend on the device.
-bool slab_resident(const Problem& p, bool backward) {
-    constexpr int64_t kResidentTiles = 1024;
-    int64_t tpc;
-    return tiles_per_slab(p, tile_chunks(p, backward), &tpc) <= kResidentTiles;
-}
-
 size_t slab_fwd_ws(const Problem& p) {
     int64_t tpc;
     return layout_ws(p, false, tiles_per_slab(p, tile_chunks(p, false), &tpc)).total;

@@ -149,10 +149,14 @@ def test_path_selection(L):
     assert sel(0, 4, 36, 1, 1, F16, NCHW, _lib.GN_PATH_ROWS) == -1         # forced path cannot serve
     assert sel(0, 2, 8, 4, 2, F32, NCHW, _lib.GN_PATH_GENERIC) == _lib.GN_PATH_GENERIC
     assert sel(0, 2, 8, 4, 3, F32, NCHW) == -1
-    # NHWC: a sample far beyond the co-resident grid streams; a small one stays cooperative
+    # NHWC streams at every size the stream kernels take (measured faster than
+    # the cooperative slab kernels throughout); past their grid limit (more
+    # than 65535 samples) the slab kernels take it; NCHW is cooperative
     for bw in (0, 1):
         assert sel(bw, 1, 128, 1024 * 2048, 16, F16, NHWC) == _lib.GN_PATH_STREAM
-        assert sel(bw, 1, 128, 64 * 130, 16, F16, NHWC) == _lib.GN_PATH_SLAB
+        assert sel(bw, 1, 128, 64 * 130, 16, F16, NHWC) == _lib.GN_PATH_STREAM
+        assert sel(bw, 2, 32, 16 * 16, 8, F32, NHWC) == _lib.GN_PATH_STREAM
+        assert sel(bw, 70000, 64, 16, 8, F16, NHWC) == _lib.GN_PATH_SLAB
         assert sel(bw, 112, 64, 512 * 512, 8, F32, NCHW) == _lib.GN_PATH_SLAB
     assert sel(0, 1, 128, 64 * 130, 16, F16, NHWC, _lib.GN_PATH_STREAM) == _lib.GN_PATH_STREAM
     assert sel(0, 2, 16, 64, 4, F32, NCHW, _lib.GN_PATH_STREAM) == -1      # stream is NHWC only

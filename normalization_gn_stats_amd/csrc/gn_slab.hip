@@ -1238,6 +1238,14 @@ bool slab_ok(const Problem& p) {
     return p.HW >= V && p.D <= kT;      // channel sums of a slab: one thread per channel
 }
 
+// Tiles per slab when each slab takes one workgroup of its own (NCHW slabs of
+// at most GN_SLAB_SOLO_BYTES), else 0.
+int64_t slab_solo_tiles(const Problem& p, bool backward) {
+    if (p.layout != GN_NCHW || p.D * p.HW * p.elem_bytes > (int64_t)GN_SLAB_SOLO_BYTES) return 0;
+    int64_t tpc;
+    return tiles_per_slab(p, tile_chunks(p, backward), &tpc);
+}
+
 size_t slab_fwd_ws(const Problem& p) {
     int64_t tpc;
     return layout_ws(p, false, tiles_per_slab(p, tile_chunks(p, false), &tpc)).total;

@@ -79,9 +79,9 @@ typedef enum gn_path {
                              grid-stride overflow tiles (one-pass backward) */
     GN_PATH_STREAM = 4    /* NHWC: a few launches of one tile per workgroup
                              (statistics, fixed-order combine, outputs); the
-                             planner's choice when a sample has more tiles than
-                             the co-resident grid holds, or a channel count the
-                             slab kernels do not take */
+                             planner's choice for every NHWC shape it takes
+                             (the slab path serves NHWC when forced, or past
+                             the stream grid limits) */
 } gn_path;
 
 /* What a call ran (filled when gn_options.info is not NULL). */

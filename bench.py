@@ -100,15 +100,26 @@ def source_files(kernel_name: str) -> list:
     return sorted(seen)
 
 
+def code_text(path: str) -> str:
+    """A source file without its comments and with runs of whitespace
+    collapsed: what the compiler sees, so that a change to a comment does not
+    count as a change to the kernels."""
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_fingerprint(kernel_name: str) -> str:
-    """sha256 over the sources a kernel is compiled from, to tell whether byte
-    counters recorded in profiles/traffic.json still describe the kernel built
-    now."""
+    """sha256 over the code of the sources a kernel is compiled from, to tell
+    whether byte counters recorded in profiles/traffic.json still describe
+    the kernel built now."""
     import hashlib
     h = hashlib.sha256()
     for p in source_files(kernel_name):
         h.update(os.path.relpath(p, CSRC).encode())
-        h.update(open(p, "rb").read())
+        h.update(code_text(p).encode())
     return h.hexdigest()[:16]
 
 

@@ -38,6 +38,25 @@ def test_fingerprint_covers_the_included_headers_only():
         assert all(os.path.exists(p) for p in bench.source_files(k))
 
 
+def test_fingerprint_ignores_comments(tmp_path, monkeypatch):
+    src = os.path.join(bench.CSRC, "gn_rows.hip")
+    text = open(src).read()
+    d = tmp_path / "pkg" / "csrc"   # the sources include ../../include/gn.h
+    d.mkdir(parents=True)
+    for f in os.listdir(bench.CSRC):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            (d / f).write_text(open(os.path.join(bench.CSRC, f)).read())
+    inc = tmp_path / "include"
+    inc.mkdir()
+    (inc / "gn.h").write_text(open(os.path.join(ROOT, "include", "gn.h")).read())
+    monkeypatch.setattr(bench, "CSRC", str(d))
+    base = bench.source_fingerprint("rows_bwd_k")
+    (d / "gn_rows.hip").write_text("// a new comment\n" + text.replace("*/", "   */", 1))
+    assert bench.source_fingerprint("rows_bwd_k") == base
+    (d / "gn_rows.hip").write_text(text + "\nint gn_rows_changed;\n")
+    assert bench.source_fingerprint("rows_bwd_k") != base
+
+
 def test_unknown_kernel_name_is_an_error():
     with pytest.raises(KeyError):
         bench.source_fingerprint("no_such_kernel")

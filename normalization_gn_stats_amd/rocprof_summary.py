@@ -211,8 +211,8 @@ def summarize(workload: str, trace: str, fetch: str, write: str, copy_mib: int, 
     if note:
         lines += [note, ""]
     fps = sorted({(KERNEL_SOURCES_FILE(r["kernel"]), fingerprint(r["kernel"])) for r in rows})
-    lines += ["Kernel source fingerprints (sha256 of the kernel's .hip file and the local headers it "
-              "includes): " + ", ".join(f"{f} `{h}`" for f, h in fps), "",
+    lines += ["Kernel source fingerprints (sha256 of the code, comments excluded, of the kernel's .hip "
+              "file and the local headers it includes): " + ", ".join(f"{f} `{h}`" for f, h in fps), "",
               "| kernel | workgroups | dispatches | avg duration (µs) | HBM read (MiB, scaled) | HBM write (MiB, scaled) |",
               "|---|---|---|---|---|---|"]
     for r in rows + calls:
@@ -236,8 +236,8 @@ def summarize(workload: str, trace: str, fetch: str, write: str, copy_mib: int, 
         traffic = {}
     traffic["note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled "
                        "by the same counters on a device copy of known size; each entry carries the fingerprint "
-                       "of the sources its kernel is compiled from (its .hip file and the local headers it "
-                       "includes)")
+                       "of the code (comments excluded) of the sources its kernel is compiled from (its .hip "
+                       "file and the local headers it includes)")
     ks = traffic.setdefault("kernels", {})
     for k in [k for k in ks if k.startswith(f"{workload}|")]:
         del ks[k]

@@ -12,10 +12,15 @@
 //
 // A team of TW workgroups works on one slab at a time (teams walk slabs
 // k, k + nteams, ...).  Member m takes the slab's tiles m, m + TW, ... (phase
-// 1), keeps the last one in registers, and after the team barrier writes the
-// outputs of that tile from registers and of the earlier tiles by reloading
-// them in reverse order (the most recently read tiles first, the ones most
-// likely still in the Infinity Cache).
+// 1), keeps the last one in registers, and once the team's partials are in
+// writes the outputs of that tile from registers and of the earlier tiles by
+// reloading them in reverse order (the most recently read tiles first, the
+// ones most likely still in the Infinity Cache).  NHWC members meet at
+// counter barriers; NCHW members publish one self-flagging 64-bit word per
+// tile and poll their slab's words, sleeping between reads of words not yet
+// published.  Slabs of at most GN_SLAB_SOLO_BYTES take a team of one
+// workgroup (no exchange, a normal launch); larger teams are launched
+// cooperatively, so that every member is resident.
 //
 // Reductions (all in a fixed order, no float atomics):
 //  forward   per thread: exact two-pass (count, mean, M2) of each tile from
@@ -748,7 +753,7 @@ __global__ __launch_bounds__(kT) void slab_nchw_fwd(const T* __restrict__ x, con
 // complete in issue order, so a late small load waits for all of it).
 template <typename T, int R>
 __device__ inline int64_t nchw_bwd_phase1(const T* __restrict__ dy, const T* __restrict__ x,
-                                          const float* __restrict__ gamma, const SlabCfg& cfg, int64_t sb, int m,
+                                          const SlabCfg& cfg, int64_t sb, int m,
                                           float mu, float r, u4v (&bx)[R], u4v (&bd)[R], uint64_t* part,
                                           float* lds) {
     constexpr int V = Vec<T>::V;
@@ -790,7 +795,7 @@ constexpr int kStage = 1024;   // tile partials staged in LDS per step of the ch
 // the caller ahead of the bulk traffic; shared through LDS (gch).
 template <typename T, int R>
 __device__ inline void nchw_bwd_phase2(const T* __restrict__ dy, const T* __restrict__ x,
-                                       const float* __restrict__ gamma, T* __restrict__ dx, const SlabCfg& cfg,
+                                       T* __restrict__ dx, const SlabCfg& cfg,
                                        int64_t sb, int m, int64_t last, float mu, float r, u4v (&bx)[R],
                                        u4v (&bd)[R], float gam, const uint64_t* part, uint32_t* err,
                                        float2* stot, float2* stage, float2* chan, float* gch) {
@@ -900,7 +905,7 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
     if (sb >= cfg.n_slabs) return;   // uniform over the team
     float mu = mean[sb], r = rstd[sb];
     float gam = (gamma && t < cfg.D) ? gamma[(sb % cfg.G) * cfg.D + t] : 1.f;
-    int64_t last = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, sb, m, mu, r, cx, cd, part, lds);
+    int64_t last = nchw_bwd_phase1<T, R>(dy, x, cfg, sb, m, mu, r, cx, cd, part, lds);
     while (true) {
         const int64_t nsb = sb + cfg.nteams;
         const bool more = nsb < cfg.n_slabs;   // uniform over the team
@@ -910,10 +915,10 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
             nmu = mean[nsb];
             nr = rstd[nsb];
             if (gamma && t < cfg.D) ngam = gamma[(nsb % cfg.G) * cfg.D + t];
-            nlast = nchw_bwd_phase1<T, R>(dy, x, gamma, cfg, nsb, m, nmu, nr, nx, nd, part, lds);
+            nlast = nchw_bwd_phase1<T, R>(dy, x, cfg, nsb, m, nmu, nr, nx, nd, part, lds);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the two slabs' phases apart
-        nchw_bwd_phase2<T, R>(dy, x, gamma, dx, cfg, sb, m, last, mu, r, cx, cd, gam, part, err, stot, stage,
+        nchw_bwd_phase2<T, R>(dy, x, dx, cfg, sb, m, last, mu, r, cx, cd, gam, part, err, stot, stage,
                               chan, gch);
         if (!more) break;
         for (int j = 0; j < R; ++j) { cx[j] = nx[j]; cd[j] = nd[j]; }   // register moves

@@ -74,7 +74,7 @@ CONFIGS = (
 # a kernel also depends on the local headers that file includes.
 KERNEL_SOURCES = (
     (("rows_",), "gn_rows.hip"),
-    (("slab_", "clear_words", "params_over_n"), "gn_slab.hip"),
+    (("slab_", "small_nchw_", "clear_words", "params_over_n"), "gn_slab.hip"),
     (("fwd_tile_stats", "fwd_finalize", "fwd_apply", "bwd_tile_sums", "col_sums", "bwd_group_ab", "bwd_dx",
       "stream_"), "gn_stream.hip"),
     (("gen_", "generic_"), "gn_generic.hip"),
@@ -575,7 +575,8 @@ def measure(workload, K, W, mode, force_path, keep_inputs=False):
             # the recorded counters)
             kname = {("rows", "fwd"): ("rows_fwd_k", "rows_fwd_lds_k", "rows_fwd_narrow_k", "rows_fwd_cs_k"),
                      ("rows", "bwd"): ("rows_bwd_k", "rows_bwd_narrow_k"),
-                     ("slab", "fwd"): (f"slab_{wl.layout}_fwd",), ("slab", "bwd"): (f"slab_{wl.layout}_bwd",),
+                     ("slab", "fwd"): (f"slab_{wl.layout}_fwd", "small_nchw_fwd"),
+                     ("slab", "bwd"): (f"slab_{wl.layout}_bwd", "small_nchw_bwd"),
                      ("stream", "fwd"): ("stream_fwd_call",), ("stream", "bwd"): ("stream_bwd_call",),
                      ("generic", "fwd"): ("generic_fwd_call",), ("generic", "bwd"): ("generic_bwd_call",),
                      }.get((path, kind))

@@ -111,15 +111,8 @@ int32_t plan(const Problem& p, bool backward, const gn_options* opts) {
     // read of each tile saves, and on the 1x128x1024x2048 image the slab
     // kernels re-read almost every tile anyway.  The slab kernels take the
     // NHWC shapes beyond the stream grid (more than 65535 samples), and NCHW.
+    (void)backward;
     if (gn::stream_ok(p)) return GN_PATH_STREAM;
-    // NCHW slabs small enough for one workgroup each, but cut into more than
-    // 16 plane-sized tiles: that workgroup walks its tiles one after another,
-    // where the generic kernels spread them over the chip (graphs of 20
-    // calls, fwd / bwd us, slab vs generic: 2x640x32x32 fp16 G32, 20 tiles,
-    // 32.1 / 37.0 vs 27.6 / 25.0; at 16 tiles, 4x512x16x16 fp16 G32, 27.1 /
-    // 31.3 vs 24.4 / 33.2; at 8 or fewer the slab kernels win, 2x32x32x32
-    // fp32 G8 12.4 / 14.7 vs 16.4 / 17.9)
-    if (gn::slab_ok(p) && gn::slab_solo_tiles(p, backward) > 16) return GN_PATH_GENERIC;
     if (gn::slab_ok(p)) return GN_PATH_SLAB;
     return GN_PATH_GENERIC;
 }

@@ -102,8 +102,7 @@ hipError_t rows_fwd(const Problem& p, const FwdArgs& a, const Launch& l);
 hipError_t rows_bwd(const Problem& p, const BwdArgs& a, const Launch& l);
 
 // ---- slab path: cooperative capped grid over contiguous slabs ---------------
-bool slab_ok(const Problem& p);
-int64_t slab_solo_tiles(const Problem& p, bool backward);   // tiles of a one-workgroup slab, else 0   // shape condition (alignment checked separately)
+bool slab_ok(const Problem& p);   // shape condition (alignment checked separately)
 size_t slab_fwd_ws(const Problem& p);
 size_t slab_bwd_ws(const Problem& p, int32_t mask);
 hipError_t slab_fwd(const Problem& p, const FwdArgs& a, const Launch& l);

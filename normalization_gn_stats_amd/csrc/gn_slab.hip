@@ -930,6 +930,193 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
     }
 }
 
+// ============================================================================
+// Small NCHW slabs
+// ============================================================================
+// A slab of at most GN_SLAB_SOLO_BYTES per tensor takes one workgroup of its
+// own and fits its registers: R chunks of V elements per thread, chunk q =
+// j*kT + t of the slab's D*HW contiguous elements (a chunk never straddles a
+// channel plane: HW is a multiple of V).  The slab is read once, its
+// statistics are an exact two-pass over the registers, and nothing is
+// exchanged between workgroups: no sync words, no clear kernel, a normal
+// launch.  grid: one workgroup per slab s = n*G + g.
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void small_nchw_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                     const float* __restrict__ beta, T* __restrict__ y,
+                                                     float* __restrict__ mean, float* __restrict__ rstd, int64_t G,
+                                                     int D, int HW, float eps) {
+    constexpr int V = Vec<T>::V;
+    __shared__ float lds[kNW * 2];
+    __shared__ float sga[kT], sbe[kT];   // gamma, beta of the slab's channels (D <= kT)
+    const int t = threadIdx.x;
+    const int64_t sb = blockIdx.x;
+    const int g = (int)(sb % G);
+    const int M = D * HW;                // elements of the slab
+    const int nq = M / V;                // chunks of the slab
+    const int cpc = HW / V;              // chunks per channel plane
+    const T* xs = x + sb * (int64_t)M;
+    if (t < D) {
+        sga[t] = gamma ? gamma[g * D + t] : 1.f;
+        sbe[t] = beta ? beta[g * D + t] : 0.f;
+    }
+    u4v buf[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {   // branch-free: past the end, the last chunk again (not used)
+        const int q = j * kT + t;
+        buf[j] = ld16_nt(xs + (int64_t)(q < nq ? q : nq - 1) * V);
+    }
+    float sum[1] = {0.f};
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * kT + t < nq) {
+            float v[V];
+            Vec<T>::unpack(buf[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) sum[0] += v[k];
+        }
+    }
+    block_sum<1, kNW>(sum, lds);
+    const float mu = sum[0] / (float)M;
+    if constexpr (sizeof(T) == 2) {   // unpack again below rather than hold the floats
+#pragma unroll
+        for (int j = 0; j < R; ++j) asm volatile("" : "+v"(buf[j]));
+    }
+    float m2[1] = {0.f};
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * kT + t < nq) {
+            float v[V];
+            Vec<T>::unpack(buf[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float d = v[k] - mu;
+                m2[0] = fmaf(d, d, m2[0]);
+            }
+        }
+    }
+    block_sum<1, kNW>(m2, lds);
+    float var = m2[0] / (float)M;
+    var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
+    const float r = 1.0f / sqrtf(var + eps);
+    if (t == 0) {
+        mean[sb] = mu;
+        rstd[sb] = r;
+    }
+    if (y == nullptr) return;
+    T* ys = y + sb * (int64_t)M;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int q = j * kT + t;
+        if (q < nq) {
+            const int cl = q / cpc;
+            const float a_c = r * sga[cl];
+            const float b_c = sbe[cl];
+            float v[V], o[V];
+            Vec<T>::unpack(buf[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu, a_c, b_c);
+            st16_nt(ys + (int64_t)q * V, Vec<T>::pack(o));
+        }
+    }
+}
+
+// Backward of a small slab: A = sum gamma_c*dy and B = sum gamma_c*dy*xhat
+// over the slab (one workgroup sum), dx from the registers, and the slab's
+// per-channel sums of dy and dy*xhat (stot[n][c], for dgamma/dbeta over the
+// samples): per-chunk sums staged in LDS, W lanes per channel (a power of two
+// <= 64, so that a channel's lanes sit in one wave) add a channel's chunks
+// with stride W, then a butterfly over the W lanes -- a fixed order.
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void small_nchw_bwd(const T* __restrict__ dy, const T* __restrict__ x,
+                                                     const float* __restrict__ mean,
+                                                     const float* __restrict__ rstd,
+                                                     const float* __restrict__ gamma, T* __restrict__ dx,
+                                                     float2* __restrict__ stot, int64_t G, int64_t C, int D, int HW,
+                                                     int want_dx) {
+    constexpr int V = Vec<T>::V;
+    __shared__ float lds[kNW * 2];
+    __shared__ float sga[kT];
+    __shared__ float2 cpart[kT * R];   // per chunk: (sum dy, sum dy*xhat)
+    const int t = threadIdx.x;
+    const int64_t sb = blockIdx.x;
+    const int64_t n = sb / G;
+    const int g = (int)(sb - n * G);
+    const int M = D * HW, nq = M / V, cpc = HW / V;
+    const float mu = mean[sb], r = rstd[sb];
+    if (t < D) sga[t] = gamma ? gamma[g * D + t] : 1.f;
+    const T* xs = x + sb * (int64_t)M;
+    const T* ds = dy + sb * (int64_t)M;
+    u4v bx[R], bd[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {   // branch-free: past the end, the last chunk again (not used)
+        const int q = j * kT + t;
+        const int64_t e = (int64_t)(q < nq ? q : nq - 1) * V;
+        bx[j] = ld16_nt(xs + e);
+        bd[j] = ld16_nt(ds + e);
+    }
+    __syncthreads();   // sga
+    float ab[2] = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int q = j * kT + t;
+        if (q < nq) {
+            const float ga = sga[q / cpc];
+            float xv[V], dv[V];
+            Vec<T>::unpack(bx[j], xv);
+            Vec<T>::unpack(bd[j], dv);
+            float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float xh = (xv[k] - mu) * r;
+                s1 += dv[k];
+                s2 = fmaf(dv[k], xh, s2);
+            }
+            cpart[q] = make_float2(s1, s2);
+            ab[0] = fmaf(ga, s1, ab[0]);
+            ab[1] = fmaf(ga, s2, ab[1]);
+        }
+    }
+    block_sum<2, kNW>(ab, lds);   // its barriers also publish cpart
+    int W = 64;
+    while (W > 1 && W * D > kT) W >>= 1;
+    const int ccl = t / W, cj = t & (W - 1);
+    float2 run = make_float2(0.f, 0.f);
+    if (ccl < D) {
+        for (int i = cj; i < cpc; i += W) {
+            const float2 v = cpart[ccl * cpc + i];
+            run.x += v.x;
+            run.y += v.y;
+        }
+    }
+    for (int o = W >> 1; o > 0; o >>= 1) {   // every lane takes part
+        run.x += __shfl_xor(run.x, o, kWave);
+        run.y += __shfl_xor(run.y, o, kWave);
+    }
+    if (cj == 0 && ccl < D) stot[n * C + (int64_t)g * D + ccl] = run;
+    if (!want_dx) return;
+    const float invM = 1.0f / (float)M;
+    const float A = ab[0] * invM, B = ab[1] * invM;
+    T* dxs = dx + sb * (int64_t)M;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int q = j * kT + t;
+        if (q < nq) {
+#pragma clang fp contract(off)
+            const float ga = sga[q / cpc];
+            float xv[V], dv[V], o[V];
+            Vec<T>::unpack(bx[j], xv);
+            Vec<T>::unpack(bd[j], dv);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float xh = (xv[k] - mu) * r;
+                const float gd = dv[k] * ga;
+                o[k] = r * ((gd - A) - xh * B);
+            }
+            st16_nt(dxs + (int64_t)q * V, Vec<T>::pack(o));
+        }
+    }
+}
+
 // ---- helpers ---------------------------------------------------------------
 // Words [0, zeros) := 0, [zeros, total) := all ones.
 __global__ void clear_words(uint32_t* p, int64_t zeros, int64_t total) {
@@ -1126,8 +1313,86 @@ auto nchw_bwd_kernel(int R) -> decltype(&slab_nchw_bwd<T, GN_SLAB_NCHW_RB>) {
     }
 }
 
+// Small NCHW slabs: one workgroup each, the slab in its registers (above).
+// Taken when the caller caps no residency (a cap asks for the cooperative
+// kernels' overflow tiles).
+bool small_slab(const Problem& p, const Launch& l) {
+    return p.layout == GN_NCHW && l.max_resident_override <= 0 &&
+           p.D * p.HW * p.elem_bytes <= (int64_t)GN_SLAB_SOLO_BYTES && p.N * p.G <= INT32_MAX;
+}
+
+// chunks per thread: the smallest power of two that covers the slab (<= 16)
+int small_r(const Problem& p) {
+    const int64_t nq = p.D * p.HW / vec_elems(p);
+    int r = 1;
+    while ((int64_t)r * kT < nq) r *= 2;
+    return r;
+}
+
+template <typename T>
+hipError_t small_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {
+    const int R = small_r(p);
+    auto k = R == 1 ? small_nchw_fwd<T, 1>
+           : R == 2 ? small_nchw_fwd<T, 2>
+           : R == 4 ? small_nchw_fwd<T, 4>
+           : R == 8 ? small_nchw_fwd<T, 8>
+                    : small_nchw_fwd<T, 16>;
+    const unsigned grid = (unsigned)(p.N * p.G);
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta, (T*)a.y, a.mean, a.rstd,
+                       p.G, (int)p.D, (int)p.HW, a.eps);
+    if ((e = hipGetLastError())) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    if (l.info) {
+        l.info->path = GN_PATH_SLAB;
+        l.info->kernels = 1;
+        l.info->grid = grid;
+        l.info->tiles = grid;
+        l.info->resident_cap = 0;
+        l.info->team = 1;
+    }
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t small_bwd(const Problem& p, const BwdArgs& a, const Launch& l) {
+    const int R = small_r(p);
+    auto k = R == 1 ? small_nchw_bwd<T, 1>
+           : R == 2 ? small_nchw_bwd<T, 2>
+           : R == 4 ? small_nchw_bwd<T, 4>
+           : R == 8 ? small_nchw_bwd<T, 8>
+                    : small_nchw_bwd<T, 16>;
+    const Plan pl = layout_ws(p, true, 1);   // the layout does not depend on the cap
+    float2* stot = (float2*)((char*)l.ws + pl.off_stot);
+    const unsigned grid = (unsigned)(p.N * p.G);
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean, a.rstd, a.gamma,
+                       (T*)a.dx, stot, p.G, p.C, (int)p.D, (int)p.HW, (a.mask & GN_GRAD_DX) ? 1 : 0);
+    if ((e = hipGetLastError())) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    int kernels = 1;
+    if (a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) {
+        hipLaunchKernelGGL(params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream, stot, p.N,
+                           p.C, a.dgamma, a.dbeta);
+        if ((e = hipGetLastError())) return e;
+        ++kernels;
+    }
+    if (l.info) {
+        l.info->path = GN_PATH_SLAB;
+        l.info->kernels = kernels;
+        l.info->grid = grid;
+        l.info->tiles = grid;
+        l.info->resident_cap = 0;
+        l.info->team = 1;
+    }
+    return hipSuccess;
+}
+
 template <typename T>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
+    if (small_slab(p, l)) return small_fwd<T>(p, a, l);
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
     auto kn = slab_nhwc_fwd<T, GN_SLAB_NHWC_RF>;
@@ -1172,6 +1437,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
 
 template <typename T>
 hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
+    if (small_slab(p, l)) return small_bwd<T>(p, a, l);
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
     auto kn = slab_nhwc_bwd<T, GN_SLAB_NHWC_RB>;
@@ -1241,14 +1507,6 @@ bool slab_ok(const Problem& p) {
         tiles_per_slab(p, tile_chunks(p, false), &tpc) >= ((int64_t)1 << 31))
         return false;                   // tile indices of a slab in 32 bits
     return p.HW >= V && p.D <= kT;      // channel sums of a slab: one thread per channel
-}
-
-// Tiles per slab when each slab takes one workgroup of its own (NCHW slabs of
-// at most GN_SLAB_SOLO_BYTES), else 0.
-int64_t slab_solo_tiles(const Problem& p, bool backward) {
-    if (p.layout != GN_NCHW || p.D * p.HW * p.elem_bytes > (int64_t)GN_SLAB_SOLO_BYTES) return 0;
-    int64_t tpc;
-    return tiles_per_slab(p, tile_chunks(p, backward), &tpc);
 }
 
 size_t slab_fwd_ws(const Problem& p) {

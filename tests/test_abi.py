@@ -158,10 +158,9 @@ def test_path_selection(L):
         assert sel(bw, 2, 32, 16 * 16, 8, F32, NHWC) == _lib.GN_PATH_STREAM
         assert sel(bw, 70000, 64, 16, 8, F16, NHWC) == _lib.GN_PATH_SLAB
         assert sel(bw, 112, 64, 512 * 512, 8, F32, NCHW) == _lib.GN_PATH_SLAB
-        # NCHW slabs of one workgroup each: slab up to 16 plane tiles, generic beyond
+        # NCHW slabs of one workgroup each (the small-slab kernel), however many planes
         assert sel(bw, 2, 32, 16 * 16, 8, F32, NCHW) == _lib.GN_PATH_SLAB
-        assert sel(bw, 2, 640, 32 * 32, 32, F16, NCHW) == _lib.GN_PATH_GENERIC
-        assert sel(bw, 2, 640, 32 * 32, 32, F16, NCHW, _lib.GN_PATH_SLAB) == _lib.GN_PATH_SLAB
+        assert sel(bw, 2, 640, 32 * 32, 32, F16, NCHW) == _lib.GN_PATH_SLAB
     assert sel(0, 1, 128, 64 * 130, 16, F16, NHWC, _lib.GN_PATH_STREAM) == _lib.GN_PATH_STREAM
     assert sel(0, 2, 16, 64, 4, F32, NCHW, _lib.GN_PATH_STREAM) == -1      # stream is NHWC only
     assert sel(0, 2, 96, 64, 4, F16, NHWC, _lib.GN_PATH_STREAM) == _lib.GN_PATH_STREAM   # 12 chunks per pixel

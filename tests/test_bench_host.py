@@ -31,6 +31,7 @@ def test_kernel_source_table_names_existing_files():
 def test_fingerprint_covers_the_included_headers_only():
     names = lambda k: {os.path.basename(p) for p in bench.source_files(k)}
     assert names("slab_nchw_bwd") == {"gn_slab.hip", "gn_device.hpp", "gn_internal.hpp", "gn_slab_plan.hpp", "gn.h"}
+    assert names("small_nchw_fwd") == names("slab_nchw_bwd")
     assert names("rows_bwd_k") == {"gn_rows.hip", "gn_device.hpp", "gn_internal.hpp", "gn.h"}
     assert names("bwd_dx") == {"gn_stream.hip", "gn_device.hpp", "gn_internal.hpp", "gn.h"}
     assert names("gen_dx") == {"gn_generic.hip", "gn_device.hpp", "gn_internal.hpp", "gn.h"}

@@ -82,6 +82,43 @@ def test_slab_many_tiles(wl, cap):
     check_against_oracle(wl, data, out)
 
 
+# Small NCHW slabs (at most 64 KiB per tensor): one workgroup each holds the
+# whole slab in registers (1 to 16 chunks per thread) and exchanges nothing;
+# taken when no residency cap is forced.
+SMALL_SLABS = [
+    W("small_nchw_f32_r16_64kib", 2, 16, 64, 64, 4, "f32", "nchw"),      # exactly 64 KiB, 16 chunks a thread
+    W("small_nchw_f16_ragged_d3", 3, 12, 24, 24, 4, "f16", "nchw"),      # 216 of 256 threads hold a chunk
+    W("small_nchw_bf16_d256", 2, 256, 2, 4, 1, "bf16", "nchw"),          # one chunk per channel, one lane each
+    W("small_nchw_f32_instance", 4, 8, 32, 32, 8, "f32", "nchw"),        # G = C
+    W("small_nchw_f32_many_n", 64, 32, 8, 8, 8, "f32", "nchw", affine="n01"),
+    W("small_nchw_f16_r2_d10", 2, 320, 16, 16, 32, "f16", "nchw"),       # ten 256-element planes, 2 chunks a thread
+]
+
+
+@pytest.mark.parametrize("wl", SMALL_SLABS, ids=lambda w: w.name)
+def test_small_slab_parity(wl):
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    say(f"[slab] {wl.name} small")
+    data = inputs.make_inputs(wl, seed=9)
+    out = run_gpu(wl, data, force_path="slab")
+    fp, bp = out["fwd_plan"], out["bwd_plan"]
+    assert fp.path == gn.GN_PATH_SLAB and bp.path == gn.GN_PATH_SLAB
+    assert fp.team == 1 and fp.kernels == 1 and fp.grid == wl.N * wl.G
+    check_against_oracle(wl, data, out)
+
+
+@pytest.mark.parametrize("mask", [gn.GN_GRAD_DX, gn.GN_GRAD_DGAMMA, gn.GN_GRAD_DBETA,
+                                  gn.GN_GRAD_DGAMMA | gn.GN_GRAD_DBETA], ids=["dx", "dgamma", "dbeta", "params"])
+def test_small_slab_masks(mask):
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    wl = SMALL_SLABS[1]
+    data = inputs.make_inputs(wl, seed=10)
+    out = run_gpu(wl, data, force_path="slab", mask=mask)
+    check_against_oracle(wl, data, out, mask=mask)
+
+
 def test_overflow_tiles_exist_under_a_cap():
     """With the cap below the tile count, members own several tiles."""
     if not torch.cuda.is_available():

@@ -220,19 +220,30 @@ __global__ __launch_bounds__(kT) void rows_fwd_cs_k(const T* __restrict__ x, con
 // staged once per workgroup in LDS ([D] each, dynamic shared memory) instead
 // of being held per lane in registers (2*NV*V of them) and reloaded for every
 // slice: fewer registers, so more waves per SIMD, and one parameter fetch per
-// workgroup instead of one per slice.  Same arithmetic as rows_fwd_k.
+// workgroup instead of one per slice.  In LDS a vector's parameters sit
+// [quarter of a vector][vector]: the lanes of a wave read consecutive
+// 16-byte quarters (no bank conflicts; with V = 8 the vector-major order put
+// lanes 32 bytes apart).  Each wave keeps at most GN_ROWS_FWD_Y_INFLIGHT y
+// stores in flight, as the wide backward does with dx.  Same arithmetic as
+// rows_fwd_k.
 #ifndef GN_ROWS_WALK_NT
 #define GN_ROWS_WALK_NT 1   // non-temporal loads of x (measured: 420 -> 398 us on 131072 x 4096 bf16)
 #endif
+// y stores in flight per wave, 131072 x 4096 bf16 with the layout above,
+// four alternating rounds: 3 -> 384-386 us, 4 -> 385-386, 5 -> 382-384,
+// 6 -> 383-384, 8 -> 385-388, unlimited -> 391-392 (vector-major layout,
+// unlimited: 391-400)
+#ifndef GN_ROWS_FWD_Y_INFLIGHT
+#define GN_ROWS_FWD_Y_INFLIGHT 5
+#endif
+static_assert(GN_ROWS_FWD_Y_INFLIGHT >= 0 && GN_ROWS_FWD_Y_INFLIGHT <= 16, "vmcnt holds 0..15 here");
 template <typename T, int NV>
 __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, const float* __restrict__ gamma,
                                                      const float* __restrict__ beta, T* __restrict__ y,
                                                      float* __restrict__ mean, float* __restrict__ rstd, int64_t N,
                                                      int64_t G, int64_t C, int D, float eps, int rms) {
     constexpr int V = Vec<T>::V;
-    extern __shared__ float4 lds_par[];   // [D/4] gamma, then [D/4] beta
-    float* sg = reinterpret_cast<float*>(lds_par);
-    float* sbeta = sg + D;
+    extern __shared__ float4 lds_par[];   // [V/4][nvec] gamma, then the same for beta
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t g = blockIdx.y;
@@ -250,9 +261,10 @@ __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, co
     };
     if (n < N) load(n, cur);
     for (int i = threadIdx.x; i < D / 4; i += kT) {
-        lds_par[i] = gamma ? *reinterpret_cast<const float4*>(gamma + g * D + 4 * i) : make_float4(1.f, 1.f, 1.f, 1.f);
-        lds_par[D / 4 + i] = beta ? *reinterpret_cast<const float4*>(beta + g * D + 4 * i)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int at = (i % (V / 4)) * nvec + i / (V / 4);   // quarter i % (V/4) of vector i / (V/4)
+        lds_par[at] = gamma ? *reinterpret_cast<const float4*>(gamma + g * D + 4 * i) : make_float4(1.f, 1.f, 1.f, 1.f);
+        lds_par[D / 4 + at] = beta ? *reinterpret_cast<const float4*>(beta + g * D + 4 * i)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
     const float invD = 1.0f / (float)D;
@@ -305,7 +317,16 @@ __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, co
                 if (vi < nvec) {
                     float o[V];
 #pragma unroll
-                    for (int k = 0; k < V; ++k) o[k] = fmaf(v[j][k] - mu, r * sg[vi * V + k], sbeta[vi * V + k]);
+                    for (int k = 0; k < V; k += 4) {
+                        const float4 ga = lds_par[(k / 4) * nvec + vi];
+                        const float4 be = lds_par[D / 4 + (k / 4) * nvec + vi];
+                        o[k] = fmaf(v[j][k] - mu, r * ga.x, be.x);
+                        o[k + 1] = fmaf(v[j][k + 1] - mu, r * ga.y, be.y);
+                        o[k + 2] = fmaf(v[j][k + 2] - mu, r * ga.z, be.z);
+                        o[k + 3] = fmaf(v[j][k + 3] - mu, r * ga.w, be.w);
+                    }
+                    if constexpr (GN_ROWS_FWD_Y_INFLIGHT > 0)
+                        __builtin_amdgcn_s_waitcnt(0x0F70 | (GN_ROWS_FWD_Y_INFLIGHT - 1));   // vmcnt(K - 1)
                     st16_nt(y + base + (int64_t)vi * V, Vec<T>::pack(o));
                 }
             }
@@ -537,6 +558,7 @@ __global__ __launch_bounds__(kT) void rows_bwd_narrow_k(const T* __restrict__ dy
 #ifndef GN_ROWS_BWD_DX_INFLIGHT
 #define GN_ROWS_BWD_DX_INFLIGHT 2
 #endif
+static_assert(GN_ROWS_BWD_DX_INFLIGHT >= 0 && GN_ROWS_BWD_DX_INFLIGHT <= 16, "vmcnt holds 0..15 here");
 #ifndef GN_ROWS_BWD_NT_WIDE
 #define GN_ROWS_BWD_NT_WIDE 1
 #endif

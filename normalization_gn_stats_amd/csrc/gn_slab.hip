@@ -20,7 +20,10 @@
 // tile and poll their slab's words, sleeping between reads of words not yet
 // published.  Slabs of at most GN_SLAB_SOLO_BYTES take a team of one
 // workgroup (no exchange, a normal launch); larger teams are launched
-// cooperatively, so that every member is resident.
+// cooperatively, so that every member is resident.  NCHW slabs that fit one
+// workgroup's registers (up to GN_SLAB_MID_FWD_BYTES forward and
+// GN_SLAB_MID_BWD_BYTES backward) skip the teams altogether: one workgroup
+// of 256 or 1024 threads per slab holds the whole slab (small_nchw_*).
 //
 // Reductions (all in a fixed order, no float atomics):
 //  forward   per thread: exact two-pass (count, mean, M2) of each tile from
@@ -933,21 +936,22 @@ __global__ __launch_bounds__(kT) void slab_nchw_bwd(const T* __restrict__ dy, co
 // ============================================================================
 // Small NCHW slabs
 // ============================================================================
-// A slab of at most GN_SLAB_SOLO_BYTES per tensor takes one workgroup of its
-// own and fits its registers: R chunks of V elements per thread, chunk q =
-// j*kT + t of the slab's D*HW contiguous elements (a chunk never straddles a
-// channel plane: HW is a multiple of V).  The slab is read once, its
-// statistics are an exact two-pass over the registers, and nothing is
-// exchanged between workgroups: no sync words, no clear kernel, a normal
+// A slab that fits one workgroup's registers takes a workgroup of its own:
+// BT threads (256, or 1024 for slabs past 64 KiB), R chunks of V elements per
+// thread, chunk q = j*BT + t of the slab's D*HW contiguous elements (a chunk
+// never straddles a channel plane: HW is a multiple of V).  The slab is read
+// once, its statistics are an exact two-pass over the registers, and nothing
+// is exchanged between workgroups: no sync words, no clear kernel, a normal
 // launch.  grid: one workgroup per slab s = n*G + g.
-template <typename T, int R>
-__global__ __launch_bounds__(kT) void small_nchw_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
+template <typename T, int R, int BT>
+__global__ __launch_bounds__(BT) void small_nchw_fwd(const T* __restrict__ x, const float* __restrict__ gamma,
                                                      const float* __restrict__ beta, T* __restrict__ y,
                                                      float* __restrict__ mean, float* __restrict__ rstd, int64_t G,
                                                      int D, int HW, float eps) {
     constexpr int V = Vec<T>::V;
-    __shared__ float lds[kNW * 2];
-    __shared__ float sga[kT], sbe[kT];   // gamma, beta of the slab's channels (D <= kT)
+    constexpr int NW = BT / kWave;
+    __shared__ float lds[NW * 2];
+    __shared__ float sga[kT], sbe[kT];   // gamma, beta of the slab's channels (D <= kT <= BT)
     const int t = threadIdx.x;
     const int64_t sb = blockIdx.x;
     const int g = (int)(sb % G);
@@ -962,20 +966,20 @@ __global__ __launch_bounds__(kT) void small_nchw_fwd(const T* __restrict__ x, co
     u4v buf[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) {   // branch-free: past the end, the last chunk again (not used)
-        const int q = j * kT + t;
+        const int q = j * BT + t;
         buf[j] = ld16_nt(xs + (int64_t)(q < nq ? q : nq - 1) * V);
     }
     float sum[1] = {0.f};
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        if (j * kT + t < nq) {
+        if (j * BT + t < nq) {
             float v[V];
             Vec<T>::unpack(buf[j], v);
 #pragma unroll
             for (int k = 0; k < V; ++k) sum[0] += v[k];
         }
     }
-    block_sum<1, kNW>(sum, lds);
+    block_sum<1, NW>(sum, lds);
     const float mu = sum[0] / (float)M;
     if constexpr (sizeof(T) == 2) {   // unpack again below rather than hold the floats
 #pragma unroll
@@ -984,7 +988,7 @@ __global__ __launch_bounds__(kT) void small_nchw_fwd(const T* __restrict__ x, co
     float m2[1] = {0.f};
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        if (j * kT + t < nq) {
+        if (j * BT + t < nq) {
             float v[V];
             Vec<T>::unpack(buf[j], v);
 #pragma unroll
@@ -994,7 +998,7 @@ __global__ __launch_bounds__(kT) void small_nchw_fwd(const T* __restrict__ x, co
             }
         }
     }
-    block_sum<1, kNW>(m2, lds);
+    block_sum<1, NW>(m2, lds);
     float var = m2[0] / (float)M;
     var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
     const float r = 1.0f / sqrtf(var + eps);
@@ -1006,7 +1010,7 @@ __global__ __launch_bounds__(kT) void small_nchw_fwd(const T* __restrict__ x, co
     T* ys = y + sb * (int64_t)M;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const int q = j * kT + t;
+        const int q = j * BT + t;
         if (q < nq) {
             const int cl = q / cpc;
             const float a_c = r * sga[cl];
@@ -1026,17 +1030,18 @@ __global__ __launch_bounds__(kT) void small_nchw_fwd(const T* __restrict__ x, co
 // samples): per-chunk sums staged in LDS, W lanes per channel (a power of two
 // <= 64, so that a channel's lanes sit in one wave) add a channel's chunks
 // with stride W, then a butterfly over the W lanes -- a fixed order.
-template <typename T, int R>
-__global__ __launch_bounds__(kT) void small_nchw_bwd(const T* __restrict__ dy, const T* __restrict__ x,
+template <typename T, int R, int BT>
+__global__ __launch_bounds__(BT) void small_nchw_bwd(const T* __restrict__ dy, const T* __restrict__ x,
                                                      const float* __restrict__ mean,
                                                      const float* __restrict__ rstd,
                                                      const float* __restrict__ gamma, T* __restrict__ dx,
                                                      float2* __restrict__ stot, int64_t G, int64_t C, int D, int HW,
                                                      int want_dx) {
     constexpr int V = Vec<T>::V;
-    __shared__ float lds[kNW * 2];
-    __shared__ float sga[kT];
-    __shared__ float2 cpart[kT * R];   // per chunk: (sum dy, sum dy*xhat)
+    constexpr int NW = BT / kWave;
+    __shared__ float lds[NW * 2];
+    __shared__ float sga[kT];          // D <= kT <= BT
+    __shared__ float2 cpart[BT * R];   // per chunk: (sum dy, sum dy*xhat)
     const int t = threadIdx.x;
     const int64_t sb = blockIdx.x;
     const int64_t n = sb / G;
@@ -1049,7 +1054,7 @@ __global__ __launch_bounds__(kT) void small_nchw_bwd(const T* __restrict__ dy, c
     u4v bx[R], bd[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) {   // branch-free: past the end, the last chunk again (not used)
-        const int q = j * kT + t;
+        const int q = j * BT + t;
         const int64_t e = (int64_t)(q < nq ? q : nq - 1) * V;
         bx[j] = ld16_nt(xs + e);
         bd[j] = ld16_nt(ds + e);
@@ -1058,7 +1063,7 @@ __global__ __launch_bounds__(kT) void small_nchw_bwd(const T* __restrict__ dy, c
     float ab[2] = {0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const int q = j * kT + t;
+        const int q = j * BT + t;
         if (q < nq) {
             const float ga = sga[q / cpc];
             float xv[V], dv[V];
@@ -1076,9 +1081,9 @@ __global__ __launch_bounds__(kT) void small_nchw_bwd(const T* __restrict__ dy, c
             ab[1] = fmaf(ga, s2, ab[1]);
         }
     }
-    block_sum<2, kNW>(ab, lds);   // its barriers also publish cpart
+    block_sum<2, NW>(ab, lds);   // its barriers also publish cpart
     int W = 64;
-    while (W > 1 && W * D > kT) W >>= 1;
+    while (W > 1 && W * D > BT) W >>= 1;
     const int ccl = t / W, cj = t & (W - 1);
     float2 run = make_float2(0.f, 0.f);
     if (ccl < D) {
@@ -1099,7 +1104,7 @@ __global__ __launch_bounds__(kT) void small_nchw_bwd(const T* __restrict__ dy, c
     T* dxs = dx + sb * (int64_t)M;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const int q = j * kT + t;
+        const int q = j * BT + t;
         if (q < nq) {
 #pragma clang fp contract(off)
             const float ga = sga[q / cpc];
@@ -1208,7 +1213,10 @@ struct Plan {
 // 128 KiB slabs still gain on their own (8 x 64 x 64 x 64 fp32: 26.6 -> 18.4
 // us), but graphs captured with such launches slowed later graphs of
 // cooperative launches in the same process threefold, which eager launches
-// did not; 512 KiB slabs run faster cooperatively.
+// did not; 512 KiB slabs run faster cooperatively.  (NCHW slabs past 64 KiB
+// that fit a 1024-thread workgroup go to small_nchw_* instead, whose graphs
+// leave later cooperative graphs at their speed: 33.2 / 34.1 us before, 32.4
+// / 33.5 us after, 2 x 32 x 128 x 128 fp32 G4 around 2 x 320 x 64 x 64 fp16.)
 #ifndef GN_SLAB_SOLO_BYTES
 #define GN_SLAB_SOLO_BYTES 65536
 #endif
@@ -1313,34 +1321,73 @@ auto nchw_bwd_kernel(int R) -> decltype(&slab_nchw_bwd<T, GN_SLAB_NCHW_RB>) {
     }
 }
 
-// Small NCHW slabs: one workgroup each, the slab in its registers (above).
-// Taken when the caller caps no residency (a cap asks for the cooperative
-// kernels' overflow tiles).
-bool small_slab(const Problem& p, const Launch& l) {
-    return p.layout == GN_NCHW && l.max_resident_override <= 0 &&
-           p.D * p.HW * p.elem_bytes <= (int64_t)GN_SLAB_SOLO_BYTES && p.N * p.G <= INT32_MAX;
+// NCHW slabs that fit one workgroup's registers: one workgroup each (above).
+// Up to GN_SLAB_SOLO_BYTES per tensor 256 threads, past that 1024 threads up
+// to GN_SLAB_MID_FWD_BYTES in the forward (16 chunks per thread) and
+// GN_SLAB_MID_BWD_BYTES in the backward (8 chunks each of x and dy; 16 would
+// need about 200 VGPRs, more than a 1024-thread workgroup has).  Graphs of 20
+// calls, forward / backward us, cooperative kernels -> one workgroup per slab:
+// 2 x 320 x 64 x 64 fp16 G32 (80 KiB slabs) 32.0 / 36.4 -> 7.4 / 13.5;
+// 16 x 320 x 64 x 64 fp16 G32 50.5 / 58.0 -> 13.6 / 30.6; 8 x 64 x 64 x 64
+// fp32 G8 (128 KiB) 30.7 / 33.8 -> 7.5 / 12.4.
+#ifndef GN_SLAB_MID_FWD_BYTES
+#define GN_SLAB_MID_FWD_BYTES (256 << 10)
+#endif
+#ifndef GN_SLAB_MID_BWD_BYTES
+#define GN_SLAB_MID_BWD_BYTES (128 << 10)
+#endif
+constexpr int kMidT = 1024;
+static_assert(GN_SLAB_SOLO_BYTES <= kT * 16 * 16, "small slabs: at most 16 chunks per thread");
+static_assert(GN_SLAB_MID_FWD_BYTES <= kMidT * 16 * 16, "mid-size forward: at most 16 chunks per thread");
+static_assert(GN_SLAB_MID_BWD_BYTES <= kMidT * 8 * 16, "mid-size backward: at most 8 chunks per thread");
+
+// Threads per workgroup of the one-workgroup-per-slab kernels for this call,
+// or 0 when they do not take it (other layouts, larger slabs, or a residency
+// cap, which asks for the cooperative kernels' overflow tiles).
+int small_bt(const Problem& p, const Launch& l, bool backward) {
+    if (p.layout != GN_NCHW || l.max_resident_override > 0 || p.N * p.G > INT32_MAX) return 0;
+    const int64_t b = p.D * p.HW * p.elem_bytes;
+    if (b <= (int64_t)GN_SLAB_SOLO_BYTES) return kT;
+    if (b <= (int64_t)(backward ? GN_SLAB_MID_BWD_BYTES : GN_SLAB_MID_FWD_BYTES)) return kMidT;
+    return 0;
 }
 
-// chunks per thread: the smallest power of two that covers the slab (<= 16)
-int small_r(const Problem& p) {
+// chunks per thread: the smallest power of two that covers the slab
+int small_r(const Problem& p, int bt) {
     const int64_t nq = p.D * p.HW / vec_elems(p);
     int r = 1;
-    while ((int64_t)r * kT < nq) r *= 2;
+    while ((int64_t)r * bt < nq) r *= 2;
     return r;
 }
 
 template <typename T>
-hipError_t small_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {
-    const int R = small_r(p);
-    auto k = R == 1 ? small_nchw_fwd<T, 1>
-           : R == 2 ? small_nchw_fwd<T, 2>
-           : R == 4 ? small_nchw_fwd<T, 4>
-           : R == 8 ? small_nchw_fwd<T, 8>
-                    : small_nchw_fwd<T, 16>;
+auto small_fwd_kernel(int bt, int R) -> decltype(&small_nchw_fwd<T, 1, kT>) {
+    if (bt == kMidT) return R <= 8 ? small_nchw_fwd<T, 8, kMidT> : R <= 16 ? small_nchw_fwd<T, 16, kMidT> : nullptr;
+    return R == 1 ? small_nchw_fwd<T, 1, kT>
+         : R == 2 ? small_nchw_fwd<T, 2, kT>
+         : R == 4 ? small_nchw_fwd<T, 4, kT>
+         : R == 8 ? small_nchw_fwd<T, 8, kT>
+         : R == 16 ? small_nchw_fwd<T, 16, kT> : nullptr;
+}
+
+template <typename T>
+auto small_bwd_kernel(int bt, int R) -> decltype(&small_nchw_bwd<T, 1, kT>) {
+    if (bt == kMidT) return R <= 8 ? small_nchw_bwd<T, 8, kMidT> : nullptr;
+    return R == 1 ? small_nchw_bwd<T, 1, kT>
+         : R == 2 ? small_nchw_bwd<T, 2, kT>
+         : R == 4 ? small_nchw_bwd<T, 4, kT>
+         : R == 8 ? small_nchw_bwd<T, 8, kT>
+         : R == 16 ? small_nchw_bwd<T, 16, kT> : nullptr;
+}
+
+template <typename T>
+hipError_t small_fwd(const Problem& p, const FwdArgs& a, const Launch& l, int bt) {
+    auto k = small_fwd_kernel<T>(bt, small_r(p, bt));
+    if (k == nullptr) return hipErrorInvalidValue;   // the byte limits above rule this out
     const unsigned grid = (unsigned)(p.N * p.G);
     hipError_t e;
     if ((e = record(l.ev_begin, l.stream))) return e;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta, (T*)a.y, a.mean, a.rstd,
+    hipLaunchKernelGGL(k, dim3(grid), dim3(bt), 0, l.stream, (const T*)a.x, a.gamma, a.beta, (T*)a.y, a.mean, a.rstd,
                        p.G, (int)p.D, (int)p.HW, a.eps);
     if ((e = hipGetLastError())) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
@@ -1356,19 +1403,15 @@ hipError_t small_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {
 }
 
 template <typename T>
-hipError_t small_bwd(const Problem& p, const BwdArgs& a, const Launch& l) {
-    const int R = small_r(p);
-    auto k = R == 1 ? small_nchw_bwd<T, 1>
-           : R == 2 ? small_nchw_bwd<T, 2>
-           : R == 4 ? small_nchw_bwd<T, 4>
-           : R == 8 ? small_nchw_bwd<T, 8>
-                    : small_nchw_bwd<T, 16>;
+hipError_t small_bwd(const Problem& p, const BwdArgs& a, const Launch& l, int bt) {
+    auto k = small_bwd_kernel<T>(bt, small_r(p, bt));
+    if (k == nullptr) return hipErrorInvalidValue;   // the byte limits above rule this out
     const Plan pl = layout_ws(p, true, 1);   // the layout does not depend on the cap
     float2* stot = (float2*)((char*)l.ws + pl.off_stot);
     const unsigned grid = (unsigned)(p.N * p.G);
     hipError_t e;
     if ((e = record(l.ev_begin, l.stream))) return e;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean, a.rstd, a.gamma,
+    hipLaunchKernelGGL(k, dim3(grid), dim3(bt), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean, a.rstd, a.gamma,
                        (T*)a.dx, stot, p.G, p.C, (int)p.D, (int)p.HW, (a.mask & GN_GRAD_DX) ? 1 : 0);
     if ((e = hipGetLastError())) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
@@ -1392,7 +1435,7 @@ hipError_t small_bwd(const Problem& p, const BwdArgs& a, const Launch& l) {
 
 template <typename T>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
-    if (small_slab(p, l)) return small_fwd<T>(p, a, l);
+    if (const int bt = small_bt(p, l, false)) return small_fwd<T>(p, a, l, bt);
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
     auto kn = slab_nhwc_fwd<T, GN_SLAB_NHWC_RF>;
@@ -1437,7 +1480,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
 
 template <typename T>
 hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
-    if (small_slab(p, l)) return small_bwd<T>(p, a, l);
+    if (const int bt = small_bt(p, l, true)) return small_bwd<T>(p, a, l, bt);
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
     auto kn = slab_nhwc_bwd<T, GN_SLAB_NHWC_RB>;

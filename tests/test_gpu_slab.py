@@ -119,6 +119,54 @@ def test_small_slab_masks(mask):
     check_against_oracle(wl, data, out, mask=mask)
 
 
+# Mid-size NCHW slabs (past 64 KiB, up to 256 KiB per tensor in the forward
+# and 128 KiB in the backward): one workgroup of 1024 threads each, 8 or 16
+# chunks per thread, the same kernels as the small slabs.  Each case says
+# whether the forward and the backward take them (larger slabs keep the
+# cooperative kernels).
+MID_SLABS = [
+    (W("mid_nchw_f16_80kib", 2, 320, 64, 64, 32, "f16", "nchw"), True, True),
+    (W("mid_nchw_f32_128kib", 2, 16, 64, 64, 2, "f32", "nchw"), True, True),        # the backward's limit
+    (W("mid_nchw_f16_ragged", 3, 20, 72, 80, 2, "f16", "nchw"), True, True),        # 7200 of 8192 chunk slots
+    (W("mid_nchw_f16_d256", 2, 256, 16, 16, 1, "f16", "nchw"), True, True),         # four lanes per channel sum
+    (W("mid_nchw_f32_175kib", 2, 30, 64, 70, 3, "f32", "nchw", affine="n01"), True, False),
+    (W("mid_nchw_bf16_256kib", 2, 64, 64, 64, 2, "bf16", "nchw"), True, False),     # the forward's limit
+]
+
+
+@pytest.mark.parametrize("case", MID_SLABS, ids=lambda c: c[0].name)
+def test_mid_slab_parity(case):
+    wl, fwd_one, bwd_one = case
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    say(f"[slab] {wl.name} mid")
+    data = inputs.make_inputs(wl, seed=11)
+    out = run_gpu(wl, data, force_path="slab")
+    fp, bp = out["fwd_plan"], out["bwd_plan"]
+    assert fp.path == gn.GN_PATH_SLAB and bp.path == gn.GN_PATH_SLAB
+    slabs = wl.N * wl.G
+    if fwd_one:
+        assert fp.team == 1 and fp.kernels == 1 and fp.grid == slabs
+    else:
+        assert fp.team > 1
+    if bwd_one:
+        assert bp.team == 1 and bp.grid == slabs
+    else:
+        assert bp.team > 1
+    check_against_oracle(wl, data, out)
+
+
+@pytest.mark.parametrize("mask", [gn.GN_GRAD_DX, gn.GN_GRAD_DGAMMA, gn.GN_GRAD_DBETA,
+                                  gn.GN_GRAD_DGAMMA | gn.GN_GRAD_DBETA], ids=["dx", "dgamma", "dbeta", "params"])
+def test_mid_slab_masks(mask):
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    wl = MID_SLABS[2][0]
+    data = inputs.make_inputs(wl, seed=12)
+    out = run_gpu(wl, data, force_path="slab", mask=mask)
+    check_against_oracle(wl, data, out, mask=mask)
+
+
 def test_overflow_tiles_exist_under_a_cap():
     """With the cap below the tile count, members own several tiles."""
     if not torch.cuda.is_available():

@@ -25,8 +25,9 @@ W = inputs.Workload
 FAIL = gn.Debug(spin_limit=64, flags=gn.GN_DEBUG_UNMET_WAITS)
 
 SLAB_CASES = [
-    W("wait_nchw_f32_c16_g4", 2, 16, 64, 70, 4, "f32", "nchw"),
-    W("wait_nchw_bf16_c12_g3", 3, 12, 80, 104, 3, "bf16", "nchw"),   # 65 KiB slabs: above the small-slab kernel
+    # slabs above 256 KiB: past the one-workgroup-per-slab kernels in both directions
+    W("wait_nchw_f32_c16_g4", 2, 16, 110, 150, 4, "f32", "nchw"),
+    W("wait_nchw_bf16_c12_g3", 3, 12, 208, 160, 3, "bf16", "nchw"),
     W("wait_nhwc_f16_c64_g8", 2, 64, 37, 29, 8, "f16", "nhwc"),
     W("wait_nhwc_f32_c32_g4", 1, 32, 50, 41, 4, "f32", "nhwc"),
 ]
@@ -110,6 +111,7 @@ def test_status_word_is_sticky_until_reset():
     (W("wait_stream_f16", 1, 128, 64, 130, 16, "f16", "nhwc", affine="n01"), "stream"),
     (W("wait_generic_f32", 2, 12, 7, 9, 3, "f32", "nchw"), "generic"),
     (W("wait_small_slab_bf16", 3, 12, 40, 52, 3, "bf16", "nchw"), "slab"),   # one workgroup per slab: no waits
+    (W("wait_mid_slab_f32", 2, 16, 64, 70, 4, "f32", "nchw"), "slab"),      # 70 KiB: 1024 threads per slab
 ], ids=lambda v: v if isinstance(v, str) else v.name)
 def test_paths_without_waits_ignore_the_flag(wl, path):
     if not torch.cuda.is_available():

@@ -102,6 +102,11 @@ typedef struct gn_plan_info {
  * wait between cooperating workgroups out of reach, so that each of them
  * expires after spin_limit polls -- for tests of the failure report only. */
 #define GN_DEBUG_UNMET_WAITS 1u
+/* gn_options.debug_flags: GN_DEBUG_NO_ONE_TILE keeps the stream path (NHWC)
+ * in its multi-kernel form (tile statistics, finalize, apply; tile sums,
+ * column sums, per-group terms, dx) also where one workgroup per sample
+ * would take the whole call -- for tests of that form only. */
+#define GN_DEBUG_NO_ONE_TILE 2u
 
 /* Optional knobs (pass NULL for defaults).
  *
@@ -136,7 +141,7 @@ typedef struct gn_options {
     uint32_t spin_limit;            /* polls before a wait gives up; 0 = default (2^20;
                                        a poll follows a sleep of 0.1 to 3.4 us,
                                        so the default gives up within seconds) */
-    uint32_t debug_flags;           /* 0, or GN_DEBUG_UNMET_WAITS (tests only) */
+    uint32_t debug_flags;           /* 0, or GN_DEBUG_* bits (tests only) */
 } gn_options;
 
 /* Workspace bytes gn_forward needs for these arguments (0 is possible).

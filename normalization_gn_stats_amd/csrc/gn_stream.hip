@@ -28,7 +28,9 @@
 // the elementwise dx.)  All reductions run in a fixed order, so the results
 // are bitwise reproducible.  Activations are read with non-temporal loads and
 // outputs written with non-temporal stores: nothing is read twice within the
-// caches' reach.
+// caches' reach.  A sample that fits one tile takes one workgroup, which runs
+// all of the steps above from its registers in one launch (fwd_one_tile,
+// bwd_one_tile).
 #include "gn_device.hpp"
 #include "gn_internal.hpp"
 
@@ -548,6 +550,208 @@ __global__ __launch_bounds__(kT) void bwd_dx(const T* __restrict__ dy, const T* 
     }
 }
 
+// ---- one tile per sample ----------------------------------------------------
+// A sample whose HW pixels fit one tile of at most kOneTileR chunks per thread
+// (HW <= PPI * kOneTileR) is one workgroup's whole call.  The forward's tile
+// statistics are then the sample's: the exact two-pass above gives each
+// group's mean and M2, the workgroup writes mean and rstd and then y from the
+// registers.  The backward's per-channel tile sums of dy and dy*xhat are the
+// sample's per-(n, c) sums: A and B of each group follow from a fixed-order
+// tree over the group's channels, and dx is written from the registers.  One
+// launch instead of three (forward) or four to five (backward).  grid (N).
+constexpr int kOneTileR = 16;
+
+template <typename T, int R, bool WHOLE>
+__global__ __launch_bounds__(kT) void fwd_one_tile(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                   const float* __restrict__ beta, T* __restrict__ y,
+                                                   float* __restrict__ mean, float* __restrict__ rstd,
+                                                   StreamCfg cfg) {
+    const TileGeom tg = tile_geom<T, R>(cfg.C);
+    constexpr int V = Vec<T>::V;
+    const int t = threadIdx.x;
+    const int C = (int)cfg.C, D = (int)cfg.D, G = (int)cfg.G;
+    const int64_t n = blockIdx.x;
+    __shared__ float s[kT * 8];     // [thread][k], then channel / group totals
+    __shared__ float grp[kMaxC];    // each group's mean, then its rstd (G <= C)
+    const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
+    u4v reg[R];
+    load_tile<T, R>(x + off, cfg.HW, cfg.C, tg.pi, tg.PPI, reg);
+    const int nv = valid_chunks<R>(tg.active, tg.pi, cfg.HW, tg.PPI);
+    float acc[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j < nv) {
+            float v[V];
+            Vec<T>::unpack(reg[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) acc[k] += v[k];
+        }
+    }
+    group_totals<V, WHOLE>(s, acc, tg, C, D);
+    const float cnt = (float)(cfg.HW * D);   // elements of a group in the sample
+    float mu[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) mu[k] = s[group_slot<V, WHOLE>((tg.q * V + k) / D, D)] / cnt;
+    for (int g = t; g < G; g += kT) grp[g] = s[group_slot<V, WHOLE>(g, D)] / cnt;
+    __syncthreads();   // every read of pass 1's totals is done before s is reused
+#pragma unroll
+    for (int k = 0; k < V; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j < nv) {
+            float v[V];
+            Vec<T>::unpack(reg[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float d = v[k] - mu[k];
+                acc[k] = fmaf(d, d, acc[k]);
+            }
+        }
+    }
+    group_totals<V, WHOLE>(s, acc, tg, C, D);
+    for (int g = t; g < G; g += kT) {   // thread t owns entries g = t, t + kT, ... of grp
+        float var = s[group_slot<V, WHOLE>(g, D)] / cnt;
+        var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
+        const float r = 1.0f / sqrtf(var + cfg.eps);
+        if (mean) mean[n * cfg.G + g] = grp[g];
+        rstd[n * cfg.G + g] = r;
+        grp[g] = r;
+    }
+    __syncthreads();
+    if (y == nullptr || !tg.active) return;   // no barrier below
+    float a[V], b[V];
+    load_params<V>(gamma, tg.q * V, 1.f, a);
+    load_params<V>(beta, tg.q * V, 0.f, b);
+#pragma unroll
+    for (int k = 0; k < V; ++k) a[k] *= grp[(tg.q * V + k) / D];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j < nv) {
+            float v[V], o[V];
+            Vec<T>::unpack(reg[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu[k], a[k], b[k]);
+            st16_nt(y + off + (int64_t)(tg.pi + j * tg.PPI) * cfg.C, Vec<T>::pack(o));
+        }
+    }
+}
+
+// stot: [N][C] float2 per-(n, c) sums for params_over_n (N > 1); with one
+// sample dgamma/dbeta are the channel sums themselves and are written here.
+template <typename T, int R, bool WHOLE>
+__global__ __launch_bounds__(kT) void bwd_one_tile(const T* __restrict__ dy, const T* __restrict__ x,
+                                                   const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                   const float* __restrict__ gamma, T* __restrict__ dx,
+                                                   float2* __restrict__ stot, float* __restrict__ dgamma,
+                                                   float* __restrict__ dbeta, StreamCfg cfg, int want_dx) {
+    const TileGeom tg = tile_geom<T, R>(cfg.C);
+    constexpr int V = Vec<T>::V;
+    const int t = threadIdx.x;
+    const int C = (int)cfg.C, D = (int)cfg.D;
+    const int64_t n = blockIdx.x;
+    __shared__ float2 lds[kT * 8];   // [thread][k], then channel totals at lds[c]
+    __shared__ float ga_s1[kMaxC], ga_s2[kMaxC];   // gamma_c * (sum dy, sum dy*xhat), then group totals
+    const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
+    u4v rx[R], rd[R];
+    load_tile<T, R>(x + off, cfg.HW, cfg.C, tg.pi, tg.PPI, rx);
+    load_tile<T, R>(dy + off, cfg.HW, cfg.C, tg.pi, tg.PPI, rd);
+    const int nv = valid_chunks<R>(tg.active, tg.pi, cfg.HW, tg.PPI);
+    float mu[V], rs[V];
+    int64_t sl[V];
+    channel_slices<V, WHOLE>(tg.q, D, n, cfg.G, sl);
+    per_channel<V, WHOLE>(mean, sl, mu);
+    per_channel<V, WHOLE>(rstd, sl, rs);
+    float s1[V], s2[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) { s1[k] = 0.f; s2[k] = 0.f; }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j < nv) {
+            float xv[V], dv[V];
+            Vec<T>::unpack(rx[j], xv);
+            Vec<T>::unpack(rd[j], dv);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                s1[k] += dv[k];
+                s2[k] = fmaf(dv[k], (xv[k] - mu[k]) * rs[k], s2[k]);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k) lds[t * V + k] = make_float2(s1[k], s2[k]);
+    __syncthreads();
+    tree_rows<V>(lds, tg);
+    // row 0 holds the sample's channel sums, channel c at lds[c]
+    for (int c = t; c < C; c += kT) {
+        const float2 v = lds[c];
+        if (cfg.N == 1) {
+            if (dbeta) dbeta[c] = v.x;
+            if (dgamma) dgamma[c] = v.y;
+        } else if (stot) {
+            stot[n * cfg.C + c] = v;
+        }
+    }
+    if (!want_dx) return;   // kernel argument: uniform
+    // gamma_c * (sum dy, sum dy*xhat) summed over each group's channels: with
+    // whole 16-byte chunks per group a thread first adds its chunk's V
+    // channels, then a tree over the group's chunks; otherwise a tree over
+    // the group's channels.  Group g's A*M then lies at ga_s1[g*seg], B*M at
+    // ga_s2[g*seg].
+    const int seg = WHOLE ? D / V : D;
+    if constexpr (WHOLE) {
+        if (t < tg.CPP) {
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float2 v = lds[t * V + k];
+                const float ga = gamma ? gamma[t * V + k] : 1.f;
+                a = fmaf(ga, v.x, a);
+                b = fmaf(ga, v.y, b);
+            }
+            ga_s1[t] = a;
+            ga_s2[t] = b;
+        }
+    } else {
+        for (int c = t; c < C; c += kT) {
+            const float2 v = lds[c];
+            const float ga = gamma ? gamma[c] : 1.f;
+            ga_s1[c] = ga * v.x;
+            ga_s2[c] = ga * v.y;
+        }
+    }
+    __syncthreads();
+    tree_groups(ga_s1, WHOLE ? tg.CPP : C, seg);
+    tree_groups(ga_s2, WHOLE ? tg.CPP : C, seg);
+    if (!tg.active) return;     // no barrier below
+    const float invM = 1.0f / (float)(cfg.D * cfg.HW);
+    float Ak[V], Bk[V], ga[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int g0 = ((tg.q * V + k) / D) * seg;
+        Ak[k] = ga_s1[g0] * invM;
+        Bk[k] = ga_s2[g0] * invM;
+    }
+    load_params<V>(gamma, tg.q * V, 1.f, ga);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j < nv) {
+#pragma clang fp contract(off)
+            float xv[V], dv[V], o[V];
+            Vec<T>::unpack(rx[j], xv);
+            Vec<T>::unpack(rd[j], dv);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float xh = (xv[k] - mu[k]) * rs[k];
+                const float gd = dv[k] * ga[k];
+                o[k] = rs[k] * ((gd - Ak[k]) - xh * Bk[k]);
+            }
+            st16_nt(dx + off + (int64_t)(tg.pi + j * tg.PPI) * cfg.C, Vec<T>::pack(o));
+        }
+    }
+}
+
 // ---- planning ---------------------------------------------------------------
 // (events, when given, bracket all kernels of a call)
 size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -594,8 +798,38 @@ BwdPlan bwd_plan(const Problem& p) {
     return b;
 }
 
+// Chunks per thread of the one-tile kernels for this call (4 or 16), or 0
+// when a sample needs more than one tile of kOneTileR chunks per thread or
+// the caller asked for the multi-kernel form.
+int one_tile_r(const Problem& p, const Launch& l) {
+    if (l.no_one_tile) return 0;
+    const int64_t ppi = kT / (p.C / vec_elems(p));   // pixels per iteration of a tile
+    if (p.HW > ppi * kOneTileR) return 0;
+    return p.HW > ppi * 4 ? kOneTileR : 4;
+}
+
+template <typename T, bool WHOLE>
+hipError_t fwd_one(const Problem& p, const FwdArgs& a, const Launch& l, int R) {
+    const StreamCfg cfg = make_cfg(p, R, R, a.eps);
+    auto k = R == 4 ? fwd_one_tile<T, 4, WHOLE> : fwd_one_tile<T, kOneTileR, WHOLE>;
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL(k, dim3((unsigned)p.N), dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta, (T*)a.y, a.mean,
+                       a.rstd, cfg);
+    if ((e = hipGetLastError())) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    if (l.info) {
+        l.info->path = GN_PATH_STREAM;
+        l.info->kernels = 1;
+        l.info->grid = p.N;
+        l.info->tiles = p.N;
+    }
+    return hipSuccess;
+}
+
 template <typename T, bool WHOLE>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
+    if (const int r1 = one_tile_r(p, l)) return fwd_one<T, WHOLE>(p, a, l, r1);
     constexpr int R = GN_STREAM_R_STATS, RO = GN_STREAM_R_APPLY;
     const StreamCfg cfg = make_cfg(p, R, RO, a.eps);
     float4* part = (float4*)l.ws;
@@ -623,7 +857,37 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
 }
 
 template <typename T, bool WHOLE>
+hipError_t bwd_one(const Problem& p, const BwdArgs& a, const Launch& l, int R) {
+    const StreamCfg cfg = make_cfg(p, R, R, 0.f);
+    float2* stot = (float2*)((char*)l.ws + bwd_plan(p).off_stot);
+    float* dg = (a.mask & GN_GRAD_DGAMMA) ? a.dgamma : nullptr;
+    float* db = (a.mask & GN_GRAD_DBETA) ? a.dbeta : nullptr;
+    auto k = R == 4 ? bwd_one_tile<T, 4, WHOLE> : bwd_one_tile<T, kOneTileR, WHOLE>;
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL(k, dim3((unsigned)p.N), dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean, a.rstd,
+                       a.gamma, (T*)a.dx, (p.N > 1 && (dg || db)) ? stot : nullptr, dg, db, cfg,
+                       (a.mask & GN_GRAD_DX) ? 1 : 0);
+    int kernels = 1;
+    if (p.N > 1 && (dg || db)) {
+        hipLaunchKernelGGL(params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream,
+                           (const float2*)stot, p.N, p.C, dg, db);
+        ++kernels;
+    }
+    if ((e = hipGetLastError())) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    if (l.info) {
+        l.info->path = GN_PATH_STREAM;
+        l.info->kernels = kernels;
+        l.info->grid = p.N;
+        l.info->tiles = p.N;
+    }
+    return hipSuccess;
+}
+
+template <typename T, bool WHOLE>
 hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
+    if (const int r1 = one_tile_r(p, l)) return bwd_one<T, WHOLE>(p, a, l, r1);
     constexpr int R = GN_STREAM_R_SUMS, RO = GN_STREAM_R_DX;
     const StreamCfg cfg = make_cfg(p, R, RO, 0.f);
     const BwdPlan b = bwd_plan(p);

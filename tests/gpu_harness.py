@@ -58,7 +58,7 @@ def img64(t: torch.Tensor, layout: str) -> np.ndarray:
     return inputs.memory_image(t, layout).detach().to("cpu", torch.float64).numpy()
 
 
-def run_gpu(wl, data, force_path=None, mask=ALL, max_resident=0):
+def run_gpu(wl, data, force_path=None, mask=ALL, max_resident=0, debug=None):
     """Returns dict of GPU outputs (torch tensors on the device) and the plans.
     Both calls report into a status word, which must read GN_OK afterwards
     (no bounded wait between workgroups gave up)."""
@@ -70,10 +70,10 @@ def run_gpu(wl, data, force_path=None, mask=ALL, max_resident=0):
     fi, bi = gn.PlanInfo(), gn.PlanInfo()
     status = gn.status_word(dev)
     y, mean, rstd = gn.forward(x, gamma, beta, wl.G, wl.eps, force_path=force_path, max_resident=max_resident,
-                               info=fi, status=status)
+                               info=fi, status=status, debug=debug)
     assert gn.read_status(status) == gn.GN_OK, f"{wl.name}: a forward wait gave up"
     dx, dg, db = gn.backward(dy, x, mean, rstd, gamma, wl.G, mask, force_path=force_path,
-                             max_resident=max_resident, info=bi, status=status)
+                             max_resident=max_resident, info=bi, status=status, debug=debug)
     assert gn.read_status(status) == gn.GN_OK, f"{wl.name}: a backward wait gave up"
     torch.cuda.synchronize()
     return dict(y=y, mean=mean, rstd=rstd, dx=dx, dgamma=dg, dbeta=db, fwd_plan=fi, bwd_plan=bi)

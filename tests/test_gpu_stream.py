@@ -1,11 +1,14 @@
 """GPU parity of the stream path (NHWC as a few launches of one tile per
-workgroup) against the fp64 oracle.
+workgroup, or one workgroup per sample when a sample fits one tile) against
+the fp64 oracle.
 
 Cases cover every activation dtype, one and several samples (dgamma/dbeta
 written by the per-group kernel or summed over the samples), a tile count
 past one column-sum chunk (the two-level channel reduction), groups of
 several 16-byte chunks (the merge tree across chunks), ragged last tiles and
-every output mask.
+every output mask.  Cases whose samples fit one tile run in both forms: the
+one-workgroup kernels the planner picks, and the multi-kernel form forced
+with GN_DEBUG_NO_ONE_TILE.
 """
 import pytest
 import torch
@@ -43,6 +46,11 @@ CASES = [
 ]
 
 
+# the multi-kernel form of the stream path also where one tile holds a sample
+SPLIT = gn.Debug(flags=gn.GN_DEBUG_NO_ONE_TILE)
+FORMS = {"auto": None, "split": SPLIT}
+
+
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no HIP device")
@@ -54,15 +62,58 @@ def _servable(wl):
     return p == gn.GN_PATH_STREAM
 
 
+@pytest.mark.parametrize("form", list(FORMS))
 @pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
-def test_stream_parity(wl):
+def test_stream_parity(wl, form):
     _need_gpu()
     if not _servable(wl):
         pytest.skip("shape outside the stream path (chunks per pixel must divide the workgroup)")
-    say(f"[stream] {wl.name}")
+    if form == "split" and not _one_tile(wl):
+        pytest.skip("samples of several tiles: both forms are the multi-kernel one")
+    say(f"[stream] {wl.name} {form}")
     data = inputs.make_inputs(wl, seed=3)
-    out = run_gpu(wl, data, force_path="stream")
+    out = run_gpu(wl, data, force_path="stream", debug=FORMS[form])
     assert out["fwd_plan"].path == gn.GN_PATH_STREAM and out["bwd_plan"].path == gn.GN_PATH_STREAM
+    if form == "split":
+        assert out["fwd_plan"].kernels >= 3
+    check_against_oracle(wl, data, out)
+
+
+def _one_tile(wl):
+    """Whether one tile of 16 chunks per thread holds a sample of wl."""
+    v = 4 if wl.dtype == "f32" else 8
+    return wl.HW <= (256 // (wl.C // v)) * 16
+
+
+# Samples that fit one tile (at most 16 chunks per thread): one workgroup per
+# sample takes the whole call
+ONE_TILE = [
+    W("one_tile_nhwc_f32_2x32x16x16_g8", 2, 32, 16, 16, 8, "f32", "nhwc"),          # 16 chunks a thread
+    W("one_tile_nhwc_f16_4x64x8x8_g8", 4, 64, 8, 8, 8, "f16", "nhwc"),              # 4 chunks a thread
+    W("one_tile_nhwc_f16_c2048_g32", 1, 2048, 2, 3, 32, "f16", "nhwc"),             # 256 chunks a pixel
+    W("one_tile_nhwc_f16_c320_g32", 2, 320, 9, 10, 32, "f16", "nhwc"),              # idle threads; D = 10
+    W("one_tile_nhwc_f16_c96_g24", 2, 96, 8, 8, 24, "f16", "nhwc"),                 # a chunk spans two groups
+    W("one_tile_nhwc_f32_n1_g1", 1, 64, 16, 16, 1, "f32", "nhwc", affine="n01"),    # dgamma/dbeta written directly
+    W("one_tile_nhwc_bf16_many_n", 64, 128, 4, 4, 32, "bf16", "nhwc"),
+    W("one_tile_nhwc_f32_c12_g12", 2, 12, 30, 31, 12, "f32", "nhwc"),               # one channel per group
+]
+
+
+@pytest.mark.parametrize("form", list(FORMS))
+@pytest.mark.parametrize("wl", ONE_TILE, ids=lambda w: w.name)
+def test_one_tile_parity(wl, form):
+    _need_gpu()
+    assert _one_tile(wl)
+    say(f"[stream] {wl.name} {form}")
+    data = inputs.make_inputs(wl, seed=13)
+    out = run_gpu(wl, data, force_path="stream", debug=FORMS[form])
+    fp, bp = out["fwd_plan"], out["bwd_plan"]
+    assert fp.path == gn.GN_PATH_STREAM and bp.path == gn.GN_PATH_STREAM
+    if form == "auto":
+        assert fp.kernels == 1 and fp.grid == wl.N
+        assert bp.kernels == (1 if wl.N == 1 else 2) and bp.grid == wl.N
+    else:
+        assert fp.kernels >= 3
     check_against_oracle(wl, data, out)
 
 
@@ -70,14 +121,17 @@ MASKS = [gn.GN_GRAD_DX, gn.GN_GRAD_DGAMMA, gn.GN_GRAD_DBETA, gn.GN_GRAD_DGAMMA |
          gn.GN_GRAD_DX | gn.GN_GRAD_DBETA, ALL]
 
 
+@pytest.mark.parametrize("form", list(FORMS))
 @pytest.mark.parametrize("mask", MASKS)
 @pytest.mark.parametrize("wl", [W("stream_mask_n1", 1, 64, 40, 41, 8, "f16", "nhwc"),
-                                W("stream_mask_n3", 3, 32, 30, 31, 4, "bf16", "nhwc")], ids=lambda w: w.name)
-def test_stream_output_mask(wl, mask):
+                                W("stream_mask_n3", 3, 32, 30, 31, 4, "bf16", "nhwc"),        # one tile a sample
+                                W("stream_mask_one_tile_n1", 1, 64, 8, 8, 8, "f16", "nhwc")],
+                         ids=lambda w: w.name)
+def test_stream_output_mask(wl, mask, form):
     _need_gpu()
-    say(f"[stream-mask] {wl.name} mask={mask}")
+    say(f"[stream-mask] {wl.name} mask={mask} {form}")
     data = inputs.make_inputs(wl, seed=5)
-    out = run_gpu(wl, data, force_path="stream", mask=mask)
+    out = run_gpu(wl, data, force_path="stream", mask=mask, debug=FORMS[form])
     assert out["bwd_plan"].path == gn.GN_PATH_STREAM
     check_against_oracle(wl, data, out, mask=mask)
     if not mask & gn.GN_GRAD_DGAMMA:

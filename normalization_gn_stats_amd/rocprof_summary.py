@@ -193,9 +193,9 @@ def summarize(workload: str, trace: str, fetch: str, write: str, copy_mib: int, 
                          read=(statistics.mean(rd) * f_scale if rd else None),
                          write=(statistics.mean(wr) * w_scale if wr else None)))
     rows.sort(key=lambda r: -r["avg_us"] * r["dispatches"])
-    mains = [r["kernel"] for r in rows[:2]]
+    mains = sorted(dict.fromkeys(r["kernel"] for r in rows[:2]))   # by name: near-equal times do not rename
     calls = call_totals(rows)
-    fname = "_".join(dict.fromkeys(mains)) + f"__{workload}.md"
+    fname = "_".join(mains) + f"__{workload}.md"
     lines = [f"# rocprofv3 summary: GroupNorm kernels on workload `{workload}`", "",
              "Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
              "```",

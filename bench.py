@@ -210,6 +210,10 @@ def main():
     ap.add_argument("--rows-sweep", action="store_true",
                     help="instead of the bench line: forward/backward times of the rows shapes the pages time on "
                          "MI350X, one JSON line per shape")
+    ap.add_argument("--oracle-sweep", action="store_true",
+                    help="instead of the bench line: the fp64 oracle's forward and backward times on the host "
+                         "cores for each benchmark configuration (a stated sample of the large ones), one JSON "
+                         "line each; needs no GPU")
     ap.add_argument("--mode", default="auto", choices=["auto", "graph", "eager"],
                     help="graph: the timed steps run as one captured HIP graph (no host in the loop)")
     args = ap.parse_args()
@@ -220,6 +224,10 @@ def main():
               "an all-reduce of dgamma/dbeta, which this library leaves to the caller",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.oracle_sweep:
+        oracle_sweep()
+        return
 
     import torch
 
@@ -765,6 +773,68 @@ def cpu_baseline(shapes, seconds, bytes_per_step):
                        f"slices), forward + backward, {elapsed:.1f} s of fp64 C oracle time "
                        f"(host copies and widening excluded); {threads} OpenMP threads on {os.cpu_count()} host "
                        f"cpus, {cpu_model()}")}
+
+
+# The oracle per benchmark configuration: (config, workload, sample shape or
+# None for the whole workload, what the sample is).  The large configurations
+# run on a sample of the same kind, whose time scales with its bytes.
+ORACLE_SWEEP = (
+    ("1", "tiny_nchw_f32_2x32x16x16_g8", None, "the whole workload"),
+    ("2", "rows_f16_4096x1024", None, "the whole workload"),
+    ("2", "rows_f16_8192x768", None, "the whole workload"),
+    ("3", "nhwc_f16_1x128x1024x2048_g16", dict(H=128), "a 1x128x128x2048 image (1/8 of its rows)"),
+    ("4", "nchw_f32_112x64x512x512_g8", dict(N=4), "4 of its 112 samples"),
+    ("5", "rows_bf16_131072x4096", dict(N=16384), "16384 of its 131072 rows"),
+)
+
+
+def oracle_sweep():
+    """The fp64 C oracle (as it stands) on the host cores, forward and
+    backward timed separately around the oracle calls only (inputs generated
+    and widened to float64 beforehand): the median of 10 runs for the small
+    configurations, also on one thread, and of 3 for the large ones.  One JSON
+    line per configuration shape; GB/s are algorithmic bytes of the timed
+    problem, and the full configuration's time is scaled from them."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import oracle
+    from normalization_gn_stats_amd import inputs
+
+    threads = oracle.num_threads()
+    for label, name, sample, what in ORACLE_SWEEP:
+        full = inputs.WORKLOADS[name]
+        wl = full.scaled(**sample) if sample else full
+        d = inputs.make_inputs(wl, seed=0)
+        x64 = inputs.memory_image(d["x"], wl.layout).to(torch.float64).numpy()
+        dy64 = inputs.memory_image(d["dy"], wl.layout).to(torch.float64).numpy()
+        g = d["gamma"].double().numpy()
+        b = d["beta"].double().numpy()
+        eps = float(np.float32(wl.eps))
+        reps = 10 if sample is None else 3
+        for nthreads in ((threads, 1) if sample is None else (threads,)):
+            oracle.set_num_threads(nthreads)
+            tf, tb = [], []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                oracle.forward(x64, g, b, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
+                t1 = time.perf_counter()
+                oracle.backward(dy64, x64, g, wl.N, wl.C, wl.HW, wl.G, eps, layout=wl.layout)
+                t2 = time.perf_counter()
+                tf.append(t1 - t0)
+                tb.append(t2 - t1)
+            f, bw = statistics.median(tf), statistics.median(tb)
+            scale_f = full.fwd_min_bytes() / wl.fwd_min_bytes()
+            scale_b = full.bwd_min_bytes() / wl.bwd_min_bytes()
+            print(json.dumps({"config": label, "workload": name, "timed": what, "threads": nthreads,
+                              "runs": reps, "fwd_ms": round(f * 1e3, 3), "bwd_ms": round(bw * 1e3, 3),
+                              "fwd_gbs": round(wl.fwd_min_bytes() / f / 1e9, 3),
+                              "bwd_gbs": round(wl.bwd_min_bytes() / bw / 1e9, 3),
+                              "full_fwd_ms": round(f * scale_f * 1e3, 2), "full_bwd_ms": round(bw * scale_b * 1e3, 2),
+                              "cpu": f"{os.cpu_count()} host cpus, {cpu_model()}"}), flush=True)
+        oracle.set_num_threads(threads)
 
 
 if __name__ == "__main__":

@@ -82,3 +82,25 @@ def test_stale_entry_gives_no_traffic(tmp_path, monkeypatch):
     entry["source_fingerprint"] = bench.source_fingerprint(kernel)
     (prof / "traffic.json").write_text(json.dumps({"kernels": {key: entry}}))
     assert bench.recorded_traffic(workload, kernel, grid) == int(entry["read_bytes"] + entry["write_bytes"])
+
+
+def test_oracle_sweep_lines(monkeypatch, capsys):
+    """--oracle-sweep: one JSON line per configuration shape and thread count,
+    with the forward and backward medians and the rate scaled to the full
+    configuration by its algorithmic bytes."""
+    from normalization_gn_stats_amd import inputs
+    monkeypatch.setattr(bench, "ORACLE_SWEEP", (
+        ("1", "tiny_nchw_f32_2x32x16x16_g8", None, "the whole workload"),
+        ("4", "nchw_f32_112x64x512x512_g8", dict(N=1, H=32, W=32), "a small sample"),
+    ))
+    bench.oracle_sweep()
+    lines = [json.loads(ln) for ln in capsys.readouterr().out.splitlines() if ln.startswith("{")]
+    assert [(d["config"], d["runs"]) for d in lines][-1] == ("4", 3)
+    assert {d["threads"] for d in lines if d["config"] == "1"} >= {1}
+    for d in lines:
+        assert d["fwd_ms"] > 0 and d["bwd_ms"] > 0
+    full = inputs.WORKLOADS["nchw_f32_112x64x512x512_g8"]
+    big = lines[-1]
+    sample = full.scaled(N=1, H=32, W=32)
+    want = big["fwd_ms"] * full.fwd_min_bytes() / sample.fwd_min_bytes()
+    assert abs(big["full_fwd_ms"] - want) <= 0.01 * want + 0.01

@@ -76,10 +76,15 @@ typedef enum gn_path {
                              elementwise */
     GN_PATH_ROWS = 2,     /* HW == 1: one wavefront per slice, slice kept in registers */
     GN_PATH_SLAB = 3,     /* cooperative capped grid over contiguous slabs with
-                             grid-stride overflow tiles (one-pass backward) */
+                             grid-stride overflow tiles (one-pass backward);
+                             NCHW slabs that fit one workgroup's registers (up
+                             to 256 KiB forward, 128 KiB backward, no
+                             max_resident_override) take one workgroup each
+                             instead (team 1, a normal launch) */
     GN_PATH_STREAM = 4    /* NHWC: a few launches of one tile per workgroup
-                             (statistics, fixed-order combine, outputs); the
-                             planner's choice for every NHWC shape it takes
+                             (statistics, fixed-order combine, outputs), or one
+                             workgroup per sample when a sample fits one tile;
+                             the planner's choice for every NHWC shape it takes
                              (the slab path serves NHWC when forced, or past
                              the stream grid limits) */
 } gn_path;

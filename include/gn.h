@@ -77,8 +77,7 @@ typedef enum gn_path {
     GN_PATH_ROWS = 2,     /* HW == 1: one wavefront per slice, slice kept in registers */
     GN_PATH_SLAB = 3,     /* cooperative capped grid over contiguous slabs with
                              grid-stride overflow tiles (one-pass backward);
-                             NCHW slabs that fit one workgroup's registers (up
-                             to 256 KiB forward, 128 KiB backward, no
+                             NCHW slabs of up to 256 KiB (no
                              max_resident_override) take one workgroup each
                              instead (team 1, a normal launch) */
     GN_PATH_STREAM = 4    /* NHWC: a few launches of one tile per workgroup

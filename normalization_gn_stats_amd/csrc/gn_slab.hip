@@ -23,7 +23,9 @@
 // cooperatively, so that every member is resident.  NCHW slabs that fit one
 // workgroup's registers (up to GN_SLAB_MID_FWD_BYTES forward and
 // GN_SLAB_MID_BWD_BYTES backward) skip the teams altogether: one workgroup
-// of 256 or 1024 threads per slab holds the whole slab (small_nchw_*).
+// of 256 or 1024 threads per slab holds the whole slab (small_nchw_*); a
+// backward slab of up to GN_SLAB_MID_BWD_STREAM_BYTES keeps part of x and dy
+// in registers and streams the rest twice (mid_nchw_bwd).
 //
 // Reductions (all in a fixed order, no float atomics):
 //  forward   per thread: exact two-pass (count, mean, M2) of each tile from
@@ -1122,6 +1124,126 @@ __global__ __launch_bounds__(BT) void small_nchw_bwd(const T* __restrict__ dy, c
     }
 }
 
+// Backward of a slab past what 1024 threads hold of both x and dy (128 KiB
+// each): the first RR chunk rounds of x and dy stay in registers; the other
+// rounds (up to kMidBwdRounds in all) are streamed in batches of RB chunks in
+// the sums pass and loaded again for dx.  Sums, channel sums and dx as in
+// small_nchw_bwd, in chunk order.
+constexpr int kMidBwdRounds = 16;
+template <typename T, int RR, int RB>
+__global__ __launch_bounds__(1024) void mid_nchw_bwd(const T* __restrict__ dy, const T* __restrict__ x,
+                                                     const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                     const float* __restrict__ gamma, T* __restrict__ dx,
+                                                     float2* __restrict__ stot, int64_t G, int64_t C, int D, int HW,
+                                                     int want_dx) {
+    constexpr int V = Vec<T>::V;
+    constexpr int BT = 1024, NW = BT / kWave;
+    __shared__ float lds[NW * 2];
+    __shared__ float sga[kT];                           // D <= kT
+    __shared__ float2 cpart[BT * kMidBwdRounds];        // per chunk: (sum dy, sum dy*xhat)
+    const int t = threadIdx.x;
+    const int64_t sb = blockIdx.x;
+    const int64_t n = sb / G;
+    const int g = (int)(sb - n * G);
+    const int M = D * HW, nq = M / V, cpc = HW / V;
+    const int nr = (nq + BT - 1) / BT;                  // chunk rounds (RR < nr <= kMidBwdRounds)
+    const float mu = mean[sb], r = rstd[sb];
+    if (t < D) sga[t] = gamma ? gamma[g * D + t] : 1.f;
+    const T* xs = x + sb * (int64_t)M;
+    const T* ds = dy + sb * (int64_t)M;
+    auto at = [&](int j) { const int q = j * BT + t; return (int64_t)(q < nq ? q : nq - 1) * V; };
+    u4v bx[RR], bd[RR];
+#pragma unroll
+    for (int j = 0; j < RR; ++j) {   // branch-free: past the end, the last chunk again (not used)
+        bx[j] = ld16_nt(xs + at(j));
+        bd[j] = ld16_nt(ds + at(j));
+    }
+    __syncthreads();   // sga
+    float ab[2] = {0.f, 0.f};
+    // one chunk's sums into cpart and this thread's (A, B) terms
+    auto sums = [&](int j, const u4v& cx, const u4v& cd) {
+        const int q = j * BT + t;
+        if (q >= nq) return;
+        const float ga = sga[q / cpc];
+        float xv[V], dv[V];
+        Vec<T>::unpack(cx, xv);
+        Vec<T>::unpack(cd, dv);
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const float xh = (xv[k] - mu) * r;
+            s1 += dv[k];
+            s2 = fmaf(dv[k], xh, s2);
+        }
+        cpart[q] = make_float2(s1, s2);
+        ab[0] = fmaf(ga, s1, ab[0]);
+        ab[1] = fmaf(ga, s2, ab[1]);
+    };
+#pragma unroll
+    for (int j = 0; j < RR; ++j) sums(j, bx[j], bd[j]);
+    for (int j0 = RR; j0 < nr; j0 += RB) {   // uniform
+        u4v ox[RB], od[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            ox[i] = ld16_nt(xs + at(j0 + i));
+            od[i] = ld16_nt(ds + at(j0 + i));
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            if (j0 + i < nr) sums(j0 + i, ox[i], od[i]);
+    }
+    block_sum<2, NW>(ab, lds);   // its barriers also publish cpart
+    int W = 64;
+    while (W > 1 && W * D > BT) W >>= 1;
+    const int ccl = t / W, cj = t & (W - 1);
+    float2 run = make_float2(0.f, 0.f);
+    if (ccl < D) {
+        for (int i = cj; i < cpc; i += W) {
+            const float2 v = cpart[ccl * cpc + i];
+            run.x += v.x;
+            run.y += v.y;
+        }
+    }
+    for (int o = W >> 1; o > 0; o >>= 1) {   // every lane takes part
+        run.x += __shfl_xor(run.x, o, kWave);
+        run.y += __shfl_xor(run.y, o, kWave);
+    }
+    if (cj == 0 && ccl < D) stot[n * C + (int64_t)g * D + ccl] = run;
+    if (!want_dx) return;
+    const float invM = 1.0f / (float)M;
+    const float A = ab[0] * invM, B = ab[1] * invM;
+    T* dxs = dx + sb * (int64_t)M;
+    auto out = [&](int j, const u4v& cx, const u4v& cd) {
+#pragma clang fp contract(off)
+        const int q = j * BT + t;
+        if (q >= nq) return;
+        const float ga = sga[q / cpc];
+        float xv[V], dv[V], o[V];
+        Vec<T>::unpack(cx, xv);
+        Vec<T>::unpack(cd, dv);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const float xh = (xv[k] - mu) * r;
+            const float gd = dv[k] * ga;
+            o[k] = r * ((gd - A) - xh * B);
+        }
+        st16_nt(dxs + (int64_t)q * V, Vec<T>::pack(o));
+    };
+#pragma unroll
+    for (int j = 0; j < RR; ++j) out(j, bx[j], bd[j]);
+    for (int j0 = RR; j0 < nr; j0 += RB) {
+        u4v ox[RB], od[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            ox[i] = ld16_nt(xs + at(j0 + i));
+            od[i] = ld16_nt(ds + at(j0 + i));
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            if (j0 + i < nr) out(j0 + i, ox[i], od[i]);
+    }
+}
+
 // ---- helpers ---------------------------------------------------------------
 // Words [0, zeros) := 0, [zeros, total) := all ones.
 __global__ void clear_words(uint32_t* p, int64_t zeros, int64_t total) {
@@ -1340,15 +1462,28 @@ constexpr int kMidT = 1024;
 static_assert(GN_SLAB_SOLO_BYTES <= kT * 16 * 16, "small slabs: at most 16 chunks per thread");
 static_assert(GN_SLAB_MID_FWD_BYTES <= kMidT * 16 * 16, "mid-size forward: at most 16 chunks per thread");
 static_assert(GN_SLAB_MID_BWD_BYTES <= kMidT * 8 * 16, "mid-size backward: at most 8 chunks per thread");
+// Backward slabs past GN_SLAB_MID_BWD_BYTES up to this size: mid_nchw_bwd,
+// eight chunk rounds of x and dy in registers and the rest streamed twice.
+// Graphs of 20 calls, backward us, cooperative kernels -> mid_nchw_bwd with 8
+// (4) rounds held: 2 x 640 x 64 x 64 fp16 G32 (160 KiB) 38.5 -> 21.9 (21.0);
+// 16 x 640 x 64 x 64 fp16 G32 90.2 -> 58.9 (63.9); 4 x 32 x 64 x 64 fp32 G2
+// (256 KiB) 33.0 -> 17.5 (17.4).
+#ifndef GN_SLAB_MID_BWD_STREAM_BYTES
+#define GN_SLAB_MID_BWD_STREAM_BYTES (256 << 10)
+#endif
+static_assert(GN_SLAB_MID_BWD_STREAM_BYTES <= kMidT * kMidBwdRounds * 16, "mid_nchw_bwd: at most 16 chunk rounds");
+constexpr int kMidStreamT = -kMidT;   // small_bt's answer for mid_nchw_bwd
 
-// Threads per workgroup of the one-workgroup-per-slab kernels for this call,
-// or 0 when they do not take it (other layouts, larger slabs, or a residency
-// cap, which asks for the cooperative kernels' overflow tiles).
+// Threads per workgroup of the one-workgroup-per-slab kernels for this call
+// (kMidStreamT: mid_nchw_bwd's 1024), or 0 when they do not take it (other
+// layouts, larger slabs, or a residency cap, which asks for the cooperative
+// kernels' overflow tiles).
 int small_bt(const Problem& p, const Launch& l, bool backward) {
     if (p.layout != GN_NCHW || l.max_resident_override > 0 || p.N * p.G > INT32_MAX) return 0;
     const int64_t b = p.D * p.HW * p.elem_bytes;
     if (b <= (int64_t)GN_SLAB_SOLO_BYTES) return kT;
     if (b <= (int64_t)(backward ? GN_SLAB_MID_BWD_BYTES : GN_SLAB_MID_FWD_BYTES)) return kMidT;
+    if (backward && b <= (int64_t)GN_SLAB_MID_BWD_STREAM_BYTES) return kMidStreamT;
     return 0;
 }
 
@@ -1404,8 +1539,9 @@ hipError_t small_fwd(const Problem& p, const FwdArgs& a, const Launch& l, int bt
 
 template <typename T>
 hipError_t small_bwd(const Problem& p, const BwdArgs& a, const Launch& l, int bt) {
-    auto k = small_bwd_kernel<T>(bt, small_r(p, bt));
+    auto k = bt == kMidStreamT ? mid_nchw_bwd<T, 8, 4> : small_bwd_kernel<T>(bt, small_r(p, bt));
     if (k == nullptr) return hipErrorInvalidValue;   // the byte limits above rule this out
+    if (bt == kMidStreamT) bt = kMidT;
     const Plan pl = layout_ws(p, true, 1);   // the layout does not depend on the cap
     float2* stot = (float2*)((char*)l.ws + pl.off_stot);
     const unsigned grid = (unsigned)(p.N * p.G);

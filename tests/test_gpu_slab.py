@@ -119,18 +119,23 @@ def test_small_slab_masks(mask):
     check_against_oracle(wl, data, out, mask=mask)
 
 
-# Mid-size NCHW slabs (past 64 KiB, up to 256 KiB per tensor in the forward
-# and 128 KiB in the backward): one workgroup of 1024 threads each, 8 or 16
-# chunks per thread, the same kernels as the small slabs.  Each case says
-# whether the forward and the backward take them (larger slabs keep the
-# cooperative kernels).
+# Mid-size NCHW slabs (past 64 KiB, up to 256 KiB per tensor): one workgroup
+# of 1024 threads each.  The forward holds 8 or 16 chunks per thread; the
+# backward holds all of x and dy up to 128 KiB, and past that keeps four chunk
+# rounds in registers and streams the others twice (mid_nchw_bwd).  Each case
+# says whether the forward and the backward take one workgroup per slab
+# (larger slabs keep the cooperative kernels).
 MID_SLABS = [
     (W("mid_nchw_f16_80kib", 2, 320, 64, 64, 32, "f16", "nchw"), True, True),
-    (W("mid_nchw_f32_128kib", 2, 16, 64, 64, 2, "f32", "nchw"), True, True),        # the backward's limit
+    (W("mid_nchw_f32_128kib", 2, 16, 64, 64, 2, "f32", "nchw"), True, True),        # all of x and dy held
     (W("mid_nchw_f16_ragged", 3, 20, 72, 80, 2, "f16", "nchw"), True, True),        # 7200 of 8192 chunk slots
     (W("mid_nchw_f16_d256", 2, 256, 16, 16, 1, "f16", "nchw"), True, True),         # four lanes per channel sum
-    (W("mid_nchw_f32_175kib", 2, 30, 64, 70, 3, "f32", "nchw", affine="n01"), True, False),
-    (W("mid_nchw_bf16_256kib", 2, 64, 64, 64, 2, "bf16", "nchw"), True, False),     # the forward's limit
+    (W("mid_nchw_f32_175kib", 2, 30, 64, 70, 3, "f32", "nchw", affine="n01"), True, True),   # 11 rounds, 7 streamed
+    (W("mid_nchw_bf16_256kib", 2, 64, 64, 64, 2, "bf16", "nchw"), True, True),      # 16 rounds: both limits
+    (W("mid_nchw_f16_160kib", 2, 640, 64, 64, 32, "f16", "nchw"), True, True),      # 10 rounds: a short last batch
+    (W("mid_nchw_f32_ragged_164kib", 3, 20, 60, 70, 2, "f32", "nchw"), True, True),  # 260 chunks in the last round
+    (W("mid_nchw_bf16_d256_256kib", 2, 256, 16, 32, 1, "bf16", "nchw"), True, True),
+    (W("mid_nchw_f32_258kib", 2, 16, 110, 150, 4, "f32", "nchw"), False, False),    # past both limits
 ]
 
 
@@ -156,12 +161,13 @@ def test_mid_slab_parity(case):
     check_against_oracle(wl, data, out)
 
 
+@pytest.mark.parametrize("case", [2, 6], ids=["held", "streamed"])
 @pytest.mark.parametrize("mask", [gn.GN_GRAD_DX, gn.GN_GRAD_DGAMMA, gn.GN_GRAD_DBETA,
                                   gn.GN_GRAD_DGAMMA | gn.GN_GRAD_DBETA], ids=["dx", "dgamma", "dbeta", "params"])
-def test_mid_slab_masks(mask):
+def test_mid_slab_masks(mask, case):
     if not torch.cuda.is_available():
         pytest.skip("no HIP device")
-    wl = MID_SLABS[2][0]
+    wl = MID_SLABS[case][0]
     data = inputs.make_inputs(wl, seed=12)
     out = run_gpu(wl, data, force_path="slab", mask=mask)
     check_against_oracle(wl, data, out, mask=mask)

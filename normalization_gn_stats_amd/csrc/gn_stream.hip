@@ -484,8 +484,8 @@ __global__ __launch_bounds__(kT) void bwd_group_ab(const float2* __restrict__ st
 }
 
 // dgamma/dbeta as sums over the samples, in sample order
-__global__ __launch_bounds__(kT) void params_over_n(const float2* __restrict__ stot, int64_t N, int64_t C,
-                                                    float* __restrict__ dgamma, float* __restrict__ dbeta) {
+__global__ __launch_bounds__(kT) void stream_params_over_n(const float2* __restrict__ stot, int64_t N, int64_t C,
+                                                           float* __restrict__ dgamma, float* __restrict__ dbeta) {
     const int64_t c = (int64_t)blockIdx.x * kT + threadIdx.x;
     if (c >= C) return;
     float a = 0.f, b = 0.f;
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(kT) void fwd_one_tile(const T* __restrict__ x, cons
     }
 }
 
-// stot: [N][C] float2 per-(n, c) sums for params_over_n (N > 1); with one
+// stot: [N][C] float2 per-(n, c) sums for stream_params_over_n (N > 1); with one
 // sample dgamma/dbeta are the channel sums themselves and are written here.
 template <typename T, int R, bool WHOLE>
 __global__ __launch_bounds__(kT) void bwd_one_tile(const T* __restrict__ dy, const T* __restrict__ x,
@@ -870,7 +870,7 @@ hipError_t bwd_one(const Problem& p, const BwdArgs& a, const Launch& l, int R) {
                        (a.mask & GN_GRAD_DX) ? 1 : 0);
     int kernels = 1;
     if (p.N > 1 && (dg || db)) {
-        hipLaunchKernelGGL(params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream,
+        hipLaunchKernelGGL(stream_params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream,
                            (const float2*)stot, p.N, p.C, dg, db);
         ++kernels;
     }
@@ -925,7 +925,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
         ++kernels;
     }
     if (p.N > 1 && (dg || db)) {
-        hipLaunchKernelGGL(params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream,
+        hipLaunchKernelGGL(stream_params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream,
                            (const float2*)stot, p.N, p.C, dg, db);
         ++kernels;
     }

@@ -104,3 +104,20 @@ def test_oracle_sweep_lines(monkeypatch, capsys):
     sample = full.scaled(N=1, H=32, W=32)
     want = big["fwd_ms"] * full.fwd_min_bytes() / sample.fwd_min_bytes()
     assert abs(big["full_fwd_ms"] - want) <= 0.01 * want + 0.01
+
+
+def test_every_kernel_maps_to_its_own_source_file():
+    """Each __global__ kernel under csrc/ resolves to the .hip file that defines
+    it, so that a profile of any kernel can be checked against its sources."""
+    import re
+    d = os.path.join(ROOT, "normalization_gn_stats_amd", "csrc")
+    names = {}
+    for f in sorted(os.listdir(d)):
+        if f.endswith(".hip"):
+            pat = r"__global__\s+(?:__launch_bounds__\([^)]*\)\s+)?void\s+(\w+)\s*\("
+            for m in re.finditer(pat, open(os.path.join(d, f)).read()):
+                names[m.group(1)] = f
+    assert len(names) > 20
+    for name, f in names.items():
+        mapped = [g for prefixes, g in bench.KERNEL_SOURCES if name.startswith(prefixes)]
+        assert mapped and mapped[0] == f, f"{name} (in {f}) maps to {mapped}"

@@ -224,7 +224,7 @@ gn_status backward_call(const void* dy, const void* x, const float* mean, const 
     gn::BwdArgs a{dy, x, mean, rstd, gamma,
                   (mask & GN_GRAD_DX) ? dx : nullptr,
                   (mask & GN_GRAD_DGAMMA) ? dgamma : nullptr,
-                  (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask};
+                  (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask, 0};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
     return with_call_events(opts, stream, [&] {
@@ -292,7 +292,7 @@ gn_status gn_forward(const void* x, const float* gamma, const float* beta, void*
     }
     const size_t need = fwd_ws(p, path);
     if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
-    gn::FwdArgs a{x, gamma, beta, y, mean, rstd, eps};
+    gn::FwdArgs a{x, gamma, beta, y, mean, rstd, eps, 0};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{path, 0, 0, 0, 0, 0};
     return with_call_events(opts, stream, [&] {
@@ -446,7 +446,7 @@ gn_status gn_forward_strided(const void* x, const int64_t* x_strides, const floa
     if (!generic_allowed(opts)) return GN_ERR_UNSUPPORTED;
     const size_t need = gn::generic_fwd_ws(p, sd);
     if (ws_bytes < need || (need > 0 && (workspace == nullptr || !aligned16(workspace)))) return GN_ERR_WORKSPACE;
-    gn::FwdArgs a{x, gamma, beta, y, mean, rstd, eps};
+    gn::FwdArgs a{x, gamma, beta, y, mean, rstd, eps, 0};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{GN_PATH_GENERIC, 0, 0, 0, 0, 0};
     return with_call_events(opts, stream, [&] { return gn::generic_fwd(p, sd, a, l); });
@@ -499,7 +499,7 @@ gn_status gn_backward_strided(const void* dy, const int64_t* dy_strides, const v
     gn::BwdArgs a{dy, x, mean, rstd, gamma,
                   (mask & GN_GRAD_DX) ? dx : nullptr,
                   (mask & GN_GRAD_DGAMMA) ? dgamma : nullptr,
-                  (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask};
+                  (mask & GN_GRAD_DBETA) ? dbeta : nullptr, mask, 0};
     gn::Launch l = make_launch(workspace, ws_bytes, stream, opts);
     if (l.info) *l.info = gn_plan_info{GN_PATH_GENERIC, 0, 0, 0, 0, 0};
     return with_call_events(opts, stream, [&] { return gn::generic_bwd(p, sd, a, l); });

@@ -106,11 +106,12 @@ typedef struct gn_plan_info {
  * wait between cooperating workgroups out of reach, so that each of them
  * expires after spin_limit polls -- for tests of the failure report only. */
 #define GN_DEBUG_UNMET_WAITS 1u
-/* gn_options.debug_flags: GN_DEBUG_NO_ONE_TILE keeps the stream path (NHWC)
- * in its multi-kernel form (tile statistics, finalize, apply; tile sums,
- * column sums, per-group terms, dx) also where one workgroup per sample
- * would take the whole call -- for tests of that form only. */
-#define GN_DEBUG_NO_ONE_TILE 2u
+/* gn_options.debug_flags: GN_DEBUG_STREAM_SPLIT keeps the stream path (NHWC)
+ * in its full multi-kernel form (tile statistics, finalize, apply; tile sums,
+ * column sums, per-group terms, dx) also where one workgroup per sample would
+ * take the whole call or the output kernels would combine a few tiles'
+ * partials themselves -- for tests of that form only. */
+#define GN_DEBUG_STREAM_SPLIT 2u
 
 /* Optional knobs (pass NULL for defaults).
  *

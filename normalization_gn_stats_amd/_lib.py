@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("GN_LIB_PATH") or os.path.join(HERE, "lib", "libgn_mi3
 GN_OK, GN_ERR_INVALID, GN_ERR_UNSUPPORTED, GN_ERR_WORKSPACE, GN_ERR_HIP, GN_ERR_WAIT = range(6)
 GN_STATUS_WAIT_EXPIRED = 1
 GN_DEBUG_UNMET_WAITS = 1
-GN_DEBUG_NO_ONE_TILE = 2
+GN_DEBUG_STREAM_SPLIT = 2
 GN_SCRATCH_BYTES = 32 << 20
 GN_F32, GN_F16, GN_BF16 = range(3)
 GN_NCHW, GN_NHWC = range(2)

@@ -147,7 +147,7 @@ gn::Launch make_launch(void* ws, size_t ws_bytes, void* stream, const gn_options
     l.status_word = opts ? opts->status_word : nullptr;
     l.spin_limit = (opts && opts->spin_limit) ? opts->spin_limit : gn::kDefaultSpinLimit;
     l.unmet_waits = (opts && (opts->debug_flags & GN_DEBUG_UNMET_WAITS)) ? 1u : 0u;
-    l.no_one_tile = (opts && (opts->debug_flags & GN_DEBUG_NO_ONE_TILE)) ? 1u : 0u;
+    l.stream_split = (opts && (opts->debug_flags & GN_DEBUG_STREAM_SPLIT)) ? 1u : 0u;
     return l;
 }
 

@@ -58,7 +58,7 @@ struct Launch {
     uint32_t* status_word; // device word for failure reports, or NULL
     uint32_t spin_limit;   // polls before a bounded wait gives up (never 0)
     uint32_t unmet_waits;  // 1: every wait's target out of reach (failure-report tests)
-    uint32_t no_one_tile;  // 1: the stream path's multi-kernel form even for one-tile samples (tests)
+    uint32_t stream_split;  // 1: the stream path's full multi-kernel form, no fused forms (tests)
 };
 
 // Polls before a bounded wait between workgroups gives up: 2^20 polls, each

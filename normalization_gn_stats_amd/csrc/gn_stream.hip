@@ -30,7 +30,9 @@
 // outputs written with non-temporal stores: nothing is read twice within the
 // caches' reach.  A sample that fits one tile takes one workgroup, which runs
 // all of the steps above from its registers in one launch (fwd_one_tile,
-// bwd_one_tile).
+// bwd_one_tile); a sample of a few tiles skips step 2 (forward) or steps 2
+// and 3 (backward), which its output kernels do themselves (fwd_apply_few,
+// bwd_dx_few).
 #include "gn_device.hpp"
 #include "gn_internal.hpp"
 
@@ -752,6 +754,175 @@ __global__ __launch_bounds__(kT) void bwd_one_tile(const T* __restrict__ dy, con
     }
 }
 
+// ---- a few tiles per sample ------------------------------------------------
+// When a sample has at most kFewTiles statistics tiles, the output kernels
+// combine the sample's tile partials themselves instead of a separate
+// finalize (forward) or column-sum and per-group launches (backward): every
+// workgroup of the sample reads the same partials (at most kFewTiles*G float4
+// or kFewTiles*C float2, from L2) and combines them in tile order, so all of
+// them derive the same statistics, and workgroup 0 of the sample writes the
+// call's outputs (mean/rstd; dgamma/dbeta or the per-(n, c) sums).
+constexpr int kFewTiles = 16;
+
+// grid (otiles, N); part: [N*G][tiles] float4 from fwd_tile_stats
+template <typename T, int R, bool WHOLE>
+__global__ __launch_bounds__(kT) void fwd_apply_few(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                    const float* __restrict__ beta, T* __restrict__ y,
+                                                    const float4* __restrict__ part, float* __restrict__ mean,
+                                                    float* __restrict__ rstd, StreamCfg cfg) {
+    const TileGeom tg = tile_geom<T, R>(cfg.C);
+    constexpr int V = Vec<T>::V;
+    const int t = threadIdx.x;
+    const int64_t tile = blockIdx.x, n = blockIdx.y;
+    __shared__ float gmu[kMaxC], grs[kMaxC];
+    for (int g = t; g < (int)cfg.G; g += kT) {   // the finalize of fwd_finalize, in tile order
+        const float4* pg = part + (n * cfg.G + g) * cfg.tiles;
+        float s0 = 0.f, s1 = 0.f;
+        for (int64_t i = 0; i < cfg.tiles; ++i) {
+            const float4 v = pg[i];
+            s0 = fmaf(v.x, v.y, s0);
+            s1 += v.x;
+        }
+        const float mu = s0 / s1;
+        float m2 = 0.f;
+        for (int64_t i = 0; i < cfg.tiles; ++i) {
+            const float4 v = pg[i];
+            const float d = v.y - mu;
+            m2 += fmaf(v.x * d, d, v.z);
+        }
+        float var = m2 / (float)(cfg.D * cfg.HW);
+        var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
+        const float r = 1.0f / sqrtf(var + cfg.eps);
+        gmu[g] = mu;
+        grs[g] = r;
+        if (tile == 0) {
+            if (mean) mean[n * cfg.G + g] = mu;
+            rstd[n * cfg.G + g] = r;
+        }
+    }
+    __syncthreads();
+    if (y == nullptr || !tg.active) return;   // no barrier below
+    const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
+    u4v reg[R];
+    const int64_t p0 = tile * tg.TP + tg.pi;
+    load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, reg);
+    float mu[V], a[V], b[V];
+    load_params<V>(gamma, tg.q * V, 1.f, a);
+    load_params<V>(beta, tg.q * V, 0.f, b);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int g = (tg.q * V + k) / (int)cfg.D;
+        mu[k] = gmu[g];
+        a[k] *= grs[g];
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t p = p0 + (int64_t)j * tg.PPI;
+        if (p < cfg.HW) {
+            float v[V], o[V];
+            Vec<T>::unpack(reg[j], v);
+#pragma unroll
+            for (int k = 0; k < V; ++k) o[k] = fmaf(v[k] - mu[k], a[k], b[k]);
+            st16_nt(y + off + p * cfg.C, Vec<T>::pack(o));
+        }
+    }
+}
+
+// grid (otiles, N) with dx, (1, N) without; part: [N][tiles][C] float2 from
+// bwd_tile_sums.  Workgroup 0 of a sample writes dgamma/dbeta (one sample) or
+// the sample's per-(n, c) sums into stot (several, for stream_params_over_n).
+template <typename T, int R, bool WHOLE>
+__global__ __launch_bounds__(kT) void bwd_dx_few(const T* __restrict__ dy, const T* __restrict__ x,
+                                                 const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                 const float* __restrict__ gamma, const float2* __restrict__ part,
+                                                 T* __restrict__ dx, float2* __restrict__ stot,
+                                                 float* __restrict__ dgamma, float* __restrict__ dbeta,
+                                                 StreamCfg cfg, int want_dx) {
+    const TileGeom tg = tile_geom<T, R>(cfg.C);
+    constexpr int V = Vec<T>::V;
+    const int t = threadIdx.x;
+    const int C = (int)cfg.C, D = (int)cfg.D;
+    const int64_t tile = blockIdx.x, n = blockIdx.y;
+    __shared__ float ga_s1[kMaxC], ga_s2[kMaxC];   // gamma_c * (sum dy, sum dy*xhat), then group totals
+    const float2* pn = part + n * cfg.tiles * cfg.C;
+    for (int c = t; c < C; c += kT) {   // the sample's channel sums, in tile order
+        float2 v = make_float2(0.f, 0.f);
+        for (int64_t i = 0; i < cfg.tiles; ++i) {
+            const float2 q = pn[i * cfg.C + c];
+            v.x += q.x;
+            v.y += q.y;
+        }
+        if (tile == 0) {
+            if (cfg.N == 1) {
+                if (dbeta) dbeta[c] = v.x;
+                if (dgamma) dgamma[c] = v.y;
+            } else if (stot) {
+                stot[n * cfg.C + c] = v;
+            }
+        }
+        const float ga = gamma ? gamma[c] : 1.f;
+        ga_s1[c] = ga * v.x;
+        ga_s2[c] = ga * v.y;
+    }
+    if (!want_dx) return;   // kernel argument: uniform
+    __syncthreads();
+    const int seg = WHOLE ? D / V : D;
+    if constexpr (WHOLE) {   // a chunk's V channels first (one group), then a tree over the group's chunks
+        float a = 0.f, b = 0.f;
+        if (t < tg.CPP) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                a += ga_s1[t * V + k];
+                b += ga_s2[t * V + k];
+            }
+        }
+        __syncthreads();   // every read of the per-channel values is done
+        if (t < tg.CPP) {
+            ga_s1[t] = a;
+            ga_s2[t] = b;
+        }
+        __syncthreads();
+    }
+    tree_groups(ga_s1, WHOLE ? tg.CPP : C, seg);
+    tree_groups(ga_s2, WHOLE ? tg.CPP : C, seg);
+    if (!tg.active) return;   // no barrier below
+    const int64_t off = n * cfg.HW * cfg.C + tg.q * V;
+    const int64_t p0 = tile * tg.TP + tg.pi;
+    const float invM = 1.0f / (float)(cfg.D * cfg.HW);
+    float mu[V], rs[V], Ak[V], Bk[V], ga[V];
+    int64_t sl[V];
+    channel_slices<V, WHOLE>(tg.q, D, n, cfg.G, sl);
+    per_channel<V, WHOLE>(mean, sl, mu);
+    per_channel<V, WHOLE>(rstd, sl, rs);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int g0 = ((tg.q * V + k) / D) * seg;
+        Ak[k] = ga_s1[g0] * invM;
+        Bk[k] = ga_s2[g0] * invM;
+    }
+    load_params<V>(gamma, tg.q * V, 1.f, ga);
+    u4v rx[R], rd[R];
+    load_tile<T, R>(x + off, cfg.HW, cfg.C, p0, tg.PPI, rx);
+    load_tile<T, R>(dy + off, cfg.HW, cfg.C, p0, tg.PPI, rd);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t p = p0 + (int64_t)j * tg.PPI;
+        if (p < cfg.HW) {
+#pragma clang fp contract(off)
+            float xv[V], dv[V], o[V];
+            Vec<T>::unpack(rx[j], xv);
+            Vec<T>::unpack(rd[j], dv);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float xh = (xv[k] - mu[k]) * rs[k];
+                const float gd = dv[k] * ga[k];
+                o[k] = rs[k] * ((gd - Ak[k]) - xh * Bk[k]);
+            }
+            st16_nt(dx + off + p * cfg.C, Vec<T>::pack(o));
+        }
+    }
+}
+
 // ---- planning ---------------------------------------------------------------
 // (events, when given, bracket all kernels of a call)
 size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -802,7 +973,7 @@ BwdPlan bwd_plan(const Problem& p) {
 // when a sample needs more than one tile of kOneTileR chunks per thread or
 // the caller asked for the multi-kernel form.
 int one_tile_r(const Problem& p, const Launch& l) {
-    if (l.no_one_tile) return 0;
+    if (l.stream_split) return 0;
     const int64_t ppi = kT / (p.C / vec_elems(p));   // pixels per iteration of a tile
     if (p.HW > ppi * kOneTileR) return 0;
     return p.HW > ppi * 4 ? kOneTileR : 4;
@@ -837,14 +1008,24 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     hipError_t e = record(l.ev_begin, l.stream);
     if (e) return e;
     hipLaunchKernelGGL((fwd_tile_stats<T, R, WHOLE>), grid, dim3(kT), 0, l.stream, (const T*)a.x, cfg, part);
-    hipLaunchKernelGGL(fwd_finalize, dim3((unsigned)(p.N * p.G)), dim3(kFinT), 0, l.stream, part, cfg, a.mean, a.rstd);
-    if ((e = hipGetLastError())) return e;
-    int kernels = 2;
-    if (a.y) {
-        hipLaunchKernelGGL((fwd_apply<T, RO, WHOLE>), ogrid, dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta, (T*)a.y,
-                           a.mean, a.rstd, cfg);
+    int kernels = 1;
+    if (!l.stream_split && cfg.tiles <= kFewTiles) {   // the output kernel combines the partials itself
+        const dim3 fgrid(a.y ? (unsigned)cfg.otiles : 1u, (unsigned)p.N);
+        hipLaunchKernelGGL((fwd_apply_few<T, RO, WHOLE>), fgrid, dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta,
+                           (T*)a.y, (const float4*)part, a.mean, a.rstd, cfg);
         if ((e = hipGetLastError())) return e;
         ++kernels;
+    } else {
+        hipLaunchKernelGGL(fwd_finalize, dim3((unsigned)(p.N * p.G)), dim3(kFinT), 0, l.stream, part, cfg, a.mean,
+                           a.rstd);
+        if ((e = hipGetLastError())) return e;
+        ++kernels;
+        if (a.y) {
+            hipLaunchKernelGGL((fwd_apply<T, RO, WHOLE>), ogrid, dim3(kT), 0, l.stream, (const T*)a.x, a.gamma, a.beta,
+                               (T*)a.y, a.mean, a.rstd, cfg);
+            if ((e = hipGetLastError())) return e;
+            ++kernels;
+        }
     }
     if ((e = record(l.ev_end, l.stream))) return e;
     if (l.info) {
@@ -907,6 +1088,28 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     hipLaunchKernelGGL((bwd_tile_sums<T, R, WHOLE>), grid, dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x, a.mean,
                        a.rstd, cfg, part);
     ++kernels;
+    if (!l.stream_split && b.tiles <= kFewTiles) {   // the dx kernel combines the tile sums itself
+        const bool params = p.N > 1 && (dg || db);
+        const dim3 fgrid(want_dx ? (unsigned)cfg.otiles : 1u, (unsigned)p.N);
+        hipLaunchKernelGGL((bwd_dx_few<T, RO, WHOLE>), fgrid, dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x,
+                           a.mean, a.rstd, a.gamma, (const float2*)part, (T*)a.dx, params ? stot : nullptr, dg, db, cfg,
+                           want_dx ? 1 : 0);
+        ++kernels;
+        if (params) {
+            hipLaunchKernelGGL(stream_params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream,
+                               (const float2*)stot, p.N, p.C, dg, db);
+            ++kernels;
+        }
+        if ((e = hipGetLastError())) return e;
+        if ((e = record(l.ev_end, l.stream))) return e;
+        if (l.info) {
+            l.info->path = GN_PATH_STREAM;
+            l.info->kernels = kernels;
+            l.info->grid = cfg.tiles * p.N;
+            l.info->tiles = cfg.tiles * p.N;
+        }
+        return hipSuccess;
+    }
     if (b.chunks > 1) {
         hipLaunchKernelGGL(col_sums, dim3(cblocks, (unsigned)b.chunks, (unsigned)p.N), dim3(kT), 0, l.stream,
                            (const float2*)part, b.tiles, p.C, kRowsPerChunk, chunk);

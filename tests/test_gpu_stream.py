@@ -6,9 +6,10 @@ Cases cover every activation dtype, one and several samples (dgamma/dbeta
 written by the per-group kernel or summed over the samples), a tile count
 past one column-sum chunk (the two-level channel reduction), groups of
 several 16-byte chunks (the merge tree across chunks), ragged last tiles and
-every output mask.  Cases whose samples fit one tile run in both forms: the
-one-workgroup kernels the planner picks, and the multi-kernel form forced
-with GN_DEBUG_NO_ONE_TILE.
+every output mask.  Cases whose samples fit one tile, or a few tiles, run in
+both forms: the fused kernels the planner picks (one workgroup per sample;
+output kernels that combine the tile partials themselves), and the full
+multi-kernel form forced with GN_DEBUG_STREAM_SPLIT.
 """
 import pytest
 import torch
@@ -46,8 +47,8 @@ CASES = [
 ]
 
 
-# the multi-kernel form of the stream path also where one tile holds a sample
-SPLIT = gn.Debug(flags=gn.GN_DEBUG_NO_ONE_TILE)
+# the full multi-kernel form of the stream path also where the fused forms apply
+SPLIT = gn.Debug(flags=gn.GN_DEBUG_STREAM_SPLIT)
 FORMS = {"auto": None, "split": SPLIT}
 
 
@@ -68,8 +69,8 @@ def test_stream_parity(wl, form):
     _need_gpu()
     if not _servable(wl):
         pytest.skip("shape outside the stream path (chunks per pixel must divide the workgroup)")
-    if form == "split" and not _one_tile(wl):
-        pytest.skip("samples of several tiles: both forms are the multi-kernel one")
+    if form == "split" and _tiles(wl) > 16:
+        pytest.skip("samples of many tiles: both forms are the multi-kernel one")
     say(f"[stream] {wl.name} {form}")
     data = inputs.make_inputs(wl, seed=3)
     out = run_gpu(wl, data, force_path="stream", debug=FORMS[form])
@@ -79,10 +80,15 @@ def test_stream_parity(wl, form):
     check_against_oracle(wl, data, out)
 
 
-def _one_tile(wl):
-    """Whether one tile of 16 chunks per thread holds a sample of wl."""
+def _tiles(wl):
+    """Statistics tiles (16 chunks per thread) per sample of wl."""
     v = 4 if wl.dtype == "f32" else 8
-    return wl.HW <= (256 // (wl.C // v)) * 16
+    tp = (256 // (wl.C // v)) * 16
+    return -(-wl.HW // tp)
+
+
+def _one_tile(wl):
+    return _tiles(wl) == 1
 
 
 # Samples that fit one tile (at most 16 chunks per thread): one workgroup per
@@ -114,6 +120,38 @@ def test_one_tile_parity(wl, form):
         assert bp.kernels == (1 if wl.N == 1 else 2) and bp.grid == wl.N
     else:
         assert fp.kernels >= 3
+    check_against_oracle(wl, data, out)
+
+
+# Samples of 2 to 16 tiles: the output kernels combine the tile partials
+# themselves (two launches forward; two backward, three with several samples).
+FEW_TILES = [
+    W("few_nhwc_f16_2x256x32x32_g32", 2, 256, 32, 32, 32, "f16", "nhwc"),           # 8 tiles
+    W("few_nhwc_f32_3x32x50x41_g4", 3, 32, 50, 41, 4, "f32", "nhwc"),               # 5, ragged
+    W("few_nhwc_f16_1x64x40x41_g8", 1, 64, 40, 41, 8, "f16", "nhwc", affine="n01"), # one sample
+    W("few_nhwc_f16_2x320x37x41_g32", 2, 320, 37, 41, 32, "f16", "nhwc"),           # 16 tiles; D = 10
+    W("few_nhwc_f32_2x96x20x21_g24", 2, 96, 20, 21, 24, "f32", "nhwc"),
+    W("few_nhwc_bf16_3x24x40x41_g3", 3, 24, 40, 41, 3, "bf16", "nhwc"),
+    W("many_nhwc_f16_1x64x1x8193_g8", 1, 64, 1, 8193, 8, "f16", "nhwc"),            # 17 tiles: the full form
+]
+
+
+@pytest.mark.parametrize("form", list(FORMS))
+@pytest.mark.parametrize("wl", FEW_TILES, ids=lambda w: w.name)
+def test_few_tiles_parity(wl, form):
+    _need_gpu()
+    t = _tiles(wl)
+    assert 1 < t <= 17
+    say(f"[stream] {wl.name} {form} tiles={t}")
+    data = inputs.make_inputs(wl, seed=14)
+    out = run_gpu(wl, data, force_path="stream", debug=FORMS[form])
+    fp, bp = out["fwd_plan"], out["bwd_plan"]
+    assert fp.path == gn.GN_PATH_STREAM and bp.path == gn.GN_PATH_STREAM
+    if form == "auto" and t <= 16:
+        assert fp.kernels == 2
+        assert bp.kernels == (2 if wl.N == 1 else 3)
+    else:
+        assert fp.kernels == 3 and bp.kernels >= 4
     check_against_oracle(wl, data, out)
 
 

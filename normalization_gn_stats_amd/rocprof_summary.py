@@ -196,6 +196,11 @@ def summarize(workload: str, trace: str, fetch: str, write: str, copy_mib: int, 
     mains = sorted(dict.fromkeys(r["kernel"] for r in rows[:2]))   # by name: near-equal times do not rename
     calls = call_totals(rows)
     fname = "_".join(mains) + f"__{workload}.md"
+    # a workload keeps the file its first summary named, although kernels of
+    # near-equal times may trade places among the two longest
+    old = sorted(f for f in os.listdir(profiles) if f.endswith(f"__{workload}.md")) if os.path.isdir(profiles) else []
+    if len(old) == 1:
+        fname = old[0]
     lines = [f"# rocprofv3 summary: GroupNorm kernels on workload `{workload}`", "",
              "Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
              "```",

@@ -74,7 +74,7 @@ CONFIGS = (
 # a kernel also depends on the local headers that file includes.
 KERNEL_SOURCES = (
     (("rows_",), "gn_rows.hip"),
-    (("slab_", "small_nchw_", "mid_nchw_", "clear_words", "params_over_n"), "gn_slab.hip"),
+    (("slab_", "small_nchw_", "mid_nchw_", "split_nchw_", "clear_words", "params_over_n"), "gn_slab.hip"),
     (("fwd_tile_stats", "fwd_finalize", "fwd_apply", "bwd_tile_sums", "col_sums", "bwd_group_ab", "bwd_dx",
       "fwd_one_tile", "bwd_one_tile", "stream_"), "gn_stream.hip"),
     (("gen_", "generic_"), "gn_generic.hip"),

@@ -79,7 +79,9 @@ typedef enum gn_path {
                              grid-stride overflow tiles (one-pass backward);
                              NCHW slabs of up to 256 KiB (no
                              max_resident_override) take one workgroup each
-                             instead (team 1, a normal launch) */
+                             instead (team 1, a normal launch), and NCHW
+                             tensors of up to 32 MiB (forward) or 64 MiB
+                             (backward) a two-launch split form (team 0) */
     GN_PATH_STREAM = 4    /* NHWC: a few launches of one tile per workgroup
                              (statistics, fixed-order combine, outputs), or one
                              workgroup per sample when a sample fits one tile;
@@ -112,6 +114,11 @@ typedef struct gn_plan_info {
  * take the whole call or the output kernels would combine a few tiles'
  * partials themselves -- for tests of that form only. */
 #define GN_DEBUG_STREAM_SPLIT 2u
+/* gn_options.debug_flags: GN_DEBUG_SLAB_COOP keeps the slab path on its
+ * cooperative kernels at the natural residency cap also where the
+ * one-workgroup-per-slab kernels or the split form would run -- for tests of
+ * the cooperative kernels only. */
+#define GN_DEBUG_SLAB_COOP 4u
 
 /* Optional knobs (pass NULL for defaults).
  *

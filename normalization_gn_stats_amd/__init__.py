@@ -20,16 +20,17 @@ import ctypes
 import math
 
 from . import _lib
-from ._lib import (GN_BF16, GN_DEBUG_STREAM_SPLIT, GN_DEBUG_UNMET_WAITS, GN_ERR_WAIT, GN_F16, GN_F32,
-                   GN_GRAD_DBETA, GN_GRAD_DGAMMA, GN_GRAD_DX, GN_NCHW, GN_NHWC, GN_OK, GN_PATH_AUTO,
-                   GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB, GN_PATH_STREAM, PATH_NAMES, GNError, PlanInfo)
+from ._lib import (GN_BF16, GN_DEBUG_SLAB_COOP, GN_DEBUG_STREAM_SPLIT, GN_DEBUG_UNMET_WAITS, GN_ERR_WAIT,
+                   GN_F16, GN_F32, GN_GRAD_DBETA, GN_GRAD_DGAMMA, GN_GRAD_DX, GN_NCHW, GN_NHWC, GN_OK,
+                   GN_PATH_AUTO, GN_PATH_GENERIC, GN_PATH_ROWS, GN_PATH_SLAB, GN_PATH_STREAM, PATH_NAMES, GNError,
+                   PlanInfo)
 
 __all__ = ["forward", "backward", "forward_into", "backward_into", "backward_scratch_into", "forward_workspace_size",
            "backward_workspace_size", "forward_strided_workspace_size", "backward_strided_workspace_size",
            "strided_dims", "common_layout", "select_path", "layout_of", "GNError", "PlanInfo",
            "rms_forward", "rms_backward", "rms_forward_into", "rms_backward_into",
            "rms_forward_workspace_size", "rms_backward_workspace_size", "status_word", "read_status",
-           "Debug", "GN_OK", "GN_ERR_WAIT", "GN_DEBUG_UNMET_WAITS", "GN_DEBUG_STREAM_SPLIT",
+           "Debug", "GN_OK", "GN_ERR_WAIT", "GN_DEBUG_UNMET_WAITS", "GN_DEBUG_STREAM_SPLIT", "GN_DEBUG_SLAB_COOP",
            "GN_GRAD_DX", "GN_GRAD_DGAMMA", "GN_GRAD_DBETA", "GN_PATH_AUTO", "GN_PATH_GENERIC",
            "GN_PATH_ROWS", "GN_PATH_SLAB", "GN_PATH_STREAM", "PATH_NAMES"]
 
@@ -135,7 +136,8 @@ class Debug:
     """Failure-report knobs of gn_options (tests): spin_limit polls before a
     wait between workgroups gives up (0: the library's default); flags
     GN_DEBUG_UNMET_WAITS makes every such wait give up; GN_DEBUG_STREAM_SPLIT
-    keeps the stream path in its full multi-kernel form (no fused forms)."""
+    keeps the stream path in its full multi-kernel form (no fused forms);
+    GN_DEBUG_SLAB_COOP keeps the slab path on its cooperative kernels."""
 
     def __init__(self, spin_limit: int = 0, flags: int = 0):
         self.spin_limit = int(spin_limit)

@@ -19,6 +19,7 @@ GN_OK, GN_ERR_INVALID, GN_ERR_UNSUPPORTED, GN_ERR_WORKSPACE, GN_ERR_HIP, GN_ERR_
 GN_STATUS_WAIT_EXPIRED = 1
 GN_DEBUG_UNMET_WAITS = 1
 GN_DEBUG_STREAM_SPLIT = 2
+GN_DEBUG_SLAB_COOP = 4
 GN_SCRATCH_BYTES = 32 << 20
 GN_F32, GN_F16, GN_BF16 = range(3)
 GN_NCHW, GN_NHWC = range(2)

@@ -148,6 +148,7 @@ gn::Launch make_launch(void* ws, size_t ws_bytes, void* stream, const gn_options
     l.spin_limit = (opts && opts->spin_limit) ? opts->spin_limit : gn::kDefaultSpinLimit;
     l.unmet_waits = (opts && (opts->debug_flags & GN_DEBUG_UNMET_WAITS)) ? 1u : 0u;
     l.stream_split = (opts && (opts->debug_flags & GN_DEBUG_STREAM_SPLIT)) ? 1u : 0u;
+    l.slab_coop = (opts && (opts->debug_flags & GN_DEBUG_SLAB_COOP)) ? 1u : 0u;
     return l;
 }
 

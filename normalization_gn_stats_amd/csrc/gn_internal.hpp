@@ -59,6 +59,7 @@ struct Launch {
     uint32_t spin_limit;   // polls before a bounded wait gives up (never 0)
     uint32_t unmet_waits;  // 1: every wait's target out of reach (failure-report tests)
     uint32_t stream_split;  // 1: the stream path's full multi-kernel form, no fused forms (tests)
+    uint32_t slab_coop;     // 1: the slab path's cooperative kernels only (tests)
 };
 
 // Polls before a bounded wait between workgroups gives up: 2^20 polls, each

@@ -25,7 +25,8 @@
 // GN_SLAB_MID_BWD_BYTES backward) skip the teams altogether: one workgroup
 // of 256 or 1024 threads per slab holds the whole slab (small_nchw_*); a
 // backward slab of up to GN_SLAB_MID_BWD_STREAM_BYTES keeps part of x and dy
-// in registers and streams the rest twice (mid_nchw_bwd).
+// in registers and streams the rest twice (mid_nchw_bwd); small NCHW tensors
+// with larger slabs take two ordinary launches (split_nchw_*).
 //
 // Reductions (all in a fixed order, no float atomics):
 //  forward   per thread: exact two-pass (count, mean, M2) of each tile from
@@ -1244,6 +1245,244 @@ __global__ __launch_bounds__(1024) void mid_nchw_bwd(const T* __restrict__ dy, c
     }
 }
 
+// ============================================================================
+// NCHW split form: statistics tiles, then outputs that combine them
+// ============================================================================
+// For tensors small enough that the cooperative kernels' fixed cost (launch,
+// clear kernel, exchange) outweighs their single pass, two ordinary launches
+// per call: a tile kernel writes each tile's statistics, and every workgroup
+// of the output kernel combines its slab's few tile partials itself, in tile
+// order (all of them derive the same values; workgroup 0 of a slab writes the
+// saved statistics or the per-(n, c) sums).  Statistics tiles are plane
+// aligned: tile k = c*tpc + i of slab s covers chunks [i*kT*R, (i+1)*kT*R) of
+// channel plane c (the last tile of a plane may be short), so a backward
+// tile's sums belong to one channel.  Output tiles are kT*RO consecutive
+// chunks of the slab.
+
+// grid (D*tpc, N*G); part[s*D*tpc + k] = (count, mean, M2, -), an exact
+// two-pass over the tile
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void split_nchw_stats(const T* __restrict__ x, int D, int HW, int tpc,
+                                                       float4* __restrict__ part) {
+    constexpr int V = Vec<T>::V;
+    __shared__ float lds[kNW * 2];
+    const int t = threadIdx.x;
+    const int64_t sb = blockIdx.y;
+    const int k = blockIdx.x, c = k / tpc, i = k - c * tpc;
+    const int cpc = HW / V;
+    const int q0 = i * kT * R;
+    const int nv = min(kT * R, cpc - q0);   // chunks of this tile
+    const T* xp = x + (sb * D + c) * (int64_t)HW;
+    u4v buf[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {   // branch-free: past the tile, its last chunk again (not used)
+        const int q = j * kT + t;
+        buf[j] = ld16_nt(xp + (int64_t)(q0 + (q < nv ? q : nv - 1)) * V);
+    }
+    const float cnt = (float)nv * V;
+    float sum[1] = {0.f};
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * kT + t < nv) {
+            float v[V];
+            Vec<T>::unpack(buf[j], v);
+#pragma unroll
+            for (int kk = 0; kk < V; ++kk) sum[0] += v[kk];
+        }
+    }
+    block_sum<1, kNW>(sum, lds);
+    const float mu = sum[0] / cnt;
+    float m2[1] = {0.f};
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * kT + t < nv) {
+            float v[V];
+            Vec<T>::unpack(buf[j], v);
+#pragma unroll
+            for (int kk = 0; kk < V; ++kk) {
+                const float d = v[kk] - mu;
+                m2[0] = fmaf(d, d, m2[0]);
+            }
+        }
+    }
+    block_sum<1, kNW>(m2, lds);
+    if (t == 0) part[sb * D * tpc + k] = make_float4(cnt, mu, m2[0], 0.f);
+}
+
+// grid (otiles or 1, N*G): the slab's statistics from its ntl = D*tpc tile
+// partials (as the finalize of the stream path), then y for one output tile
+template <typename T, int RO>
+__global__ __launch_bounds__(kT) void split_nchw_apply(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                       const float* __restrict__ beta, T* __restrict__ y,
+                                                       const float4* __restrict__ part, float* __restrict__ mean,
+                                                       float* __restrict__ rstd, int64_t G, int D, int HW, int ntl,
+                                                       float eps) {
+    constexpr int V = Vec<T>::V;
+    __shared__ float sga[kT], sbe[kT];   // D <= kT
+    const int t = threadIdx.x;
+    const int64_t sb = blockIdx.y;
+    const int g = (int)(sb % G);
+    const float4* ps = part + sb * ntl;
+    float s0 = 0.f, s1 = 0.f;
+    for (int k = 0; k < ntl; ++k) {   // every thread, the same order
+        const float4 v = ps[k];
+        s0 = fmaf(v.x, v.y, s0);
+        s1 += v.x;
+    }
+    const float mu = s0 / s1;
+    float m2 = 0.f;
+    for (int k = 0; k < ntl; ++k) {
+        const float4 v = ps[k];
+        const float d = v.y - mu;
+        m2 += fmaf(v.x * d, d, v.z);
+    }
+    float var = m2 / ((float)D * (float)HW);
+    var = var < 0.f ? 0.f : var;   // rounding below zero clamped; NaN passes through
+    const float r = 1.0f / sqrtf(var + eps);
+    if (blockIdx.x == 0 && t == 0) {
+        mean[sb] = mu;
+        rstd[sb] = r;
+    }
+    if (y == nullptr) return;   // uniform
+    if (t < D) {
+        sga[t] = gamma ? gamma[g * D + t] : 1.f;
+        sbe[t] = beta ? beta[g * D + t] : 0.f;
+    }
+    __syncthreads();
+    const int cpc = HW / V, nq = D * cpc;
+    const int64_t base = sb * (int64_t)D * HW;
+    const int q0 = blockIdx.x * kT * RO;
+    u4v buf[RO];
+#pragma unroll
+    for (int j = 0; j < RO; ++j) {
+        const int q = q0 + j * kT + t;
+        buf[j] = ld16_nt(x + base + (int64_t)(q < nq ? q : nq - 1) * V);
+    }
+#pragma unroll
+    for (int j = 0; j < RO; ++j) {
+        const int q = q0 + j * kT + t;
+        if (q < nq) {
+            const int cl = q / cpc;
+            const float a_c = r * sga[cl], b_c = sbe[cl];
+            float v[V], o[V];
+            Vec<T>::unpack(buf[j], v);
+#pragma unroll
+            for (int kk = 0; kk < V; ++kk) o[kk] = fmaf(v[kk] - mu, a_c, b_c);
+            st16_nt(y + base + (int64_t)q * V, Vec<T>::pack(o));
+        }
+    }
+}
+
+// grid (D*tpc, N*G); part[s*D*tpc + k] = (sum dy, sum dy*xhat) over the tile
+template <typename T, int R>
+__global__ __launch_bounds__(kT) void split_nchw_sums(const T* __restrict__ dy, const T* __restrict__ x,
+                                                      const float* __restrict__ mean,
+                                                      const float* __restrict__ rstd, int D, int HW, int tpc,
+                                                      float2* __restrict__ part) {
+    constexpr int V = Vec<T>::V;
+    __shared__ float lds[kNW * 2];
+    const int t = threadIdx.x;
+    const int64_t sb = blockIdx.y;
+    const int k = blockIdx.x, c = k / tpc, i = k - c * tpc;
+    const int cpc = HW / V;
+    const int q0 = i * kT * R;
+    const int nv = min(kT * R, cpc - q0);
+    const int64_t off = (sb * D + c) * (int64_t)HW;
+    const float mu = mean[sb], r = rstd[sb];
+    u4v bx[R], bd[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int q = j * kT + t;
+        const int64_t e = off + (int64_t)(q0 + (q < nv ? q : nv - 1)) * V;
+        bx[j] = ld16_nt(x + e);
+        bd[j] = ld16_nt(dy + e);
+    }
+    float acc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * kT + t < nv) {
+            float xv[V], dv[V];
+            Vec<T>::unpack(bx[j], xv);
+            Vec<T>::unpack(bd[j], dv);
+#pragma unroll
+            for (int kk = 0; kk < V; ++kk) {
+                acc[0] += dv[kk];
+                acc[1] = fmaf(dv[kk], (xv[kk] - mu) * r, acc[1]);
+            }
+        }
+    }
+    block_sum<2, kNW>(acc, lds);
+    if (t == 0) part[sb * D * tpc + k] = make_float2(acc[0], acc[1]);
+}
+
+// grid (otiles or 1, N*G): per-channel sums of the slab from its tile sums (in
+// tile order), A and B (one workgroup sum), then dx for one output tile;
+// workgroup 0 writes the per-(n, c) sums into stot (for params_over_n)
+template <typename T, int RO>
+__global__ __launch_bounds__(kT) void split_nchw_dx(const T* __restrict__ dy, const T* __restrict__ x,
+                                                    const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                    const float* __restrict__ gamma,
+                                                    const float2* __restrict__ part, T* __restrict__ dx,
+                                                    float2* __restrict__ stot, int64_t G, int64_t C, int D, int HW,
+                                                    int tpc, int want_dx) {
+    constexpr int V = Vec<T>::V;
+    __shared__ float lds[kNW * 2];
+    __shared__ float sga[kT];   // D <= kT
+    const int t = threadIdx.x;
+    const int64_t sb = blockIdx.y;
+    const int64_t n = sb / G;
+    const int g = (int)(sb - n * G);
+    float ab[2] = {0.f, 0.f};
+    if (t < D) {
+        const float2* pc = part + sb * D * tpc + t * tpc;
+        float2 v = make_float2(0.f, 0.f);
+        for (int i = 0; i < tpc; ++i) {
+            const float2 q = pc[i];
+            v.x += q.x;
+            v.y += q.y;
+        }
+        if (blockIdx.x == 0 && stot) stot[n * C + (int64_t)g * D + t] = v;
+        const float ga = gamma ? gamma[g * D + t] : 1.f;
+        sga[t] = ga;
+        ab[0] = ga * v.x;
+        ab[1] = ga * v.y;
+    }
+    if (!want_dx) return;   // kernel argument: uniform
+    block_sum<2, kNW>(ab, lds);   // its barriers also publish sga
+    const float mu = mean[sb], r = rstd[sb];
+    const float invM = 1.0f / ((float)D * (float)HW);
+    const float A = ab[0] * invM, B = ab[1] * invM;
+    const int cpc = HW / V, nq = D * cpc;
+    const int64_t base = sb * (int64_t)D * HW;
+    const int q0 = blockIdx.x * kT * RO;
+    u4v bx[RO], bd[RO];
+#pragma unroll
+    for (int j = 0; j < RO; ++j) {
+        const int q = q0 + j * kT + t;
+        const int64_t e = base + (int64_t)(q < nq ? q : nq - 1) * V;
+        bx[j] = ld16_nt(x + e);
+        bd[j] = ld16_nt(dy + e);
+    }
+#pragma unroll
+    for (int j = 0; j < RO; ++j) {
+        const int q = q0 + j * kT + t;
+        if (q < nq) {
+#pragma clang fp contract(off)
+            const float ga = sga[q / cpc];
+            float xv[V], dv[V], o[V];
+            Vec<T>::unpack(bx[j], xv);
+            Vec<T>::unpack(bd[j], dv);
+#pragma unroll
+            for (int kk = 0; kk < V; ++kk) {
+                const float xh = (xv[kk] - mu) * r;
+                const float gd = dv[kk] * ga;
+                o[kk] = r * ((gd - A) - xh * B);
+            }
+            st16_nt(dx + base + (int64_t)q * V, Vec<T>::pack(o));
+        }
+    }
+}
+
 // ---- helpers ---------------------------------------------------------------
 // Words [0, zeros) := 0, [zeros, total) := all ones.
 __global__ void clear_words(uint32_t* p, int64_t zeros, int64_t total) {
@@ -1479,7 +1718,7 @@ constexpr int kMidStreamT = -kMidT;   // small_bt's answer for mid_nchw_bwd
 // layouts, larger slabs, or a residency cap, which asks for the cooperative
 // kernels' overflow tiles).
 int small_bt(const Problem& p, const Launch& l, bool backward) {
-    if (p.layout != GN_NCHW || l.max_resident_override > 0 || p.N * p.G > INT32_MAX) return 0;
+    if (p.layout != GN_NCHW || l.max_resident_override > 0 || l.slab_coop || p.N * p.G > INT32_MAX) return 0;
     const int64_t b = p.D * p.HW * p.elem_bytes;
     if (b <= (int64_t)GN_SLAB_SOLO_BYTES) return kT;
     if (b <= (int64_t)(backward ? GN_SLAB_MID_BWD_BYTES : GN_SLAB_MID_FWD_BYTES)) return kMidT;
@@ -1569,9 +1808,123 @@ hipError_t small_bwd(const Problem& p, const BwdArgs& a, const Launch& l, int bt
     return hipSuccess;
 }
 
+// NCHW split form (split_nchw_*): tensors up to GN_SLAB_SPLIT_FWD_BYTES
+// (forward) or GN_SLAB_SPLIT_BWD_BYTES (backward) whose slabs are past the
+// one-workgroup kernels, at most kSplitMaxTiles statistics tiles per slab.
+// Past those sizes the cooperative kernels' single pass over the data wins.
+// Graphs of 20 calls, forward / backward us, cooperative -> split: 2 x 32 x
+// 128 x 128 fp32 G4 (4 MiB) 32.5 / 34.2 -> 9.9 / 9.7; 1 x 128 x 256 x 256 fp16
+// G32 (16 MiB) 33.9 / 40.8 -> 14.9 / 18.7; 8 x 64 x 128 x 128 fp32 G8 (32 MiB)
+// 35.7 / 45.4 -> 21.7 / 29.3; 1 x 512 x 256 x 256 fp16 G32 (64 MiB) 45.7 /
+// 69.0 -> 50.3 / 58.6; at 128 MiB (2 x 512 x 256 x 256 fp16) 74.6 / 107.0 ->
+// 95.8 / 108.9.
+#ifndef GN_SLAB_SPLIT_FWD_BYTES
+#define GN_SLAB_SPLIT_FWD_BYTES (32 << 20)
+#endif
+#ifndef GN_SLAB_SPLIT_BWD_BYTES
+#define GN_SLAB_SPLIT_BWD_BYTES (64 << 20)
+#endif
+constexpr int kSplitR = 8, kSplitRO = 4, kSplitMaxTiles = 256;
+
+struct SplitPlan {
+    int R, tpc, ntl, otiles;
+    size_t off_stot, total;   // workspace: tile partials, then (backward) [N][C] float2
+};
+
+// The split form's plan for this problem, or false when it does not apply
+// (the caps and limits above; a residency cap asks for the cooperative kernels).
+bool split_plan(const Problem& p, int32_t max_resident_override, bool backward, SplitPlan* sp) {
+    if (p.layout != GN_NCHW || max_resident_override > 0 || p.N * p.G > 65535) return false;
+    const int64_t limit = backward ? (int64_t)GN_SLAB_SPLIT_BWD_BYTES : (int64_t)GN_SLAB_SPLIT_FWD_BYTES;
+    if ((int64_t)p.N * p.C * p.HW * p.elem_bytes > limit) return false;
+    const int V = vec_elems(p);
+    const int64_t cpc = p.HW / V;
+    int R = 1;
+    while (R < kSplitR && (int64_t)kT * R < cpc) R *= 2;
+    const int64_t tpc = (cpc + (int64_t)kT * R - 1) / ((int64_t)kT * R);
+    if (p.D * tpc > kSplitMaxTiles) return false;
+    sp->R = R;
+    sp->tpc = (int)tpc;
+    sp->ntl = (int)(p.D * tpc);
+    sp->otiles = (int)((p.D * cpc + (int64_t)kT * kSplitRO - 1) / ((int64_t)kT * kSplitRO));
+    const size_t part = al((size_t)p.N * p.G * sp->ntl * (backward ? sizeof(float2) : sizeof(float4)));
+    sp->off_stot = part;
+    sp->total = part + (backward ? al((size_t)p.N * p.C * sizeof(float2)) : 0);
+    return true;
+}
+
+template <typename T>
+hipError_t split_fwd(const Problem& p, const FwdArgs& a, const Launch& l, const SplitPlan& sp) {
+    auto ks = sp.R == 1 ? split_nchw_stats<T, 1>
+            : sp.R == 2 ? split_nchw_stats<T, 2>
+            : sp.R == 4 ? split_nchw_stats<T, 4>
+                        : split_nchw_stats<T, kSplitR>;
+    float4* part = (float4*)l.ws;
+    const unsigned slabs = (unsigned)(p.N * p.G);
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL(ks, dim3((unsigned)sp.ntl, slabs), dim3(kT), 0, l.stream, (const T*)a.x, (int)p.D, (int)p.HW,
+                       sp.tpc, part);
+    hipLaunchKernelGGL((split_nchw_apply<T, kSplitRO>), dim3(a.y ? (unsigned)sp.otiles : 1u, slabs), dim3(kT), 0,
+                       l.stream, (const T*)a.x, a.gamma, a.beta, (T*)a.y, (const float4*)part, a.mean, a.rstd, p.G,
+                       (int)p.D, (int)p.HW, sp.ntl, a.eps);
+    if ((e = hipGetLastError())) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    if (l.info) {
+        l.info->path = GN_PATH_SLAB;
+        l.info->kernels = 2;
+        l.info->grid = (int64_t)sp.ntl * slabs;
+        l.info->tiles = (int64_t)sp.ntl * slabs;
+        l.info->resident_cap = 0;
+        l.info->team = 0;
+    }
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t split_bwd(const Problem& p, const BwdArgs& a, const Launch& l, const SplitPlan& sp) {
+    auto ks = sp.R == 1 ? split_nchw_sums<T, 1>
+            : sp.R == 2 ? split_nchw_sums<T, 2>
+            : sp.R == 4 ? split_nchw_sums<T, 4>
+                        : split_nchw_sums<T, kSplitR>;
+    float2* part = (float2*)l.ws;
+    float2* stot = (float2*)((char*)l.ws + sp.off_stot);
+    const bool want_dx = (a.mask & GN_GRAD_DX) != 0;
+    const bool params = (a.mask & (GN_GRAD_DGAMMA | GN_GRAD_DBETA)) != 0;
+    const unsigned slabs = (unsigned)(p.N * p.G);
+    hipError_t e;
+    if ((e = record(l.ev_begin, l.stream))) return e;
+    hipLaunchKernelGGL(ks, dim3((unsigned)sp.ntl, slabs), dim3(kT), 0, l.stream, (const T*)a.dy, (const T*)a.x,
+                       a.mean, a.rstd, (int)p.D, (int)p.HW, sp.tpc, part);
+    hipLaunchKernelGGL((split_nchw_dx<T, kSplitRO>), dim3(want_dx ? (unsigned)sp.otiles : 1u, slabs), dim3(kT), 0,
+                       l.stream, (const T*)a.dy, (const T*)a.x, a.mean, a.rstd, a.gamma, (const float2*)part,
+                       (T*)a.dx, params ? stot : nullptr, p.G, p.C, (int)p.D, (int)p.HW, sp.tpc, want_dx ? 1 : 0);
+    if ((e = hipGetLastError())) return e;
+    if ((e = record(l.ev_end, l.stream))) return e;
+    int kernels = 2;
+    if (params) {
+        hipLaunchKernelGGL(params_over_n, dim3((unsigned)((p.C + kT - 1) / kT)), dim3(kT), 0, l.stream, stot, p.N,
+                           p.C, (a.mask & GN_GRAD_DGAMMA) ? a.dgamma : nullptr,
+                           (a.mask & GN_GRAD_DBETA) ? a.dbeta : nullptr);
+        if ((e = hipGetLastError())) return e;
+        ++kernels;
+    }
+    if (l.info) {
+        l.info->path = GN_PATH_SLAB;
+        l.info->kernels = kernels;
+        l.info->grid = (int64_t)sp.ntl * slabs;
+        l.info->tiles = (int64_t)sp.ntl * slabs;
+        l.info->resident_cap = 0;
+        l.info->team = 0;
+    }
+    return hipSuccess;
+}
+
 template <typename T>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     if (const int bt = small_bt(p, l, false)) return small_fwd<T>(p, a, l, bt);
+    SplitPlan sp;
+    if (!l.slab_coop && split_plan(p, l.max_resident_override, false, &sp)) return split_fwd<T>(p, a, l, sp);
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
     auto kn = slab_nhwc_fwd<T, GN_SLAB_NHWC_RF>;
@@ -1617,6 +1970,8 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
 template <typename T>
 hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     if (const int bt = small_bt(p, l, true)) return small_bwd<T>(p, a, l, bt);
+    SplitPlan sp;
+    if (!l.slab_coop && split_plan(p, l.max_resident_override, true, &sp)) return split_bwd<T>(p, a, l, sp);
     const int cus = device_info().cu_count;
     const bool nhwc = p.layout == GN_NHWC;
     auto kn = slab_nhwc_bwd<T, GN_SLAB_NHWC_RB>;
@@ -1688,14 +2043,20 @@ bool slab_ok(const Problem& p) {
     return p.HW >= V && p.D <= kT;      // channel sums of a slab: one thread per channel
 }
 
+// The larger of the cooperative kernels' layout and the split form's: a size
+// query does not know whether the call will cap the residency.
 size_t slab_fwd_ws(const Problem& p) {
     int64_t tpc;
-    return layout_ws(p, false, tiles_per_slab(p, tile_chunks(p, false), &tpc)).total;
+    const size_t coop = layout_ws(p, false, tiles_per_slab(p, tile_chunks(p, false), &tpc)).total;
+    SplitPlan sp;
+    return split_plan(p, 0, false, &sp) ? std::max(coop, sp.total) : coop;
 }
 
 size_t slab_bwd_ws(const Problem& p, int32_t) {
     int64_t tpc;
-    return layout_ws(p, true, tiles_per_slab(p, tile_chunks(p, true), &tpc)).total;
+    const size_t coop = layout_ws(p, true, tiles_per_slab(p, tile_chunks(p, true), &tpc)).total;
+    SplitPlan sp;
+    return split_plan(p, 0, true, &sp) ? std::max(coop, sp.total) : coop;
 }
 
 hipError_t slab_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {

@@ -41,19 +41,28 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("cap", [0, 1, 3, 8], ids=lambda c: f"cap{c}")
+# cap0: the planner's form at the natural cap (one workgroup per slab, the
+# split form or the cooperative kernels); coop0: the cooperative kernels at
+# the natural cap (GN_DEBUG_SLAB_COOP); capK: the cooperative kernels capped
+# at K workgroups
+@pytest.mark.parametrize("cap", [0, "coop0", 1, 3, 8], ids=lambda c: c if isinstance(c, str) else f"cap{c}")
 @pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
 def test_slab_parity(wl, cap):
     if not torch.cuda.is_available():
         pytest.skip("no HIP device")
     say(f"[slab] {wl.name} cap={cap}")
     data = inputs.make_inputs(wl, seed=2)
-    out = run_gpu(wl, data, force_path="slab", max_resident=cap)
+    coop = cap == "coop0"
+    cap = 0 if coop else cap
+    out = run_gpu(wl, data, force_path="slab", max_resident=cap,
+                  debug=gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP) if coop else None)
     fp, bp = out["fwd_plan"], out["bwd_plan"]
     assert fp.path == gn.GN_PATH_SLAB and bp.path == gn.GN_PATH_SLAB
     if cap:
         assert fp.grid <= cap and bp.grid <= cap
         assert bp.resident_cap == cap
+    if coop:
+        assert fp.resident_cap > 0 and bp.resident_cap > 0   # the cooperative kernels ran
     check_against_oracle(wl, data, out)
 
 
@@ -124,7 +133,7 @@ def test_small_slab_masks(mask):
 # backward holds all of x and dy up to 128 KiB, and past that keeps four chunk
 # rounds in registers and streams the others twice (mid_nchw_bwd).  Each case
 # says whether the forward and the backward take one workgroup per slab
-# (larger slabs keep the cooperative kernels).
+# (larger slabs take the split form or the cooperative kernels).
 MID_SLABS = [
     (W("mid_nchw_f16_80kib", 2, 320, 64, 64, 32, "f16", "nchw"), True, True),
     (W("mid_nchw_f32_128kib", 2, 16, 64, 64, 2, "f32", "nchw"), True, True),        # all of x and dy held
@@ -152,12 +161,12 @@ def test_mid_slab_parity(case):
     slabs = wl.N * wl.G
     if fwd_one:
         assert fp.team == 1 and fp.kernels == 1 and fp.grid == slabs
-    else:
-        assert fp.team > 1
+    else:   # the split form or the cooperative kernels
+        assert fp.team != 1
     if bwd_one:
         assert bp.team == 1 and bp.grid == slabs
     else:
-        assert bp.team > 1
+        assert bp.team != 1
     check_against_oracle(wl, data, out)
 
 
@@ -169,6 +178,54 @@ def test_mid_slab_masks(mask, case):
         pytest.skip("no HIP device")
     wl = MID_SLABS[case][0]
     data = inputs.make_inputs(wl, seed=12)
+    out = run_gpu(wl, data, force_path="slab", mask=mask)
+    check_against_oracle(wl, data, out, mask=mask)
+
+
+# NCHW tensors of at most 32 MiB (forward) or 64 MiB (backward) whose slabs
+# are past 256 KiB: the split form (a statistics-tile launch, then output
+# kernels that combine the slab's tile partials; two launches each way, plus
+# params_over_n for dgamma/dbeta), up to 256 tiles per slab.  Each case says
+# whether the forward and the backward take it.
+SPLIT = [
+    (W("split_nchw_f32_2x32x128x128_g4", 2, 32, 128, 128, 4, "f32", "nchw"), True, True),     # 16 tiles a slab
+    (W("split_nchw_f16_1x128x256x256_g32", 1, 128, 256, 256, 32, "f16", "nchw"), True, True),  # 512 KiB slabs
+    (W("split_nchw_bf16_ragged", 3, 12, 200, 200, 3, "bf16", "nchw", affine="n01"), True, True),  # short last tile
+    (W("split_nchw_f16_d256", 1, 256, 32, 24, 1, "f16", "nchw"), True, True),                  # 256 one-chunk tiles
+    (W("split_nchw_f32_instance", 2, 4, 400, 200, 4, "f32", "nchw"), True, True),              # G = C
+    (W("split_nchw_f32_40mib", 1, 128, 256, 320, 16, "f32", "nchw"), False, True),             # backward only
+    (W("split_nchw_f16_512_tiles", 1, 32, 512, 512, 1, "f16", "nchw"), False, False),          # too many tiles
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: c[0].name)
+def test_split_parity(case):
+    wl, fwd_split, bwd_split = case
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    say(f"[slab] {wl.name} split={fwd_split},{bwd_split}")
+    data = inputs.make_inputs(wl, seed=15)
+    out = run_gpu(wl, data, force_path="slab")
+    fp, bp = out["fwd_plan"], out["bwd_plan"]
+    assert fp.path == gn.GN_PATH_SLAB and bp.path == gn.GN_PATH_SLAB
+    if fwd_split:
+        assert fp.kernels == 2 and fp.team == 0 and fp.resident_cap == 0
+    else:
+        assert fp.team > 0
+    if bwd_split:
+        assert bp.kernels == 3 and bp.team == 0   # with dgamma/dbeta: params_over_n
+    else:
+        assert bp.team > 0
+    check_against_oracle(wl, data, out)
+
+
+@pytest.mark.parametrize("mask", [gn.GN_GRAD_DX, gn.GN_GRAD_DGAMMA, gn.GN_GRAD_DBETA,
+                                  gn.GN_GRAD_DGAMMA | gn.GN_GRAD_DBETA], ids=["dx", "dgamma", "dbeta", "params"])
+def test_split_masks(mask):
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    wl = SPLIT[2][0]
+    data = inputs.make_inputs(wl, seed=16)
     out = run_gpu(wl, data, force_path="slab", mask=mask)
     check_against_oracle(wl, data, out, mask=mask)
 

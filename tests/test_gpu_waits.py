@@ -23,9 +23,11 @@ from gpu_harness import ALL, check_against_oracle, say
 pytestmark = pytest.mark.gpu
 W = inputs.Workload
 FAIL = gn.Debug(spin_limit=64, flags=gn.GN_DEBUG_UNMET_WAITS)
+# the slab path's cooperative kernels also where the one-workgroup or split forms would run
+FAIL_COOP = gn.Debug(spin_limit=64, flags=gn.GN_DEBUG_UNMET_WAITS | gn.GN_DEBUG_SLAB_COOP)
+COOP = gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP)
 
 SLAB_CASES = [
-    # slabs above 256 KiB: past the one-workgroup-per-slab kernels in both directions
     W("wait_nchw_f32_c16_g4", 2, 16, 110, 150, 4, "f32", "nchw"),
     W("wait_nchw_bf16_c12_g3", 3, 12, 208, 160, 3, "bf16", "nchw"),
     W("wait_nhwc_f16_c64_g8", 2, 64, 37, 29, 8, "f16", "nhwc"),
@@ -79,14 +81,14 @@ def test_expired_waits_are_reported_and_poison_outputs(wl, cap):
                        dtype=torch.uint8, device=dev)
     status = gn.status_word(dev)
 
-    bad = _calls(wl, data, ws_f, ws_b, cap, FAIL, status)
+    bad = _calls(wl, data, ws_f, ws_b, cap, FAIL_COOP, status)
     assert bad["fwd_status"] == gn.GN_ERR_WAIT
     assert bad["bwd_status"] == gn.GN_ERR_WAIT
     for k in ("y", "mean", "rstd", "dx", "dgamma", "dbeta"):
         _all_nan(bad[k], f"{wl.name} {k} after expired waits")
 
     # the same workspaces, no forced failure: correct again, status clean
-    good = _calls(wl, data, ws_f, ws_b, cap, None, status)
+    good = _calls(wl, data, ws_f, ws_b, cap, COOP, status)
     assert good["fwd_status"] == gn.GN_OK and good["bwd_status"] == gn.GN_OK
     check_against_oracle(wl, {k: data[k].cpu() for k in ("x", "dy", "gamma", "beta")}, good)
 
@@ -99,8 +101,9 @@ def test_status_word_is_sticky_until_reset():
     dev = torch.device("cuda", 0)
     data = {k: v.to(dev) for k, v in inputs.make_inputs(wl, seed=6).items()}
     status = gn.status_word(dev)
-    gn.forward(data["x"], data["gamma"], data["beta"], wl.G, wl.eps, force_path="slab", status=status, debug=FAIL)
-    gn.forward(data["x"], data["gamma"], data["beta"], wl.G, wl.eps, force_path="slab", status=status)
+    gn.forward(data["x"], data["gamma"], data["beta"], wl.G, wl.eps, force_path="slab", status=status,
+               debug=FAIL_COOP)
+    gn.forward(data["x"], data["gamma"], data["beta"], wl.G, wl.eps, force_path="slab", status=status, debug=COOP)
     assert gn.read_status(status, reset=False) == gn.GN_ERR_WAIT
     assert gn.read_status(status, reset=True) == gn.GN_ERR_WAIT
     assert gn.read_status(status) == gn.GN_OK

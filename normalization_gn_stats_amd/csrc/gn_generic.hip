@@ -715,8 +715,12 @@ Box plane_box(const Strides& sd, const int64_t* const* st, int nt) {
 
 bool rowconst(const Box& b) { return b.cw[0] == 0 && b.sw[0] == 0; }
 
+// Workgroups of the elementwise passes, which walk the tiles: at most 64 per
+// CU (the 510 x 510 crops of the 112 x 64 x 512 x 512 fp32 images, two
+// alternating rounds: 16 per CU 4.70 / 6.96-7.02 ms, 64 per CU 4.57 /
+// 6.79-6.87 ms, one per tile 4.61-4.65 / 6.88-6.89 ms, forward / backward).
 int elem_grid(const Tiling& t) {
-    const int64_t cap = (int64_t)device_info().cu_count * 16;
+    const int64_t cap = (int64_t)device_info().cu_count * 64;
     return (int)std::max<int64_t>(1, std::min<int64_t>(t.tiles, cap));
 }
 

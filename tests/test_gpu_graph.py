@@ -12,18 +12,25 @@ pytestmark = pytest.mark.gpu
 W = inputs.Workload
 
 
-@pytest.mark.parametrize("wl,force", [
-    (W("graph_rows_f16", 512, 1024, 1, 1, 1, "f16", "nchw"), None),
-    (W("graph_gen_bf16", 2, 16, 20, 21, 4, "bf16", "nhwc"), "generic"),
-    (inputs.TINY, None),
-    (W("graph_slab_nhwc_f16", 2, 64, 37, 29, 8, "f16", "nhwc"), "slab"),
-    (W("graph_slab_nchw_bf16", 2, 8, 64, 600, 2, "bf16", "nchw"), "slab"),   # 12 polled tile words per slab
-    (W("graph_stream_nhwc_f16", 2, 64, 130, 131, 8, "f16", "nhwc"), "stream"),
-    (W("graph_rows_narrow_f16", 3000, 64, 1, 1, 1, "f16", "nchw"), None),
-    (W("graph_crop_f32", 2, 16, 20, 21, 4, "f32", "nchw", crop=1), None),   # strided views, in place
-    (W("graph_crop_planes_bf16", 2, 8, 24, 70, 2, "bf16", "nchw", crop=2), None),   # plane-sum backward
-], ids=lambda v: getattr(v, "name", str(v)))
-def test_graph_replays_match_eager(wl, force):
+COOP = gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP)
+
+
+@pytest.mark.parametrize("wl,force,debug", [
+    (W("graph_rows_f16", 512, 1024, 1, 1, 1, "f16", "nchw"), None, None),
+    (W("graph_gen_bf16", 2, 16, 20, 21, 4, "bf16", "nhwc"), "generic", None),
+    (inputs.TINY, None, None),                                                         # one workgroup per slab
+    (W("graph_slab_nhwc_f16", 2, 64, 37, 29, 8, "f16", "nhwc"), "slab", None),
+    (W("graph_slab_nchw_bf16", 2, 8, 64, 600, 2, "bf16", "nchw"), "slab", COOP),     # 12 polled tile words per slab
+    (W("graph_split_nchw_bf16", 2, 8, 64, 600, 2, "bf16", "nchw"), None, None),      # the split form
+    (W("graph_mid_nchw_f16", 2, 640, 64, 64, 32, "f16", "nchw"), None, None),        # 1024-thread slabs, streamed dx
+    (W("graph_stream_nhwc_f16", 2, 64, 130, 131, 8, "f16", "nhwc"), "stream", None),
+    (W("graph_one_tile_nhwc_f16", 4, 64, 8, 8, 8, "f16", "nhwc"), None, None),       # one workgroup per sample
+    (W("graph_few_tiles_nhwc_f16", 2, 256, 32, 32, 32, "f16", "nhwc"), None, None),  # 8 tiles per sample
+    (W("graph_rows_narrow_f16", 3000, 64, 1, 1, 1, "f16", "nchw"), None, None),
+    (W("graph_crop_f32", 2, 16, 20, 21, 4, "f32", "nchw", crop=1), None, None),      # strided views, in place
+    (W("graph_crop_planes_bf16", 2, 8, 24, 70, 2, "bf16", "nchw", crop=2), None, None),   # plane-sum backward
+], ids=lambda v: getattr(v, "name", None) or ("coop" if isinstance(v, gn.Debug) else str(v)))
+def test_graph_replays_match_eager(wl, force, debug):
     if not torch.cuda.is_available():
         pytest.skip("no HIP device")
     say(f"[graph] {wl.name}")
@@ -51,9 +58,9 @@ def test_graph_replays_match_eager(wl, force):
 
     def step(stream_handle):
         gn.forward_into(d["x"], d["gamma"], d["beta"], G, wl.eps, out["y"], out["mean"], out["rstd"], fws,
-                        force_path=force, stream=stream_handle)
+                        force_path=force, stream=stream_handle, debug=debug)
         gn.backward_into(d["dy"], d["x"], out["mean"], out["rstd"], d["gamma"], G, ALL, out["dx"], out["dgamma"],
-                         out["dbeta"], bws, force_path=force, stream=stream_handle)
+                         out["dbeta"], bws, force_path=force, stream=stream_handle, debug=debug)
 
     step(torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()

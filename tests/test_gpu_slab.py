@@ -250,11 +250,14 @@ def test_auto_selects_slab_for_nchw():
     assert gn.select_path(False, 2, 32, 256, 8, 0, gn._lib.GN_NCHW) == gn.GN_PATH_SLAB
 
 
-@pytest.mark.parametrize("wl", [W("reuse_nchw_f32", 3, 16, 64, 70, 4, "f32", "nchw"),
-                                W("reuse_nhwc_f16", 2, 64, 37, 29, 8, "f16", "nhwc"),
-                                W("reuse_rows_bf16", 300, 2048, 1, 1, 2, "bf16", "nchw")],
-                         ids=lambda w: w.name)
-def test_same_workspace_new_inputs(wl):
+@pytest.mark.parametrize("wl,debug", [
+    (W("reuse_nchw_f32", 3, 16, 64, 70, 4, "f32", "nchw"), None),                           # one workgroup a slab
+    (W("reuse_nchw_f32_coop", 3, 16, 64, 70, 4, "f32", "nchw"), gn.GN_DEBUG_SLAB_COOP),     # polled tile words
+    (W("reuse_split_bf16", 3, 12, 200, 200, 3, "bf16", "nchw"), None),                      # the split form
+    (W("reuse_nhwc_f16", 2, 64, 37, 29, 8, "f16", "nhwc"), None),
+    (W("reuse_rows_bf16", 300, 2048, 1, 1, 2, "bf16", "nchw"), None),
+], ids=lambda v: getattr(v, "name", None) or ("coop" if v else "auto"))
+def test_same_workspace_new_inputs(wl, debug):
     """Back-to-back calls through the same buffers and workspace with different
     inputs: no call may see values (partial sums, counters) of the previous
     one -- identical inputs would hide that, so each call draws new ones."""
@@ -275,8 +278,17 @@ def test_same_workspace_new_inputs(wl):
         for k in bufs:
             bufs[k].copy_(data[k])
         say(f"[reuse] {wl.name} seed={seed}")
-        gn.forward_into(bufs["x"], bufs["gamma"], bufs["beta"], G, wl.eps, out["y"], out["mean"], out["rstd"], fws)
+        dbg = gn.Debug(flags=debug) if debug else None
+        fp, bp = gn.PlanInfo(), gn.PlanInfo()
+        gn.forward_into(bufs["x"], bufs["gamma"], bufs["beta"], G, wl.eps, out["y"], out["mean"], out["rstd"], fws,
+                        info=fp, debug=dbg)
         gn.backward_into(bufs["dy"], bufs["x"], out["mean"], out["rstd"], bufs["gamma"], G, 7, out["dx"],
-                         out["dgamma"], out["dbeta"], bws)
+                         out["dgamma"], out["dbeta"], bws, info=bp, debug=dbg)
         torch.cuda.synchronize()
+        if wl.name.startswith("reuse_nchw"):
+            # the one-workgroup kernels, or the cooperative ones with their tile words
+            want = (lambda t: t > 1) if debug else (lambda t: t == 1)
+            assert fp.path == bp.path == gn.GN_PATH_SLAB and want(fp.team) and want(bp.team), (fp.team, bp.team)
+        elif wl.name.startswith("reuse_split"):
+            assert fp.path == bp.path == gn.GN_PATH_SLAB and fp.team == bp.team == 0
         check_against_oracle(wl, data, out)

@@ -55,6 +55,8 @@ SMALL = [
     (W("rows_cs4_bf16_g2_77x8192", 77, 8192, 1, 1, 2, "bf16", "nhwc"), None, gn.GN_PATH_ROWS),
     (W("rows_cs4_f32_g2_65x4096", 65, 4096, 1, 1, 2, "f32", "nchw"), None, gn.GN_PATH_ROWS),
     (W("rows_cs4_f16_g2_31x6144", 31, 6144, 1, 1, 2, "f16", "nchw"), None, gn.GN_PATH_ROWS),
+    # several blocks per backward workgroup, two or three of them (an odd count ends the walk mid-pair)
+    (W("rows_cs4_bf16_2999x4096", 2999, 4096, 1, 1, 1, "bf16", "nchw"), None, gn.GN_PATH_ROWS),
     # narrow slices (at most 32 vectors): several slices per wavefront, from
     # 64 slices per wave (one vector each) to 2 (32 vectors each), with idle
     # lanes (6 vectors on 8 lanes) and ragged last row sets

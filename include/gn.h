@@ -27,6 +27,12 @@
  * the caller; the library allocates and frees nothing.  Work is enqueued on
  * `stream` (a hipStream_t; NULL is the null stream) and the calls return
  * before it completes.  The workspace is borrowed until that work ends.
+ * Once per process and device, the first call whose stream is not capturing
+ * a graph also enqueues one empty one-workgroup cooperative launch ahead of
+ * its own kernels: the HIP runtime fixes a state at a process's first
+ * cooperative launch, and when that launch is a full-chip grid coming after
+ * several captured multi-node graphs, all later cooperative launches of the
+ * process run about three times slower.
  *
  * Determinism: every reduction runs in a fixed order and no float atomics are
  * used, so repeated calls with the same inputs and options give bitwise equal

@@ -152,10 +152,45 @@ gn::Launch make_launch(void* ws, size_t ws_bytes, void* stream, const gn_options
     return l;
 }
 
+// ---- one empty cooperative launch per device, early -------------------------
+// The HIP runtime sets, at a process's first cooperative launch, a state that
+// then holds for every cooperative launch of the process.  Measured on MI355X
+// (ROCm 7): when that first launch is one of the slab kernels' full-chip grids
+// and three or more graphs of several kernel nodes each (any kernels) were
+// captured before it, every later cooperative launch, eager or in a graph,
+// runs about three times slower (1x512x256x256 fp16 G32: 46 / 61 us -> 153 /
+// 126 us per forward / backward call).  With an empty one-workgroup
+// cooperative launch as the process's first, the same sequences run at full
+// speed, whether that launch comes before or after the graphs.  So the first
+// call on a device whose stream is not capturing makes that launch on its
+// stream; a call under capture leaves it to a later call.
+__global__ void coop_first_k() {}
+
+std::mutex g_coop_mu;
+bool g_coop_done[64];
+
+void coop_first(hipStream_t s) {
+    const gn::DeviceInfo& d = gn::device_info();
+    if (d.device < 0 || d.device >= 64 || !d.coop_supported) return;
+    std::lock_guard<std::mutex> lk(g_coop_mu);
+    if (g_coop_done[d.device]) return;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {   // e.g. the legacy stream while another captures
+        (void)hipGetLastError();
+        return;
+    }
+    if (cs != hipStreamCaptureStatusNone) return;
+    void* none[1] = {nullptr};
+    if (hipLaunchCooperativeKernel((const void*)coop_first_k, dim3(1), dim3(64), none, 0, s) != hipSuccess)
+        (void)hipGetLastError();   // not retried: the calls themselves report launch failures
+    g_coop_done[d.device] = true;
+}
+
 // Runs one launcher between the caller's whole-call events (if any).
 template <typename F>
 gn_status with_call_events(const gn_options* opts, void* stream, F&& launch) {
     hipStream_t s = (hipStream_t)stream;
+    coop_first(s);
     if (opts && opts->event_begin && gn::record((hipEvent_t)opts->event_begin, s) != hipSuccess) return GN_ERR_HIP;
     if (launch() != hipSuccess) return GN_ERR_HIP;
     if (opts && opts->event_end && gn::record((hipEvent_t)opts->event_end, s) != hipSuccess) return GN_ERR_HIP;

@@ -30,9 +30,13 @@
  * Once per process and device, the first call whose stream is not capturing
  * a graph also enqueues one empty one-workgroup cooperative launch ahead of
  * its own kernels: the HIP runtime fixes a state at a process's first
- * cooperative launch, and when that launch is a full-chip grid coming after
- * several captured multi-node graphs, all later cooperative launches of the
- * process run about three times slower.
+ * cooperative launch, and when that launch comes after several captured
+ * multi-node graphs, all later cooperative launches of the process run about
+ * three times slower.  While a process that has made cooperative launches
+ * runs, the runtime refuses them to other processes on the device; a slab
+ * call whose cooperative launch is refused takes the split form or the
+ * generic kernels instead (same results within the tolerances; gn_plan_info
+ * reports what ran).
  *
  * Determinism: every reduction runs in a fixed order and no float atomics are
  * used, so repeated calls with the same inputs and options give bitwise equal

@@ -152,18 +152,20 @@ gn::Launch make_launch(void* ws, size_t ws_bytes, void* stream, const gn_options
     return l;
 }
 
-// ---- one empty cooperative launch per device, early -------------------------
+// ---- one empty cooperative launch per process and device, early --------------
 // The HIP runtime sets, at a process's first cooperative launch, a state that
 // then holds for every cooperative launch of the process.  Measured on MI355X
-// (ROCm 7): when that first launch is one of the slab kernels' full-chip grids
-// and three or more graphs of several kernel nodes each (any kernels) were
-// captured before it, every later cooperative launch, eager or in a graph,
-// runs about three times slower (1x512x256x256 fp16 G32: 46 / 61 us -> 153 /
-// 126 us per forward / backward call).  With an empty one-workgroup
-// cooperative launch as the process's first, the same sequences run at full
-// speed, whether that launch comes before or after the graphs.  So the first
-// call on a device whose stream is not capturing makes that launch on its
-// stream; a call under capture leaves it to a later call.
+// (ROCm 7): when that first launch comes after three or more captured graphs of
+// several kernel nodes each (of any kernels), every later cooperative launch,
+// eager or in a graph, runs about three times slower (1x512x256x256 fp16 G32:
+// 46 / 61 us -> 153 / 126 us per forward / backward call); when a cooperative
+// launch came before those graphs, they change nothing.  So the library's first
+// call on a device, whatever its path, makes one empty one-workgroup
+// cooperative launch on its stream ahead of its own kernels, unless the stream
+// is capturing (then a later call does); it counts as done once the runtime
+// accepts it.  The price: while this process runs, other processes on the
+// device find their cooperative launches refused (their slab calls then take
+// the split or generic kernels).
 __global__ void coop_first_k() {}
 
 std::mutex g_coop_mu;
@@ -181,9 +183,10 @@ void coop_first(hipStream_t s) {
     }
     if (cs != hipStreamCaptureStatusNone) return;
     void* none[1] = {nullptr};
-    if (hipLaunchCooperativeKernel((const void*)coop_first_k, dim3(1), dim3(64), none, 0, s) != hipSuccess)
-        (void)hipGetLastError();   // not retried: the calls themselves report launch failures
-    g_coop_done[d.device] = true;
+    if (hipLaunchCooperativeKernel((const void*)coop_first_k, dim3(1), dim3(64), none, 0, s) == hipSuccess)
+        g_coop_done[d.device] = true;
+    else
+        (void)hipGetLastError();   // refused (another process holds the state): a later call tries again
 }
 
 // Runs one launcher between the caller's whole-call events (if any).

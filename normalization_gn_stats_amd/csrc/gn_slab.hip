@@ -1833,10 +1833,13 @@ struct SplitPlan {
 
 // The split form's plan for this problem, or false when it does not apply
 // (the caps and limits above; a residency cap asks for the cooperative kernels).
-bool split_plan(const Problem& p, int32_t max_resident_override, bool backward, SplitPlan* sp) {
-    if (p.layout != GN_NCHW || max_resident_override > 0 || p.N * p.G > 65535) return false;
+// any_size: the form wherever it can tile the slabs (the fallback of a refused
+// cooperative launch), not only where it is the faster one.
+bool split_plan(const Problem& p, int32_t max_resident_override, bool backward, SplitPlan* sp,
+                bool any_size = false) {
+    if (p.layout != GN_NCHW || p.N * p.G > 65535) return false;
     const int64_t limit = backward ? (int64_t)GN_SLAB_SPLIT_BWD_BYTES : (int64_t)GN_SLAB_SPLIT_FWD_BYTES;
-    if ((int64_t)p.N * p.C * p.HW * p.elem_bytes > limit) return false;
+    if (!any_size && (max_resident_override > 0 || (int64_t)p.N * p.C * p.HW * p.elem_bytes > limit)) return false;
     const int V = vec_elems(p);
     const int64_t cpc = p.HW / V;
     int R = 1;
@@ -1920,6 +1923,27 @@ hipError_t split_bwd(const Problem& p, const BwdArgs& a, const Launch& l, const 
     return hipSuccess;
 }
 
+// ---- a refused cooperative launch --------------------------------------------
+// The runtime refuses hipLaunchCooperativeKernel (hipErrorIllegalState) while
+// another process on the device has made cooperative launches and is still
+// running (measured on MI355X, ROCm 7).  Such a call takes kernels that need no
+// co-residency instead: the split form wherever it can tile the slabs, else the
+// generic kernels.  The workspace size queries cover both; the sync words the
+// clear kernel already wrote are not read by them.
+template <typename T>
+hipError_t fwd_refused(const Problem& p, const FwdArgs& a, const Launch& l) {
+    SplitPlan sp;
+    if (split_plan(p, 0, false, &sp, true)) return split_fwd<T>(p, a, l, sp);
+    return generic_fwd(p, dense_strides(p), a, l);
+}
+
+template <typename T>
+hipError_t bwd_refused(const Problem& p, const BwdArgs& a, const Launch& l) {
+    SplitPlan sp;
+    if (split_plan(p, 0, true, &sp, true)) return split_bwd<T>(p, a, l, sp);
+    return generic_bwd(p, dense_strides(p), a, l);
+}
+
 template <typename T>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     if (const int bt = small_bt(p, l, false)) return small_fwd<T>(p, a, l, bt);
@@ -1954,6 +1978,10 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     void* args[] = {&x, &gamma, &beta, &y, &mean, &rstd, &cfg, &ctr, &err, &part, &res};
     const bool coop = cfg.team > 1;
     e = nhwc ? launch_coop(kn, grid, args, l.stream, coop) : launch_coop(kc, grid, args, l.stream, coop);
+    if (e && coop) {
+        (void)hipGetLastError();
+        return fwd_refused<T>(p, a, l);
+    }
     if (e) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
     if (l.info) {
@@ -2005,6 +2033,10 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     void* args[] = {&dy, &x, &mean, &rstd, &gamma, &dx, &cfg, &ctr, &err, &part, &stot, &res};
     const bool coop = cfg.team > 1;
     e = nhwc ? launch_coop(kn, grid, args, l.stream, coop) : launch_coop(kc, grid, args, l.stream, coop);
+    if (e && coop) {
+        (void)hipGetLastError();
+        return bwd_refused<T>(p, a, l);
+    }
     if (e) return e;
     if ((e = record(l.ev_end, l.stream))) return e;
     int kernels = 2;
@@ -2043,20 +2075,24 @@ bool slab_ok(const Problem& p) {
     return p.HW >= V && p.D <= kT;      // channel sums of a slab: one thread per channel
 }
 
-// The larger of the cooperative kernels' layout and the split form's: a size
-// query does not know whether the call will cap the residency.
+// The largest of the cooperative kernels' layout and the other forms a call may
+// take (the split form, or the generic kernels where the split form cannot
+// tile the slabs): a size query does not know whether the call will cap the
+// residency or find its cooperative launch refused.
 size_t slab_fwd_ws(const Problem& p) {
     int64_t tpc;
     const size_t coop = layout_ws(p, false, tiles_per_slab(p, tile_chunks(p, false), &tpc)).total;
-    SplitPlan sp;
-    return split_plan(p, 0, false, &sp) ? std::max(coop, sp.total) : coop;
+    SplitPlan sp;   // the split form (also a refused cooperative launch's), else the generic kernels
+    const size_t other = split_plan(p, 0, false, &sp, true) ? sp.total : generic_fwd_ws(p, dense_strides(p));
+    return std::max(coop, other);
 }
 
-size_t slab_bwd_ws(const Problem& p, int32_t) {
+size_t slab_bwd_ws(const Problem& p, int32_t mask) {
     int64_t tpc;
     const size_t coop = layout_ws(p, true, tiles_per_slab(p, tile_chunks(p, true), &tpc)).total;
     SplitPlan sp;
-    return split_plan(p, 0, true, &sp) ? std::max(coop, sp.total) : coop;
+    const size_t other = split_plan(p, 0, true, &sp, true) ? sp.total : generic_bwd_ws(p, dense_strides(p), mask);
+    return std::max(coop, other);
 }
 
 hipError_t slab_fwd(const Problem& p, const FwdArgs& a, const Launch& l) {

@@ -1,0 +1,74 @@
+"""A cooperative launch the runtime refuses: while one process on the device
+has made cooperative launches and still runs, another process's
+hipLaunchCooperativeKernel fails (hipErrorIllegalState).  That process's slab
+calls must then take the kernels that need no co-residency -- the split form
+where it can tile the slabs, else the generic kernels -- and still match the
+oracle.  This process makes a cooperative launch first; a child process makes
+the calls (the only way to get a second process on the device)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import normalization_gn_stats_amd as gn
+from normalization_gn_stats_amd import inputs
+
+from gpu_harness import run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+CHILD = r"""
+import json, sys
+sys.path.insert(0, sys.argv[1])
+import normalization_gn_stats_amd as gn
+from normalization_gn_stats_amd import inputs
+from gpu_harness import run_gpu, check_against_oracle
+W = inputs.Workload
+CASES = [   # (workload, forced path); the cooperative kernels at the natural cap
+    (W("refused_nchw_f32_split", 2, 16, 64, 80, 4, "f32", "nchw"), None),        # 80 KiB slabs: split form
+    (W("refused_nchw_f16_generic", 1, 64, 256, 512, 1, "f16", "nchw"), None),    # 512 tiles a slab: generic
+    (W("refused_nhwc_f16_generic", 2, 64, 37, 29, 8, "f16", "nhwc"), "slab"),    # NHWC slab: generic
+]
+for wl, force in CASES:
+    print("[refused] " + wl.name, flush=True)
+    data = inputs.make_inputs(wl, seed=31)
+    out = run_gpu(wl, data, force_path=force, debug=gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP))
+    fp, bp = out["fwd_plan"], out["bwd_plan"]
+    check_against_oracle(wl, data, out)
+    print(json.dumps({"case": wl.name, "fwd": [fp.path, fp.team], "bwd": [bp.path, bp.team]}), flush=True)
+"""
+
+EXPECT = {   # path and team of the kernels that ran instead
+    "refused_nchw_f32_split": [gn.GN_PATH_SLAB, 0],
+    "refused_nchw_f16_generic": [gn.GN_PATH_GENERIC, None],
+    "refused_nhwc_f16_generic": [gn.GN_PATH_GENERIC, None],
+}
+
+
+def test_refused_cooperative_launch_takes_other_kernels():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    # this process's own cooperative launch, so that the child's are refused
+    wl = inputs.Workload("refused_holder_f32", 2, 16, 64, 80, 4, "f32", "nchw")
+    out = run_gpu(wl, inputs.make_inputs(wl, seed=30), debug=gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP))
+    assert out["fwd_plan"].team > 1 and out["bwd_plan"].team > 1
+    say("[refused] child process")
+    env = dict(os.environ)
+    env["PYTHONPATH"] = ROOT + os.pathsep + env.get("PYTHONPATH", "")
+    r = subprocess.run([sys.executable, "-u", "-c", CHILD, HERE], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=110)
+    out = r.stdout + r.stderr
+    assert r.returncode == 0, out[-4000:]
+    got = {d["case"]: d for d in (json.loads(l) for l in r.stdout.splitlines() if l.startswith("{"))}
+    assert set(got) == set(EXPECT), out[-4000:]
+    for case, (path, team) in EXPECT.items():
+        for kind in ("fwd", "bwd"):
+            p, t = got[case][kind]
+            assert p == path and (team is None or t == team), f"{case} {kind}: path {p}, team {t}"

@@ -3,7 +3,8 @@ skipped while the call's stream captures a graph, so a process whose very
 first library call is made under capture still captures and replays
 correctly, and the next eager calls, cooperative ones included, run and
 match.  Runs in a child process, the only way to make the library's first
-call there."""
+call there; when the test runner itself has made cooperative launches, the
+child's are refused and take the split form (tests/test_gpu_coop_refused.py)."""
 import os
 import subprocess
 import sys
@@ -50,7 +51,12 @@ for flags in (gn.GN_DEBUG_SLAB_COOP, 0):
     assert gn.read_status(st) == gn.GN_OK
     err = (yy.float() - ref(d["x"], wl.G, d["gamma"], d["beta"], wl.eps)).abs().max().item()
     assert err < 1e-2, ("eager", flags, err)
-    assert (info.team > 1) == bool(flags), (flags, info.team)
+    # with the flag the cooperative kernels, unless another process on the device holds the
+    # runtime's cooperative state (the test runner, after its own cooperative calls): then the split form
+    if flags:
+        assert info.team > 1 or info.team == 0, info.team
+    else:
+        assert info.team == 1, info.team
 print("[first_coop] eager ok", flush=True)
 """
 

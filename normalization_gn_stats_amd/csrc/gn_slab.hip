@@ -1841,6 +1841,9 @@ bool split_plan(const Problem& p, int32_t max_resident_override, bool backward, 
     const int64_t limit = backward ? (int64_t)GN_SLAB_SPLIT_BWD_BYTES : (int64_t)GN_SLAB_SPLIT_FWD_BYTES;
     if (!any_size && (max_resident_override > 0 || (int64_t)p.N * p.C * p.HW * p.elem_bytes > limit)) return false;
     const int V = vec_elems(p);
+    // the kernels take HW and a slab's chunk index (up to D*HW/V, plus one
+    // output tile past it) as 32-bit integers
+    if (p.HW > INT32_MAX || p.D * (p.HW / V) + (int64_t)kT * kSplitRO >= INT32_MAX) return false;
     const int64_t cpc = p.HW / V;
     int R = 1;
     while (R < kSplitR && (int64_t)kT * R < cpc) R *= 2;

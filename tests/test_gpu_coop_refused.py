@@ -72,3 +72,53 @@ def test_refused_cooperative_launch_takes_other_kernels():
         for kind in ("fwd", "bwd"):
             p, t = got[case][kind]
             assert p == path and (team is None or t == team), f"{case} {kind}: path {p}, team {t}"
+
+
+CHILD_MAX = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import normalization_gn_stats_amd as gn
+from normalization_gn_stats_amd import inputs
+from gpu_harness import TOL, run_gpu, say
+from test_gpu_maxsize import _check_params_with_oracle, _check_slice
+wl = inputs.Workload("refused_max_nchw_f32", 129, 64, 512, 512, 8, "f32", "nchw")
+say(f"[refused] {wl.name}: {wl.E} elements, generating on the device")
+data = inputs.make_inputs(wl, seed=1, device="cuda")
+out = run_gpu(wl, data)
+fp, bp = out["fwd_plan"], out["bwd_plan"]
+say(f"[refused] plans: forward path {fp.path} team {fp.team}, backward path {bp.path} team {bp.team}")
+assert fp.path == bp.path == gn.GN_PATH_SLAB and fp.team == bp.team == 0, "the split form did not run"
+rtol, atol = TOL[wl.dtype]
+eps = float(np.float32(wl.eps))
+for n, g in [(0, 0), (127, 7), (128, 0), (128, 7)]:
+    say(f"[refused] slice ({n}, {g})")
+    _check_slice(wl, data, out, n, g, eps, rtol, atol, wl.name)
+_check_params_with_oracle(wl, data, out, wl.name)
+say("[refused] within tolerance")
+"""
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_refused_cooperative_launch_past_2to31_elements():
+    """The split form as the fallback at the full 129 x 64 x 512 x 512 fp32
+    size (more than 2^31 elements per tensor, offsets past 2^31): sampled
+    slices and every channel's dgamma/dbeta against the oracle."""
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    wl = inputs.Workload("refused_holder_f32", 2, 16, 64, 80, 4, "f32", "nchw")
+    out = run_gpu(wl, inputs.make_inputs(wl, seed=30), debug=gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP))
+    assert out["fwd_plan"].team > 1
+    say("[refused] child process, 129 x 64 x 512 x 512 fp32")
+    env = dict(os.environ)
+    env["PYTHONPATH"] = ROOT + os.pathsep + env.get("PYTHONPATH", "")
+    proc = subprocess.Popen([sys.executable, "-u", "-c", CHILD_MAX, HERE], cwd=ROOT, env=env,
+                            stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    lines = []
+    for line in proc.stdout:   # the child's progress, as it comes
+        print(line, end="", flush=True)
+        lines.append(line)
+    rc = proc.wait(timeout=60)
+    assert rc == 0, "".join(lines)[-4000:]
+    assert any("within tolerance" in l for l in lines), "".join(lines)[-4000:]

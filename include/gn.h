@@ -36,7 +36,9 @@
  * runs, the runtime refuses them to other processes on the device; a slab
  * call whose cooperative launch is refused takes the split form or the
  * generic kernels instead (same results within the tolerances; gn_plan_info
- * reports what ran).
+ * reports what ran).  Under stream capture a refusal would only show at
+ * replay, as a kernel silently skipped, so a call captured before this
+ * process has had a cooperative launch accepted records those kernels too.
  *
  * Determinism: every reduction runs in a fixed order and no float atomics are
  * used, so repeated calls with the same inputs and options give bitwise equal

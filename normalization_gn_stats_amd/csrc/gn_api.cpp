@@ -189,6 +189,20 @@ void coop_first(hipStream_t s) {
         (void)hipGetLastError();   // refused (another process holds the state): a later call tries again
 }
 
+}  // namespace
+
+bool gn::coop_accepted() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return false;
+    }
+    std::lock_guard<std::mutex> lk(g_coop_mu);
+    return g_coop_done[dev];
+}
+
+namespace {
+
 // Runs one launcher between the caller's whole-call events (if any).
 template <typename F>
 gn_status with_call_events(const gn_options* opts, void* stream, F&& launch) {

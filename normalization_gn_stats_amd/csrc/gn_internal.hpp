@@ -76,6 +76,12 @@ struct DeviceInfo {
 };
 const DeviceInfo& device_info();
 
+// Whether this process's runtime has accepted a cooperative launch on the
+// current device (the library's early one, gn_api.cpp): it then keeps the
+// cooperative state for the process, and later cooperative launches, eager or
+// recorded into a graph, are not refused.
+bool coop_accepted();
+
 // Records ev (if any) on the stream; returns hipSuccess or the error.
 hipError_t record(hipEvent_t ev, hipStream_t s);
 

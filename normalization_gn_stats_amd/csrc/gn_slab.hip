@@ -1947,6 +1947,20 @@ hipError_t bwd_refused(const Problem& p, const BwdArgs& a, const Launch& l) {
     return generic_bwd(p, dense_strides(p), a, l);
 }
 
+// Under stream capture a refused cooperative launch is not reported: it is
+// recorded, and every replay of the graph then skips the kernel without an
+// error (measured: y left as it was).  So a call recorded before this
+// process's runtime has accepted a cooperative launch takes the kernels above.
+bool coop_unsafe_to_record(hipStream_t s) {
+    if (coop_accepted()) return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
 template <typename T>
 hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     if (const int bt = small_bt(p, l, false)) return small_fwd<T>(p, a, l, bt);
@@ -1963,6 +1977,7 @@ hipError_t fwd_t(const Problem& p, const FwdArgs& a, const Launch& l) {
     cfg.N = p.N; cfg.C = p.C; cfg.HW = p.HW; cfg.G = p.G; cfg.D = p.D; cfg.eps = a.eps;
     cfg.want_dx = 0; cfg.dgamma = nullptr; cfg.dbeta = nullptr;
     cfg.spin_limit = l.spin_limit; cfg.unmet = l.unmet_waits;
+    if (cfg.team > 1 && coop_unsafe_to_record(l.stream)) return fwd_refused<T>(p, a, l);
     const int64_t grid = pl.grid;   // <= cap: every workgroup co-resident
     char* ws = (char*)l.ws;
     uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);
@@ -2017,6 +2032,7 @@ hipError_t bwd_t(const Problem& p, const BwdArgs& a, const Launch& l) {
     cfg.dgamma = one_slab_params ? a.dgamma : nullptr;
     cfg.dbeta = one_slab_params ? a.dbeta : nullptr;
     cfg.spin_limit = l.spin_limit; cfg.unmet = l.unmet_waits;
+    if (cfg.team > 1 && coop_unsafe_to_record(l.stream)) return bwd_refused<T>(p, a, l);
     const int64_t grid = pl.grid;   // <= cap: every workgroup co-resident
     char* ws = (char*)l.ws;
     uint32_t* ctr = (uint32_t*)(ws + pl.off_ctr);

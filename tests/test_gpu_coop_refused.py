@@ -4,7 +4,8 @@ hipLaunchCooperativeKernel fails (hipErrorIllegalState).  That process's slab
 calls must then take the kernels that need no co-residency -- the split form
 where it can tile the slabs, else the generic kernels -- and still match the
 oracle.  This process makes a cooperative launch first; a child process makes
-the calls (the only way to get a second process on the device)."""
+the calls (the only way to get a second process on the device), eagerly and
+recorded into a graph."""
 import json
 import os
 import subprocess
@@ -36,13 +37,45 @@ CASES = [   # (workload, forced path); the cooperative kernels at the natural ca
     (W("refused_nchw_f16_generic", 1, 64, 256, 512, 1, "f16", "nchw"), None),    # 512 tiles a slab: generic
     (W("refused_nhwc_f16_generic", 2, 64, 37, 29, 8, "f16", "nhwc"), "slab"),    # NHWC slab: generic
 ]
+import torch
+dbg = gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP)
 for wl, force in CASES:
     print("[refused] " + wl.name, flush=True)
     data = inputs.make_inputs(wl, seed=31)
-    out = run_gpu(wl, data, force_path=force, debug=gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP))
+    out = run_gpu(wl, data, force_path=force, debug=dbg)
     fp, bp = out["fwd_plan"], out["bwd_plan"]
     check_against_oracle(wl, data, out)
-    print(json.dumps({"case": wl.name, "fwd": [fp.path, fp.team], "bwd": [bp.path, bp.team]}), flush=True)
+    # the same calls recorded into a graph: a refused cooperative launch would be
+    # recorded and then skipped silently at every replay
+    d = {k: v.cuda() for k, v in data.items()}
+    code = {"f32": 0, "f16": 1, "bf16": 2}[wl.dtype]
+    lay = gn.layout_of(d["x"])
+    y, dx = torch.empty_like(d["x"]), torch.empty_like(d["x"])
+    m, r = torch.empty(wl.N * wl.G, device="cuda"), torch.empty(wl.N * wl.G, device="cuda")
+    dg, db = torch.empty(wl.C, device="cuda"), torch.empty(wl.C, device="cuda")
+    fws = torch.empty(gn.forward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, force), dtype=torch.uint8,
+                      device="cuda")
+    bws = torch.empty(gn.backward_workspace_size(wl.N, wl.C, wl.HW, wl.G, code, lay, 7, force), dtype=torch.uint8,
+                      device="cuda")
+    gfp, gbp = gn.PlanInfo(), gn.PlanInfo()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        gn.forward_into(d["x"], d["gamma"], d["beta"], wl.G, wl.eps, y, m, r, fws, force_path=force, info=gfp,
+                        debug=dbg)
+        gn.backward_into(d["dy"], d["x"], m, r, d["gamma"], wl.G, 7, dx, dg, db, bws, force_path=force, info=gbp,
+                         debug=dbg)
+    for i in range(3):
+        for t in (y, dx, m, r, dg, db):
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, name in ((y, out["y"], "y"), (m, out["mean"].reshape(-1), "mean"),
+                                (r, out["rstd"].reshape(-1), "rstd"), (dx, out["dx"], "dx"),
+                                (dg, out["dgamma"], "dgamma"), (db, out["dbeta"], "dbeta")):
+            assert torch.equal(got, want), (wl.name, "replay", i, name)
+    print(json.dumps({"case": wl.name, "fwd": [fp.path, fp.team], "bwd": [bp.path, bp.team],
+                      "graph": [gfp.path, gfp.team, gbp.path, gbp.team]}), flush=True)
 """
 
 EXPECT = {   # path and team of the kernels that ran instead
@@ -72,6 +105,8 @@ def test_refused_cooperative_launch_takes_other_kernels():
         for kind in ("fwd", "bwd"):
             p, t = got[case][kind]
             assert p == path and (team is None or t == team), f"{case} {kind}: path {p}, team {t}"
+        fp, ft, bp, bt = got[case]["graph"]   # recorded: the same kernels as the eager calls
+        assert [fp, bp] == [path, path] and (team is None or ft == bt == team), f"{case} graph: {got[case]['graph']}"
 
 
 CHILD_MAX = r"""

@@ -229,6 +229,11 @@ __global__ __launch_bounds__(kT) void rows_fwd_cs_k(const T* __restrict__ x, con
 #ifndef GN_ROWS_WALK_NT
 #define GN_ROWS_WALK_NT 1   // non-temporal loads of x (measured: 420 -> 398 us on 131072 x 4096 bf16)
 #endif
+// Each y store is issued at wave priority 2 (s_setprio), back to 0 after it:
+// 131072 x 4096 bf16, four alternating rounds on two boxes, 382.5-384.7 ->
+// 379.2-380.7 us and 379.6-381.7 -> 375.9-376.9 us; priority 3 no better; the
+// next slice's loads at priority 3 unchanged; the wide backward's dx stores at
+// priority 2 slower (545-547 -> 552-554 us).
 // y stores in flight per wave, 131072 x 4096 bf16 with the layout above,
 // four alternating rounds: 3 -> 384-386 us, 4 -> 385-386, 5 -> 382-384,
 // 6 -> 383-384, 8 -> 385-388, unlimited -> 391-392 (vector-major layout,
@@ -327,7 +332,10 @@ __global__ __launch_bounds__(kT) void rows_fwd_lds_k(const T* __restrict__ x, co
                     }
                     if constexpr (GN_ROWS_FWD_Y_INFLIGHT > 0)
                         __builtin_amdgcn_s_waitcnt(0x0F70 | (GN_ROWS_FWD_Y_INFLIGHT - 1));   // vmcnt(K - 1)
+                    // the wave's store goes out ahead of other waves' arithmetic
+                    __builtin_amdgcn_s_setprio(2);
                     st16_nt(y + base + (int64_t)vi * V, Vec<T>::pack(o));
+                    __builtin_amdgcn_s_setprio(0);
                 }
             }
         }

@@ -9,6 +9,7 @@ that are and are not whole 16-byte chunks (slab or generic), and rows (HW =
 1).  Every output the mask selects is compared element by element with the
 fp64 oracle at the tolerances of the other parity tests.
 """
+import os
 import random
 
 import pytest
@@ -62,16 +63,19 @@ def _cases(n=96, seed=20261202):
     return out
 
 
-CASES = _cases()
+# GN_RANDOM_CASES / GN_RANDOM_SEED widen the sweep (e.g. 3000 cases, seed 9001)
+CASES = _cases(n=int(os.environ.get("GN_RANDOM_CASES", "96")), seed=int(os.environ.get("GN_RANDOM_SEED", "20261202")))
+# each case on the planner's path; NCHW images also on the cooperative kernels
+RUNS = [(c, False) for c in CASES] + [(c, True) for c in CASES if c[0].layout == "nchw" and c[0].HW > 1]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0].name)
-def test_random_shape_parity(case):
-    wl, mask = case
+@pytest.mark.parametrize("run", RUNS, ids=lambda r: r[0][0].name + ("-coop" if r[1] else ""))
+def test_random_shape_parity(run):
+    (wl, mask), coop = run
     if not torch.cuda.is_available():
         pytest.skip("no HIP device")
     data = inputs.make_inputs(wl, seed=17)
-    out = run_gpu(wl, data, mask=mask)
-    say(f"[rand] {wl.name} mask={mask} fwd {gn.PATH_NAMES[out['fwd_plan'].path]} "
+    out = run_gpu(wl, data, mask=mask, debug=gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP) if coop else None)
+    say(f"[rand] {wl.name} mask={mask} coop={coop} fwd {gn.PATH_NAMES[out['fwd_plan'].path]} "
         f"({out['fwd_plan'].kernels} kernels) bwd {gn.PATH_NAMES[out['bwd_plan'].path]}")
     check_against_oracle(wl, data, out, mask=mask)

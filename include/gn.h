@@ -29,10 +29,10 @@
  * before it completes.  The workspace is borrowed until that work ends.
  * Once per process and device, the first call whose stream is not capturing
  * a graph also enqueues one empty one-workgroup cooperative launch ahead of
- * its own kernels: the HIP runtime fixes a state at a process's first
- * cooperative launch, and when that launch comes after several captured
- * multi-node graphs, all later cooperative launches of the process run about
- * three times slower.  While a process that has made cooperative launches
+ * its own kernels (GN_EARLY_COOP=0 in the environment leaves it out): the HIP
+ * runtime fixes a state at a process's first cooperative launch, and when
+ * that launch comes after several captured multi-node graphs, all later
+ * cooperative launches of the process run about three times slower.  While a process that has made cooperative launches
  * runs, the runtime refuses them to other processes on the device; a slab
  * call whose cooperative launch is refused takes the split form or the
  * generic kernels instead (same results within the tolerances; gn_plan_info

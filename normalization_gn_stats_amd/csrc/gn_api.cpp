@@ -4,6 +4,7 @@
 // the queried size, zero extent is a successful no-op), path selection and
 // dispatch to the kernel launchers.
 #include <math.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <mutex>
@@ -171,7 +172,19 @@ __global__ void coop_first_k() {}
 std::mutex g_coop_mu;
 bool g_coop_done[64];
 
+// GN_EARLY_COOP=0 in the environment leaves the early launch out, for processes
+// that should not hold the cooperative state (e.g. several processes on one
+// device, only some of which need the cooperative kernels).
+bool early_coop_wanted() {
+    static const bool wanted = [] {
+        const char* v = getenv("GN_EARLY_COOP");
+        return !(v && v[0] == '0' && v[1] == '\0');
+    }();
+    return wanted;
+}
+
 void coop_first(hipStream_t s) {
+    if (!early_coop_wanted()) return;
     const gn::DeviceInfo& d = gn::device_info();
     if (d.device < 0 || d.device >= 64 || !d.coop_supported) return;
     std::lock_guard<std::mutex> lk(g_coop_mu);

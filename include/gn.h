@@ -348,6 +348,17 @@ gn_status gn_rms_backward(const void* dy, const void* x, const float* rstd, cons
  * NULL) receives the word as read.  Not for use under stream capture. */
 gn_status gn_read_status(uint32_t* status_word, void* stream, int32_t reset, uint32_t* word_out);
 
+/* The state of this process's cooperative launches on the current device,
+ * for callers that want to know why slab calls take the split or generic
+ * kernels: GN_COOP_NOT_TRIED (no call has made the early empty cooperative
+ * launch yet, or GN_EARLY_COOP=0 leaves it out), GN_COOP_ACCEPTED (the
+ * runtime accepted it: the cooperative kernels run, eagerly and under
+ * capture), GN_COOP_REFUSED (the runtime refused it, e.g. while another
+ * process that has made cooperative launches runs on the device; later
+ * calls try again).  Host only; enqueues nothing. */
+enum { GN_COOP_NOT_TRIED = 0, GN_COOP_ACCEPTED = 1, GN_COOP_REFUSED = 2 };
+int32_t gn_cooperative_state(void);
+
 /* Static description of a status code (never NULL). */
 const char* gn_status_string(gn_status status);
 

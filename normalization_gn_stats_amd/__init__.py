@@ -29,7 +29,7 @@ __all__ = ["forward", "backward", "forward_into", "backward_into", "backward_scr
            "backward_workspace_size", "forward_strided_workspace_size", "backward_strided_workspace_size",
            "strided_dims", "common_layout", "select_path", "layout_of", "GNError", "PlanInfo",
            "rms_forward", "rms_backward", "rms_forward_into", "rms_backward_into",
-           "rms_forward_workspace_size", "rms_backward_workspace_size", "status_word", "read_status",
+           "rms_forward_workspace_size", "rms_backward_workspace_size", "status_word", "read_status", "cooperative_state", "COOP_NOT_TRIED", "COOP_ACCEPTED", "COOP_REFUSED",
            "Debug", "GN_OK", "GN_ERR_WAIT", "GN_DEBUG_UNMET_WAITS", "GN_DEBUG_STREAM_SPLIT", "GN_DEBUG_SLAB_COOP",
            "GN_GRAD_DX", "GN_GRAD_DGAMMA", "GN_GRAD_DBETA", "GN_PATH_AUTO", "GN_PATH_GENERIC",
            "GN_PATH_ROWS", "GN_PATH_SLAB", "GN_PATH_STREAM", "PATH_NAMES"]
@@ -175,6 +175,16 @@ def status_word(device=None):
     element): the kernels OR their failure reports into it."""
     torch = _torch()
     return torch.zeros(1, dtype=torch.int32, device=device if device is not None else "cuda")
+
+
+COOP_NOT_TRIED, COOP_ACCEPTED, COOP_REFUSED = 0, 1, 2
+
+
+def cooperative_state() -> int:
+    """gn_cooperative_state: COOP_NOT_TRIED, COOP_ACCEPTED or COOP_REFUSED for
+    this process on the current device."""
+    _torch()
+    return int(_lib.lib().gn_cooperative_state())
 
 
 def read_status(status, reset: bool = True, stream=None) -> int:

@@ -34,7 +34,7 @@ EXPORTED = ("gn_forward_workspace_size", "gn_forward", "gn_backward_workspace_si
             "gn_backward_strided",
             "gn_select_path", "gn_status_string", "gn_version", "gn_rms_forward_workspace_size",
             "gn_rms_forward", "gn_rms_backward_workspace_size", "gn_rms_backward", "gn_read_status",
-            "gn_backward_scratch")
+            "gn_backward_scratch", "gn_cooperative_state")
 
 
 class PlanInfo(ctypes.Structure):
@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.gn_backward_scratch.restype = i32
     L.gn_read_status.argtypes = [vp, vp, i32, ctypes.POINTER(ctypes.c_uint32)]
     L.gn_read_status.restype = i32
+    L.gn_cooperative_state.argtypes = []
+    L.gn_cooperative_state.restype = i32
     L.gn_status_string.argtypes = [i32]
     L.gn_status_string.restype = ctypes.c_char_p
     L.gn_version.restype = i32

@@ -171,6 +171,7 @@ __global__ void coop_first_k() {}
 
 std::mutex g_coop_mu;
 bool g_coop_done[64];
+bool g_coop_refused[64];   // the last early launch was refused
 
 // GN_EARLY_COOP=0 in the environment leaves the early launch out, for processes
 // that should not hold the cooperative state (e.g. several processes on one
@@ -196,10 +197,13 @@ void coop_first(hipStream_t s) {
     }
     if (cs != hipStreamCaptureStatusNone) return;
     void* none[1] = {nullptr};
-    if (hipLaunchCooperativeKernel((const void*)coop_first_k, dim3(1), dim3(64), none, 0, s) == hipSuccess)
+    if (hipLaunchCooperativeKernel((const void*)coop_first_k, dim3(1), dim3(64), none, 0, s) == hipSuccess) {
         g_coop_done[d.device] = true;
-    else
+        g_coop_refused[d.device] = false;
+    } else {
         (void)hipGetLastError();   // refused (another process holds the state): a later call tries again
+        g_coop_refused[d.device] = true;
+    }
 }
 
 }  // namespace
@@ -666,6 +670,16 @@ gn_status gn_read_status(uint32_t* status_word, void* stream, int32_t reset, uin
         }
     }
     return (w & GN_STATUS_WAIT_EXPIRED) ? GN_ERR_WAIT : GN_OK;
+}
+
+int32_t gn_cooperative_state(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return GN_COOP_NOT_TRIED;
+    }
+    std::lock_guard<std::mutex> lk(g_coop_mu);
+    return g_coop_done[dev] ? GN_COOP_ACCEPTED : g_coop_refused[dev] ? GN_COOP_REFUSED : GN_COOP_NOT_TRIED;
 }
 
 const char* gn_status_string(gn_status s) {

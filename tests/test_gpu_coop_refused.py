@@ -157,3 +157,37 @@ def test_refused_cooperative_launch_past_2to31_elements():
     rc = proc.wait(timeout=60)
     assert rc == 0, "".join(lines)[-4000:]
     assert any("within tolerance" in l for l in lines), "".join(lines)[-4000:]
+
+
+CHILD_STATE = r"""
+import json
+import torch
+import normalization_gn_stats_amd as gn
+x = torch.randn(64, 1024, device="cuda", dtype=torch.float16)
+gn.forward(x.view(64, 1024, 1, 1), torch.ones(1024, device="cuda"), torch.zeros(1024, device="cuda"), 1, 1e-5)
+torch.cuda.synchronize()
+print(json.dumps({"state": gn.cooperative_state()}), flush=True)
+"""
+
+
+def test_cooperative_state_and_early_launch_opt_out():
+    """gn_cooperative_state in this process (accepted after its cooperative
+    calls) and in child processes that make one rows call: refused by
+    default (this process holds the runtime's cooperative state), not tried
+    with GN_EARLY_COOP=0 (the early launch left out)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    wl = inputs.Workload("refused_holder_f32", 2, 16, 64, 80, 4, "f32", "nchw")
+    out = run_gpu(wl, inputs.make_inputs(wl, seed=30), debug=gn.Debug(flags=gn.GN_DEBUG_SLAB_COOP))
+    assert out["fwd_plan"].team > 1
+    assert gn.cooperative_state() == gn.COOP_ACCEPTED
+    for early, want in (("1", gn.COOP_REFUSED), ("0", gn.COOP_NOT_TRIED)):
+        env = dict(os.environ)
+        env["PYTHONPATH"] = ROOT + os.pathsep + env.get("PYTHONPATH", "")
+        env["GN_EARLY_COOP"] = early
+        say(f"[refused] child with GN_EARLY_COOP={early}")
+        r = subprocess.run([sys.executable, "-u", "-c", CHILD_STATE], cwd=ROOT, env=env, capture_output=True,
+                           text=True, timeout=110)
+        assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+        got = [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]
+        assert got and got[-1]["state"] == want, (early, got, r.stderr[-2000:])
